@@ -1,0 +1,226 @@
+"""Python binding of libqf (include/qf.h): MI355X simulated quantization.
+
+Argument marshalling only.  Each function has the name of the C entry point
+it calls, takes torch tensors that live on the GPU (bf16 data as
+torch.bfloat16, packed bytes as torch.uint8, scales as torch.float32),
+passes their device pointers, sizes and strides plus torch's current HIP
+stream, and raises QFError on a non-zero status.  Outputs that are not
+given are allocated with torch (device memory is torch's job here); every
+computation runs in the library's HIP kernels.
+"""
+
+import ctypes
+
+import torch
+
+from ._lib import TensorDesc, lib
+
+QF_OK = 0
+QF_FMT_NVFP4, QF_FMT_MXFP4, QF_FMT_Q4K = 0, 1, 2
+MAX_GROUPED = 16
+BLOCK = {QF_FMT_NVFP4: 16, QF_FMT_MXFP4: 32, QF_FMT_Q4K: 256}
+
+
+class QFError(RuntimeError):
+    def __init__(self, status, where):
+        msg = lib().qf_status_str(status).decode()
+        if status == 5:
+            msg += f" (hipError {lib().qf_last_hip_error()})"
+        super().__init__(f"{where}: {msg} (status {status})")
+        self.status = status
+
+
+def _check(status, where):
+    if status != QF_OK:
+        raise QFError(status, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _mat(x, name):
+    """rows, cols, row stride of a 2-D tensor with unit column stride."""
+    if x.dim() != 2 or (x.shape[1] > 1 and x.stride(1) != 1):
+        raise ValueError(f"{name} must be a 2-D tensor with contiguous rows")
+    return x.shape[0], x.shape[1], x.stride(0) if x.shape[0] > 1 else max(x.shape[1], x.stride(0))
+
+
+def _bf16(x, name):
+    if x.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be torch.bfloat16")
+    return x
+
+
+def _out_like(x, y):
+    return torch.empty(x.shape, dtype=torch.bfloat16, device=x.device) if y is None else _bf16(y, "y")
+
+
+def _packed(fmt, rows, cols, device, codes, scales):
+    if codes is None:
+        codes = torch.empty((rows, cols // 2) if fmt != QF_FMT_Q4K else (rows, cols // 256, 144),
+                            dtype=torch.uint8, device=device)
+    if scales is None and fmt != QF_FMT_Q4K:
+        scales = torch.empty((rows, cols // BLOCK[fmt]), dtype=torch.uint8, device=device)
+    return codes, scales
+
+
+# ------------------------------------------------------------ helpers ----
+def qf_version():
+    v = lib().qf_version()
+    return (v >> 16, (v >> 8) & 0xFF, v & 0xFF)
+
+
+def qf_packed_bytes(fmt, rows, cols):
+    return lib().qf_packed_bytes(fmt, rows, cols)
+
+
+def _descs(items):
+    n = len(items)
+    arr = (TensorDesc * max(n, 1))()
+    for i, it in enumerate(items):
+        x = _bf16(it["x"], "x")
+        rows, cols, ldx = _mat(x, "x")
+        d = arr[i]
+        d.x, d.rows, d.cols, d.ldx = x.data_ptr(), rows, cols, ldx
+        y = it.get("y")
+        if y is not None:
+            _bf16(y, "y")
+            d.y, d.ldy = y.data_ptr(), _mat(y, "y")[2]
+        d.codes = it["codes"].data_ptr() if it.get("codes") is not None else None
+        d.scales = it["scales"].data_ptr() if it.get("scales") is not None else None
+        d.group = int(it.get("group", 0))
+    return arr, n
+
+
+# --------------------------------------------------- NVFP4 tensor scale ---
+def qf_nvfp4_tensor_scale_workspace(items):
+    arr, n = _descs(items)
+    return lib().qf_nvfp4_tensor_scale_workspace(ctypes.byref(arr), n)
+
+
+def qf_nvfp4_tensor_scale_grouped(items, n_groups, d_scales=None, d_nonfinite=None, ws=None):
+    """items: list of dict(x=bf16 tensor, group=int).  Returns the device float32 scales."""
+    dev = items[0]["x"].device if items else torch.device("cuda")
+    arr, n = _descs(items)
+    need = lib().qf_nvfp4_tensor_scale_workspace(ctypes.byref(arr), n)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    if d_scales is None:
+        d_scales = torch.empty(n_groups, dtype=torch.float32, device=dev)
+    _check(lib().qf_nvfp4_tensor_scale_grouped(ctypes.byref(arr), n, n_groups, _p(d_scales), _p(d_nonfinite),
+                                                _p(ws), ws.numel() * ws.element_size(), _stream()),
+           "qf_nvfp4_tensor_scale_grouped")
+    return d_scales
+
+
+def qf_nvfp4_tensor_scale(x, d_scale=None, d_nonfinite=None, ws=None):
+    return qf_nvfp4_tensor_scale_grouped([dict(x=x, group=0)], 1, d_scale, d_nonfinite, ws)
+
+
+# ------------------------------------------------------------ QDQ/pack ----
+def qf_qdq_nvfp4(x, d_scale, y=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    y = _out_like(x, y)
+    _check(lib().qf_qdq_nvfp4(_p(x), rows, cols, ldx, _p(d_scale), _p(y), _mat(y, "y")[2], _stream()), "qf_qdq_nvfp4")
+    return y
+
+
+def qf_pack_nvfp4(x, d_scale, codes=None, scales=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    codes, scales = _packed(QF_FMT_NVFP4, rows, cols, x.device, codes, scales)
+    _check(lib().qf_pack_nvfp4(_p(x), rows, cols, ldx, _p(d_scale), _p(codes), _p(scales), _stream()), "qf_pack_nvfp4")
+    return codes, scales
+
+
+def qf_qdq_pack_nvfp4(x, d_scale, y=None, codes=None, scales=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    y = _out_like(x, y)
+    codes, scales = _packed(QF_FMT_NVFP4, rows, cols, x.device, codes, scales)
+    _check(lib().qf_qdq_pack_nvfp4(_p(x), rows, cols, ldx, _p(d_scale), _p(y), _mat(y, "y")[2], _p(codes), _p(scales),
+                                   _stream()), "qf_qdq_pack_nvfp4")
+    return y, codes, scales
+
+
+def qf_qdq_pack_nvfp4_grouped(items, d_scales):
+    """items: list of dict(x, y=None, codes=None, scales=None, group)."""
+    arr, n = _descs(items)
+    _check(lib().qf_qdq_pack_nvfp4_grouped(ctypes.byref(arr), n, _p(d_scales), _stream()), "qf_qdq_pack_nvfp4_grouped")
+
+
+def qf_qdq_mxfp4(x, y=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    y = _out_like(x, y)
+    _check(lib().qf_qdq_mxfp4(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], _stream()), "qf_qdq_mxfp4")
+    return y
+
+
+def qf_pack_mxfp4(x, codes=None, scales=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    codes, scales = _packed(QF_FMT_MXFP4, rows, cols, x.device, codes, scales)
+    _check(lib().qf_pack_mxfp4(_p(x), rows, cols, ldx, _p(codes), _p(scales), _stream()), "qf_pack_mxfp4")
+    return codes, scales
+
+
+def qf_qdq_pack_mxfp4(x, y=None, codes=None, scales=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    y = _out_like(x, y)
+    codes, scales = _packed(QF_FMT_MXFP4, rows, cols, x.device, codes, scales)
+    _check(lib().qf_qdq_pack_mxfp4(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], _p(codes), _p(scales), _stream()),
+           "qf_qdq_pack_mxfp4")
+    return y, codes, scales
+
+
+def qf_qdq_pack_mxfp4_grouped(items):
+    arr, n = _descs(items)
+    _check(lib().qf_qdq_pack_mxfp4_grouped(ctypes.byref(arr), n, _stream()), "qf_qdq_pack_mxfp4_grouped")
+
+
+def qf_qdq_q4k(x, y=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    y = _out_like(x, y)
+    _check(lib().qf_qdq_q4k(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], _stream()), "qf_qdq_q4k")
+    return y
+
+
+def qf_pack_q4k(x, blocks=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    blocks, _ = _packed(QF_FMT_Q4K, rows, cols, x.device, blocks, None)
+    _check(lib().qf_pack_q4k(_p(x), rows, cols, ldx, _p(blocks), _stream()), "qf_pack_q4k")
+    return blocks
+
+
+def qf_qdq_pack_q4k(x, y=None, blocks=None):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    y = _out_like(x, y)
+    blocks, _ = _packed(QF_FMT_Q4K, rows, cols, x.device, blocks, None)
+    _check(lib().qf_qdq_pack_q4k(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], _p(blocks), _stream()), "qf_qdq_pack_q4k")
+    return y, blocks
+
+
+def qf_qdq_pack_q4k_grouped(items):
+    arr, n = _descs(items)
+    _check(lib().qf_qdq_pack_q4k_grouped(ctypes.byref(arr), n, _stream()), "qf_qdq_pack_q4k_grouped")
+
+
+# ----------------------------------------------------------------- STE ----
+def qf_ste_backward(g_q, g_latent=None, accumulate=False):
+    _bf16(g_q, "g_q")
+    if not g_q.is_contiguous():
+        raise ValueError("g_q must be contiguous")
+    if g_latent is None:
+        g_latent = torch.empty(g_q.shape, dtype=torch.float32, device=g_q.device)
+    if g_latent.dtype != torch.float32 or not g_latent.is_contiguous() or g_latent.numel() != g_q.numel():
+        raise ValueError("g_latent must be a contiguous float32 tensor with g_q's element count")
+    _check(lib().qf_ste_backward(_p(g_q), _p(g_latent), g_q.numel(), int(bool(accumulate)), _stream()), "qf_ste_backward")
+    return g_latent
+
+
+def qf_selftest_conversions(device="cuda"):
+    counts = torch.zeros(8, dtype=torch.int64, device=device)
+    _check(lib().qf_selftest_conversions(_p(counts), _stream()), "qf_selftest_conversions")
+    return counts

@@ -1,0 +1,299 @@
+// C ABI of libqf: argument validation, descriptor marshalling and launches.
+// Every operation and its error behaviour is specified in include/qf.h.
+#include <string.h>
+
+#include "qf_kernels.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+qf_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return QF_OK;
+  g_last_hip_error = (int)e;
+  return QF_ERR_HIP;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int block_of(int fmt) {
+  switch (fmt) {
+    case QF_FMT_NVFP4: return 16;
+    case QF_FMT_MXFP4: return 32;
+    case QF_FMT_Q4K: return 256;
+    default: return 0;
+  }
+}
+
+// Validates one descriptor for format fmt; use_y / use_p: which outputs are written.
+qf_status check_desc(const qf_tensor_desc& d, int fmt, bool use_y, bool use_p) {
+  const int blk = block_of(fmt);
+  if (d.rows < 0 || d.cols < 0) return QF_ERR_SHAPE;
+  if (d.rows == 0 || d.cols == 0) return QF_OK;
+  if (d.cols % blk != 0) return QF_ERR_SHAPE;
+  if (!d.x) return QF_ERR_NULL;
+  if (d.ldx < d.cols) return QF_ERR_SHAPE;
+  if (!aligned(d.x, 16) || d.ldx % 8 != 0) return QF_ERR_ALIGN;
+  const uint64_t chunks = (uint64_t)d.rows * (uint64_t)(d.cols / 8);
+  if (chunks >= (1ull << 32) || (d.rows - 1) >= (1ll << 32)) return QF_ERR_SHAPE;
+  if (use_y) {
+    if (!d.y) return QF_ERR_NULL;
+    if (d.ldy < d.cols) return QF_ERR_SHAPE;
+    if (!aligned(d.y, 16) || d.ldy % 8 != 0) return QF_ERR_ALIGN;
+  }
+  if (use_p) {
+    if (!d.codes) return QF_ERR_NULL;
+    if (fmt == QF_FMT_Q4K) {
+      if (!aligned(d.codes, 16)) return QF_ERR_ALIGN;
+    } else {
+      if (!d.scales) return QF_ERR_NULL;
+      if (!aligned(d.codes, 4)) return QF_ERR_ALIGN;
+    }
+  }
+  return QF_OK;
+}
+
+// Fills QArgs from descriptors; tiles are laid out tensor after tensor.
+void fill_args(qf::QArgs& a, const qf_tensor_desc* d, int n) {
+  memset(&a, 0, sizeof(a));
+  int tiles = 0;
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].rows == 0 || d[i].cols == 0) continue;
+    qf::QTensor& t = a.t[k++];
+    t.x = d[i].x;
+    t.y = d[i].y;
+    t.codes = d[i].codes;
+    t.scales = d[i].scales;
+    t.ldx = d[i].ldx;
+    t.ldy = d[i].y ? d[i].ldy : d[i].cols;
+    t.cpr = (uint32_t)(d[i].cols / 8);
+    t.nchunks = (uint32_t)((uint64_t)d[i].rows * t.cpr);
+    t.tile_begin = tiles;
+    t.group = d[i].group;
+    t.contig_x = d[i].ldx == d[i].cols;
+    t.contig_y = t.ldy == d[i].cols;
+    tiles += (int)((t.nchunks + qf::TILE_CHUNKS - 1) / qf::TILE_CHUNKS);
+  }
+  a.n = k;
+  a.total_tiles = tiles;
+}
+
+int64_t tiles_of(const qf_tensor_desc& d) {
+  if (d.rows <= 0 || d.cols <= 0) return 0;
+  const uint64_t chunks = (uint64_t)d.rows * (uint64_t)(d.cols / 8);
+  return (int64_t)((chunks + qf::TILE_CHUNKS - 1) / qf::TILE_CHUNKS);
+}
+
+// Grouped quantization; each descriptor's NULL outputs are skipped.
+qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_scales, hipStream_t s) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n > 0 && !d) return QF_ERR_NULL;
+  if (fmt == QF_FMT_NVFP4 && !d_scales) return QF_ERR_NULL;
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) {
+    const bool uy = d[i].y != nullptr, up = d[i].codes != nullptr;
+    if (!uy && !up && d[i].rows > 0 && d[i].cols > 0) return QF_ERR_NULL;
+    const qf_status st = check_desc(d[i], fmt, uy, up);
+    if (st != QF_OK) return st;
+    if (fmt == QF_FMT_NVFP4 && d[i].group < 0) return QF_ERR_ARG;
+    tiles += tiles_of(d[i]);
+  }
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (tiles == 0) return QF_OK;
+  // one launch per distinct output combination (a grouped call normally has one)
+  for (int combo = 0; combo < 3; ++combo) {
+    const bool wy = combo != 2, wp = combo != 1;   // 0: both, 1: y only, 2: packed only
+    qf_tensor_desc sel[QF_MAX_GROUPED];
+    int k = 0;
+    for (int i = 0; i < n; ++i) {
+      const bool uy = d[i].y != nullptr, up = d[i].codes != nullptr;
+      if (uy == wy && up == wp) sel[k++] = d[i];
+    }
+    if (k == 0) continue;
+    qf::QArgs a;
+    fill_args(a, sel, k);
+    a.tscale = d_scales;
+    const hipError_t e = qf::launch_quant(fmt, wy, wp, a, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return QF_OK;
+}
+
+qf_tensor_desc one(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                   uint8_t* codes, uint8_t* scales) {
+  qf_tensor_desc d;
+  d.x = x;
+  d.rows = rows;
+  d.cols = cols;
+  d.ldx = ldx;
+  d.y = y;
+  d.ldy = ldy;
+  d.codes = codes;
+  d.scales = scales;
+  d.group = 0;
+  return d;
+}
+
+qf_status single(int fmt, const qf_tensor_desc& d, const float* d_scale, void* stream, bool wy, bool wp) {
+  // the single-tensor calls require the outputs they name
+  if (wy && d.rows > 0 && d.cols > 0 && !d.y) return QF_ERR_NULL;
+  if (wp && d.rows > 0 && d.cols > 0 && !d.codes) return QF_ERR_NULL;
+  return quant_grouped(fmt, &d, 1, d_scale, (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+uint32_t qf_version(void) { return (0u << 16) | (1u << 8) | 0u; }
+
+const char* qf_status_str(qf_status s) {
+  switch (s) {
+    case QF_OK: return "ok";
+    case QF_ERR_NULL: return "null pointer";
+    case QF_ERR_SHAPE: return "invalid shape";
+    case QF_ERR_ALIGN: return "misaligned pointer or stride";
+    case QF_ERR_WORKSPACE: return "workspace missing or too small";
+    case QF_ERR_HIP: return "HIP launch failed";
+    case QF_ERR_NOT_IMPLEMENTED: return "not implemented";
+    case QF_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+int qf_last_hip_error(void) { return g_last_hip_error; }
+
+size_t qf_packed_bytes(int fmt, int64_t rows, int64_t cols) {
+  const int blk = block_of(fmt);
+  if (!blk || rows < 0 || cols < 0 || cols % blk) return 0;
+  const size_t n = (size_t)rows * (size_t)cols;
+  switch (fmt) {
+    case QF_FMT_NVFP4: return n / 2 + n / 16;
+    case QF_FMT_MXFP4: return n / 2 + n / 32;
+    default: return n / 256 * 144;
+  }
+}
+
+// ------------------------------------------------------ NVFP4 tensor scale --
+size_t qf_nvfp4_tensor_scale_workspace(const qf_tensor_desc* d, int n) {
+  if (n < 0 || (n > 0 && !d)) return 0;
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) tiles += tiles_of(d[i]);
+  return (size_t)(tiles > 0 ? tiles : 1) * sizeof(uint32_t);
+}
+
+qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_groups, float* d_scales,
+                                        uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0 || n > QF_MAX_GROUPED || n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
+  if ((n > 0 && !d) || !d_scales) return QF_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const qf_status st = check_desc(d[i], QF_FMT_NVFP4, false, false);
+    if (st != QF_OK) return st;
+    if (d[i].group < 0 || d[i].group >= n_groups) return QF_ERR_ARG;
+  }
+  const size_t need = qf_nvfp4_tensor_scale_workspace(d, n);
+  if (!ws || ws_bytes < need) return QF_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return QF_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  qf::QArgs a;
+  fill_args(a, d, n);
+  a.partial = (uint32_t*)ws;
+  qf::ReduceArgs r;
+  memset(&r, 0, sizeof(r));
+  int k = 0;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].rows == 0 || d[i].cols == 0) continue;
+    r.tile_begin[k] = a.t[k].tile_begin;
+    r.group[k] = d[i].group;
+    ++k;
+  }
+  r.tile_begin[k] = a.total_tiles;
+  r.n = k;
+  r.n_groups = n_groups;
+  r.partial = (const uint32_t*)ws;
+  r.tscale = d_scales;
+  r.nonfinite = d_nonfinite;
+  hipError_t e = qf::launch_nvfp4_amax(a, s);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(qf::launch_nvfp4_scale_reduce(r, s));
+}
+
+qf_status qf_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* d_scale,
+                                uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+  const qf_tensor_desc d = one(x, rows, cols, ldx, nullptr, 0, nullptr, nullptr);
+  return qf_nvfp4_tensor_scale_grouped(&d, 1, 1, d_scale, d_nonfinite, ws, ws_bytes, stream);
+}
+
+// -------------------------------------------------------------- NVFP4 QDQ --
+qf_status qf_qdq_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const float* d_scale,
+                       uint16_t* y, int64_t ldy, void* stream) {
+  return single(QF_FMT_NVFP4, one(x, rows, cols, ldx, y, ldy, nullptr, nullptr), d_scale, stream, true, false);
+}
+qf_status qf_pack_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const float* d_scale,
+                        uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows > 0 && cols > 0 && !scales) return QF_ERR_NULL;
+  return single(QF_FMT_NVFP4, one(x, rows, cols, ldx, nullptr, 0, codes, scales), d_scale, stream, false, true);
+}
+qf_status qf_qdq_pack_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, const float* d_scale,
+                            uint16_t* y, int64_t ldy, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows > 0 && cols > 0 && !scales) return QF_ERR_NULL;
+  return single(QF_FMT_NVFP4, one(x, rows, cols, ldx, y, ldy, codes, scales), d_scale, stream, true, true);
+}
+qf_status qf_qdq_pack_nvfp4_grouped(const qf_tensor_desc* d, int n, const float* d_scales, void* stream) {
+  return quant_grouped(QF_FMT_NVFP4, d, n, d_scales, (hipStream_t)stream);
+}
+
+// -------------------------------------------------------------- MXFP4 QDQ --
+qf_status qf_qdq_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                       void* stream) {
+  return single(QF_FMT_MXFP4, one(x, rows, cols, ldx, y, ldy, nullptr, nullptr), nullptr, stream, true, false);
+}
+qf_status qf_pack_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* codes,
+                        uint8_t* scales, void* stream) {
+  if (rows > 0 && cols > 0 && !scales) return QF_ERR_NULL;
+  return single(QF_FMT_MXFP4, one(x, rows, cols, ldx, nullptr, 0, codes, scales), nullptr, stream, false, true);
+}
+qf_status qf_qdq_pack_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y,
+                            int64_t ldy, uint8_t* codes, uint8_t* scales, void* stream) {
+  if (rows > 0 && cols > 0 && !scales) return QF_ERR_NULL;
+  return single(QF_FMT_MXFP4, one(x, rows, cols, ldx, y, ldy, codes, scales), nullptr, stream, true, true);
+}
+qf_status qf_qdq_pack_mxfp4_grouped(const qf_tensor_desc* d, int n, void* stream) {
+  return quant_grouped(QF_FMT_MXFP4, d, n, nullptr, (hipStream_t)stream);
+}
+
+// --------------------------------------------------------------- Q4_K QDQ --
+qf_status qf_qdq_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                     void* stream) {
+  return single(QF_FMT_Q4K, one(x, rows, cols, ldx, y, ldy, nullptr, nullptr), nullptr, stream, true, false);
+}
+qf_status qf_pack_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint8_t* blocks, void* stream) {
+  return single(QF_FMT_Q4K, one(x, rows, cols, ldx, nullptr, 0, blocks, nullptr), nullptr, stream, false, true);
+}
+qf_status qf_qdq_pack_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                          uint8_t* blocks, void* stream) {
+  return single(QF_FMT_Q4K, one(x, rows, cols, ldx, y, ldy, blocks, nullptr), nullptr, stream, true, true);
+}
+qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream) {
+  return quant_grouped(QF_FMT_Q4K, d, n, nullptr, (hipStream_t)stream);
+}
+
+// -------------------------------------------------------------------- STE --
+qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int accumulate, void* stream) {
+  if (n < 0) return QF_ERR_SHAPE;
+  if (n == 0) return QF_OK;
+  if (!g_q || !g_latent) return QF_ERR_NULL;
+  if (!aligned(g_q, 16) || !aligned(g_latent, 16)) return QF_ERR_ALIGN;
+  if (((n >> 3) + qf::TILE_CHUNKS - 1) / qf::TILE_CHUNKS >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_ste(g_q, g_latent, n, accumulate != 0, (hipStream_t)stream));
+}
+
+// ------------------------------------------------------ conformance test ---
+qf_status qf_selftest_conversions(unsigned long long* d_counts, void* stream) {
+  if (!d_counts) return QF_ERR_NULL;
+  if (!aligned(d_counts, 8)) return QF_ERR_ALIGN;
+  return hip_status(qf::launch_selftest_conversions(d_counts, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,108 @@
+// Device-side number formats and cross-lane reductions for gfx950 (CDNA4).
+//
+// Format rules follow the QATFactory project page ("Supported formats" table):
+// E2M1 elements, E4M3 and E8M0 block scales, FP16 super-block scales, BF16
+// values.  The bit-level rules (RNE everywhere, saturation, signed zeros) are
+// the library's stated choices, documented in include/qf.h.
+//
+// Four gfx950 conversion instructions are used directly; each agrees bit for
+// bit with the software definition next to it over its whole input domain
+// (checked on the device by qf_selftest_conversions):
+//   v_cvt_pk_bf16_f32            two f32 -> two bf16, RNE, subnormals kept
+//   v_cvt_scalef32_pk_fp4_f32    two f32 -> two E2M1 codes, RNE, saturating at 6,
+//                                divided by 2^(e-127) where e is the exponent field
+//                                of the scale operand (1.0f: no scaling); NaN -> 7
+//   v_cvt_scalef32_pk_fp4_bf16   the same from two bf16
+//   v_cvt_scalef32_pk_{f32,bf16}_fp4  E2M1 code * 2^(e-127), exact
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qf {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// ----------------------------------------------------------------- bf16 ----
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Two f32 -> packed bf16 pair (lo in bits 0..15), RNE (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Software reference of the same rounding (finite inputs): RNE on the 16 dropped bits.
+__device__ __forceinline__ uint32_t bf16_rne_sw(float f) {
+  uint32_t b = __float_as_uint(f);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Largest |x| of 8 bf16 values (one 16-byte chunk) as the bits of a non-negative bf16.
+// Non-negative bf16 patterns order like their values, so an unsigned max suffices.
+__device__ __forceinline__ uint32_t amax_bits8(uint4 w) {
+  const uint32_t M = 0x7FFF7FFFu;
+  u16x2_t a = __builtin_bit_cast(u16x2_t, w.x & M);
+  u16x2_t b = __builtin_bit_cast(u16x2_t, w.y & M);
+  u16x2_t c = __builtin_bit_cast(u16x2_t, w.z & M);
+  u16x2_t d = __builtin_bit_cast(u16x2_t, w.w & M);
+  u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return m.x > m.y ? m.x : m.y;
+}
+
+// ----------------------------------------------------------------- E4M3 ----
+// E4M3 ("FN": bias 7, max 448, no Inf) code of u >= 0: round to nearest even,
+// anything at or above 448 gives 448 (0x7E).  Below 2^-6 the step is 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode(float u) {
+  if (!(u < 448.0f)) return 0x7Eu;
+  if (u < 0.015625f) return (uint32_t)__builtin_rintf(u * 512.0f);   // 0..8; 8 is 2^-6
+  uint32_t b = __float_as_uint(u);
+  b += 0x7FFFFu + ((b >> 20) & 1u);                                   // RNE to 3 mantissa bits
+  return (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  uint32_t e = c >> 3, m = c & 7u;
+  if (e == 0) return (float)m * 0.001953125f;                        // m * 2^-9, exact
+  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// ----------------------------------------------------------------- fp16 ----
+// f32 -> IEEE binary16 bits for 0 <= f (finite): RNE with subnormals, saturating at 65504.
+__device__ __forceinline__ uint32_t f16_bits_sat(float f) {
+  if (!(f < 65504.0f)) return 0x7BFFu;
+  uint32_t b = __float_as_uint(f);
+  int e = (int)(b >> 23) - 127;
+  if (e >= -14) {                                                     // normal fp16
+    uint32_t r = b + 0xFFFu + ((b >> 13) & 1u);                       // RNE to 10 mantissa bits
+    return ((((r >> 23) - 112u) << 10) | ((r >> 13) & 0x3FFu));
+  }
+  // subnormal fp16: value = k * 2^-24, k = rint(f * 2^24) (exact scaling)
+  return (uint32_t)__builtin_rintf(f * 16777216.0f);                 // 0..1024; 1024 = 2^-14
+}
+
+__device__ __forceinline__ float f16_value(uint32_t h) {
+  uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
+  if (e == 0) return (float)m * 5.9604644775390625e-8f;               // m * 2^-24, exact
+  return __uint_as_float(((e + 112u) << 23) | (m << 13));
+}
+
+// ------------------------------------------------------- cross-lane ops ----
+// DPP patterns: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
+// row_half_mirror (lane i <-> 7 - i inside 8), row_mirror (i <-> 15 - i inside 16),
+// and ds_swizzle xor 16 inside 32.  For quad-uniform (resp. 8-, 16-uniform)
+// values the mirrors pair each lane with the other half, which is all a
+// max/min/or reduction needs.
+__device__ __forceinline__ uint32_t dpp_xor1(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true); }
+__device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true); }
+__device__ __forceinline__ uint32_t dpp_hmirror(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true); }
+__device__ __forceinline__ uint32_t dpp_mirror(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true); }
+__device__ __forceinline__ uint32_t swz_xor16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
+
+__device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+}  // namespace qf

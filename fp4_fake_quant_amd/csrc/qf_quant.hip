@@ -1,0 +1,439 @@
+// Memory-bound kernels of the simulated-quantization hot path on gfx950:
+// NVFP4 tensor amax (pass 1) and its reduction to tied-group FP32 scales,
+// block QDQ + engine-layout packing for NVFP4 / MXFP4 / Q4_K (one pass over
+// the input, any subset of {QDQ'd bf16, packed codes + scales}), the identity
+// STE backward, and the device self-test of the conversion instructions.
+//
+// What is computed: QATFactory project page, "Method" (QDQ forward, STE
+// backward, tied NVFP4 tensor scales for fused projections, engine-layout
+// export) and the "Supported formats" table.  Bit-level rules: include/qf.h.
+//
+// Layout of the work: a workgroup of 256 lanes owns a tile of 1024 chunks of
+// 8 bf16 (16 bytes); lane t handles chunks t, t+256, t+512, t+768 of the tile,
+// issuing all four 128-bit loads before any arithmetic.  A quantization block
+// therefore sits in 2 (NVFP4), 4 (MXFP4) or 32 (Q4_K) adjacent lanes and its
+// statistics are reduced with DPP row operations (and one ds_swizzle for the
+// 32-lane Q4_K super-block); no LDS and no barriers are needed.
+#include <float.h>
+
+#include "qf_device.h"
+#include "qf_kernels.h"
+
+namespace qf {
+
+__device__ __forceinline__ int find_tensor(const QArgs& a, int b) {
+  int i = 0;
+#pragma unroll 1
+  while (i + 1 < a.n && b >= a.t[i + 1].tile_begin) ++i;
+  return i;
+}
+
+// Element offset of chunk c of a [rows, cols] tensor with row stride ld.
+__device__ __forceinline__ uint64_t chunk_offset(uint32_t c, uint32_t cpr, int64_t ld, int contig) {
+  if (contig) return (uint64_t)c * 8u;
+  uint32_t row = c / cpr;
+  uint32_t col8 = c - row * cpr;
+  return (uint64_t)row * (uint64_t)ld + (uint64_t)col8 * 8u;
+}
+
+__device__ __forceinline__ uint4 load_chunk(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// -------------------------------------------------- NVFP4 pass 1: amax -----
+__global__ __launch_bounds__(WG) void k_nvfp4_amax(QArgs a) {
+  const int b = blockIdx.x;
+  const int ti = find_tensor(a, b);
+  const QTensor& T = a.t[ti];
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
+  uint4 w[CHUNKS_PER_LANE];
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    w[j] = make_uint4(0, 0, 0, 0);
+    if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+  }
+  uint32_t m = 0;
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) m = umax(m, amax_bits8(w[j]));
+  // wave maximum: within 16 lanes by DPP, across 32 by swizzle, across 64 by readlane
+  m = umax(m, dpp_xor1(m));
+  m = umax(m, dpp_xor2(m));
+  m = umax(m, dpp_hmirror(m));
+  m = umax(m, dpp_mirror(m));
+  m = umax(m, swz_xor16(m));
+  m = umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
+  __shared__ uint32_t wmax[WG / 64];
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = wmax[0];
+#pragma unroll
+    for (int i = 1; i < WG / 64; ++i) r = umax(r, wmax[i]);
+    a.partial[b] = r;
+  }
+}
+
+// One workgroup: per-group maximum of the tile partials, then the tensor scale.
+__global__ __launch_bounds__(WG) void k_nvfp4_scale_reduce(ReduceArgs a) {
+  __shared__ uint32_t gmax[QF_MAX_GROUPS];
+  for (int g = threadIdx.x; g < a.n_groups; g += WG) gmax[g] = 0;
+  __syncthreads();
+  for (int i = 0; i < a.n; ++i) {
+    uint32_t m = 0;
+    for (int t = a.tile_begin[i] + threadIdx.x; t < a.tile_begin[i + 1]; t += WG) m = umax(m, a.partial[t]);
+    if (m) atomicMax(&gmax[a.group[i]], m);
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < a.n_groups; g += WG) {
+    const uint32_t bits = gmax[g];
+    if (bits >= 0x7F80u && a.nonfinite) *a.nonfinite = 1u;
+    const float A = __uint_as_float(bits << 16);
+    a.tscale[g] = (A == 0.0f) ? 1.0f : A / 2688.0f;
+  }
+}
+
+// ------------------------------------------------- NVFP4 pass 2: QDQ -------
+// Lanes 2i and 2i+1 hold one 16-block.
+template <bool WY, bool WP>
+__global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
+  const int b = blockIdx.x;
+  const int ti = find_tensor(a, b);
+  const QTensor& T = a.t[ti];
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
+  const float s_t = a.tscale[T.group];
+  const float k = 6.0f * s_t;
+  uint4 w[CHUNKS_PER_LANE];
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    w[j] = make_uint4(0, 0, 0, 0);
+    if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+  }
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    uint32_t m = amax_bits8(w[j]);
+    m = umax(m, dpp_xor1(m));
+    const float amax = __uint_as_float(m << 16);
+    const uint32_t S = e4m3_encode(amax / k);
+    const float s = e4m3_value(S);
+    const float d = s * s_t;
+    const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
+    const uint32_t wv[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+    float y[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[2 * e] = bf16_lo(wv[e]) * r;
+      y[2 * e + 1] = bf16_hi(wv[e]) * r;
+    }
+    if (__builtin_expect(r > FLT_MAX, 0)) {
+      // 1/d overflowed (the whole tied group lies below ~1e-35): 0 * inf must still
+      // give magnitude 0 with the element's own sign.
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = bf16_lo(wv[e]), hi = bf16_hi(wv[e]);
+        if (lo == 0.0f) y[2 * e] = lo;
+        if (hi == 0.0f) y[2 * e + 1] = hi;
+      }
+    }
+    uint32_t codes = 0;
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[0], y[1], 1.0f, 0);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[4], y[5], 1.0f, 2);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[6], y[7], 1.0f, 3);
+    if (c < T.nchunks) {
+      if (WY) {
+        f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+        f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+        f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+        f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+        uint4 o;
+        o.x = pack_bf16x2((v0.x * s) * s_t, (v0.y * s) * s_t);
+        o.y = pack_bf16x2((v1.x * s) * s_t, (v1.y * s) * s_t);
+        o.z = pack_bf16x2((v2.x * s) * s_t, (v2.y * s) * s_t);
+        o.w = pack_bf16x2((v3.x * s) * s_t, (v3.y * s) * s_t);
+        *reinterpret_cast<uint4*>(T.y + chunk_offset(c, T.cpr, T.ldy, T.contig_y)) = o;
+      }
+      if (WP) {
+        reinterpret_cast<uint32_t*>(T.codes)[c] = codes;
+        if ((threadIdx.x & 1) == 0) T.scales[c >> 1] = (uint8_t)S;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MXFP4 ----
+// Lanes 4i..4i+3 hold one 32-block.
+template <bool WY, bool WP>
+__global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
+  const int b = blockIdx.x;
+  const int ti = find_tensor(a, b);
+  const QTensor& T = a.t[ti];
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
+  uint4 w[CHUNKS_PER_LANE];
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    w[j] = make_uint4(0, 0, 0, 0);
+    if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+  }
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    uint32_t m = amax_bits8(w[j]);
+    m = umax(m, dpp_xor1(m));
+    m = umax(m, dpp_xor2(m));
+    // E = floor(log2 amax) - 2 + 127 clamped to [0, 254]: the bf16 exponent field minus 2
+    // (0 for zero and subnormal maxima, whose floor(log2) is below -126).
+    const int ef = (int)(m >> 7);
+    const uint32_t E = (uint32_t)(ef > 2 ? ef - 2 : 0);
+    const float sc = __uint_as_float(E << 23);
+    uint32_t codes = 0;
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w[j].x), sc, 0);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w[j].y), sc, 1);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w[j].z), sc, 2);
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w[j].w), sc, 3);
+    if (c < T.nchunks) {
+      if (WY) {
+        uint4 o;
+        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+        *reinterpret_cast<uint4*>(T.y + chunk_offset(c, T.cpr, T.ldy, T.contig_y)) = o;
+      }
+      if (WP) {
+        reinterpret_cast<uint32_t*>(T.codes)[c] = codes;
+        if ((threadIdx.x & 3) == 0) T.scales[c >> 2] = (uint8_t)E;
+      }
+    }
+  }
+}
+
+// ----------------------------------------------------------------- Q4_K ----
+// Lanes 32i..32i+31 hold one 256 super-block; lanes 4j..4j+3 of it sub-block j.
+__device__ __forceinline__ float fbits(uint32_t u) { return __uint_as_float(u); }
+__device__ __forceinline__ uint32_t ubits(float f) { return __float_as_uint(f); }
+
+template <bool WY, bool WP>
+__global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
+  const int b = blockIdx.x;
+  const int ti = find_tensor(a, b);
+  const QTensor& T = a.t[ti];
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
+  const uint32_t lane32 = threadIdx.x & 31u;
+  const uint32_t sub = lane32 >> 2;
+  uint4 w[CHUNKS_PER_LANE];
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    w[j] = make_uint4(0, 0, 0, 0);
+    if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+  }
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const uint32_t c = base + j * WG + threadIdx.x;
+    const uint32_t wv[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
+    float xv[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      xv[2 * e] = bf16_lo(wv[e]);
+      xv[2 * e + 1] = bf16_hi(wv[e]);
+    }
+    float mn = xv[0], mx = xv[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) {
+      mn = fminf(mn, xv[e]);
+      mx = fmaxf(mx, xv[e]);
+    }
+    mn = fminf(mn, fbits(dpp_xor1(ubits(mn))));
+    mn = fminf(mn, fbits(dpp_xor2(ubits(mn))));
+    mx = fmaxf(mx, fbits(dpp_xor1(ubits(mx))));
+    mx = fmaxf(mx, fbits(dpp_xor2(ubits(mx))));
+    mn = fminf(mn, 0.0f);
+    if (mn == 0.0f) mn = 0.0f;        // a zero extreme counts as +0
+    if (mx == 0.0f) mx = 0.0f;
+    const float scale = (mx - mn) / 15.0f;
+    const float off = 0.0f - mn;
+    // super-block maxima of the (non-negative) scales and offsets: unsigned max on bits
+    uint32_t sb = ubits(scale), ob = ubits(off);
+    sb = umax(sb, dpp_hmirror(sb));
+    ob = umax(ob, dpp_hmirror(ob));
+    sb = umax(sb, dpp_mirror(sb));
+    ob = umax(ob, dpp_mirror(ob));
+    sb = umax(sb, swz_xor16(sb));
+    ob = umax(ob, swz_xor16(ob));
+    const uint32_t dh = f16_bits_sat(fbits(sb) / 63.0f);
+    const uint32_t dmh = f16_bits_sat(fbits(ob) / 63.0f);
+    const float d = f16_value(dh), dmin = f16_value(dmh);
+    const float scq = (d == 0.0f) ? 0.0f : fminf(fmaxf(__builtin_rintf(scale / d), 0.0f), 63.0f);
+    const float mq = (dmin == 0.0f) ? 0.0f : fminf(fmaxf(__builtin_rintf(off / dmin), 0.0f), 63.0f);
+    const float D = d * scq, M = dmin * mq;
+    const float r = (D == 0.0f) ? 0.0f : 1.0f / D;
+    uint32_t qword = 0;
+    float q[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      q[e] = fminf(fmaxf(__builtin_rintf((xv[e] + M) * r), 0.0f), 15.0f);
+      qword |= (uint32_t)q[e] << (4 * e);
+    }
+    if (WP) {
+      // 96-bit scale stream: sc_j at bits 6j, m_j at bits 48 + 6j; OR over the super-block
+      const uint64_t A = (uint64_t)(uint32_t)scq << (6 * sub);
+      const uint64_t Bm = (uint64_t)(uint32_t)mq << (6 * sub);
+      const uint64_t lo = A | (Bm << 48);
+      uint32_t s0 = (uint32_t)lo, s1 = (uint32_t)(lo >> 32), s2 = (uint32_t)(Bm >> 16);
+      s0 |= dpp_hmirror(s0); s1 |= dpp_hmirror(s1); s2 |= dpp_hmirror(s2);
+      s0 |= dpp_mirror(s0);  s1 |= dpp_mirror(s1);  s2 |= dpp_mirror(s2);
+      s0 |= swz_xor16(s0);   s1 |= swz_xor16(s1);   s2 |= swz_xor16(s2);
+      if (c < T.nchunks) {
+        uint8_t* blk = T.codes + (uint64_t)(c >> 5) * 144u;
+        reinterpret_cast<uint32_t*>(blk + 16)[lane32] = qword;
+        if (lane32 == 0) *reinterpret_cast<uint4*>(blk) = make_uint4(dh | (dmh << 16), s0, s1, s2);
+      }
+    }
+    if (WY && c < T.nchunks) {
+      uint4 o;
+      o.x = pack_bf16x2(__builtin_fmaf(D, q[0], -M), __builtin_fmaf(D, q[1], -M));
+      o.y = pack_bf16x2(__builtin_fmaf(D, q[2], -M), __builtin_fmaf(D, q[3], -M));
+      o.z = pack_bf16x2(__builtin_fmaf(D, q[4], -M), __builtin_fmaf(D, q[5], -M));
+      o.w = pack_bf16x2(__builtin_fmaf(D, q[6], -M), __builtin_fmaf(D, q[7], -M));
+      *reinterpret_cast<uint4*>(T.y + chunk_offset(c, T.cpr, T.ldy, T.contig_y)) = o;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ STE ----
+// Identity STE: 8 bf16 gradients per lane -> 8 fp32, optionally accumulated.
+template <bool ACC>
+__global__ __launch_bounds__(WG) void k_ste(const uint16_t* __restrict__ g, float* __restrict__ out, int64_t n) {
+  const int64_t nv = n >> 3;
+  const int64_t base = (int64_t)blockIdx.x * TILE_CHUNKS;
+#pragma unroll
+  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+    const int64_t i = base + j * WG + threadIdx.x;
+    if (i < nv) {
+      const uint4 w = load_chunk(g + i * 8);
+      float4 lo = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+      float4 hi = make_float4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w));
+      float4* o = reinterpret_cast<float4*>(out + i * 8);
+      if (ACC) {
+        const float4 p = o[0], q = o[1];
+        lo.x += p.x; lo.y += p.y; lo.z += p.z; lo.w += p.w;
+        hi.x += q.x; hi.y += q.y; hi.z += q.z; hi.w += q.w;
+      }
+      o[0] = lo;
+      o[1] = hi;
+    }
+  }
+  // ragged tail (n % 8 elements) handled by the first lanes of the first workgroup
+  if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
+    const int64_t i = nv * 8 + threadIdx.x;
+    const float v = __uint_as_float((uint32_t)g[i] << 16);
+    out[i] = ACC ? out[i] + v : v;
+  }
+}
+
+// ------------------------------------------------------ conformance test ---
+__device__ __forceinline__ uint32_t sw_e2m1(float y) {   // code of y (sign from y), RNE, saturating
+  const float a = fabsf(y);
+  const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return m | ((__float_as_uint(y) >> 31) << 3);
+}
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float v = m == 0 ? 0.f : m == 1 ? .5f : m == 2 ? 1.f : m == 3 ? 1.5f : m == 4 ? 2.f : m == 5 ? 3.f : m == 6 ? 4.f : 6.f;
+  return (c & 8u) ? -v : v;
+}
+
+// counts[0]: v_cvt_pk_bf16_f32 over every finite fp32 (2^28 patterns per launch)
+// counts[1]: v_cvt_scalef32_pk_fp4_f32 with scale 1.0 over every non-NaN fp32
+__global__ __launch_bounds__(WG) void k_self_fp32(uint32_t base, unsigned long long* counts) {
+  const uint32_t bits = base + blockIdx.x * WG + threadIdx.x;
+  const float f = __uint_as_float(bits);
+  uint32_t bad0 = 0, bad1 = 0;
+  if (fabsf(f) <= 3.3895313e38f) {                          // finite, no bf16 overflow
+    bad0 = pack_bf16x2(f, -f) != (bf16_rne_sw(f) | (bf16_rne_sw(-f) << 16));
+  }
+  if (f == f) bad1 = (__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, f, -f, 1.0f, 0) & 0xFFu) !=
+                     (sw_e2m1(f) | (sw_e2m1(-f) << 4));
+  if (bad0) atomicAdd(&counts[0], 1ull);
+  if (bad1) atomicAdd(&counts[1], 1ull);
+}
+
+// counts[2], counts[3]: E8M0-scaled bf16 / f32 -> E2M1 over every bf16 and every E
+// counts[4], counts[5]: E8M0-scaled E2M1 -> bf16 / f32 over every code and E
+__global__ __launch_bounds__(WG) void k_self_scaled(unsigned long long* counts) {
+  const uint32_t E = blockIdx.y;                           // 0..254
+  const uint32_t hb = blockIdx.x * WG + threadIdx.x;       // 0..65535
+  const float x = __uint_as_float(hb << 16);
+  const float sc = __uint_as_float(E << 23);
+  const float X = ldexpf(1.0f, (int)E - 127);
+  if (x == x && fabsf(x) <= FLT_MAX) {
+    const uint32_t want = sw_e2m1(x / X);
+    const bf16x2_t v = __builtin_bit_cast(bf16x2_t, hb | (hb << 16));
+    if ((__builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, v, sc, 0) & 15u) != want) atomicAdd(&counts[2], 1ull);
+    if ((__builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x, x, sc, 0) & 15u) != want) atomicAdd(&counts[3], 1ull);
+  }
+  if (hb < 16) {
+    const float want = e2m1_value(hb) * X;
+    const uint32_t code = hb | (hb << 4);
+    const uint32_t gb = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(code, sc, 0));
+    if (gb != (bf16_rne_sw(want) * 0x10001u)) atomicAdd(&counts[4], 1ull);
+    const f32x2_t gf = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, sc, 0);
+    if (__float_as_uint(gf.x) != __float_as_uint(want) || __float_as_uint(gf.y) != __float_as_uint(want))
+      atomicAdd(&counts[5], 1ull);
+    const f32x2_t g1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0);
+    if (__float_as_uint(g1.x) != __float_as_uint(e2m1_value(hb))) atomicAdd(&counts[5], 1ull);
+  }
+}
+
+// ------------------------------------------------------------- launchers ---
+hipError_t launch_nvfp4_amax(const QArgs& a, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_nvfp4_amax, dim3(a.total_tiles), dim3(WG), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_nvfp4_scale_reduce(const ReduceArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_nvfp4_scale_reduce, dim3(1), dim3(WG), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s) {
+  if (a.total_tiles == 0) return hipSuccess;
+  const dim3 g(a.total_tiles), blk(WG);
+#define QF_DISPATCH(KERNEL)                                                     \
+  if (wy && wp) hipLaunchKernelGGL((KERNEL<true, true>), g, blk, 0, s, a);      \
+  else if (wy) hipLaunchKernelGGL((KERNEL<true, false>), g, blk, 0, s, a);      \
+  else hipLaunchKernelGGL((KERNEL<false, true>), g, blk, 0, s, a);
+  switch (fmt) {
+    case QF_FMT_NVFP4: QF_DISPATCH(k_nvfp4); break;
+    case QF_FMT_MXFP4: QF_DISPATCH(k_mxfp4); break;
+    case QF_FMT_Q4K: QF_DISPATCH(k_q4k); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef QF_DISPATCH
+  return hipGetLastError();
+}
+
+hipError_t launch_ste(const uint16_t* g, float* out, int64_t n, bool acc, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t nv = n >> 3;
+  int64_t tiles = (nv + TILE_CHUNKS - 1) / TILE_CHUNKS;
+  if (tiles == 0) tiles = 1;                                // tail-only input
+  if (acc) hipLaunchKernelGGL(k_ste<true>, dim3((uint32_t)tiles), dim3(WG), 0, s, g, out, n);
+  else hipLaunchKernelGGL(k_ste<false>, dim3((uint32_t)tiles), dim3(WG), 0, s, g, out, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_selftest_conversions(unsigned long long* counts, hipStream_t s) {
+  for (uint32_t part = 0; part < 16; ++part) {
+    hipLaunchKernelGGL(k_self_fp32, dim3((1u << 28) / WG), dim3(WG), 0, s, part << 28, counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(k_self_scaled, dim3(65536 / WG, 255), dim3(WG), 0, s, counts);
+  return hipGetLastError();
+}
+
+}  // namespace qf

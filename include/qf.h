@@ -1,0 +1,203 @@
+/*
+ * qf.h -- C ABI of libqf, the MI355X (gfx950) simulated-quantization hot path.
+ *
+ * What the library computes is described on the QATFactory project page:
+ *   - "Method" section, "Framework overview": the forward pass applies a lossy
+ *     quantize-dequantize (QDQ) transform that reproduces inference numerics;
+ *     the backward pass is a straight-through estimator (STE) onto the
+ *     continuous latent weights.
+ *   - "Method" section, "Deployment-aligned simulated quantization": the
+ *     engine's values, block sizes and scaling rules; under NVFP4 the
+ *     projections the engines fuse (QKV, gate/up) share one FP32 tensor scale.
+ *   - "Supported formats" table: NVFP4 (E2M1, block 16, E4M3 block scale +
+ *     FP32 tensor scale, 4.50 bpw), MXFP4 (E2M1, block 32, E8M0 block scale,
+ *     4.25 bpw), Q4_K (unsigned INT4, 32-blocks in 256 super-blocks, 6-bit
+ *     block scales, FP16 super-block scales, asymmetric, 4.50 bpw).
+ *   - "Method" section, "Quantization-aware distillation": LoRA merges the
+ *     adapters into the frozen base before quantization, one MoE expert at a
+ *     time.
+ *   - "Method" section, "Export" and "Quantization-aware reinforcement
+ *     learning": codes and scales are packed into the engine's layout so the
+ *     engine never requantizes.
+ *   - "Overview": every matrix multiplication runs in BF16 (weights, and
+ *     optionally activations, are QDQ'd first).
+ * The bit-level rules (scale mapping, rounding, signed zeros, packed layouts)
+ * are stated choices; they are written out next to each call below.
+ *
+ * Conventions for every call
+ *   - Tensors are row-major [rows, cols]; blocks run along cols (the
+ *     contiguous, input / K axis).  ld* are row strides in elements.
+ *   - BF16 travels as uint16_t bit patterns.
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or keeps a pointer after the call returns.
+ *     Descriptor arrays (qf_tensor_desc*) are HOST memory, read during the call.
+ *   - stream is a hipStream_t (NULL = the default stream).  Calls only enqueue
+ *     work and return; results are ready when the stream reaches that point.
+ *   - Argument errors are detected before anything is enqueued and return a
+ *     status; nothing is written then.  A failed launch returns QF_ERR_HIP and
+ *     qf_last_hip_error() gives the hipError_t of the calling thread.
+ *   - Alignment: bf16 tensors (x, y) and their row strides must be 16-byte
+ *     aligned (ld % 8 == 0); packed code arrays 4-byte aligned; Q4_K block
+ *     arrays and fp32 gradient arrays 16-byte aligned.  Else QF_ERR_ALIGN.
+ *   - Shapes: cols must be a multiple of the format's block (16 / 32 / 256),
+ *     else QF_ERR_SHAPE; rows * cols / 8 must be below 2^32 per tensor.
+ *     rows == 0 or cols == 0 is a valid no-op.
+ *   - Inputs must be finite.  Results for Inf/NaN inputs are unspecified (the
+ *     NVFP4 tensor-scale pass raises a flag when it sees one).
+ *   - Calls are reentrant and keep no state between calls.
+ */
+#ifndef QF_H
+#define QF_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qf_status {
+  QF_OK = 0,
+  QF_ERR_NULL = 1,            /* a required pointer is NULL                        */
+  QF_ERR_SHAPE = 2,           /* negative size, cols not a block multiple, ld < cols */
+  QF_ERR_ALIGN = 3,           /* pointer or stride misaligned                      */
+  QF_ERR_WORKSPACE = 4,       /* workspace missing or smaller than required         */
+  QF_ERR_HIP = 5,             /* a HIP launch failed; see qf_last_hip_error()       */
+  QF_ERR_NOT_IMPLEMENTED = 6, /* reserved                                           */
+  QF_ERR_ARG = 7              /* other invalid argument (count, flag, group index)  */
+} qf_status;
+
+enum qf_format { QF_FMT_NVFP4 = 0, QF_FMT_MXFP4 = 1, QF_FMT_Q4K = 2 };
+
+/* Most tensors one grouped call accepts. */
+#define QF_MAX_GROUPED 16
+/* Most tied groups one grouped tensor-scale call accepts. */
+#define QF_MAX_GROUPS 64
+
+/* ------------------------------------------------------------ helpers ---- */
+uint32_t qf_version(void);                 /* (major << 16) | (minor << 8) | patch */
+const char* qf_status_str(qf_status s);
+int qf_last_hip_error(void);               /* hipError_t of this thread's last failed launch */
+
+/* Packed bytes of one [rows, cols] tensor (codes + block scales; Q4_K blocks).
+ * NVFP4: rows*cols/2 + rows*cols/16 (the 4-byte FP32 tensor scale per group is
+ * the caller's float).  MXFP4: rows*cols/2 + rows*cols/32.  Q4_K:
+ * rows*cols/256*144.  These are the table's 4.50 / 4.25 / 4.50 bits per weight.
+ * Returns 0 for invalid arguments. */
+size_t qf_packed_bytes(int fmt, int64_t rows, int64_t cols);
+
+/* One tensor of a grouped call.
+ *   x      input bf16 [rows, ldx]
+ *   y      QDQ'd bf16 output [rows, ldy], or NULL to skip it (x == y with
+ *          ldx == ldy is allowed: in place)
+ *   codes  NVFP4/MXFP4: packed codes [rows, cols/2] bytes, element 2i in the
+ *          low nibble and 2i+1 in the high nibble; Q4_K: the 144-byte blocks
+ *          [rows, cols/256, 144].  NULL skips packing.
+ *   scales NVFP4: E4M3 bytes [rows, cols/16]; MXFP4: E8M0 bytes [rows, cols/32];
+ *          unused for Q4_K (its scales live inside the blocks).  NULL iff codes is NULL.
+ *   group  NVFP4 tied-group index (0 <= group < n_groups); ignored otherwise. */
+typedef struct qf_tensor_desc {
+  const uint16_t* x;
+  int64_t rows, cols, ldx;
+  uint16_t* y;
+  int64_t ldy;
+  uint8_t* codes;
+  uint8_t* scales;
+  int32_t group;
+} qf_tensor_desc;
+
+/* ------------------------------------------------- NVFP4 tensor scale ---- */
+/* Pass 1 of NVFP4 ("Method", tying of fused projections; "Supported formats",
+ * FP32 tensor scale).  For each tied group g: A_g = max |x| over every element
+ * of every tensor with group == g; d_scales[g] = (A_g == 0) ? 1.0f :
+ * fl(A_g / 2688.0f)  (2688 = 6 * 448: the group's largest block maps onto the
+ * top of the E4M3 range).  d_scales is a device float[n_groups]; it stays on
+ * the device for pass 2 (no host synchronisation).  d_nonfinite (device
+ * uint32, may be NULL) is set to 1 if any element is Inf or NaN, and left
+ * unchanged otherwise.  ws: device workspace of at least
+ * qf_nvfp4_tensor_scale_workspace(d, n) bytes (no initialisation needed).
+ * Only x, rows, cols, ldx and group of each descriptor are read. */
+size_t qf_nvfp4_tensor_scale_workspace(const qf_tensor_desc* d, int n);
+qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_groups,
+                                        float* d_scales, uint32_t* d_nonfinite,
+                                        void* ws, size_t ws_bytes, void* stream);
+/* Single tensor (a group of one). ws sized by qf_nvfp4_tensor_scale_workspace. */
+qf_status qf_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                                float* d_scale, uint32_t* d_nonfinite,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ----------------------------------------------------------- NVFP4 QDQ ---- */
+/* Pass 2 of NVFP4, per 16-block of each row, with s_t = *d_scale:
+ *   k = fl(6 s_t); a = max |x|; S = E4M3 RNE-satfinite(fl(a / k)); s = value(S);
+ *   d = fl(s s_t); magnitude code = 0 if d == 0 else E2M1 RNE-saturating(fl(|x| fl(1/d)))
+ *   (a zero element always gets magnitude 0); code sign = sign bit of x;
+ *   y = sign | bf16(fl(fl(v s) s_t)).
+ * qf_qdq_* writes only y; qf_pack_* writes only codes and scales; qf_qdq_pack_*
+ * writes all three in one pass over x. */
+qf_status qf_qdq_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                       const float* d_scale, uint16_t* y, int64_t ldy, void* stream);
+qf_status qf_pack_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        const float* d_scale, uint8_t* codes, uint8_t* scales, void* stream);
+qf_status qf_qdq_pack_nvfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            const float* d_scale, uint16_t* y, int64_t ldy,
+                            uint8_t* codes, uint8_t* scales, void* stream);
+/* Grouped: one launch over up to QF_MAX_GROUPED tensors; tensor i uses
+ * d_scales[d[i].group]. */
+qf_status qf_qdq_pack_nvfp4_grouped(const qf_tensor_desc* d, int n, const float* d_scales,
+                                    void* stream);
+
+/* ----------------------------------------------------------- MXFP4 QDQ ---- */
+/* Per 32-block: a = max |x|; E = 0 if a == 0 else clamp(floor(log2 a) - 2 + 127, 0, 254)
+ * (largest element's exponent minus E2M1's largest exponent); X = 2^(E-127);
+ * code = sign(x) | E2M1 RNE-saturating(|x| / X); y = sign | bf16(v X) (exact,
+ * bf16 subnormals kept).  scales hold E. */
+qf_status qf_qdq_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                       uint16_t* y, int64_t ldy, void* stream);
+qf_status qf_pack_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                        uint8_t* codes, uint8_t* scales, void* stream);
+qf_status qf_qdq_pack_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                            uint16_t* y, int64_t ldy, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+qf_status qf_qdq_pack_mxfp4_grouped(const qf_tensor_desc* d, int n, void* stream);
+
+/* ------------------------------------------------------------ Q4_K QDQ ---- */
+/* Per 256 super-block of eight 32-sub-blocks j (min/max round-to-nearest):
+ *   mn_j = min(min x, 0), mx_j = max x (a zero extreme counts as +0);
+ *   scale_j = fl(fl(mx_j - mn_j) / 15); off_j = fl(0 - mn_j);
+ *   d = fp16(fl(max_j scale_j / 63)), dmin = fp16(fl(max_j off_j / 63)) (RNE, saturating);
+ *   sc_j = d == 0 ? 0 : clamp(rint(fl(scale_j / d)), 0, 63); m_j likewise with off_j, dmin;
+ *   D_j = d sc_j, M_j = dmin m_j; q = D_j == 0 ? 0 : clamp(rint(fl(fl(x + M_j) fl(1/D_j))), 0, 15);
+ *   y = bf16(fl(D_j q - M_j)).
+ * Block layout (144 bytes): d (fp16 LE) | dmin (fp16 LE) | 12 bytes holding a
+ * 96-bit little-endian stream with sc_j at bits 6j.. and m_j at bits 48+6j.. |
+ * 128 bytes of codes, element 2i low nibble, 2i+1 high nibble.  For the
+ * single-tensor calls `blocks` is [rows, cols/256, 144]. */
+qf_status qf_qdq_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                     uint16_t* y, int64_t ldy, void* stream);
+qf_status qf_pack_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                      uint8_t* blocks, void* stream);
+qf_status qf_qdq_pack_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+                          uint16_t* y, int64_t ldy, uint8_t* blocks, void* stream);
+qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream);
+
+/* ---------------------------------------------------------------- STE ---- */
+/* Identity straight-through estimator ("Method", "Framework overview"):
+ * g_latent[i] = f32(g_q[i]) (accumulate == 0) or g_latent[i] += f32(g_q[i])
+ * (accumulate != 0; one fp32 rounding).  g_q: device bf16[n], 16-byte aligned;
+ * g_latent: device float[n], 16-byte aligned. */
+qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int accumulate,
+                          void* stream);
+
+/* ---------------------------------------------------- conformance test ---- */
+/* Checks on the device that the gfx950 conversion instructions the kernels
+ * rely on agree bit for bit with the software definitions above (bf16 RNE over
+ * every finite fp32; E2M1 RNE-saturating over every fp32 and over every bf16 x
+ * every E8M0 scale; E8M0-scaled E2M1 -> bf16/fp32 for every code and scale).
+ * d_counts: device uint64[8], zeroed by the caller; each entry receives the
+ * number of mismatches of one check (all zero on a conforming device). */
+qf_status qf_selftest_conversions(unsigned long long* d_counts, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QF_H */

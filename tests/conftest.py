@@ -17,3 +17,18 @@ def pytest_configure(config):
 def single():
     import workloads
     return workloads.single_256x512()
+
+
+def pytest_collection_modifyitems(config, items):
+    """GPU tests need a visible GPU; without one they are skipped, never faked."""
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="no GPU visible")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

@@ -1,0 +1,94 @@
+"""The C-ABI library loads and exports every entry point include/qf.h declares.
+
+Host-only checks (no GPU needed): symbol table, helper results, and argument
+validation, which returns before anything is enqueued.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from fp4_fake_quant_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qf.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qf_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    names = declared_functions()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    # the Python signatures cover exactly the declared entry points
+    assert sorted(_lib.SIGNATURES) == names
+
+
+def test_helpers_host_only():
+    L = _lib.lib()
+    assert L.qf_version() >> 8 == 1
+    assert L.qf_status_str(0) == b"ok"
+    assert L.qf_packed_bytes(0, 256, 512) == 73_728          # + 4 bytes of fp32 tensor scale = 73,732
+    assert L.qf_packed_bytes(1, 256, 512) == 69_632
+    assert L.qf_packed_bytes(2, 256, 512) == 73_728
+    assert L.qf_packed_bytes(0, 256, 24) == 0                # not a block multiple
+    assert L.qf_packed_bytes(7, 1, 16) == 0
+
+
+def _addr(v):
+    return ctypes.c_void_p(v)
+
+
+@pytest.mark.parametrize("case", ["null_x", "bad_cols", "ld_small", "misaligned", "neg_rows"])
+def test_argument_validation_returns_before_launch(case):
+    """Invalid arguments come back as status codes; fake non-null addresses are never touched."""
+    L = _lib.lib()
+    good = 0x10000000
+    x, y = good, good + 0x100000
+    rows, cols, ldx, ldy = 4, 64, 64, 64
+    if case == "null_x":
+        x = 0
+    if case == "bad_cols":
+        cols = ldx = ldy = 40
+    if case == "ld_small":
+        ldx = 32
+    if case == "misaligned":
+        x = good + 2
+    if case == "neg_rows":
+        rows = -1
+    st = L.qf_qdq_mxfp4(_addr(x) if x else None, rows, cols, ldx, _addr(y), ldy, None)
+    expect = {"null_x": 1, "bad_cols": 2, "ld_small": 2, "misaligned": 3, "neg_rows": 2}[case]
+    assert st == expect
+
+
+def test_validation_of_other_entry_points():
+    L = _lib.lib()
+    p = _addr(0x10000000)
+    q = _addr(0x10100000)
+    assert L.qf_qdq_nvfp4(p, 4, 64, 64, None, q, 64, None) == 1            # missing tensor scale
+    assert L.qf_qdq_q4k(p, 4, 128, 128, q, 128, None) == 2                 # 128 is not a 256 multiple
+    assert L.qf_pack_mxfp4(p, 4, 64, 64, q, None, None) == 1               # missing scales
+    assert L.qf_pack_q4k(p, 4, 256, 256, _addr(0x10100004), None) == 3     # blocks must be 16-byte aligned
+    assert L.qf_ste_backward(p, _addr(0x10100004), 100, 0, None) == 3
+    assert L.qf_ste_backward(None, q, 100, 0, None) == 1
+    assert L.qf_ste_backward(p, q, 0, 0, None) == 0                        # empty: no-op
+    assert L.qf_qdq_mxfp4(p, 0, 64, 64, q, 64, None) == 0                  # empty: no-op
+    assert L.qf_selftest_conversions(None, None) == 1
+    # tensor scale: workspace must be given and large enough
+    d = (_lib.TensorDesc * 1)()
+    d[0].x, d[0].rows, d[0].cols, d[0].ldx, d[0].group = 0x10000000, 1024, 4096, 4096, 0
+    need = L.qf_nvfp4_tensor_scale_workspace(ctypes.byref(d), 1)
+    assert need == 4 * (1024 * 4096 // 8192)
+    assert L.qf_nvfp4_tensor_scale_grouped(ctypes.byref(d), 1, 1, q, None, None, 0, None) == 4
+    assert L.qf_nvfp4_tensor_scale_grouped(ctypes.byref(d), 1, 1, q, None, q, need - 4, None) == 4
+    d[0].group = 3
+    assert L.qf_nvfp4_tensor_scale_grouped(ctypes.byref(d), 1, 2, q, None, q, need, None) == 7
+    assert L.qf_qdq_pack_mxfp4_grouped(ctypes.byref(d), 17, None) == 7      # too many tensors
