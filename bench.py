@@ -1,0 +1,301 @@
+"""Throughput of the simulated-quantization hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+Prints ONE JSON line.  The default workload is the dense 8B-class transformer
+layer (fused QKV 6144x4096, fused gate/up 28672x4096, down 4096x14336, O
+4096x4096, bf16), quantized NVFP4 W4A16.  One step is the whole hot path over
+that layer:
+  1. grouped tensor scales (one tied group per fused matrix): amax pass + reduce,
+  2. grouped QDQ + pack of all four matrices in one launch (bf16 QDQ'd weights
+     for the BF16 matmul, packed E2M1 codes + E4M3 block scales for the engine),
+  3. the identity STE backward of the upstream gradient of all four matrices
+     (one contiguous bf16 buffer -> fp32).
+Inputs are resident in HBM before timing starts.  `value` is algorithmic bytes
+per step / time per step; the roofline object describes the step's dominant
+kernel, timed with HIP events on the stream it runs on.  The CPU baseline is
+the oracle (test infrastructure) on a bounded sample of the same workload.
+
+Other workloads: --workload q4k_set (Q4_K grouped QDQ + pack over the layer set
+plus a 151936x4096 vocabulary projection) and the ones listed by --help.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+METRIC = "QDQ+pack GB/s (% HBM peak) per format; fused W4A4 QDQ-GEMM TFLOP/s (% MFMA)"
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(os.path.join(ROOT, "fp4_fake_quant_amd", "csrc"))):
+        with open(os.path.join(ROOT, "fp4_fake_quant_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key, launches_per_step):
+    """HBM-side bytes per launch of the dominant kernel from the committed counter summary,
+    or None when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(kernel_key)
+    if not entry or entry.get("source_hash") != kernel_source_hash():
+        return None
+    return entry.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------ workloads ----
+class DenseLayerNVFP4:
+    name = "dense_layer_8b_nvfp4_w4a16"
+
+    def __init__(self, torch, fq):
+        import numpy as np
+        import workloads
+        self.torch, self.fq = torch, fq
+        layer = workloads.dense_layer_8b(with_grad=True)
+        self.names = list(layer)
+        dev = torch.device("cuda")
+
+        def to_dev(b):
+            return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.host = layer
+        self.W = {n: to_dev(layer[n][0]) for n in self.names}
+        self.numel = sum(self.W[n].numel() for n in self.names)
+        # one contiguous upstream-gradient buffer for the whole layer (a flat grad buffer)
+        self.G = torch.empty(self.numel, dtype=torch.bfloat16, device=dev)
+        off = 0
+        for n in self.names:
+            k = self.W[n].numel()
+            self.G[off:off + k].copy_(to_dev(layer[n][1]).reshape(-1))
+            off += k
+        self.g_latent = torch.empty(self.numel, dtype=torch.float32, device=dev)
+        self.Y = {n: torch.empty_like(self.W[n]) for n in self.names}
+        self.codes = {n: torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev) for n, w in self.W.items()}
+        self.scl = {n: torch.empty((w.shape[0], w.shape[1] // 16), dtype=torch.uint8, device=dev) for n, w in self.W.items()}
+        self.amax_items = [dict(x=self.W[n], group=i) for i, n in enumerate(self.names)]
+        self.qitems = [dict(x=self.W[n], y=self.Y[n], codes=self.codes[n], scales=self.scl[n], group=i)
+                       for i, n in enumerate(self.names)]
+        self.ws = torch.empty(fq.qf_nvfp4_tensor_scale_workspace(self.amax_items), dtype=torch.uint8, device=dev)
+        self.scales = torch.empty(len(self.names), dtype=torch.float32, device=dev)
+        n = self.numel
+        # algorithmic bytes: amax reads bf16 (2 B); QDQ+pack reads bf16, writes bf16 + codes
+        # (0.5 B) + E4M3 scales (1/16 B); STE reads bf16 and writes fp32
+        self.kernels = {
+            "nvfp4_amax": 2 * n,
+            "nvfp4_qdq_pack": n * (2 + 2 + 0.5 + 1 / 16),
+            "ste_backward": n * (2 + 4),
+        }
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {
+            "workload": self.name,
+            "matrices": {k: list(v.shape) for k, v in self.W.items()},
+            "elements": n,
+            "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale tied per fused matrix)",
+            "tied_groups": len(self.names),
+        }
+
+    def step(self, ev=None):
+        fq = self.fq
+        t = (lambda k, i: ev[k][i].record()) if ev is not None else (lambda k, i: None)
+        t("nvfp4_amax", 0)
+        fq.qf_nvfp4_tensor_scale_grouped(self.amax_items, len(self.names), self.scales, None, self.ws)
+        t("nvfp4_amax", 1)
+        t("nvfp4_qdq_pack", 0)
+        fq.qf_qdq_pack_nvfp4_grouped(self.qitems, self.scales)
+        t("nvfp4_qdq_pack", 1)
+        t("ste_backward", 0)
+        fq.qf_ste_backward(self.G, self.g_latent)
+        t("ste_backward", 1)
+
+    def cpu_baseline(self, budget_s=15.0):
+        """The oracle's full step on the first rows of every matrix, sized to ~budget_s."""
+        import numpy as np
+        from oracle import nvfp4, ste
+
+        def run(frac):
+            t0 = time.perf_counter()
+            nbytes = 0.0
+            for n in self.names:
+                W, G = self.host[n]
+                r = max(1, int(W.shape[0] * frac))
+                Ws, Gs = W[:r], G[:r]
+                s_t = nvfp4.tensor_scale([Ws])
+                c, S = nvfp4.quantize(Ws, s_t)
+                nvfp4.dequantize(c, S, s_t)
+                nvfp4.pack(c, S)
+                ste.ste_backward(Gs)
+                nbytes += Ws.size * (2 + 4.5625 + 6)
+            return time.perf_counter() - t0, nbytes
+
+        dt, nb = run(0.002)
+        frac = min(1.0, 0.002 * budget_s / max(dt, 1e-3))
+        dt, nb = run(frac)
+        return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the oracle's amax + QDQ + pack + STE on the first {frac * 100:.2f}% of rows of each "
+                          f"of the four matrices ({nb / 12.5625 / 1e6:.1f} M elements, {dt:.1f} s, numpy, 1 thread)"}
+
+
+class Q4KSet:
+    """Q4_K weight-only QDQ + GGUF-style packing in one grouped launch over the Q4_K set:
+    the 256x512 matrix, the four 8B-layer matrices and the 151936x4096 vocabulary
+    projection (inputs drawn on the device with the same recipe as the tests' set)."""
+    name = "q4k_set_qdq_pack"
+
+    def __init__(self, torch, fq):
+        import workloads
+        self.torch, self.fq = torch, fq
+        self.T = workloads.q4k_set_device(seed=0)
+        dev = torch.device("cuda")
+        self.items = []
+        for n, w in self.T.items():
+            y = torch.empty_like(w)
+            b = torch.empty((w.shape[0], w.shape[1] // 256, 144), dtype=torch.uint8, device=dev)
+            self.items.append(dict(x=w, y=y, codes=b))
+        n = sum(w.numel() for w in self.T.values())
+        self.numel = n
+        self.kernels = {"q4k_qdq_pack": n * (2 + 2 + 144 / 256)}
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {"workload": self.name, "matrices": {k: list(v.shape) for k, v in self.T.items()},
+                       "elements": n, "format": "Q4_K (INT4, 32-blocks in 256 super-blocks, 6-bit scales/mins, FP16 d/dmin)"}
+
+    def step(self, ev=None):
+        if ev is not None:
+            ev["q4k_qdq_pack"][0].record()
+        self.fq.qf_qdq_pack_q4k_grouped(self.items)
+        if ev is not None:
+            ev["q4k_qdq_pack"][1].record()
+
+    def cpu_baseline(self, budget_s=10.0):
+        import numpy as np
+        import workloads
+        from oracle import q4k
+        W = workloads.q4k_set(names=["o"])["o"]
+        t0 = time.perf_counter()
+        r = 64
+        p = q4k.quantize(W[:r]); q4k.dequantize(p); q4k.pack(p)
+        dt = time.perf_counter() - t0
+        r = max(64, min(W.shape[0], int(64 * budget_s / max(dt, 1e-3))))
+        t0 = time.perf_counter()
+        p = q4k.quantize(W[:r]); q4k.dequantize(p); q4k.pack(p)
+        dt = time.perf_counter() - t0
+        nb = W[:r].size * (2 + 2 + 144 / 256)
+        return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the oracle's Q4_K QDQ + pack on the first {r} rows of the 4096x4096 matrix ({dt:.1f} s)"}
+
+
+class MXFP4Operands:
+    """MXFP4 QDQ + pack of the W4A4 GEMM operands, X 32768x4096 (activations, Student-t
+    with outlier columns) and W 14336x4096, one grouped launch."""
+    name = "mxfp4_gemm_operands_qdq_pack"
+
+    def __init__(self, torch, fq):
+        import workloads
+        self.torch, self.fq = torch, fq
+        g = workloads.w4a4_gemm_device(seed=0)
+        dev = torch.device("cuda")
+        self.items = []
+        for w in (g["X"], g["W"]):
+            self.items.append(dict(x=w, y=torch.empty_like(w),
+                                   codes=torch.empty((w.shape[0], w.shape[1] // 2), dtype=torch.uint8, device=dev),
+                                   scales=torch.empty((w.shape[0], w.shape[1] // 32), dtype=torch.uint8, device=dev)))
+        n = sum(it["x"].numel() for it in self.items)
+        self.kernels = {"mxfp4_qdq_pack": n * (2 + 2 + 0.5 + 1 / 32)}
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {"workload": self.name, "matrices": {"X": [32768, 4096], "W": [14336, 4096]}, "elements": n,
+                       "format": "MXFP4 (E2M1, block 32, E8M0)"}
+
+    def step(self, ev=None):
+        if ev is not None:
+            ev["mxfp4_qdq_pack"][0].record()
+        self.fq.qf_qdq_pack_mxfp4_grouped(self.items)
+        if ev is not None:
+            ev["mxfp4_qdq_pack"][1].record()
+
+
+WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DenseLayerNVFP4.name, choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for {args.gpus}): the hot path here is a "
+              "single-GPU kernel set and no multi-GPU run is made", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import fp4_fake_quant_amd as fq
+    torch.cuda.set_device(0)
+    wl = WORKLOADS[args.workload](torch, fq)
+
+    for _ in range(args.warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    # headline: K steps back to back, nothing else on the stream
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        wl.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    # per-kernel durations: the same K steps again with a HIP event pair around every
+    # kernel (events add a few microseconds between kernels, so they stay out of the
+    # headline loop); the events sit on torch's current stream, where the library launches
+    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+          for k in wl.kernels}
+    for i in range(args.steps):
+        wl.step({k: ev[k][i] for k in wl.kernels})
+    torch.cuda.synchronize()
+    kern = {}
+    for k, nbytes in wl.kernels.items():
+        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(args.steps)) / args.steps
+        kern[k] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
+                   "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes)}
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    achieved = kern[dom]["GB/s"]
+    traffic = traffic_from_profile(f"{wl.name}:{dom}", 1)
+    value = wl.bytes_per_step / (ms_per_step / 1e3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": wl.config,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "kernels": kern,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = wl.cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

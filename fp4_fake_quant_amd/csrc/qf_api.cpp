@@ -53,8 +53,8 @@ qf_status check_desc(const qf_tensor_desc& d, int fmt, bool use_y, bool use_p) {
   return QF_OK;
 }
 
-// Fills QArgs from descriptors; tiles are laid out tensor after tensor.
-void fill_args(qf::QArgs& a, const qf_tensor_desc* d, int n) {
+// Fills QArgs from descriptors; tiles of tile_chunks chunks are laid out tensor after tensor.
+void fill_args(qf::QArgs& a, const qf_tensor_desc* d, int n, int tile_chunks) {
   memset(&a, 0, sizeof(a));
   int tiles = 0;
   int k = 0;
@@ -73,16 +73,26 @@ void fill_args(qf::QArgs& a, const qf_tensor_desc* d, int n) {
     t.group = d[i].group;
     t.contig_x = d[i].ldx == d[i].cols;
     t.contig_y = t.ldy == d[i].cols;
-    tiles += (int)((t.nchunks + qf::TILE_CHUNKS - 1) / qf::TILE_CHUNKS);
+    tiles += (int)((t.nchunks + tile_chunks - 1) / tile_chunks);
   }
   a.n = k;
   a.total_tiles = tiles;
 }
 
-int64_t tiles_of(const qf_tensor_desc& d) {
+int64_t tiles_of(const qf_tensor_desc& d, int tile_chunks) {
   if (d.rows <= 0 || d.cols <= 0) return 0;
   const uint64_t chunks = (uint64_t)d.rows * (uint64_t)(d.cols / 8);
-  return (int64_t)((chunks + qf::TILE_CHUNKS - 1) / qf::TILE_CHUNKS);
+  return (int64_t)((chunks + tile_chunks - 1) / tile_chunks);
+}
+
+constexpr int AMAX_TILE = qf::WG * qf::L_AMAX;
+
+// Rows of amax partials a tensor-scale call needs: highest group with a non-empty tensor, plus one.
+int partial_groups(const qf_tensor_desc* d, int n) {
+  int g = 0;
+  for (int i = 0; i < n; ++i)
+    if (d[i].rows > 0 && d[i].cols > 0 && d[i].group + 1 > g) g = d[i].group + 1;
+  return g;
 }
 
 // Grouped quantization; each descriptor's NULL outputs are skipped.
@@ -90,6 +100,7 @@ qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_
   if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
   if (n > 0 && !d) return QF_ERR_NULL;
   if (fmt == QF_FMT_NVFP4 && !d_scales) return QF_ERR_NULL;
+  const int tile_chunks = qf::WG * qf::chunks_per_lane(fmt);
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) {
     const bool uy = d[i].y != nullptr, up = d[i].codes != nullptr;
@@ -97,7 +108,7 @@ qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_
     const qf_status st = check_desc(d[i], fmt, uy, up);
     if (st != QF_OK) return st;
     if (fmt == QF_FMT_NVFP4 && d[i].group < 0) return QF_ERR_ARG;
-    tiles += tiles_of(d[i]);
+    tiles += tiles_of(d[i], tile_chunks);
   }
   if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
   if (tiles == 0) return QF_OK;
@@ -112,7 +123,7 @@ qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_
     }
     if (k == 0) continue;
     qf::QArgs a;
-    fill_args(a, sel, k);
+    fill_args(a, sel, k, tile_chunks);
     a.tscale = d_scales;
     const hipError_t e = qf::launch_quant(fmt, wy, wp, a, s);
     if (e != hipSuccess) return hip_status(e);
@@ -179,38 +190,36 @@ size_t qf_packed_bytes(int fmt, int64_t rows, int64_t cols) {
 size_t qf_nvfp4_tensor_scale_workspace(const qf_tensor_desc* d, int n) {
   if (n < 0 || (n > 0 && !d)) return 0;
   int64_t tiles = 0;
-  for (int i = 0; i < n; ++i) tiles += tiles_of(d[i]);
-  return (size_t)(tiles > 0 ? tiles : 1) * sizeof(uint32_t);
+  for (int i = 0; i < n; ++i) tiles += tiles_of(d[i], AMAX_TILE);
+  const int64_t grid = tiles < qf::AMAX_GRID ? tiles : qf::AMAX_GRID;
+  const int64_t words = grid * partial_groups(d, n);
+  return (size_t)(words > 0 ? words : 1) * sizeof(uint32_t);
 }
 
 qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_groups, float* d_scales,
                                         uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
   if (n < 0 || n > QF_MAX_GROUPED || n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
   if ((n > 0 && !d) || !d_scales) return QF_ERR_NULL;
+  int64_t tiles = 0;
   for (int i = 0; i < n; ++i) {
     const qf_status st = check_desc(d[i], QF_FMT_NVFP4, false, false);
     if (st != QF_OK) return st;
     if (d[i].group < 0 || d[i].group >= n_groups) return QF_ERR_ARG;
+    tiles += tiles_of(d[i], AMAX_TILE);
   }
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
   const size_t need = qf_nvfp4_tensor_scale_workspace(d, n);
   if (!ws || ws_bytes < need) return QF_ERR_WORKSPACE;
   if (!aligned(ws, 4)) return QF_ERR_ALIGN;
   hipStream_t s = (hipStream_t)stream;
   qf::QArgs a;
-  fill_args(a, d, n);
+  fill_args(a, d, n, AMAX_TILE);
   a.partial = (uint32_t*)ws;
+  a.n_groups = partial_groups(d, n);
   qf::ReduceArgs r;
-  memset(&r, 0, sizeof(r));
-  int k = 0;
-  for (int i = 0; i < n; ++i) {
-    if (d[i].rows == 0 || d[i].cols == 0) continue;
-    r.tile_begin[k] = a.t[k].tile_begin;
-    r.group[k] = d[i].group;
-    ++k;
-  }
-  r.tile_begin[k] = a.total_tiles;
-  r.n = k;
   r.n_groups = n_groups;
+  r.n_partial_groups = a.n_groups;
+  r.grid = qf::amax_grid(a.total_tiles);
   r.partial = (const uint32_t*)ws;
   r.tscale = d_scales;
   r.nonfinite = d_nonfinite;
@@ -285,7 +294,7 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
   if (n == 0) return QF_OK;
   if (!g_q || !g_latent) return QF_ERR_NULL;
   if (!aligned(g_q, 16) || !aligned(g_latent, 16)) return QF_ERR_ALIGN;
-  if (((n >> 3) + qf::TILE_CHUNKS - 1) / qf::TILE_CHUNKS >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (((n >> 3) + qf::WG * qf::L_STE - 1) / (qf::WG * qf::L_STE) >= (1ll << 31)) return QF_ERR_SHAPE;
   return hip_status(qf::launch_ste(g_q, g_latent, n, accumulate != 0, (hipStream_t)stream));
 }
 

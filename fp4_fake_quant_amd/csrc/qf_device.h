@@ -84,11 +84,40 @@ __device__ __forceinline__ uint32_t f16_bits_sat(float f) {
   return (uint32_t)__builtin_rintf(f * 16777216.0f);                 // 0..1024; 1024 = 2^-14
 }
 
+// The same conversion through v_cvt_f16_f32 (RNE, fp16 subnormals kept): clamping
+// to 65504 first makes the result saturate instead of overflowing.  Agrees with
+// f16_bits_sat for every non-negative finite fp32 (device self-test).
+__device__ __forceinline__ uint32_t f16_bits_sat_hw(float f) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)fminf(f, 65504.0f));
+}
+
 __device__ __forceinline__ float f16_value(uint32_t h) {
   uint32_t e = (h >> 10) & 0x1Fu, m = h & 0x3FFu;
   if (e == 0) return (float)m * 5.9604644775390625e-8f;               // m * 2^-24, exact
   return __uint_as_float(((e + 112u) << 23) | (m << 13));
 }
+
+// fp16 bits -> f32 through v_cvt_f32_f16 (exact, subnormals included; self-test).
+__device__ __forceinline__ float f16_value_hw(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+}
+// Bits of a value already on the fp16 grid.
+__device__ __forceinline__ uint32_t f16_bits_of(float v) {
+  return (uint32_t)__builtin_bit_cast(unsigned short, (_Float16)v);
+}
+
+// ------------------------------------------------- division by constants ----
+// fl(x / y) for a constant y with inv_y = fl(1 / y): the product x * inv_y is
+// corrected once with the exact remainder r = x - q y (one FMA), then
+// q + r * inv_y is rounded once.  For y = 15 and y = 63 this equals the IEEE
+// quotient for every non-negative finite x (device self-test, exhaustive).
+__device__ __forceinline__ float div_const(float x, float y, float inv_y) {
+  const float q = x * inv_y;
+  const float r = __builtin_fmaf(-q, y, x);
+  return __builtin_fmaf(r, inv_y, q);
+}
+__device__ __forceinline__ float div15(float x) { return div_const(x, 15.0f, 1.0f / 15.0f); }
+__device__ __forceinline__ float div63(float x) { return div_const(x, 63.0f, 1.0f / 63.0f); }
 
 // ------------------------------------------------------- cross-lane ops ----
 // DPP patterns: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1] (lane ^ 2),
@@ -101,6 +130,9 @@ __device__ __forceinline__ uint32_t dpp_xor2(uint32_t v) { return (uint32_t)__bu
 __device__ __forceinline__ uint32_t dpp_hmirror(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true); }
 __device__ __forceinline__ uint32_t dpp_mirror(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true); }
 __device__ __forceinline__ uint32_t swz_xor16(uint32_t v) { return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F); }
+// Broadcast lane 0 (resp. 1) of every quad to the whole quad.
+__device__ __forceinline__ uint32_t quad_bcast0(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, true); }
+__device__ __forceinline__ uint32_t quad_bcast1(uint32_t v) { return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, true); }
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }

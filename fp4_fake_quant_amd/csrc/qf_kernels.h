@@ -11,12 +11,40 @@ namespace qf {
 
 // A quantization launch works on "chunks" of 8 consecutive bf16 (16 bytes):
 // one 128-bit load per lane.  A workgroup of 256 lanes handles a tile of
-// TILE_CHUNKS chunks (4 per lane, at stride 256 so that every load
-// instruction of the workgroup covers 4 KiB of contiguous memory).  Tiles
-// never straddle two tensors; a tensor's last tile may be partial.
+// 256 * L chunks (L per lane, at stride 256 so that every load instruction of
+// the workgroup covers 4 KiB of contiguous memory).  Tiles never straddle two
+// tensors; a tensor's last tile may be partial.  L is chosen per kernel from
+// measurements (more, smaller workgroups stream writes better on gfx950).
 constexpr int WG = 256;
-constexpr int CHUNKS_PER_LANE = 4;
-constexpr int TILE_CHUNKS = WG * CHUNKS_PER_LANE;   // 1024 chunks = 8192 elements
+#ifndef QF_L_AMAX
+#define QF_L_AMAX 2
+#endif
+#ifndef QF_L_NVFP4
+#define QF_L_NVFP4 1
+#endif
+#ifndef QF_L_MXFP4
+#define QF_L_MXFP4 1
+#endif
+#ifndef QF_L_Q4K
+#define QF_L_Q4K 2
+#endif
+#ifndef QF_L_STE
+#define QF_L_STE 1
+#endif
+#ifndef QF_REVERSE_PASS2
+#define QF_REVERSE_PASS2 1
+#endif
+#ifndef QF_AMAX_GRID
+#define QF_AMAX_GRID 2048
+#endif
+constexpr int L_AMAX = QF_L_AMAX, L_NVFP4 = QF_L_NVFP4, L_MXFP4 = QF_L_MXFP4, L_Q4K = QF_L_Q4K, L_STE = QF_L_STE;
+// The amax pass runs a persistent grid of at most AMAX_GRID workgroups, each
+// keeping one maximum per tied group.
+constexpr int AMAX_GRID = QF_AMAX_GRID;
+
+inline int chunks_per_lane(int fmt) {
+  return fmt == QF_FMT_NVFP4 ? L_NVFP4 : fmt == QF_FMT_MXFP4 ? L_MXFP4 : L_Q4K;
+}
 
 struct QTensor {
   const uint16_t* x;
@@ -37,19 +65,21 @@ struct QArgs {
   int n;
   int total_tiles;
   const float* tscale;  // NVFP4: device float per group
-  uint32_t* partial;    // NVFP4 pass 1: one uint32 per tile (amax bits | nonfinite << 31)
+  uint32_t* partial;    // NVFP4 pass 1: [n_groups][grid] maxima (abs bf16 bits)
+  int n_groups;         // NVFP4 pass 1: groups that own a partial row
 };
 
 struct ReduceArgs {
-  int32_t tile_begin[QF_MAX_GROUPED + 1];
-  int32_t group[QF_MAX_GROUPED];
-  int n;
-  int n_groups;
+  int n_groups;         // groups to write
+  int n_partial_groups; // groups with a row of partials (the others have no tensor)
+  int grid;             // partials per group
   const uint32_t* partial;
   float* tscale;
   uint32_t* nonfinite;
 };
 
+// Workgroups of the amax pass for a launch with `tiles` tiles of 256 * L_AMAX chunks.
+inline int amax_grid(int tiles) { return tiles < AMAX_GRID ? tiles : AMAX_GRID; }
 hipError_t launch_nvfp4_amax(const QArgs& a, hipStream_t s);
 hipError_t launch_nvfp4_scale_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_quant(int fmt, bool write_y, bool write_packed, const QArgs& a, hipStream_t s);

@@ -8,12 +8,12 @@
 // backward, tied NVFP4 tensor scales for fused projections, engine-layout
 // export) and the "Supported formats" table.  Bit-level rules: include/qf.h.
 //
-// Layout of the work: a workgroup of 256 lanes owns a tile of 1024 chunks of
-// 8 bf16 (16 bytes); lane t handles chunks t, t+256, t+512, t+768 of the tile,
-// issuing all four 128-bit loads before any arithmetic.  A quantization block
-// therefore sits in 2 (NVFP4), 4 (MXFP4) or 32 (Q4_K) adjacent lanes and its
-// statistics are reduced with DPP row operations (and one ds_swizzle for the
-// 32-lane Q4_K super-block); no LDS and no barriers are needed.
+// Layout of the work: a workgroup of 256 lanes owns a tile of 256 * L chunks of
+// 8 bf16 (16 bytes); lane t handles chunks t, t+256, ..., t+256(L-1) of the
+// tile, issuing all L 128-bit loads before any arithmetic.  A quantization
+// block therefore sits in 2 (NVFP4), 4 (MXFP4) or 32 (Q4_K) adjacent lanes and
+// its statistics are reduced with DPP row operations (and one ds_swizzle for
+// the 32-lane Q4_K super-block); no LDS and no barriers are needed.
 #include <float.h>
 
 #include "qf_device.h"
@@ -39,51 +39,67 @@ __device__ __forceinline__ uint64_t chunk_offset(uint32_t c, uint32_t cpr, int64
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // -------------------------------------------------- NVFP4 pass 1: amax -----
-__global__ __launch_bounds__(WG) void k_nvfp4_amax(QArgs a) {
-  const int b = blockIdx.x;
-  const int ti = find_tensor(a, b);
-  const QTensor& T = a.t[ti];
-  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
-  uint4 w[CHUNKS_PER_LANE];
-#pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
-    const uint32_t c = base + j * WG + threadIdx.x;
-    w[j] = make_uint4(0, 0, 0, 0);
-    if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
-  }
-  uint32_t m = 0;
-#pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) m = umax(m, amax_bits8(w[j]));
-  // wave maximum: within 16 lanes by DPP, across 32 by swizzle, across 64 by readlane
+// Persistent grid: workgroup w walks tiles w, w + grid, ...; every wave folds
+// its tile maximum into an LDS slot of the tile's tied group; at the end the
+// workgroup writes one maximum per group to partial[g * grid + w].
+__device__ __forceinline__ uint32_t wave_umax(uint32_t m) {
   m = umax(m, dpp_xor1(m));
   m = umax(m, dpp_xor2(m));
   m = umax(m, dpp_hmirror(m));
   m = umax(m, dpp_mirror(m));
   m = umax(m, swz_xor16(m));
-  m = umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
-  __shared__ uint32_t wmax[WG / 64];
-  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t r = wmax[0];
-#pragma unroll
-    for (int i = 1; i < WG / 64; ++i) r = umax(r, wmax[i]);
-    a.partial[b] = r;
-  }
+  return umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
 }
 
-// One workgroup: per-group maximum of the tile partials, then the tensor scale.
-__global__ __launch_bounds__(WG) void k_nvfp4_scale_reduce(ReduceArgs a) {
+template <int L>
+__global__ __launch_bounds__(WG) void k_nvfp4_amax(QArgs a) {
   __shared__ uint32_t gmax[QF_MAX_GROUPS];
   for (int g = threadIdx.x; g < a.n_groups; g += WG) gmax[g] = 0;
   __syncthreads();
-  for (int i = 0; i < a.n; ++i) {
+  for (int b = blockIdx.x; b < a.total_tiles; b += gridDim.x) {
+    const int ti = find_tensor(a, b);
+    const QTensor& T = a.t[ti];
+    const uint32_t base = (uint32_t)(b - T.tile_begin) * (WG * L);
+    uint4 w[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const uint32_t c = base + j * WG + threadIdx.x;
+      w[j] = make_uint4(0, 0, 0, 0);
+      if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+    }
     uint32_t m = 0;
-    for (int t = a.tile_begin[i] + threadIdx.x; t < a.tile_begin[i + 1]; t += WG) m = umax(m, a.partial[t]);
-    if (m) atomicMax(&gmax[a.group[i]], m);
+#pragma unroll
+    for (int j = 0; j < L; ++j) m = umax(m, amax_bits8(w[j]));
+    m = wave_umax(m);
+    if ((threadIdx.x & 63) == 0 && m) atomicMax(&gmax[T.group], m);
   }
   __syncthreads();
-  for (int g = threadIdx.x; g < a.n_groups; g += WG) {
+  for (int g = threadIdx.x; g < a.n_groups; g += WG) a.partial[g * gridDim.x + blockIdx.x] = gmax[g];
+}
+
+// One workgroup of 1024 lanes: per-group maximum of the partials (every load of
+// a lane issued before any is used), then the tensor scale of every group.
+constexpr int RED_WG = 1024;
+__global__ __launch_bounds__(RED_WG) void k_nvfp4_scale_reduce(ReduceArgs a) {
+  __shared__ uint32_t gmax[QF_MAX_GROUPS];
+  for (int g = threadIdx.x; g < a.n_groups; g += RED_WG) gmax[g] = 0;
+  __syncthreads();
+  const int total = a.n_partial_groups * a.grid;
+  for (int i0 = threadIdx.x; i0 < total; i0 += 8 * RED_WG) {
+    uint32_t v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = i0 + k * RED_WG;
+      v[k] = i < total ? a.partial[i] : 0u;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int i = i0 + k * RED_WG;
+      if (v[k]) atomicMax(&gmax[i / a.grid], v[k]);
+    }
+  }
+  __syncthreads();
+  for (int g = threadIdx.x; g < a.n_groups; g += RED_WG) {
     const uint32_t bits = gmax[g];
     if (bits >= 0x7F80u && a.nonfinite) *a.nonfinite = 1u;
     const float A = __uint_as_float(bits << 16);
@@ -93,23 +109,29 @@ __global__ __launch_bounds__(WG) void k_nvfp4_scale_reduce(ReduceArgs a) {
 
 // ------------------------------------------------- NVFP4 pass 2: QDQ -------
 // Lanes 2i and 2i+1 hold one 16-block.
-template <bool WY, bool WP>
+template <bool WY, bool WP, int L>
 __global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
+#if QF_REVERSE_PASS2
+  // last tiles first: they are the ones the amax pass read last, so part of them
+  // is still in the memory-side cache
+  const int b = a.total_tiles - 1 - (int)blockIdx.x;
+#else
   const int b = blockIdx.x;
+#endif
   const int ti = find_tensor(a, b);
   const QTensor& T = a.t[ti];
-  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * (WG * L);
   const float s_t = a.tscale[T.group];
   const float k = 6.0f * s_t;
-  uint4 w[CHUNKS_PER_LANE];
+  uint4 w[L];
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     w[j] = make_uint4(0, 0, 0, 0);
     if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
   }
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     uint32_t m = amax_bits8(w[j]);
     m = umax(m, dpp_xor1(m));
@@ -163,21 +185,21 @@ __global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
 
 // ---------------------------------------------------------------- MXFP4 ----
 // Lanes 4i..4i+3 hold one 32-block.
-template <bool WY, bool WP>
+template <bool WY, bool WP, int L>
 __global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
   const int b = blockIdx.x;
   const int ti = find_tensor(a, b);
   const QTensor& T = a.t[ti];
-  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
-  uint4 w[CHUNKS_PER_LANE];
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * (WG * L);
+  uint4 w[L];
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     w[j] = make_uint4(0, 0, 0, 0);
     if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
   }
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     uint32_t m = amax_bits8(w[j]);
     m = umax(m, dpp_xor1(m));
@@ -214,23 +236,23 @@ __global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
 __device__ __forceinline__ float fbits(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t ubits(float f) { return __float_as_uint(f); }
 
-template <bool WY, bool WP>
+template <bool WY, bool WP, int L>
 __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
   const int b = blockIdx.x;
   const int ti = find_tensor(a, b);
   const QTensor& T = a.t[ti];
-  const uint32_t base = (uint32_t)(b - T.tile_begin) * TILE_CHUNKS;
+  const uint32_t base = (uint32_t)(b - T.tile_begin) * (WG * L);
   const uint32_t lane32 = threadIdx.x & 31u;
   const uint32_t sub = lane32 >> 2;
-  uint4 w[CHUNKS_PER_LANE];
+  uint4 w[L];
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     w[j] = make_uint4(0, 0, 0, 0);
     if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
   }
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     const uint32_t wv[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
     float xv[8];
@@ -252,7 +274,7 @@ __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
     mn = fminf(mn, 0.0f);
     if (mn == 0.0f) mn = 0.0f;        // a zero extreme counts as +0
     if (mx == 0.0f) mx = 0.0f;
-    const float scale = (mx - mn) / 15.0f;
+    const float scale = div15(mx - mn);
     const float off = 0.0f - mn;
     // super-block maxima of the (non-negative) scales and offsets: unsigned max on bits
     uint32_t sb = ubits(scale), ob = ubits(off);
@@ -262,11 +284,16 @@ __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
     ob = umax(ob, dpp_mirror(ob));
     sb = umax(sb, swz_xor16(sb));
     ob = umax(ob, swz_xor16(ob));
-    const uint32_t dh = f16_bits_sat(fbits(sb) / 63.0f);
-    const uint32_t dmh = f16_bits_sat(fbits(ob) / 63.0f);
-    const float d = f16_value(dh), dmin = f16_value(dmh);
-    const float scq = (d == 0.0f) ? 0.0f : fminf(fmaxf(__builtin_rintf(scale / d), 0.0f), 63.0f);
-    const float mq = (dmin == 0.0f) ? 0.0f : fminf(fmaxf(__builtin_rintf(off / dmin), 0.0f), 63.0f);
+    // Lanes of a quad share the work: lane 0 derives d (from the largest scale), lane 1
+    // dmin (from the largest offset), in one division and one fp16 conversion ...
+    const bool odd = (threadIdx.x & 1u) != 0;
+    const uint32_t h = f16_bits_sat_hw(div63(fbits(odd ? ob : sb)));
+    const float d = f16_value_hw(quad_bcast0(h)), dmin = f16_value_hw(quad_bcast1(h));
+    const uint32_t dh = f16_bits_of(d), dmh = f16_bits_of(dmin);
+    // ... then lane 0 rounds scale / d to sc and lane 1 off / dmin to m, in one division.
+    const float num = odd ? off : scale, den = odd ? dmin : d;
+    const float t63 = (den == 0.0f) ? 0.0f : fminf(fmaxf(__builtin_rintf(num / den), 0.0f), 63.0f);
+    const float scq = fbits(quad_bcast0(ubits(t63))), mq = fbits(quad_bcast1(ubits(t63)));
     const float D = d * scq, M = dmin * mq;
     const float r = (D == 0.0f) ? 0.0f : 1.0f / D;
     uint32_t qword = 0;
@@ -304,12 +331,12 @@ __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
 
 // ------------------------------------------------------------------ STE ----
 // Identity STE: 8 bf16 gradients per lane -> 8 fp32, optionally accumulated.
-template <bool ACC>
+template <bool ACC, int L>
 __global__ __launch_bounds__(WG) void k_ste(const uint16_t* __restrict__ g, float* __restrict__ out, int64_t n) {
   const int64_t nv = n >> 3;
-  const int64_t base = (int64_t)blockIdx.x * TILE_CHUNKS;
+  const int64_t base = (int64_t)blockIdx.x * (WG * L);
 #pragma unroll
-  for (int j = 0; j < CHUNKS_PER_LANE; ++j) {
+  for (int j = 0; j < L; ++j) {
     const int64_t i = base + j * WG + threadIdx.x;
     if (i < nv) {
       const uint4 w = load_chunk(g + i * 8);
@@ -360,6 +387,19 @@ __global__ __launch_bounds__(WG) void k_self_fp32(uint32_t base, unsigned long l
   if (bad1) atomicAdd(&counts[1], 1ull);
 }
 
+// counts[6]: v_cvt_f16_f32 with clamp vs the software fp16 conversion, every x >= 0 finite
+// counts[7]: FMA-corrected division by 15 and by 63 vs IEEE division, every x >= 0 finite
+__global__ __launch_bounds__(WG) void k_self_nonneg(uint32_t base, unsigned long long* counts) {
+  const uint32_t bits = base + blockIdx.x * WG + threadIdx.x;     // base < 2^31: x >= 0
+  const float x = __uint_as_float(bits);
+  if (!(x <= FLT_MAX)) return;
+  if (f16_bits_sat_hw(x) != f16_bits_sat(x)) atomicAdd(&counts[6], 1ull);
+  if (bits < 0x7C00u && __float_as_uint(f16_value_hw(bits)) != __float_as_uint(f16_value(bits)))
+    atomicAdd(&counts[6], 1ull);
+  if (__float_as_uint(div15(x)) != __float_as_uint(x / 15.0f) ||
+      __float_as_uint(div63(x)) != __float_as_uint(x / 63.0f)) atomicAdd(&counts[7], 1ull);
+}
+
 // counts[2], counts[3]: E8M0-scaled bf16 / f32 -> E2M1 over every bf16 and every E
 // counts[4], counts[5]: E8M0-scaled E2M1 -> bf16 / f32 over every code and E
 __global__ __launch_bounds__(WG) void k_self_scaled(unsigned long long* counts) {
@@ -390,26 +430,26 @@ __global__ __launch_bounds__(WG) void k_self_scaled(unsigned long long* counts) 
 // ------------------------------------------------------------- launchers ---
 hipError_t launch_nvfp4_amax(const QArgs& a, hipStream_t s) {
   if (a.total_tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_nvfp4_amax, dim3(a.total_tiles), dim3(WG), 0, s, a);
+  hipLaunchKernelGGL(k_nvfp4_amax<L_AMAX>, dim3(amax_grid(a.total_tiles)), dim3(WG), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_nvfp4_scale_reduce(const ReduceArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_nvfp4_scale_reduce, dim3(1), dim3(WG), 0, s, a);
+  hipLaunchKernelGGL(k_nvfp4_scale_reduce, dim3(1), dim3(RED_WG), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s) {
   if (a.total_tiles == 0) return hipSuccess;
   const dim3 g(a.total_tiles), blk(WG);
-#define QF_DISPATCH(KERNEL)                                                     \
-  if (wy && wp) hipLaunchKernelGGL((KERNEL<true, true>), g, blk, 0, s, a);      \
-  else if (wy) hipLaunchKernelGGL((KERNEL<true, false>), g, blk, 0, s, a);      \
-  else hipLaunchKernelGGL((KERNEL<false, true>), g, blk, 0, s, a);
+#define QF_DISPATCH(KERNEL, L)                                                     \
+  if (wy && wp) hipLaunchKernelGGL((KERNEL<true, true, L>), g, blk, 0, s, a);      \
+  else if (wy) hipLaunchKernelGGL((KERNEL<true, false, L>), g, blk, 0, s, a);      \
+  else hipLaunchKernelGGL((KERNEL<false, true, L>), g, blk, 0, s, a);
   switch (fmt) {
-    case QF_FMT_NVFP4: QF_DISPATCH(k_nvfp4); break;
-    case QF_FMT_MXFP4: QF_DISPATCH(k_mxfp4); break;
-    case QF_FMT_Q4K: QF_DISPATCH(k_q4k); break;
+    case QF_FMT_NVFP4: QF_DISPATCH(k_nvfp4, L_NVFP4); break;
+    case QF_FMT_MXFP4: QF_DISPATCH(k_mxfp4, L_MXFP4); break;
+    case QF_FMT_Q4K: QF_DISPATCH(k_q4k, L_Q4K); break;
     default: return hipErrorInvalidValue;
   }
 #undef QF_DISPATCH
@@ -419,16 +459,21 @@ hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s
 hipError_t launch_ste(const uint16_t* g, float* out, int64_t n, bool acc, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int64_t nv = n >> 3;
-  int64_t tiles = (nv + TILE_CHUNKS - 1) / TILE_CHUNKS;
+  int64_t tiles = (nv + WG * L_STE - 1) / (WG * L_STE);
   if (tiles == 0) tiles = 1;                                // tail-only input
-  if (acc) hipLaunchKernelGGL(k_ste<true>, dim3((uint32_t)tiles), dim3(WG), 0, s, g, out, n);
-  else hipLaunchKernelGGL(k_ste<false>, dim3((uint32_t)tiles), dim3(WG), 0, s, g, out, n);
+  if (acc) hipLaunchKernelGGL((k_ste<true, L_STE>), dim3((uint32_t)tiles), dim3(WG), 0, s, g, out, n);
+  else hipLaunchKernelGGL((k_ste<false, L_STE>), dim3((uint32_t)tiles), dim3(WG), 0, s, g, out, n);
   return hipGetLastError();
 }
 
 hipError_t launch_selftest_conversions(unsigned long long* counts, hipStream_t s) {
   for (uint32_t part = 0; part < 16; ++part) {
     hipLaunchKernelGGL(k_self_fp32, dim3((1u << 28) / WG), dim3(WG), 0, s, part << 28, counts);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (uint32_t part = 0; part < 8; ++part) {
+    hipLaunchKernelGGL(k_self_nonneg, dim3((1u << 28) / WG), dim3(WG), 0, s, part << 28, counts);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

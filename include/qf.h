@@ -189,12 +189,20 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
                           void* stream);
 
 /* ---------------------------------------------------- conformance test ---- */
-/* Checks on the device that the gfx950 conversion instructions the kernels
- * rely on agree bit for bit with the software definitions above (bf16 RNE over
- * every finite fp32; E2M1 RNE-saturating over every fp32 and over every bf16 x
- * every E8M0 scale; E8M0-scaled E2M1 -> bf16/fp32 for every code and scale).
- * d_counts: device uint64[8], zeroed by the caller; each entry receives the
- * number of mismatches of one check (all zero on a conforming device). */
+/* Checks on the device that the gfx950 instructions and shortcuts the kernels
+ * rely on agree bit for bit with the software definitions above, over their
+ * whole input domains:
+ *   [0] v_cvt_pk_bf16_f32 vs bf16 RNE, every finite fp32
+ *   [1] v_cvt_scalef32_pk_fp4_f32 (scale 1) vs E2M1 RNE-saturating, every non-NaN fp32
+ *   [2] v_cvt_scalef32_pk_fp4_bf16 with an E8M0 scale, every bf16 x every E
+ *   [3] v_cvt_scalef32_pk_fp4_f32 with an E8M0 scale, every bf16 x every E
+ *   [4] v_cvt_scalef32_pk_bf16_fp4, every code x every E
+ *   [5] v_cvt_scalef32_pk_f32_fp4, every code x every E, and with scale 1
+ *   [6] v_cvt_f16_f32 after clamping to 65504 vs fp16 RNE-saturating, every fp32 >= 0;
+ *       v_cvt_f32_f16 vs the exact fp16 value, every finite non-negative fp16
+ *   [7] FMA-corrected division by 15 and by 63 vs IEEE division, every fp32 >= 0
+ * d_counts: device uint64[8], zeroed by the caller; entry i receives the
+ * number of mismatches of check i (all zero on a conforming device). */
 qf_status qf_selftest_conversions(unsigned long long* d_counts, void* stream);
 
 #ifdef __cplusplus
