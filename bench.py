@@ -57,6 +57,59 @@ def traffic_from_profile(kernel_key, launches_per_step):
     return entry.get("bytes_per_launch")
 
 
+def _counter_rows(folder):
+    import csv
+    rows = []
+    for root, _, files in os.walk(folder):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                with open(os.path.join(root, f)) as fh:
+                    rows += list(csv.DictReader(fh))
+    return rows
+
+
+def pmc_summary(fetch_dir, write_dir, workload):
+    """Average FETCH_SIZE / WRITE_SIZE (KiB per dispatch) per kernel, scaled by the same
+    counters of the 1 GiB calibration copy (the last device copy of the run), written to
+    profiles/traffic.json under the current kernel-source hash."""
+    out = {}
+    per = {}
+    for counter, folder in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(folder) if r.get("Counter_Name") == counter]
+        by_dispatch = {}
+        for r in rows:
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            by_dispatch[key] = by_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+        copies = sorted((int(d), v) for (d, k), v in by_dispatch.items() if "copyBuffer" in k)
+        if not copies:
+            raise SystemExit(f"{folder}: no calibration copy dispatch found")
+        kib_copy = copies[-1][1]
+        scale = (1 << 30) / (kib_copy * 1024.0)           # true bytes per counted byte
+        for (d, k), v in by_dispatch.items():
+            if "copyBuffer" in k:
+                continue
+            per.setdefault(k, {}).setdefault(counter, []).append(v * 1024.0 * scale)
+        out.setdefault("_calibration", {})[counter] = {"copy_KiB_counted": kib_copy, "scale": scale}
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    short = {"k_nvfp4_amax": "nvfp4_amax", "k_nvfp4_scale_reduce": "nvfp4_amax", "k_nvfp4<": "nvfp4_qdq_pack",
+             "k_mxfp4<": "mxfp4_qdq_pack", "k_q4k<": "q4k_qdq_pack", "k_ste<": "ste_backward"}
+    for k, cnt in per.items():
+        tag = next((v for s_, v in short.items() if s_ in k), None)
+        if tag is None:
+            continue
+        f = sum(cnt.get("FETCH_SIZE", [0])) / max(1, len(cnt.get("FETCH_SIZE", [1])))
+        w = sum(cnt.get("WRITE_SIZE", [0])) / max(1, len(cnt.get("WRITE_SIZE", [1])))
+        entry = data.setdefault(f"{workload}:{tag}", {"kernels": {}, "source_hash": kernel_source_hash()})
+        entry["source_hash"] = kernel_source_hash()
+        entry["kernels"][k] = {"fetch_bytes": round(f), "write_bytes": round(w)}
+        entry["bytes_per_launch"] = sum(v["fetch_bytes"] + v["write_bytes"] for v in entry["kernels"].values())
+    data["_calibration"] = out["_calibration"]
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    print(json.dumps(data, indent=1, sort_keys=True))
+
+
 # ------------------------------------------------------------ workloads ----
 class DenseLayerNVFP4:
     name = "dense_layer_8b_nvfp4_w4a16"
@@ -226,7 +279,85 @@ class MXFP4Operands:
             ev["mxfp4_qdq_pack"][1].record()
 
 
-WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands)}
+class Single256x512:
+    """The 256x512 matrix (N(0, 0.02^2) with 131 N(0, 0.5^2) outliers) under each format:
+    launch-latency bound, reported in microseconds per call."""
+    name = "single_256x512_all_formats"
+
+    def __init__(self, torch, fq):
+        import numpy as np
+        import workloads
+        self.torch, self.fq = torch, fq
+        w = workloads.single_256x512()
+        dev = torch.device("cuda")
+
+        def to_dev(b):
+            return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+
+        self.W, self.G = to_dev(w["W"]), to_dev(w["G"])
+        self.g = torch.empty(self.G.shape, dtype=torch.float32, device=dev)
+        self.items = [dict(x=self.W, group=0)]
+        self.ws = torch.empty(fq.qf_nvfp4_tensor_scale_workspace(self.items), dtype=torch.uint8, device=dev)
+        self.sc = torch.empty(1, dtype=torch.float32, device=dev)
+        self.y = torch.empty_like(self.W)
+        self.c = torch.empty((256, 256), dtype=torch.uint8, device=dev)
+        self.s16 = torch.empty((256, 32), dtype=torch.uint8, device=dev)
+        self.s32 = torch.empty((256, 16), dtype=torch.uint8, device=dev)
+        self.b = torch.empty((256, 2, 144), dtype=torch.uint8, device=dev)
+        n = self.W.numel()
+        self.kernels = {"nvfp4_tensor_scale": 2 * n, "nvfp4_qdq_pack": n * 4.5625, "mxfp4_qdq_pack": n * 4.53125,
+                        "q4k_qdq_pack": n * 4.5625, "ste_backward": 6 * n}
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {"workload": self.name, "matrices": {"W": [256, 512]}, "elements": n}
+
+    def step(self, ev=None):
+        fq = self.fq
+        t = (lambda k, i: ev[k][i].record()) if ev is not None else (lambda k, i: None)
+        t("nvfp4_tensor_scale", 0)
+        fq.qf_nvfp4_tensor_scale(self.W, self.sc, None, self.ws)
+        t("nvfp4_tensor_scale", 1)
+        t("nvfp4_qdq_pack", 0)
+        fq.qf_qdq_pack_nvfp4(self.W, self.sc, self.y, self.c, self.s16)
+        t("nvfp4_qdq_pack", 1)
+        t("mxfp4_qdq_pack", 0)
+        fq.qf_qdq_pack_mxfp4(self.W, self.y, self.c, self.s32)
+        t("mxfp4_qdq_pack", 1)
+        t("q4k_qdq_pack", 0)
+        fq.qf_qdq_pack_q4k(self.W, self.y, self.b)
+        t("q4k_qdq_pack", 1)
+        t("ste_backward", 0)
+        fq.qf_ste_backward(self.G, self.g)
+        t("ste_backward", 1)
+
+
+WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512)}
+# measured next to the headline workload in a default run (fewer steps each)
+SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name]
+
+
+def measure(torch, wl, steps, warmup):
+    """(ms per step over `steps` back-to-back steps, per-kernel dict from a second, event-bracketed pass)."""
+    for _ in range(warmup):
+        wl.step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wl.step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
+    # per-kernel durations: the same steps again with a HIP event pair around every kernel
+    # (events add a few microseconds between kernels, so they stay out of the headline
+    # loop); the events sit on torch's current stream, where the library launches
+    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)] for k in wl.kernels}
+    for i in range(steps):
+        wl.step({k: ev[k][i] for k in wl.kernels})
+    torch.cuda.synchronize()
+    kern = {}
+    for k, nbytes in wl.kernels.items():
+        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(steps)) / steps
+        kern[k] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
+                   "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes)}
+    return ms_per_step, kern
 
 
 def main():
@@ -236,7 +367,15 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=DenseLayerNVFP4.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads of a default run")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="end with one 1 GiB device copy (the counter reference of a rocprofv3 --pmc run)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc output folders into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary, workload=args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): the hot path here is a "
               "single-GPU kernel set and no multi-GPU run is made", file=sys.stderr)
@@ -247,29 +386,7 @@ def main():
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload](torch, fq)
 
-    for _ in range(args.warmup):
-        wl.step()
-    torch.cuda.synchronize()
-    # headline: K steps back to back, nothing else on the stream
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        wl.step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    # per-kernel durations: the same K steps again with a HIP event pair around every
-    # kernel (events add a few microseconds between kernels, so they stay out of the
-    # headline loop); the events sit on torch's current stream, where the library launches
-    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-          for k in wl.kernels}
-    for i in range(args.steps):
-        wl.step({k: ev[k][i] for k in wl.kernels})
-    torch.cuda.synchronize()
-    kern = {}
-    for k, nbytes in wl.kernels.items():
-        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(args.steps)) / args.steps
-        kern[k] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
-                   "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes)}
+    ms_per_step, kern = measure(torch, wl, args.steps, args.warmup)
     dom = max(kern, key=lambda k: kern[k]["ms"])
     achieved = kern[dom]["GB/s"]
     traffic = traffic_from_profile(f"{wl.name}:{dom}", 1)
@@ -292,8 +409,30 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels": kern,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
         line["cpu_baseline"] = wl.cpu_baseline()
+    if args.calibrate_copy:
+        # a plain device copy of exactly 1 GiB (read 1 GiB, write 1 GiB): the reference
+        # that scales the FETCH_SIZE / WRITE_SIZE counters of a --pmc run to bytes
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.workload == DenseLayerNVFP4.name and not args.no_secondary:
+        # the other formats' QDQ+pack throughput, each on its own inputs, fewer steps
+        del wl
+        torch.cuda.empty_cache()
+        other = {}
+        for name in SECONDARY:
+            w2 = WORKLOADS[name](torch, fq)
+            ms2, kern2 = measure(torch, w2, max(5, args.steps // 10), 3)
+            other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5),
+                           "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1), "kernels": kern2}
+            del w2
+            torch.cuda.empty_cache()
+        line["per_workload"] = other
     print(json.dumps(line))
 
 
