@@ -330,9 +330,61 @@ class Single256x512:
         t("ste_backward", 1)
 
 
-WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512)}
+MFMA_BF16_PEAK_TFS = 2516.6     # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (dense)
+
+
+class W4A4GemmMXFP4:
+    """Y = QDQ(X) . QDQ(W)^T, X 32768x4096 (Student-t activations with outlier columns),
+    W 14336x4096, MXFP4 QDQ of both operands fused into the BF16 MFMA GEMM; controls:
+    the same kernel without QDQ (flags = 0) and torch.matmul (hipBLASLt) on the raw
+    operands, each timed the same way."""
+    name = "w4a4_mxfp4_gemm"
+
+    def __init__(self, torch, fq):
+        import workloads
+        self.torch, self.fq = torch, fq
+        g = workloads.w4a4_gemm_device(seed=0)
+        self.X, self.W = g["X"], g["W"]
+        self.M, self.K = self.X.shape
+        self.N = self.W.shape[0]
+        self.Y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
+        self.flop = 2.0 * self.M * self.N * self.K
+        self.kernels = {"gemm_mxfp4_fused": self.flop}
+        self.bytes_per_step = self.flop
+        self.config = {"workload": self.name, "M": self.M, "N": self.N, "K": self.K,
+                       "format": "MXFP4 W4A4 (E2M1, block 32, E8M0), BF16 MFMA, fp32 accumulate, bf16 out"}
+
+    def step(self, ev=None):
+        if ev is not None:
+            ev["gemm_mxfp4_fused"][0].record()
+        self.fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=3)
+        if ev is not None:
+            ev["gemm_mxfp4_fused"][1].record()
+
+    def controls(self, reps=10):
+        """ms of the plain-BF16 run of the same kernel and of torch.matmul."""
+        torch = self.torch
+        out = {}
+        for name, fn in (("gemm_bf16_same_kernel", lambda: self.fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
+                         ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y))):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            out[name] = {"ms": round(ms, 4), "TFLOP/s": round(self.flop / ms / 1e9, 1),
+                         "frac_mfma": round(self.flop / ms / 1e9 / MFMA_BF16_PEAK_TFS, 4)}
+        return out
+
+
+WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4)}
 # measured next to the headline workload in a default run (fewer steps each)
-SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name]
+SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name]
 
 
 def measure(torch, wl, steps, warmup):
@@ -428,8 +480,13 @@ def main():
         for name in SECONDARY:
             w2 = WORKLOADS[name](torch, fq)
             ms2, kern2 = measure(torch, w2, max(5, args.steps // 10), 3)
-            other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5),
-                           "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1), "kernels": kern2}
+            if isinstance(w2, W4A4GemmMXFP4):
+                tf = w2.flop / ms2 / 1e9
+                other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5), "TFLOP/s": round(tf, 1),
+                               "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4), "controls": w2.controls()}
+            else:
+                other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5),
+                               "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1), "kernels": kern2}
             del w2
             torch.cuda.empty_cache()
         line["per_workload"] = other

@@ -16,6 +16,7 @@ import torch
 from ._lib import TensorDesc, lib
 
 QF_OK = 0
+QF_QDQ_A, QF_QDQ_W = 1, 2
 QF_FMT_NVFP4, QF_FMT_MXFP4, QF_FMT_Q4K = 0, 1, 2
 MAX_GROUPED = 16
 BLOCK = {QF_FMT_NVFP4: 16, QF_FMT_MXFP4: 32, QF_FMT_Q4K: 256}
@@ -218,6 +219,21 @@ def qf_ste_backward(g_q, g_latent=None, accumulate=False):
         raise ValueError("g_latent must be a contiguous float32 tensor with g_q's element count")
     _check(lib().qf_ste_backward(_p(g_q), _p(g_latent), g_q.numel(), int(bool(accumulate)), _stream()), "qf_ste_backward")
     return g_latent
+
+
+# ---------------------------------------------------------------- GEMM ----
+def qf_gemm_mxfp4(X, W, Y=None, flags=QF_QDQ_A | QF_QDQ_W):
+    """Y[M, N] = QDQ(X)[M, K] . QDQ(W)[N, K]^T (bf16 in, fp32 accumulate, bf16 out)."""
+    M, K, ldx = _mat(_bf16(X, "X"), "X")
+    N, K2, ldw = _mat(_bf16(W, "W"), "W")
+    if K2 != K:
+        raise ValueError(f"X has K={K} but W has K={K2}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _bf16(Y, "Y")
+    _check(lib().qf_gemm_mxfp4(_p(X), ldx, _p(W), ldw, _p(Y), _mat(Y, "Y")[2], M, N, K, int(flags), _stream()),
+           "qf_gemm_mxfp4")
+    return Y
 
 
 def qf_selftest_conversions(device="cuda"):

@@ -52,6 +52,7 @@ SIGNATURES = {
     "qf_qdq_pack_q4k_grouped": (c_int, [c_void_p, c_int, c_void_p]),
     "qf_ste_backward": (c_int, [c_void_p, c_void_p, c_i64, c_int, c_void_p]),
     "qf_selftest_conversions": (c_int, [c_void_p, c_void_p]),
+    "qf_gemm_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint, c_void_p]),
 }
 
 _lib = None

@@ -298,6 +298,21 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
   return hip_status(qf::launch_ste(g_q, g_latent, n, accumulate != 0, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------ W4A4 GEMM --
+qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
+                        int64_t M, int64_t N, int64_t K, unsigned flags, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
+  if (flags & ~(QF_QDQ_A | QF_QDQ_W)) return QF_ERR_ARG;
+  if (M == 0 || N == 0) return QF_OK;
+  if (!X || !W || !Y) return QF_ERR_NULL;
+  if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 2) || ldx % 8 || ldw % 8) return QF_ERR_ALIGN;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_gemm_mxfp4(X, ldx, W, ldw, Y, ldy, (int)M, (int)N, (int)K, flags,
+                                          (hipStream_t)stream));
+}
+
 // ------------------------------------------------------ conformance test ---
 qf_status qf_selftest_conversions(unsigned long long* d_counts, void* stream) {
   if (!d_counts) return QF_ERR_NULL;

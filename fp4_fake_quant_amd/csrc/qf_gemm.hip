@@ -1,0 +1,208 @@
+// W4A4 MXFP4 simulated-quantization GEMM on gfx950: Y = QDQ(X) . QDQ(W)^T.
+//
+// What is computed: QATFactory project page, "Overview" (weights, and
+// optionally activations, rounded onto the format's grid while every matrix
+// multiplication runs in BF16) and "Key findings" 02 (MXFP4 benefits from
+// quantizing activations too, i.e. W4A4 training).  X is [M, K] (tokens x
+// hidden), W is [N, K] (out x in), both bf16 row-major; the MXFP4 blocks run
+// along K.  Products are accumulated in fp32 by the BF16 MFMA units; Y is
+// rounded to bf16 (RNE) once.
+//
+// Structure:
+//   - a workgroup of 256 lanes (4 waves, 2 x 2) owns a 256 x 256 tile of Y;
+//     each wave a 128 x 128 sub-tile = 4 x 4 v_mfma_f32_32x32x16_bf16 tiles
+//     (256 fp32 accumulators per lane);
+//   - K advances 64 at a time through two LDS stages of X and W slices
+//     (2 x 64 KiB).  16-byte chunks are XOR-swizzled by row so that the MFMA
+//     fragment reads (32 rows x 16 bytes per half-wave) hit distinct banks;
+//   - QDQ on load: the slice for step k+1 is loaded from global memory into
+//     registers while step k's MFMAs run; each MXFP4 block of 32 elements sits
+//     in 4 adjacent lanes (one 16-byte chunk each), its maximum is reduced with
+//     two DPP steps and the block is rounded onto the MXFP4 grid with the gfx950
+//     scaled FP4 conversions (bf16 -> E2M1 codes -> bf16, E8M0 scale in the
+//     operand's exponent field) before it is written to LDS.  The MFMAs then
+//     consume bf16 values that are exactly QDQ(X) and QDQ(W);
+//   - W is passed as the MFMA "A" operand and X as "B", so each lane ends
+//     with runs of 4 consecutive output columns of one output row (8-byte
+//     stores);
+//   - workgroups are mapped XCD-aware: consecutive workgroup ids go to the
+//     eight XCDs in turn, so XCD x is handed the x-th eighth of a grouped
+//     tile order (8 tile rows at a time) and its concurrently running
+//     workgroups share X and W panels in its L2.
+#include "qf_device.h"
+#include "qf_kernels.h"
+
+namespace qf {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int GBM = 256, GBN = 256, GBK = 64;
+constexpr int G_THREADS = 256;
+constexpr int G_CHUNKS = GBK / 8;                      // 16-byte chunks per row of a K slice
+constexpr int G_SLICE_BYTES = GBM * GBK * 2;           // one operand slice in LDS
+constexpr int G_LOADS = GBM * G_CHUNKS / G_THREADS;    // chunks per lane per operand per K step (8)
+constexpr int G_GROUP_M = 8;                           // tile rows per group of the tile order
+
+// LDS byte offset of chunk c of row r in a slice: chunks XOR-swizzled by (r & 7).
+__device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
+  return (r * G_CHUNKS + (c ^ (r & 7u))) * 16u;
+}
+
+// MXFP4 QDQ of one 16-byte chunk; lanes 4i..4i+3 hold one 32-element block.
+__device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
+  uint32_t m = amax_bits8(w);
+  m = umax(m, dpp_xor1(m));
+  m = umax(m, dpp_xor2(m));
+  const int ef = (int)(m >> 7);
+  const float sc = __uint_as_float((uint32_t)(ef > 2 ? ef - 2 : 0) << 23);
+  uint32_t codes = 0;
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.y), sc, 1);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.z), sc, 2);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.w), sc, 3);
+  uint4 o;
+  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0));
+  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1));
+  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2));
+  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3));
+  return o;
+}
+
+// Loads this lane's 8 chunks of a 256 x 64 slice (rows r0.., K offset k0).  Rows past
+// `rows` read as zero.
+__device__ __forceinline__ void load_slice(uint4 (&v)[G_LOADS], const uint16_t* __restrict__ p, int64_t ld,
+                                           int r0, int rows, int k0) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t c = t & 7u;
+#pragma unroll
+  for (int i = 0; i < G_LOADS; ++i) {
+    const int r = r0 + (int)(t >> 3) + 32 * i;
+    v[i] = make_uint4(0, 0, 0, 0);
+    if (r < rows) v[i] = *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + k0 + c * 8);
+  }
+}
+
+template <bool QDQ>
+__device__ __forceinline__ void store_slice(uint8_t* lds, const uint4 (&v)[G_LOADS]) {
+  const uint32_t t = threadIdx.x;
+  const uint32_t c = t & 7u;
+#pragma unroll
+  for (int i = 0; i < G_LOADS; ++i) {
+    const uint32_t r = (t >> 3) + 32u * i;
+    const uint4 q = QDQ ? mxfp4_qdq_chunk(v[i]) : v[i];
+    *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = q;
+  }
+}
+
+template <bool QA, bool QW>
+__global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
+                                                             const uint16_t* __restrict__ W, int64_t ldw,
+                                                             uint16_t* __restrict__ Y, int64_t ldy,
+                                                             int M, int N, int K, int y_vec) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];   // 128 KiB of the 160 KiB
+  // stage b holds the X slice at smem + 2b * G_SLICE_BYTES and the W slice right after it
+
+  // ---- tile of this workgroup (XCD-aware grouped order) ----
+  const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int group = t / (G_GROUP_M * tiles_n);
+  const int first_m = group * G_GROUP_M;
+  const int gsize = min(tiles_m - first_m, G_GROUP_M);
+  const int in_group = t - group * G_GROUP_M * tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * GBM, n0 = tn * GBN;
+
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave = threadIdx.x >> 6;
+  const uint32_t wm = wave >> 1, wn = wave & 1u;          // 2 x 2 waves
+  const uint32_t frow = lane & 31u, fhalf = lane >> 5;    // MFMA fragment row, k half
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  uint4 vx[G_LOADS], vw[G_LOADS];
+  load_slice(vx, X, ldx, m0, M, 0);
+  load_slice(vw, W, ldw, n0, N, 0);
+  store_slice<QA>(smem, vx);
+  store_slice<QW>(smem + G_SLICE_BYTES, vw);
+  __syncthreads();
+
+  const int nk = K / GBK;
+  for (int ks = 0; ks < nk; ++ks) {
+    const int cur = ks & 1;
+    if (ks + 1 < nk) {
+      load_slice(vx, X, ldx, m0, M, (ks + 1) * GBK);
+      load_slice(vw, W, ldw, n0, N, (ks + 1) * GBK);
+    }
+    const uint8_t* ax = smem + 2 * cur * G_SLICE_BYTES;
+    const uint8_t* aw = ax + G_SLICE_BYTES;
+#pragma unroll
+    for (int s = 0; s < GBK / 16; ++s) {
+      const uint32_t c = 2u * s + fhalf;
+      bf16x8_t fx[4], fw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fx[i] = *reinterpret_cast<const bf16x8_t*>(ax + lds_off(wm * 128 + i * 32 + frow, c));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const bf16x8_t*>(aw + lds_off(wn * 128 + j * 32 + frow, c));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fx[i], acc[i][j], 0, 0, 0);
+    }
+    if (ks + 1 < nk) {
+      uint8_t* nx = smem + 2 * (cur ^ 1) * G_SLICE_BYTES;
+      store_slice<QA>(nx, vx);
+      store_slice<QW>(nx + G_SLICE_BYTES, vw);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + (int)(wm * 128 + i * 32 + frow);
+    if (row >= M) continue;
+    uint16_t* yr = Y + (int64_t)row * ldy;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + (int)(wn * 128 + j * 32 + 8 * g + 4 * fhalf);
+        const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        if (y_vec && col + 3 < N) {
+          *reinterpret_cast<uint2*>(yr + col) = make_uint2(lo, hi);
+        } else {
+          const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+          for (int e = 0; e < 4; ++e)
+            if (col + e < N) yr[col + e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
+                             int64_t ldy, int M, int N, int K, unsigned flags, hipStream_t s) {
+  const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+  const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
+  const dim3 g(tiles), b(G_THREADS);
+  // 8-byte output stores need 8-byte aligned rows; otherwise the epilogue stores bf16 by bf16
+  const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  if (qa && qw) hipLaunchKernelGGL((k_gemm_mxfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  else if (qa) hipLaunchKernelGGL((k_gemm_mxfp4<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  else if (qw) hipLaunchKernelGGL((k_gemm_mxfp4<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  else hipLaunchKernelGGL((k_gemm_mxfp4<false, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  return hipGetLastError();
+}
+
+}  // namespace qf

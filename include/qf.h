@@ -188,6 +188,30 @@ qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream);
 qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int accumulate,
                           void* stream);
 
+/* ------------------------------------------------- W4A4 MXFP4 GEMM ---- */
+/* Y = QDQ(X) . QDQ(W)^T with fp32 accumulation and one bf16 rounding of Y
+ * ("Overview": weights and optionally activations rounded onto the grid, every
+ * matmul in BF16; "Key findings" 02: MXFP4 trains best with W4A4).
+ *   X  bf16 [M, ldx] (activations, tokens x hidden), W bf16 [N, ldw] (out x in),
+ *   Y  bf16 [M, ldy] output.  QDQ is the MXFP4 rule of qf_qdq_mxfp4 along K,
+ *   applied to X when flags has QF_QDQ_A and to W when flags has QF_QDQ_W;
+ *   flags == 0 is a plain BF16 GEMM.  The QDQ happens on the way into the
+ *   matrix cores: no QDQ'd copy of X or W is written.
+ * Constraints: M, N >= 0 (any value; a zero extent is a no-op), K a positive
+ * multiple of 64 (QF_ERR_SHAPE), ldx, ldw >= K and ldy >= N; X and W 16-byte
+ * aligned with ldx, ldw multiples of 8, Y 2-byte aligned (QF_ERR_ALIGN);
+ * M, N < 2^30.  Output rows are written 8 bytes at a time when ldy is a
+ * multiple of 4 and Y is 8-byte aligned, element by element otherwise.
+ * Accuracy: fp32 accumulation in an unspecified order; every element obeys
+ * |y - y_ref| <= 2^-8 |y_ref| + (1 + 2^-8) gamma_K sum_k |xq_k wq_k|,
+ * gamma_K = K 2^-24 / (1 - K 2^-24), against the exact product of the QDQ'd
+ * operands. */
+#define QF_QDQ_A 1u
+#define QF_QDQ_W 2u
+qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                        uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                        unsigned flags, void* stream);
+
 /* ---------------------------------------------------- conformance test ---- */
 /* Checks on the device that the gfx950 instructions and shortcuts the kernels
  * rely on agree bit for bit with the software definitions above, over their

@@ -1,0 +1,88 @@
+"""GPU parity of the fused W4A4 MXFP4 GEMM against the float64 oracle.
+
+Y = QDQ(X) . QDQ(W)^T is checked element by element against the per-element bound
+|y - y_ref| <= 2^-8 |y_ref| + (1 + 2^-8) gamma_K sum_k |xq_k wq_k| (fp32 accumulation
+in any order plus one bf16 rounding) and in relative Frobenius norm (<= 1e-2), where
+y_ref is the exact float64 product of the oracle's bit-exact MXFP4 QDQ of X and W.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_fake_quant_amd as fq
+import workloads
+from oracle import gemm, mxfp4
+from oracle import primitives as P
+from tests.gpu_util import dev, host, sample_rows
+
+pytestmark = pytest.mark.gpu
+RNG = np.random.default_rng(99)
+
+
+def _check(Y, Xq, Wq, K, what):
+    y_ref = gemm.reference(Xq, Wq)
+    bound = gemm.elementwise_bound(y_ref, gemm.abs_dot(Xq, Wq), K)
+    y = P.bf16_to_f32(Y).astype(np.float64)
+    err = np.abs(y - y_ref)
+    bad = np.argwhere(err > bound)
+    assert bad.size == 0, f"{what}: {bad.shape[0]} elements over the bound, first {tuple(bad[0])}: " \
+                          f"got {y[tuple(bad[0])]} want {y_ref[tuple(bad[0])]} bound {bound[tuple(bad[0])]}"
+    rel = np.linalg.norm(y - y_ref) / max(np.linalg.norm(y_ref), 1e-300)
+    assert rel <= 1e-2, f"{what}: relative Frobenius error {rel}"
+    return rel
+
+
+def _ops(M, N, K, scale_x=0.5, scale_w=0.02):
+    X = P.f32_to_bf16((RNG.standard_t(3, size=(M, K)) * scale_x).astype(np.float32))
+    W = P.f32_to_bf16((RNG.standard_normal((N, K)) * scale_w).astype(np.float32))
+    return X, W
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 64), (300, 200, 128), (33, 517, 192), (1, 1, 64), (513, 257, 256)])
+@pytest.mark.parametrize("flags", [3, 1, 2, 0])
+def test_gemm_small_shapes(shape, flags):
+    M, N, K = shape
+    X, W = _ops(M, N, K)
+    Y = fq.qf_gemm_mxfp4(dev(X), dev(W), flags=flags)
+    Xq = mxfp4.qdq(X) if flags & 1 else X
+    Wq = mxfp4.qdq(W) if flags & 2 else W
+    _check(host(Y), Xq, Wq, K, f"{shape} flags={flags}")
+
+
+def test_gemm_strided_operands_and_output():
+    M, N, K = 320, 288, 192
+    X, W = _ops(M, N, K)
+    Xb = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    Xb[:, 32:32 + K] = dev(X)
+    Wb = torch.zeros((N, K + 128), dtype=torch.bfloat16, device="cuda")
+    Wb[:, :K] = dev(W)
+    Yb = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device="cuda")
+    fq.qf_gemm_mxfp4(Xb[:, 32:32 + K], Wb[:, :K], Yb[:, 8:8 + N])
+    _check(host(Yb[:, 8:8 + N]), mxfp4.qdq(X), mxfp4.qdq(W), K, "strided")
+    assert torch.all(Yb[:, :8] == 7.0) and torch.all(Yb[:, 8 + N:] == 7.0)
+
+
+def test_gemm_outlier_columns_and_zero_rows():
+    M, N, K = 256, 256, 256
+    X, W = _ops(M, N, K)
+    X[:, 5] = P.f32_to_bf16(np.full(M, 300.0, np.float32))     # an outlier channel
+    X[7] = 0
+    X[9] = 0x8000
+    W[3] = 0
+    Y = fq.qf_gemm_mxfp4(dev(X), dev(W))
+    _check(host(Y), mxfp4.qdq(X), mxfp4.qdq(W), K, "outliers")
+    assert np.all(P.bf16_to_f32(host(Y))[7] == 0) and np.all(P.bf16_to_f32(host(Y))[:, 3] == 0)
+
+
+def test_gemm_w4a4_full_size_sampled():
+    """The 32768 x 14336 x 4096 workload in the launch the benchmark times; the oracle
+    checks 64 sampled rows x 64 sampled columns (plus the first and last of each)."""
+    g = workloads.w4a4_gemm()
+    X, W = g["X"], g["W"]
+    Y = fq.qf_gemm_mxfp4(dev(X), dev(W))
+    rows = sample_rows(X.shape[0], 64, seed=1)
+    cols = sample_rows(W.shape[0], 64, seed=2)
+    Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    rel = _check(Ys, mxfp4.qdq(X[rows]), mxfp4.qdq(W[cols]), X.shape[1], "full size")
+    assert rel < 2e-3
