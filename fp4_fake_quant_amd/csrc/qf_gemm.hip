@@ -69,31 +69,24 @@ __device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
   return o;
 }
 
-// Loads this lane's 8 chunks of a 256 x 64 slice (rows r0.., K offset k0).  Rows past
-// `rows` read as zero.
-__device__ __forceinline__ void load_slice(uint4 (&v)[G_LOADS], const uint16_t* __restrict__ p, int64_t ld,
-                                           int r0, int rows, int k0) {
-  const uint32_t t = threadIdx.x;
-  const uint32_t c = t & 7u;
-#pragma unroll
-  for (int i = 0; i < G_LOADS; ++i) {
-    const int r = r0 + (int)(t >> 3) + 32 * i;
-    v[i] = make_uint4(0, 0, 0, 0);
-    if (r < rows) v[i] = *reinterpret_cast<const uint4*>(p + (int64_t)r * ld + k0 + c * 8);
-  }
+// Buffer resource over the `rows_left` (<= 256) rows of a tile starting at p: loads past
+// the last row come back as zero, which is how partial tiles are handled.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* p, int64_t ld, int rows_left) {
+  const int rows = rows_left < GBM ? rows_left : GBM;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, (short)0, (int)((int64_t)rows * ld * 2), 0x00020000);
+}
+
+__device__ __forceinline__ uint4 load_chunk_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
 template <bool QDQ>
-__device__ __forceinline__ void store_slice(uint8_t* lds, const uint4 (&v)[G_LOADS]) {
-  const uint32_t t = threadIdx.x;
-  const uint32_t c = t & 7u;
-#pragma unroll
-  for (int i = 0; i < G_LOADS; ++i) {
-    const uint32_t r = (t >> 3) + 32u * i;
-    const uint4 q = QDQ ? mxfp4_qdq_chunk(v[i]) : v[i];
-    *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = q;
-  }
+__device__ __forceinline__ void store_chunk(uint8_t* lds, uint32_t r, uint32_t c, uint4 v) {
+  const uint4 q = QDQ ? mxfp4_qdq_chunk(v) : v;
+  *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = q;
 }
+
+#define QF_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <bool QA, bool QW>
 __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
@@ -121,6 +114,13 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
   const uint32_t wm = wave >> 1, wn = wave & 1u;          // 2 x 2 waves
   const uint32_t frow = lane & 31u, fhalf = lane >> 5;    // MFMA fragment row, k half
 
+  // global -> register loads: lane t takes chunk (t & 7) of rows (t >> 3) + 32 i
+  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(X + (int64_t)m0 * ldx, ldx, M - m0);
+  const __amdgpu_buffer_rsrc_t rw = tile_rsrc(W + (int64_t)n0 * ldw, ldw, N - n0);
+  const uint32_t lrow = threadIdx.x >> 3, lchunk = threadIdx.x & 7u;
+  const uint32_t xoff = (uint32_t)(lrow * ldx + lchunk * 8) * 2u, xstep = (uint32_t)(32 * ldx) * 2u;
+  const uint32_t woff = (uint32_t)(lrow * ldw + lchunk * 8) * 2u, wstep = (uint32_t)(32 * ldw) * 2u;
+
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -129,41 +129,77 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  uint4 vx[G_LOADS], vw[G_LOADS];
-  load_slice(vx, X, ldx, m0, M, 0);
-  load_slice(vw, W, ldw, n0, N, 0);
-  store_slice<QA>(smem, vx);
-  store_slice<QW>(smem + G_SLICE_BYTES, vw);
-  __syncthreads();
+  // Raw slices live in one register set, chunk by chunk: during K step k, chunk i holds
+  // step k+1's data (loaded during step k-1); right after it is QDQ'd and written to the
+  // other LDS stage, the same registers are refilled with step k+2's chunk i.  Every
+  // global load therefore has a whole K step of MFMA work to arrive in, and the QDQ
+  // arithmetic is spread between the MFMAs.
+  uint4 raw[2 * G_LOADS];                                  // 8 X chunks, then 8 W chunks
+  auto issue_load = [&](int idx, uint32_t kbyte) {
+    if (idx < G_LOADS) raw[idx] = load_chunk_buf(rx, xoff + idx * xstep + kbyte);
+    else raw[idx] = load_chunk_buf(rw, woff + (idx - G_LOADS) * wstep + kbyte);
+  };
+  auto stage_chunk = [&](int idx, uint8_t* stage) {
+    if (idx < G_LOADS) store_chunk<QA>(stage, lrow + 32 * idx, lchunk, raw[idx]);
+    else store_chunk<QW>(stage + G_SLICE_BYTES, lrow + 32 * (idx - G_LOADS), lchunk, raw[idx]);
+  };
 
   const int nk = K / GBK;
+#pragma unroll
+  for (int idx = 0; idx < 2 * G_LOADS; ++idx) issue_load(idx, 0);
+#pragma unroll
+  for (int idx = 0; idx < 2 * G_LOADS; ++idx) {
+    stage_chunk(idx, smem);
+    issue_load(idx, (uint32_t)min(1, nk - 1) * GBK * 2u);
+  }
+  __syncthreads();
+
+  // fragments of substep s: fx[i] = X rows wm*128 + 32i + frow, fw[j] = W rows wn*128 + 32j + frow,
+  // k chunk 2s + fhalf; two register sets, so substep s+1's fragments load during substep s
+  bf16x8_t fx[2][4], fw[2][4];
+  auto read_x = [&](int set, const uint8_t* base, int s, int i) {
+    fx[set][i] = *reinterpret_cast<const bf16x8_t*>(base + lds_off(wm * 128 + i * 32 + frow, 2u * s + fhalf));
+  };
+  auto read_w = [&](int set, const uint8_t* base, int s, int j) {
+    fw[set][j] = *reinterpret_cast<const bf16x8_t*>(base + G_SLICE_BYTES + lds_off(wn * 128 + j * 32 + frow, 2u * s + fhalf));
+  };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) read_x(0, smem, 0, i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) read_w(0, smem, 0, j);
+
+  // The loop body has no branches, so the wait for chunk i's load can be exact (the 15
+  // loads issued after it may stay in flight): the last two steps reload the last K
+  // slice instead of skipping the load, and the last step stages into the idle LDS
+  // stage, which nothing reads afterwards.
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
-    if (ks + 1 < nk) {
-      load_slice(vx, X, ldx, m0, M, (ks + 1) * GBK);
-      load_slice(vw, W, ldw, n0, N, (ks + 1) * GBK);
-    }
-    const uint8_t* ax = smem + 2 * cur * G_SLICE_BYTES;
-    const uint8_t* aw = ax + G_SLICE_BYTES;
+    const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
+    uint8_t* next = smem + 2 * (cur ^ 1) * G_SLICE_BYTES;
+    const uint32_t kb2 = (uint32_t)min(ks + 2, nk - 1) * GBK * 2u;
 #pragma unroll
     for (int s = 0; s < GBK / 16; ++s) {
-      const uint32_t c = 2u * s + fhalf;
-      bf16x8_t fx[4], fw[4];
+      const int fs = s & 1;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fx[i] = *reinterpret_cast<const bf16x8_t*>(ax + lds_off(wm * 128 + i * 32 + frow, c));
+      for (int q = 0; q < 4; ++q) {
+        const int item = 4 * s + q;                         // 0..15
 #pragma unroll
-      for (int j = 0; j < 4; ++j) fw[j] = *reinterpret_cast<const bf16x8_t*>(aw + lds_off(wn * 128 + j * 32 + frow, c));
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[j], fx[i], acc[i][j], 0, 0, 0);
-    }
-    if (ks + 1 < nk) {
-      uint8_t* nx = smem + 2 * (cur ^ 1) * G_SLICE_BYTES;
-      store_slice<QA>(nx, vx);
-      store_slice<QW>(nx + G_SLICE_BYTES, vw);
+        for (int j = 0; j < 4; ++j)
+          acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fs][j], fx[fs][q], acc[q][j], 0, 0, 0);
+        if (s < 3) {
+          if (q < 2) { read_x(fs ^ 1, base, s + 1, 2 * q); read_x(fs ^ 1, base, s + 1, 2 * q + 1); }
+          else { read_w(fs ^ 1, base, s + 1, 2 * q - 4); read_w(fs ^ 1, base, s + 1, 2 * q - 3); }
+        }
+        stage_chunk(item, next);                            // step ks+1's chunk (loaded during ks-1)
+        issue_load(item, kb2);                              // step ks+2's chunk
+        QF_FENCE();
+      }
     }
     __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) read_x(0, next, 0, i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) read_w(0, next, 0, j);
   }
 
   // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
