@@ -44,18 +44,26 @@ constexpr int G_SLICE_BYTES = GBM * GBK * 2;           // one operand slice in L
 constexpr int G_LOADS = GBM * G_CHUNKS / G_THREADS;    // chunks per lane per operand per K step (8)
 constexpr int G_GROUP_M = 8;                           // tile rows per group of the tile order
 
-// LDS byte offset of chunk c of row r in a slice: chunks XOR-swizzled by (r & 7).
+// LDS byte offset of chunk c of row r in a slice (rows of 128 bytes).  Chunks are
+// XOR-swizzled with f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), which takes 8 distinct values
+// on any 8 consecutive rows and, on 16 consecutive rows, 8 distinct values on each row
+// parity: a 16-byte-per-lane fragment read (one chunk of 32 consecutive rows) then hits
+// distinct banks whether the LDS serves 8 or 16 lanes of it per cycle.
 __device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
-  return (r * G_CHUNKS + (c ^ (r & 7u))) * 16u;
+  const uint32_t f = ((r >> 1) & 7u) ^ ((r & 1u) << 2);
+  return (r * G_CHUNKS + (c ^ f)) * 16u;
 }
 
 // MXFP4 QDQ of one 16-byte chunk; lanes 4i..4i+3 hold one 32-element block.
+// The scale operand carries E in its exponent field: E = max(floor(log2 amax) - 2 + 127, 0)
+// is the block maximum's bf16 exponent field minus 2, clamped at 0 (a saturating
+// subtract on the field moved to bits 23..30).
 __device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
   uint32_t m = amax_bits8(w);
   m = umax(m, dpp_xor1(m));
   m = umax(m, dpp_xor2(m));
-  const int ef = (int)(m >> 7);
-  const float sc = __uint_as_float((uint32_t)(ef > 2 ? ef - 2 : 0) << 23);
+  const uint32_t ebits = __builtin_elementwise_sub_sat((m << 16) & 0x7F800000u, 0x01000000u);
+  const float sc = __uint_as_float(ebits);
   uint32_t codes = 0;
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.y), sc, 1);
@@ -145,12 +153,20 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
   };
 
   const int nk = K / GBK;
+  // Chunks are staged and reloaded in "slot" order: slot j (0..11) handles chunk j, and
+  // slots 0..3 also chunk j + 12.  The prologue uses the same order as the loop, so the
+  // loads pending at the loop head are the same on entry and on the back edge and every
+  // wait counts exactly the loads issued after the one it needs.
 #pragma unroll
   for (int idx = 0; idx < 2 * G_LOADS; ++idx) issue_load(idx, 0);
+  const uint32_t kb1 = (uint32_t)min(1, nk - 1) * GBK * 2u;
 #pragma unroll
-  for (int idx = 0; idx < 2 * G_LOADS; ++idx) {
-    stage_chunk(idx, smem);
-    issue_load(idx, (uint32_t)min(1, nk - 1) * GBK * 2u);
+  for (int slot = 0; slot < 12; ++slot) {
+    stage_chunk(slot, smem);
+    if (slot < 4) stage_chunk(slot + 12, smem);
+    issue_load(slot, kb1);
+    if (slot < 4) issue_load(slot + 12, kb1);
+    QF_FENCE();
   }
   __syncthreads();
 
@@ -171,7 +187,9 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
   // The loop body has no branches, so the wait for chunk i's load can be exact (the 15
   // loads issued after it may stay in flight): the last two steps reload the last K
   // slice instead of skipping the load, and the last step stages into the idle LDS
-  // stage, which nothing reads afterwards.
+  // stage, which nothing reads afterwards.  The 16 chunks are staged during substeps
+  // 0-2 (two independent chunks in the first four slots), so the step's barrier can sit
+  // before substep 3 and the next step's first fragments load under its MFMAs.
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
     const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
@@ -180,26 +198,29 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
 #pragma unroll
     for (int s = 0; s < GBK / 16; ++s) {
       const int fs = s & 1;
+      if (s == 3) {
+        __syncthreads();                                    // step ks+1's slice is in `next`
+      }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int item = 4 * s + q;                         // 0..15
+        const int slot = 4 * s + q;                         // 0..15
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fs][j], fx[fs][q], acc[q][j], 0, 0, 0);
         if (s < 3) {
           if (q < 2) { read_x(fs ^ 1, base, s + 1, 2 * q); read_x(fs ^ 1, base, s + 1, 2 * q + 1); }
           else { read_w(fs ^ 1, base, s + 1, 2 * q - 4); read_w(fs ^ 1, base, s + 1, 2 * q - 3); }
+          stage_chunk(slot, next);                          // step ks+1's chunks (loaded during ks-1)
+          if (slot < 4) stage_chunk(slot + 12, next);
+          issue_load(slot, kb2);                            // step ks+2's chunks
+          if (slot < 4) issue_load(slot + 12, kb2);
+        } else {
+          if (q < 2) { read_x(0, next, 0, 2 * q); read_x(0, next, 0, 2 * q + 1); }
+          else { read_w(0, next, 0, 2 * q - 4); read_w(0, next, 0, 2 * q - 3); }
         }
-        stage_chunk(item, next);                            // step ks+1's chunk (loaded during ks-1)
-        issue_load(item, kb2);                              // step ks+2's chunk
         QF_FENCE();
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) read_x(0, next, 0, i);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) read_w(0, next, 0, j);
   }
 
   // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
