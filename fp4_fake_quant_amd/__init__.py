@@ -13,7 +13,7 @@ import ctypes
 
 import torch
 
-from ._lib import TensorDesc, lib
+from ._lib import LoraDesc, TensorDesc, lib
 
 QF_OK = 0
 QF_QDQ_A, QF_QDQ_W = 1, 2
@@ -219,6 +219,63 @@ def qf_ste_backward(g_q, g_latent=None, accumulate=False):
         raise ValueError("g_latent must be a contiguous float32 tensor with g_q's element count")
     _check(lib().qf_ste_backward(_p(g_q), _p(g_latent), g_q.numel(), int(bool(accumulate)), _stream()), "qf_ste_backward")
     return g_latent
+
+
+# ---------------------------------------------------------------- LoRA ----
+def _lora_descs(items):
+    """items: list of dict(W, A, B, M, group, y=None, codes=None, scales=None, G=None, dA=None, dB=None)."""
+    arr = (LoraDesc * max(len(items), 1))()
+    for i, it in enumerate(items):
+        W = _bf16(it["W"], "W")
+        rows, cols, ldw = _mat(W, "W")
+        A, B = _bf16(it["A"], "A"), _bf16(it["B"], "B")
+        if A.dim() != 2 or B.dim() != 2 or not A.is_contiguous() or not B.is_contiguous():
+            raise ValueError("A [r, cols] and B [rows, r] must be contiguous 2-D tensors")
+        r = A.shape[0]
+        if A.shape[1] != cols or B.shape != (rows, r):
+            raise ValueError(f"adapter shapes {tuple(A.shape)}, {tuple(B.shape)} do not fit W {rows}x{cols}")
+        d = arr[i]
+        d.W, d.rows, d.cols, d.ldw = W.data_ptr(), rows, cols, ldw
+        d.A, d.B, d.r, d.group = A.data_ptr(), B.data_ptr(), r, int(it.get("group", 0))
+        for name in ("M", "y", "codes", "scales", "G", "dA", "dB"):
+            t = it.get(name)
+            if t is not None and not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            setattr(d, name, t.data_ptr() if t is not None else None)
+    return arr, len(items)
+
+
+def qf_lora_workspace(items):
+    arr, n = _lora_descs(items)
+    return lib().qf_lora_workspace(ctypes.byref(arr), n)
+
+
+def qf_lora_merge_tensor_scale_nvfp4(items, n_groups, d_scales=None, d_nonfinite=None, ws=None):
+    arr, n = _lora_descs(items)
+    dev = items[0]["W"].device
+    need = lib().qf_lora_workspace(ctypes.byref(arr), n)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    if d_scales is None:
+        d_scales = torch.empty(n_groups, dtype=torch.float32, device=dev)
+    _check(lib().qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(arr), n, n_groups, _p(d_scales), _p(d_nonfinite),
+                                                   _p(ws), ws.numel() * ws.element_size(), _stream()),
+           "qf_lora_merge_tensor_scale_nvfp4")
+    return d_scales
+
+
+def qf_lora_qdq_pack_nvfp4(items, d_scales):
+    arr, n = _lora_descs(items)
+    _check(lib().qf_lora_qdq_pack_nvfp4(ctypes.byref(arr), n, _p(d_scales), _stream()), "qf_lora_qdq_pack_nvfp4")
+
+
+def qf_lora_adapter_grads(items, accumulate=False, ws=None):
+    arr, n = _lora_descs(items)
+    need = lib().qf_lora_workspace(ctypes.byref(arr), n)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=items[0]["W"].device)
+    _check(lib().qf_lora_adapter_grads(ctypes.byref(arr), n, int(bool(accumulate)), _p(ws),
+                                       ws.numel() * ws.element_size(), _stream()), "qf_lora_adapter_grads")
 
 
 # ---------------------------------------------------------------- GEMM ----

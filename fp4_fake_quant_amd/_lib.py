@@ -29,6 +29,18 @@ class TensorDesc(ctypes.Structure):
     ]
 
 
+class LoraDesc(ctypes.Structure):
+    """Mirror of qf_lora_desc in include/qf.h."""
+    _fields_ = [
+        ("W", c_void_p),
+        ("rows", c_i64), ("cols", c_i64), ("ldw", c_i64),
+        ("A", c_void_p), ("B", c_void_p),
+        ("r", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("M", c_void_p), ("y", c_void_p), ("codes", c_void_p), ("scales", c_void_p),
+        ("G", c_void_p), ("dA", c_void_p), ("dB", c_void_p),
+    ]
+
+
 # name -> (restype, argtypes); every entry point declared in include/qf.h
 SIGNATURES = {
     "qf_version": (c_u32, []),
@@ -52,6 +64,10 @@ SIGNATURES = {
     "qf_qdq_pack_q4k_grouped": (c_int, [c_void_p, c_int, c_void_p]),
     "qf_ste_backward": (c_int, [c_void_p, c_void_p, c_i64, c_int, c_void_p]),
     "qf_selftest_conversions": (c_int, [c_void_p, c_void_p]),
+    "qf_lora_workspace": (c_size_t, [c_void_p, c_int]),
+    "qf_lora_merge_tensor_scale_nvfp4": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qf_lora_qdq_pack_nvfp4": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
+    "qf_lora_adapter_grads": (c_int, [c_void_p, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "qf_gemm_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint, c_void_p]),
 }
 

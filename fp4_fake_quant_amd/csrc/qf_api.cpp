@@ -298,6 +298,152 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
   return hip_status(qf::launch_ste(g_q, g_latent, n, accumulate != 0, (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------------ LoRA --
+namespace {
+
+qf_status check_lora(const qf_lora_desc& d) {
+  if (d.rows < 0 || d.cols < 0) return QF_ERR_SHAPE;
+  if (d.rows == 0 || d.cols == 0) return QF_OK;
+  if (d.cols % 32 != 0 || d.cols > QF_LORA_MAX_COLS || d.ldw < d.cols) return QF_ERR_SHAPE;
+  if (d.r < 1 || d.r > qf::LORA_MAX_R) return QF_ERR_ARG;
+  if (d.group < 0) return QF_ERR_ARG;
+  if ((uint64_t)d.rows * (uint64_t)(d.cols / 8) >= (1ull << 32)) return QF_ERR_SHAPE;
+  return QF_OK;
+}
+
+struct LoraCounts {
+  int64_t merge_wg = 0, dB_waves = 0, dA_wg = 0, dA_part = 0;
+};
+
+int64_t slabs_of(int64_t cols) { return (cols + qf::LORA_SLAB - 1) / qf::LORA_SLAB; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Fills a (when given) and returns the launch sizes of a descriptor list.
+LoraCounts lora_layout(const qf_lora_desc* d, int n, qf::LoraArgs* a, float* dA_part) {
+  LoraCounts c;
+  if (a) memset(a, 0, sizeof(*a));
+  int k = 0, groups = 0;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].rows <= 0 || d[i].cols <= 0) continue;
+    const int64_t slabs = slabs_of(d[i].cols);
+    const int64_t mu = ceil_div(d[i].rows, qf::LORA_ROWS) * slabs;
+    const int64_t dblk = ceil_div(d[i].rows, qf::LORA_DA_ROWS);
+    const int64_t du = dblk * slabs;
+    if (a) {
+      qf::LoraTensor& t = a->d[k];
+      t.W = d[i].W; t.A = d[i].A; t.B = d[i].B; t.M = d[i].M; t.G = d[i].G;
+      t.dA = d[i].dA; t.dB = d[i].dB;
+      t.dA_partial = dA_part ? dA_part + c.dA_part : nullptr;
+      t.rows = d[i].rows; t.cols = d[i].cols; t.ldw = d[i].ldw;
+      t.r = d[i].r; t.group = d[i].group;
+      t.slabs = (int32_t)slabs;
+      t.merge_units = (int32_t)mu; t.merge_wg_begin = (int32_t)c.merge_wg;
+      t.dB_wave_begin = (int32_t)c.dB_waves;
+      t.dA_units = (int32_t)du; t.dA_wg_begin = (int32_t)c.dA_wg;
+    }
+    ++k;
+    if (d[i].group + 1 > groups) groups = d[i].group + 1;
+    c.merge_wg += ceil_div(mu, 4);
+    c.dB_waves += ceil_div(d[i].rows, 16);
+    c.dA_wg += ceil_div(du, 4);
+    c.dA_part += dblk * qf::LORA_MAX_R * d[i].cols;
+  }
+  if (a) {
+    a->n = k;
+    a->n_groups = groups;
+  }
+  return c;
+}
+
+int lora_groups(const qf_lora_desc* d, int n) {
+  int g = 0;
+  for (int i = 0; i < n; ++i)
+    if (d[i].rows > 0 && d[i].cols > 0 && d[i].group + 1 > g) g = d[i].group + 1;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qf_lora_workspace(const qf_lora_desc* d, int n) {
+  if (n < 0 || n > QF_MAX_GROUPED || (n > 0 && !d)) return 0;
+  for (int i = 0; i < n; ++i)
+    if (check_lora(d[i]) != QF_OK) return 0;
+  const LoraCounts c = lora_layout(d, n, nullptr, nullptr);
+  const int64_t merge_words = c.merge_wg * lora_groups(d, n);
+  const int64_t words = merge_words > c.dA_part ? merge_words : c.dA_part;
+  return (size_t)(words > 0 ? words : 1) * 4;
+}
+
+qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
+                                           uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0 || n > QF_MAX_GROUPED || n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
+  if ((n > 0 && !d) || !d_scales) return QF_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const qf_status st = check_lora(d[i]);
+    if (st != QF_OK) return st;
+    if (d[i].rows == 0 || d[i].cols == 0) continue;
+    if (d[i].group >= n_groups) return QF_ERR_ARG;
+    if (!d[i].W || !d[i].A || !d[i].B || !d[i].M) return QF_ERR_NULL;
+    if (!aligned(d[i].W, 16) || !aligned(d[i].A, 16) || !aligned(d[i].B, 4) || !aligned(d[i].M, 16) || d[i].ldw % 8)
+      return QF_ERR_ALIGN;
+  }
+  if (!ws || ws_bytes < qf_lora_workspace(d, n)) return QF_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return QF_ERR_ALIGN;
+  qf::LoraArgs a;
+  const LoraCounts c = lora_layout(d, n, &a, nullptr);
+  if (c.merge_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  a.partial = (uint32_t*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = qf::launch_lora_merge(a, (int)c.merge_wg, s);
+  if (e != hipSuccess) return hip_status(e);
+  qf::ReduceArgs r;
+  r.n_groups = n_groups;
+  r.n_partial_groups = a.n_groups;
+  r.grid = (int)c.merge_wg;
+  r.partial = (const uint32_t*)ws;
+  r.tscale = d_scales;
+  r.nonfinite = d_nonfinite;
+  return hip_status(qf::launch_nvfp4_scale_reduce(r, s));
+}
+
+qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_scales, void* stream) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n > 0 && !d) return QF_ERR_NULL;
+  qf_tensor_desc t[QF_MAX_GROUPED];
+  for (int i = 0; i < n; ++i) {
+    const qf_status st = check_lora(d[i]);
+    if (st != QF_OK) return st;
+    t[i] = one(d[i].M, d[i].rows, d[i].cols, d[i].cols, d[i].y, d[i].cols, d[i].codes, d[i].scales);
+    t[i].group = d[i].group;
+  }
+  return quant_grouped(QF_FMT_NVFP4, t, n, d_scales, (hipStream_t)stream);
+}
+
+qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n > 0 && !d) return QF_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const qf_status st = check_lora(d[i]);
+    if (st != QF_OK) return st;
+    if (d[i].rows == 0 || d[i].cols == 0) continue;
+    if (!d[i].A || !d[i].B || !d[i].G || !d[i].dA || !d[i].dB) return QF_ERR_NULL;
+    if (!aligned(d[i].A, 16) || !aligned(d[i].B, 4) || !aligned(d[i].G, 16) || !aligned(d[i].dB, 4) ||
+        !aligned(d[i].dA, 4))
+      return QF_ERR_ALIGN;
+  }
+  if (!ws || ws_bytes < qf_lora_workspace(d, n)) return QF_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return QF_ERR_ALIGN;
+  qf::LoraArgs a;
+  const LoraCounts c = lora_layout(d, n, &a, (float*)ws);
+  if (c.dB_waves >= (1ll << 31) || c.dA_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_lora_grads(a, (int)c.dB_waves, (int)c.dA_wg, accumulate != 0, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
 // ------------------------------------------------------------ W4A4 GEMM --
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
                         int64_t M, int64_t N, int64_t K, unsigned flags, void* stream) {

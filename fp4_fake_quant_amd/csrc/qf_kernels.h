@@ -78,6 +78,42 @@ struct ReduceArgs {
   uint32_t* nonfinite;
 };
 
+// ------------------------------------------------------------------ LoRA ---
+constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
+constexpr int LORA_SLAB = 512;      // columns per wave: 64 lanes x 8
+constexpr int LORA_ROWS = 32;       // rows per merge unit
+constexpr int LORA_DA_ROWS = 256;   // rows per dA unit (one partial per unit)
+
+// A unit is one wave's work: a slab of LORA_SLAB columns of a run of rows.  Units
+// of a descriptor are numbered row block major, and every descriptor starts on a
+// fresh workgroup of 4 waves, so a workgroup never mixes descriptors.
+struct LoraTensor {
+  const uint16_t* W;
+  const uint16_t* A;
+  const uint16_t* B;
+  uint16_t* M;
+  const uint16_t* G;
+  float* dA;
+  float* dB;
+  float* dA_partial;   // workspace: [row blocks][LORA_MAX_R][cols]
+  int64_t rows, cols, ldw;
+  int32_t r, group;
+  int32_t slabs;            // ceil(cols / LORA_SLAB)
+  int32_t merge_units, merge_wg_begin;
+  int32_t dB_wave_begin;    // dB: one wave per 16 rows
+  int32_t dA_units, dA_wg_begin;
+};
+
+struct LoraArgs {
+  LoraTensor d[QF_MAX_GROUPED];
+  int n;
+  int n_groups;        // rows of merge partials
+  uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
+};
+
+hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s);
+hipError_t launch_lora_grads(const LoraArgs& a, int dB_waves, int dA_grid, int accumulate, hipStream_t s);
+
 // Workgroups of the amax pass for a launch with `tiles` tiles of 256 * L_AMAX chunks.
 inline int amax_grid(int tiles) { return tiles < AMAX_GRID ? tiles : AMAX_GRID; }
 hipError_t launch_nvfp4_amax(const QArgs& a, hipStream_t s);

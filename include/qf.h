@@ -188,6 +188,67 @@ qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream);
 qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int accumulate,
                           void* stream);
 
+/* ---------------------------------------------- LoRA, one expert at a time */
+/* "Method" section, "Quantization-aware distillation": LoRA keeps one frozen
+ * base W, trains only the adapters A (r x cols) and B (rows x r), and quantizes
+ * the merged weight; MoE models merge and quantize one expert at a time.  With
+ * the identity STE the gradient G of the QDQ'd merged weight gives
+ * dB = G . A^T and dA = B^T . G.
+ *
+ * One descriptor per matrix (an expert's fused gate/up or its down matrix):
+ *   W  bf16 [rows, ldw] frozen base;  A bf16 [r, cols] and B bf16 [rows, r],
+ *      both contiguous;  r in 1..16.
+ *   M  bf16 [rows, cols] contiguous scratch for the merged weight (written by
+ *      pass 1, read by pass 2; one expert's worth is the bounded scratch).
+ *   y, codes, scales  pass-2 outputs as in qf_qdq_pack_nvfp4 (y contiguous,
+ *      ldy = cols; y or codes may be NULL to skip it).
+ *   G  bf16 [rows, cols] contiguous; dA fp32 [r, cols]; dB fp32 [rows, r].
+ *   group  tied-group index for the NVFP4 tensor scale (one per expert per
+ *      fused matrix: experts never share a scale).
+ * Shapes: cols a multiple of 32 and at most QF_LORA_MAX_COLS; rows >= 0; ldw a
+ * multiple of 8.  W, A, M, G 16-byte aligned; B, dA, dB 4-byte aligned; the packed
+ * arrays as in qf_qdq_pack_nvfp4.  With r odd, the row of B that ends the array
+ * may be read as a whole 4-byte word (the 2 bytes after B, never used).
+ * Empty descriptors (rows or cols 0) are skipped.  Errors: QF_ERR_SHAPE for a
+ * shape outside these limits, QF_ERR_ARG for r outside 1..16, a negative group or
+ * one >= n_groups, QF_ERR_NULL / QF_ERR_ALIGN for pointers, QF_ERR_WORKSPACE
+ * when ws is smaller than qf_lora_workspace; nothing is launched then.
+ *
+ * Merge (bit-exact): acc = 0; for k = 0..r-1 in order, acc = fl(acc + B[i,k] A[k,j])
+ * (the products are exact in fp32); M[i,j] = bf16(fl(W[i,j] + acc)); no alpha/r
+ * factor.  Gradients are fp32 sums in an unspecified but fixed order: the same
+ * inputs always give the same bits. */
+#define QF_LORA_MAX_COLS 65536
+
+typedef struct qf_lora_desc {
+  const uint16_t* W;
+  int64_t rows, cols, ldw;
+  const uint16_t* A;
+  const uint16_t* B;
+  int32_t r;
+  int32_t group;
+  uint16_t* M;
+  uint16_t* y;
+  uint8_t* codes;
+  uint8_t* scales;
+  const uint16_t* G;
+  float* dA;
+  float* dB;
+} qf_lora_desc;
+
+/* Device workspace (bytes) the LoRA calls need for these descriptors (0 when a
+ * descriptor is invalid). */
+size_t qf_lora_workspace(const qf_lora_desc* d, int n);
+/* Pass 1: merge into M and the NVFP4 tensor scale of every tied group
+ * (d_scales[g] as in qf_nvfp4_tensor_scale_grouped, computed from M). */
+qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
+                                           uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream);
+/* Pass 2: NVFP4 QDQ + pack of M (exactly qf_qdq_pack_nvfp4 on M with d_scales[group]). */
+qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_scales, void* stream);
+/* STE to the adapters: dB = G . A^T, dA = B^T . G (fp32; accumulate != 0 adds). */
+qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
+                                void* stream);
+
 /* ------------------------------------------------- W4A4 MXFP4 GEMM ---- */
 /* Y = QDQ(X) . QDQ(W)^T with fp32 accumulation and one bf16 rounding of Y
  * ("Overview": weights and optionally activations rounded onto the grid, every

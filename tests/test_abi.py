@@ -92,3 +92,37 @@ def test_validation_of_other_entry_points():
     d[0].group = 3
     assert L.qf_nvfp4_tensor_scale_grouped(ctypes.byref(d), 1, 2, q, None, q, need, None) == 7
     assert L.qf_qdq_pack_mxfp4_grouped(ctypes.byref(d), 17, None) == 7      # too many tensors
+
+
+def test_lora_validation():
+    """LoRA calls check rank, shape, group and workspace before launching."""
+    L = _lib.lib()
+    q = _addr(0x10100000)
+    d = (_lib.LoraDesc * 2)()
+    for i in range(2):
+        d[i].W, d[i].rows, d[i].cols, d[i].ldw = 0x10000000, 100, 1056, 1056
+        d[i].A, d[i].B, d[i].r, d[i].group = 0x10200000, 0x10300000, 16, i
+        d[i].M, d[i].G, d[i].dA, d[i].dB = 0x10400000, 0x10500000, 0x10600000, 0x10700000
+    need = L.qf_lora_workspace(ctypes.byref(d), 2)
+    assert need > 0 and need % 4 == 0
+    # merge partials: ceil(ceil(100/32) * 3 slabs / 4) = 3 workgroups per matrix, 2 groups
+    # dA partials: 1 row block x 16 x 1056 per matrix
+    assert need == 4 * max(6 * 2, 2 * 16 * 1056)
+    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need - 4, None) == 4
+    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 1, q, None, q, need, None) == 7   # group 1 >= 1
+    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, None, 0, None) == 4
+    d[1].r = 17
+    assert L.qf_lora_workspace(ctypes.byref(d), 2) == 0
+    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need, None) == 7
+    d[1].r = 16
+    d[1].cols = d[1].ldw = 1048                                     # not a multiple of 32
+    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 2
+    d[1].cols = d[1].ldw = 1056
+    d[1].B = 0x10300002                                             # B must be 4-byte aligned
+    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 3
+    d[1].B = 0x10300000
+    d[0].M = 0
+    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need, None) == 1
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 17, q, None) == 7
+    d[0].rows = d[1].rows = 0                                       # empty: nothing to do
+    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, 4, None) == 0

@@ -1,0 +1,180 @@
+"""GPU parity: LoRA merge-then-quantize per MoE expert and the adapter gradients.
+
+The merged weight M, the tied NVFP4 tensor scales, the QDQ'd values, the packed
+codes and the block scales are compared with the oracle bit for bit.  The fp32
+adapter gradients are compared with the float64 reference within Higham's bound
+for fp32 sums in any order (Accuracy and Stability of Numerical Algorithms,
+sec. 3.1): |g - g_ref| <= gamma_n * sum |products| with n the number of terms.
+Cases: ragged shapes (rows not a multiple of the 32-row unit, a partial last
+512-column slab), strided W, odd rank (B rows starting on odd elements), rank 1,
+several descriptors in one launch with shared and separate tied groups, the
+accumulate flag, and one full-size MoE expert (gate/up 3072x3072 and down
+3072x1536, rank 16).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_fake_quant_amd as fq
+import workloads
+from oracle import lora, nvfp4
+from oracle import primitives as P
+from oracle.gemm import gamma
+from tests.gpu_util import dev, host, u8, f32bits, first_mismatch, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(x):
+    return P.f32_to_bf16(np.asarray(x, np.float32))
+
+
+def assert_same(got, want, what):
+    assert np.array_equal(got, want), f"{what}: {first_mismatch(got, want)}"
+
+
+def make_case(rows, cols, r, seed, w_scale=0.02, a_scale=0.01, b_scale=0.001):
+    rng = np.random.default_rng(seed)
+    return dict(
+        W=_bits(rng.standard_normal((rows, cols)) * w_scale),
+        A=_bits(rng.standard_normal((r, cols)) * a_scale),
+        B=_bits(rng.standard_normal((rows, r)) * b_scale),
+        G=_bits(rng.standard_normal((rows, cols))),
+    )
+
+
+def device_item(c, group, ldw_pad=0):
+    rows, cols = c["W"].shape
+    r = c["A"].shape[0]
+    if ldw_pad:
+        Wfull = torch.zeros((rows, cols + ldw_pad), dtype=torch.bfloat16, device="cuda")
+        Wfull[:, :cols] = dev(c["W"])
+        W = Wfull[:, :cols]
+    else:
+        W = dev(c["W"])
+    return dict(
+        W=W, A=dev(c["A"]), B=dev(c["B"]), G=dev(c["G"]), group=group,
+        M=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"),
+        y=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda"),
+        codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+        scales=torch.empty((rows, cols // 16), dtype=torch.uint8, device="cuda"),
+        dA=torch.empty((r, cols), dtype=torch.float32, device="cuda"),
+        dB=torch.empty((rows, r), dtype=torch.float32, device="cuda"),
+    )
+
+
+def check_grads(c, dA, dB, what, extra_terms=0):
+    dA_ref, dB_ref = lora.adapter_grads(c["G"], c["A"], c["B"])
+    G = np.abs(P.bf16_to_f32(c["G"]).astype(np.float64))
+    A = np.abs(P.bf16_to_f32(c["A"]).astype(np.float64))
+    B = np.abs(P.bf16_to_f32(c["B"]).astype(np.float64))
+    rows, cols = G.shape
+    # dB sums cols products per entry, dA rows products (plus the partial sums)
+    bound_dB = gamma(cols) * (G @ A.T)
+    bound_dA = gamma(rows + extra_terms + 16) * (B.T @ G)
+    errB = np.abs(dB.astype(np.float64) - dB_ref)
+    errA = np.abs(dA.astype(np.float64) - dA_ref)
+    assert np.all(errB <= bound_dB), f"{what} dB: worst excess {np.max(errB - bound_dB):.3e}"
+    assert np.all(errA <= bound_dA), f"{what} dA: worst excess {np.max(errA - bound_dA):.3e}"
+
+
+def run_merge_quant(items, n_groups):
+    scales = fq.qf_lora_merge_tensor_scale_nvfp4(items, n_groups)
+    fq.qf_lora_qdq_pack_nvfp4(items, scales)
+    torch.cuda.synchronize()
+    return scales.cpu().numpy()
+
+
+def check_merge_quant(cases, groups, items, s_got, n_groups):
+    Ms = [lora.merge(c["W"], c["A"], c["B"]) for c in cases]
+    for i, (M, it) in enumerate(zip(Ms, items)):
+        assert_same(host(it["M"]), M, f"M[{i}]")
+    s_want = []
+    for g in range(n_groups):
+        members = [M for M, gg in zip(Ms, groups) if gg == g]
+        s_want.append(nvfp4.tensor_scale(members) if members else np.float32(1.0))
+    assert_same(f32bits(s_got), f32bits(s_want), "tensor scales")
+    for i, (M, it, g) in enumerate(zip(Ms, items, groups)):
+        c, S = nvfp4.quantize(M, s_want[g])
+        pc, ps = nvfp4.pack(c, S)
+        assert_same(host(it["y"]), nvfp4.dequantize(c, S, s_want[g]), f"y[{i}]")
+        assert_same(u8(it["codes"]), pc, f"codes[{i}]")
+        assert_same(u8(it["scales"]), ps, f"block scales[{i}]")
+
+
+@pytest.mark.parametrize("rows,cols,r", [(100, 1056, 16), (37, 544, 7), (64, 32, 1), (33, 512, 16)])
+def test_lora_single_descriptor(rows, cols, r):
+    c = make_case(rows, cols, r, seed=rows * 7 + r)
+    it = device_item(c, 0)
+    s = run_merge_quant([it], 1)
+    check_merge_quant([c], [0], [it], s, 1)
+    fq.qf_lora_adapter_grads([it])
+    torch.cuda.synchronize()
+    check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"{rows}x{cols} r{r}")
+
+
+def test_lora_grouped_strided_and_large_adapters():
+    """Four descriptors in one launch, groups [0, 1, 0, 2], strided W, adapters big enough
+    that the B.A term moves most bf16 values."""
+    shapes = [(96, 1024, 16), (70, 608, 5), (129, 1056, 16), (16, 64, 3)]
+    cases = [make_case(r_, c_, k_, seed=11 + i, a_scale=0.1, b_scale=0.1) for i, (r_, c_, k_) in enumerate(shapes)]
+    groups = [0, 1, 0, 2]
+    items = [device_item(c, g, ldw_pad=(64 if i == 2 else 0)) for i, (c, g) in enumerate(zip(cases, groups))]
+    s = run_merge_quant(items, 4)                                 # group 3 has no member: scale 1
+    check_merge_quant(cases, groups, items, s, 4)
+    fq.qf_lora_adapter_grads(items)
+    torch.cuda.synchronize()
+    for i, (c, it) in enumerate(zip(cases, items)):
+        check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"desc {i}")
+
+
+def test_lora_zero_adapter_is_identity():
+    """B = 0 gives M = W bit for bit, so the result is the plain NVFP4 QDQ of W."""
+    c = make_case(64, 512, 16, seed=5)
+    c["B"] = np.zeros_like(c["B"])
+    it = device_item(c, 0)
+    s = run_merge_quant([it], 1)
+    assert_same(host(it["M"]), c["W"], "M == W")
+    y_plain = fq.qf_qdq_nvfp4(dev(c["W"]), torch.from_numpy(s).cuda())
+    torch.cuda.synchronize()
+    assert_same(host(it["y"]), host(y_plain), "y == plain NVFP4 QDQ")
+
+
+def test_lora_accumulate_adds():
+    c = make_case(80, 544, 16, seed=9)
+    it = device_item(c, 0)
+    fq.qf_lora_adapter_grads([it])
+    dA1, dB1 = it["dA"].clone(), it["dB"].clone()
+    fq.qf_lora_adapter_grads([it], accumulate=True)
+    torch.cuda.synchronize()
+    assert_same(f32bits(it["dA"].cpu().numpy()), f32bits((dA1 + dA1).cpu().numpy()), "dA accumulate")
+    assert_same(f32bits(it["dB"].cpu().numpy()), f32bits((dB1 + dB1).cpu().numpy()), "dB accumulate")
+
+
+def test_lora_full_size_expert():
+    """One MoE expert at its real shape: both fused matrices in one launch, each its own group."""
+    e = workloads.moe_expert(3)
+    cases, items = [], []
+    for g, name in enumerate(("gate_up", "down")):
+        W, A, B, G = e[name]
+        c = dict(W=W, A=A, B=B, G=G)
+        cases.append(c)
+        items.append(device_item(c, g))
+    s = run_merge_quant(items, 2)
+    Ms = [lora.merge(c["W"], c["A"], c["B"]) for c in cases]
+    for i, (M, it) in enumerate(zip(Ms, items)):
+        assert_same(host(it["M"]), M, f"M[{i}]")
+    s_want = [nvfp4.tensor_scale([M]) for M in Ms]
+    assert_same(f32bits(s), f32bits(s_want), "tensor scales")
+    for i, (M, it) in enumerate(zip(Ms, items)):
+        rows_ = sample_rows(M.shape[0], 48, seed=i)
+        c, S = nvfp4.quantize(M[rows_], s_want[i])
+        pc, ps = nvfp4.pack(c, S)
+        assert_same(host(it["y"])[rows_], nvfp4.dequantize(c, S, s_want[i]), f"y[{i}] sampled rows")
+        assert_same(u8(it["codes"])[rows_], pc, f"codes[{i}] sampled rows")
+        assert_same(u8(it["scales"])[rows_], ps, f"block scales[{i}] sampled rows")
+    fq.qf_lora_adapter_grads(items)
+    torch.cuda.synchronize()
+    for i, (c, it) in enumerate(zip(cases, items)):
+        check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"expert 3 matrix {i}")
