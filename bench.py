@@ -111,6 +111,10 @@ def pmc_summary(fetch_dir, write_dir, workload):
 
 
 # ------------------------------------------------------------ workloads ----
+def _no_mark(kernel, edge):
+    pass
+
+
 class DenseLayerNVFP4:
     name = "dense_layer_8b_nvfp4_w4a16"
 
@@ -161,9 +165,9 @@ class DenseLayerNVFP4:
             "tied_groups": len(self.names),
         }
 
-    def step(self, ev=None):
+    def step(self, mark=None):
         fq = self.fq
-        t = (lambda k, i: ev[k][i].record()) if ev is not None else (lambda k, i: None)
+        t = mark or _no_mark
         t("nvfp4_amax", 0)
         fq.qf_nvfp4_tensor_scale_grouped(self.amax_items, len(self.names), self.scales, None, self.ws)
         t("nvfp4_amax", 1)
@@ -225,12 +229,11 @@ class Q4KSet:
         self.config = {"workload": self.name, "matrices": {k: list(v.shape) for k, v in self.T.items()},
                        "elements": n, "format": "Q4_K (INT4, 32-blocks in 256 super-blocks, 6-bit scales/mins, FP16 d/dmin)"}
 
-    def step(self, ev=None):
-        if ev is not None:
-            ev["q4k_qdq_pack"][0].record()
+    def step(self, mark=None):
+        t = mark or _no_mark
+        t("q4k_qdq_pack", 0)
         self.fq.qf_qdq_pack_q4k_grouped(self.items)
-        if ev is not None:
-            ev["q4k_qdq_pack"][1].record()
+        t("q4k_qdq_pack", 1)
 
     def cpu_baseline(self, budget_s=10.0):
         import numpy as np
@@ -271,12 +274,11 @@ class MXFP4Operands:
         self.config = {"workload": self.name, "matrices": {"X": [32768, 4096], "W": [14336, 4096]}, "elements": n,
                        "format": "MXFP4 (E2M1, block 32, E8M0)"}
 
-    def step(self, ev=None):
-        if ev is not None:
-            ev["mxfp4_qdq_pack"][0].record()
+    def step(self, mark=None):
+        t = mark or _no_mark
+        t("mxfp4_qdq_pack", 0)
         self.fq.qf_qdq_pack_mxfp4_grouped(self.items)
-        if ev is not None:
-            ev["mxfp4_qdq_pack"][1].record()
+        t("mxfp4_qdq_pack", 1)
 
 
 class Single256x512:
@@ -310,9 +312,9 @@ class Single256x512:
         self.bytes_per_step = sum(self.kernels.values())
         self.config = {"workload": self.name, "matrices": {"W": [256, 512]}, "elements": n}
 
-    def step(self, ev=None):
+    def step(self, mark=None):
         fq = self.fq
-        t = (lambda k, i: ev[k][i].record()) if ev is not None else (lambda k, i: None)
+        t = mark or _no_mark
         t("nvfp4_tensor_scale", 0)
         fq.qf_nvfp4_tensor_scale(self.W, self.sc, None, self.ws)
         t("nvfp4_tensor_scale", 1)
@@ -354,12 +356,11 @@ class W4A4GemmMXFP4:
         self.config = {"workload": self.name, "M": self.M, "N": self.N, "K": self.K,
                        "format": "MXFP4 W4A4 (E2M1, block 32, E8M0), BF16 MFMA, fp32 accumulate, bf16 out"}
 
-    def step(self, ev=None):
-        if ev is not None:
-            ev["gemm_mxfp4_fused"][0].record()
+    def step(self, mark=None):
+        t = mark or _no_mark
+        t("gemm_mxfp4_fused", 0)
         self.fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=3)
-        if ev is not None:
-            ev["gemm_mxfp4_fused"][1].record()
+        t("gemm_mxfp4_fused", 1)
 
     def controls(self, reps=10):
         """ms of the plain-BF16 run of the same kernel and of torch.matmul."""
@@ -382,9 +383,126 @@ class W4A4GemmMXFP4:
         return out
 
 
-WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4)}
+class MoELoRANVFP4:
+    """MoE layer share with LoRA: 128 experts, each with a fused gate/up 3072x3072 and a
+    down 3072x1536 bf16 base weight and rank-16 adapters.  Per expert, in expert order:
+      1. merge M = W + B.A into a bounded scratch and the NVFP4 tensor scale of each
+         fused matrix (one tied group per expert per matrix),
+      2. NVFP4 QDQ + pack of M (QDQ'd bf16 into scratch; packed codes and E4M3 block
+         scales of every expert are kept),
+      3. the adapter gradients dA = B^T.G, dB = G.A^T from the upstream gradient G of
+         the QDQ'd weight (identity STE).
+    `experts_per_launch` experts share one launch of each call; the scratch holds that
+    many experts' merged and QDQ'd weights."""
+    name = "moe_lora_nvfp4"
+
+    def __init__(self, torch, fq, experts_per_launch=1):
+        import workloads
+        self.torch, self.fq = torch, fq
+        mo = workloads.MOE
+        E, r = mo["experts"], mo["rank"]
+        k = experts_per_launch
+        assert E % k == 0 and 2 * k <= 16
+        x = workloads.moe_experts_device(seed=0)
+        dev = torch.device("cuda")
+        mats = ("gate_up", "down")
+        self.x = x
+        scratch = {m: (torch.empty((k,) + tuple(x[m]["W"].shape[1:]), dtype=torch.bfloat16, device=dev),
+                       torch.empty((k,) + tuple(x[m]["W"].shape[1:]), dtype=torch.bfloat16, device=dev)) for m in mats}
+        self.scratch = scratch
+        self.codes, self.scl, self.dA, self.dB = {}, {}, {}, {}
+        for m in mats:
+            _, rows, cols = x[m]["W"].shape
+            self.codes[m] = torch.empty((E, rows, cols // 2), dtype=torch.uint8, device=dev)
+            self.scl[m] = torch.empty((E, rows, cols // 16), dtype=torch.uint8, device=dev)
+            self.dA[m] = torch.empty((E, r, cols), dtype=torch.float32, device=dev)
+            self.dB[m] = torch.empty((E, rows, r), dtype=torch.float32, device=dev)
+        self.tscale = torch.empty(2 * E, dtype=torch.float32, device=dev)
+        self.chunks = []
+        for c0 in range(0, E, k):
+            items = []
+            for e in range(c0, c0 + k):
+                for j, m in enumerate(mats):
+                    items.append(dict(W=x[m]["W"][e], A=x[m]["A"][e], B=x[m]["B"][e], G=x[m]["G"][e],
+                                      M=scratch[m][0][e - c0], y=scratch[m][1][e - c0],
+                                      codes=self.codes[m][e], scales=self.scl[m][e],
+                                      dA=self.dA[m][e], dB=self.dB[m][e], group=2 * (e - c0) + j))
+            self.chunks.append((fq.LoraBatch(items), self.tscale[2 * c0: 2 * (c0 + k)]))
+        self.ws = torch.empty(self.chunks[0][0].workspace_bytes, dtype=torch.uint8, device=dev)
+        n = sum(x[m]["W"].numel() for m in mats)
+        adapters = sum(x[m]["A"].numel() + x[m]["B"].numel() for m in mats)
+        self.numel = n
+        # algorithmic bytes: pass 1 reads W and the adapters, writes the merged bf16 weight
+        # to scratch; pass 2 reads it back, writes the QDQ'd bf16 + E2M1 codes (0.5 B) + E4M3
+        # scales (1/16 B); the gradients read G and the adapters and write fp32 dA, dB
+        self.kernels = {
+            "lora_merge_amax": n * 4 + adapters * 2,
+            "lora_qdq_pack": n * (2 + 2 + 0.5 + 1 / 16),
+            "lora_adapter_grads": n * 2 + adapters * (2 + 4),
+        }
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {"workload": self.name,
+                       "experts": E, "matrices_per_expert": {m: list(x[m]["W"].shape[1:]) for m in mats},
+                       "rank": r, "elements": n, "experts_per_launch": k,
+                       "scratch_bytes": sum(t.numel() * 2 for p in scratch.values() for t in p),
+                       "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale per expert per fused matrix)"}
+
+    def step(self, mark=None):
+        fq, ws = self.fq, self.ws
+        t = mark or _no_mark
+        for items, sc in self.chunks:
+            t("lora_merge_amax", 0)
+            fq.qf_lora_merge_tensor_scale_nvfp4(items, items.n, sc, None, ws)
+            t("lora_merge_amax", 1)
+            t("lora_qdq_pack", 0)
+            fq.qf_lora_qdq_pack_nvfp4(items, sc)
+            t("lora_qdq_pack", 1)
+            t("lora_adapter_grads", 0)
+            fq.qf_lora_adapter_grads(items, ws=ws)
+            t("lora_adapter_grads", 1)
+
+    def cpu_baseline(self, budget_s=15.0):
+        """The oracle's merge + tensor scale + NVFP4 QDQ + pack + adapter gradients on the first
+        rows of expert 0's two matrices (host-drawn with the same recipe)."""
+        import workloads
+        from oracle import lora, nvfp4
+        e0 = workloads.moe_expert(0)
+
+        def run(rows):
+            t0 = time.perf_counter()
+            nb = 0.0
+            for m in ("gate_up", "down"):
+                W, A, B, G = e0[m]
+                M = lora.merge(W[:rows], A, B[:rows])
+                s_t = nvfp4.tensor_scale([M])
+                c, S = nvfp4.quantize(M, s_t)
+                nvfp4.dequantize(c, S, s_t)
+                nvfp4.pack(c, S)
+                lora.adapter_grads(G[:rows], A, B[:rows])
+                nb += M.size * (4 + 4.5625 + 2)
+            return time.perf_counter() - t0, nb
+
+        dt, _ = run(16)
+        rows = max(16, min(3072, int(16 * budget_s / max(dt, 1e-3))))
+        dt, nb = run(rows)
+        return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the oracle's merge + tensor scale + QDQ + pack + adapter gradients on the first {rows} "
+                          f"rows of expert 0's gate/up and down matrices ({dt:.1f} s, numpy)"}
+
+
+class MoELoRANVFP4x8(MoELoRANVFP4):
+    """The same step with 8 experts per launch (scratch of 8 experts)."""
+    name = "moe_lora_nvfp4_x8"
+
+    def __init__(self, torch, fq):
+        super().__init__(torch, fq, experts_per_launch=8)
+
+
+WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4,
+                                 MoELoRANVFP4, MoELoRANVFP4x8)}
 # measured next to the headline workload in a default run (fewer steps each)
-SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name]
+SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
+             MoELoRANVFP4x8.name]
 
 
 def measure(torch, wl, steps, warmup):
@@ -397,18 +515,25 @@ def measure(torch, wl, steps, warmup):
         wl.step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
-    # per-kernel durations: the same steps again with a HIP event pair around every kernel
+    # per-kernel durations: the same steps again with a HIP event pair around every launch
     # (events add a few microseconds between kernels, so they stay out of the headline
     # loop); the events sit on torch's current stream, where the library launches
-    ev = {k: [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)] for k in wl.kernels}
-    for i in range(steps):
-        wl.step({k: ev[k][i] for k in wl.kernels})
+    pairs = {k: [] for k in wl.kernels}
+
+    def mark(kernel, edge):
+        if edge == 0:
+            pairs[kernel].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+        pairs[kernel][-1][edge].record()
+
+    for _ in range(steps):
+        wl.step(mark)
     torch.cuda.synchronize()
     kern = {}
     for k, nbytes in wl.kernels.items():
-        ms = sum(ev[k][i][0].elapsed_time(ev[k][i][1]) for i in range(steps)) / steps
+        ms = sum(a.elapsed_time(b) for a, b in pairs[k]) / steps
         kern[k] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
-                   "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes)}
+                   "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes),
+                   "launches_per_step": len(pairs[k]) // steps}
     return ms_per_step, kern
 
 

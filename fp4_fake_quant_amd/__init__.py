@@ -222,59 +222,75 @@ def qf_ste_backward(g_q, g_latent=None, accumulate=False):
 
 
 # ---------------------------------------------------------------- LoRA ----
-def _lora_descs(items):
-    """items: list of dict(W, A, B, M, group, y=None, codes=None, scales=None, G=None, dA=None, dB=None)."""
-    arr = (LoraDesc * max(len(items), 1))()
-    for i, it in enumerate(items):
-        W = _bf16(it["W"], "W")
-        rows, cols, ldw = _mat(W, "W")
-        A, B = _bf16(it["A"], "A"), _bf16(it["B"], "B")
-        if A.dim() != 2 or B.dim() != 2 or not A.is_contiguous() or not B.is_contiguous():
-            raise ValueError("A [r, cols] and B [rows, r] must be contiguous 2-D tensors")
-        r = A.shape[0]
-        if A.shape[1] != cols or B.shape != (rows, r):
-            raise ValueError(f"adapter shapes {tuple(A.shape)}, {tuple(B.shape)} do not fit W {rows}x{cols}")
-        d = arr[i]
-        d.W, d.rows, d.cols, d.ldw = W.data_ptr(), rows, cols, ldw
-        d.A, d.B, d.r, d.group = A.data_ptr(), B.data_ptr(), r, int(it.get("group", 0))
-        for name in ("M", "y", "codes", "scales", "G", "dA", "dB"):
-            t = it.get(name)
-            if t is not None and not t.is_contiguous():
-                raise ValueError(f"{name} must be contiguous")
-            setattr(d, name, t.data_ptr() if t is not None else None)
-    return arr, len(items)
+class LoraBatch:
+    """Descriptor array for the qf_lora_* calls, built once and reusable.
+
+    items: list of dict(W, A, B, group, M=None, y=None, codes=None, scales=None,
+    G=None, dA=None, dB=None) of device tensors; W [rows, cols] bf16 with contiguous
+    rows, A [r, cols] and B [rows, r] contiguous bf16.  The tensors must stay alive
+    (and keep their storage) while the batch is used.
+    """
+
+    def __init__(self, items):
+        self.items = items
+        self.arr = (LoraDesc * max(len(items), 1))()
+        self.n = len(items)
+        self.device = items[0]["W"].device if items else torch.device("cuda")
+        for i, it in enumerate(items):
+            W = _bf16(it["W"], "W")
+            rows, cols, ldw = _mat(W, "W")
+            A, B = _bf16(it["A"], "A"), _bf16(it["B"], "B")
+            if A.dim() != 2 or B.dim() != 2 or not A.is_contiguous() or not B.is_contiguous():
+                raise ValueError("A [r, cols] and B [rows, r] must be contiguous 2-D tensors")
+            r = A.shape[0]
+            if A.shape[1] != cols or tuple(B.shape) != (rows, r):
+                raise ValueError(f"adapter shapes {tuple(A.shape)}, {tuple(B.shape)} do not fit W {rows}x{cols}")
+            d = self.arr[i]
+            d.W, d.rows, d.cols, d.ldw = W.data_ptr(), rows, cols, ldw
+            d.A, d.B, d.r, d.group = A.data_ptr(), B.data_ptr(), r, int(it.get("group", 0))
+            for name in ("M", "y", "codes", "scales", "G", "dA", "dB"):
+                t = it.get(name)
+                if t is not None and not t.is_contiguous():
+                    raise ValueError(f"{name} must be contiguous")
+                setattr(d, name, t.data_ptr() if t is not None else None)
+        self.ref = ctypes.byref(self.arr)
+        self.workspace_bytes = lib().qf_lora_workspace(self.ref, self.n)
+
+
+def _batch(items):
+    return items if isinstance(items, LoraBatch) else LoraBatch(items)
+
+
+def _lora_ws(b, ws):
+    if ws is None:
+        ws = torch.empty(max(b.workspace_bytes, 4), dtype=torch.uint8, device=b.device)
+    return ws
 
 
 def qf_lora_workspace(items):
-    arr, n = _lora_descs(items)
-    return lib().qf_lora_workspace(ctypes.byref(arr), n)
+    return _batch(items).workspace_bytes
 
 
 def qf_lora_merge_tensor_scale_nvfp4(items, n_groups, d_scales=None, d_nonfinite=None, ws=None):
-    arr, n = _lora_descs(items)
-    dev = items[0]["W"].device
-    need = lib().qf_lora_workspace(ctypes.byref(arr), n)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    b = _batch(items)
+    ws = _lora_ws(b, ws)
     if d_scales is None:
-        d_scales = torch.empty(n_groups, dtype=torch.float32, device=dev)
-    _check(lib().qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(arr), n, n_groups, _p(d_scales), _p(d_nonfinite),
+        d_scales = torch.empty(n_groups, dtype=torch.float32, device=b.device)
+    _check(lib().qf_lora_merge_tensor_scale_nvfp4(b.ref, b.n, n_groups, _p(d_scales), _p(d_nonfinite),
                                                    _p(ws), ws.numel() * ws.element_size(), _stream()),
            "qf_lora_merge_tensor_scale_nvfp4")
     return d_scales
 
 
 def qf_lora_qdq_pack_nvfp4(items, d_scales):
-    arr, n = _lora_descs(items)
-    _check(lib().qf_lora_qdq_pack_nvfp4(ctypes.byref(arr), n, _p(d_scales), _stream()), "qf_lora_qdq_pack_nvfp4")
+    b = _batch(items)
+    _check(lib().qf_lora_qdq_pack_nvfp4(b.ref, b.n, _p(d_scales), _stream()), "qf_lora_qdq_pack_nvfp4")
 
 
 def qf_lora_adapter_grads(items, accumulate=False, ws=None):
-    arr, n = _lora_descs(items)
-    need = lib().qf_lora_workspace(ctypes.byref(arr), n)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=items[0]["W"].device)
-    _check(lib().qf_lora_adapter_grads(ctypes.byref(arr), n, int(bool(accumulate)), _p(ws),
+    b = _batch(items)
+    ws = _lora_ws(b, ws)
+    _check(lib().qf_lora_adapter_grads(b.ref, b.n, int(bool(accumulate)), _p(ws),
                                        ws.numel() * ws.element_size(), _stream()), "qf_lora_adapter_grads")
 
 

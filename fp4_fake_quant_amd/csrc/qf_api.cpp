@@ -344,8 +344,8 @@ LoraCounts lora_layout(const qf_lora_desc* d, int n, qf::LoraArgs* a, float* dA_
     ++k;
     if (d[i].group + 1 > groups) groups = d[i].group + 1;
     c.merge_wg += ceil_div(mu, 4);
-    c.dB_waves += ceil_div(d[i].rows, 16);
-    c.dA_wg += ceil_div(du, 4);
+    c.dB_waves += ceil_div(d[i].rows, qf::LORA_DB_ROWS);
+    c.dA_wg += du;
     c.dA_part += dblk * qf::LORA_MAX_R * d[i].cols;
   }
   if (a) {

@@ -25,6 +25,24 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
+// ------------------------------------------------------- buffer access ----
+// Raw buffer loads and stores with the hardware range check: an access whose byte
+// offset is at or past the resource's size reads 0 and writes nothing.  Offsets of
+// BUF_OOR or more are always out of range (sizes stay below 2^31 bytes).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr uint32_t BUF_OOR = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void* p, int64_t bytes) {
+  // word 3: 32-bit data format, as plain dword loads and stores need
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, 0);
+}
+
 // ----------------------------------------------------------------- bf16 ----
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }

@@ -82,7 +82,11 @@ struct ReduceArgs {
 constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
 constexpr int LORA_SLAB = 512;      // columns per wave: 64 lanes x 8
 constexpr int LORA_ROWS = 32;       // rows per merge unit
-constexpr int LORA_DA_ROWS = 256;   // rows per dA unit (one partial per unit)
+constexpr int LORA_DA_ROWS = 256;   // rows per dA workgroup (one partial per workgroup)
+#ifndef QF_LORA_DB_ROWS
+#define QF_LORA_DB_ROWS 16
+#endif
+constexpr int LORA_DB_ROWS = QF_LORA_DB_ROWS;   // rows per dB wave (a multiple of 16)
 
 // A unit is one wave's work: a slab of LORA_SLAB columns of a run of rows.  Units
 // of a descriptor are numbered row block major, and every descriptor starts on a
@@ -100,8 +104,8 @@ struct LoraTensor {
   int32_t r, group;
   int32_t slabs;            // ceil(cols / LORA_SLAB)
   int32_t merge_units, merge_wg_begin;
-  int32_t dB_wave_begin;    // dB: one wave per 16 rows
-  int32_t dA_units, dA_wg_begin;
+  int32_t dB_wave_begin;    // dB: one wave per LORA_DB_ROWS rows
+  int32_t dA_units, dA_wg_begin;   // dA: one workgroup per unit
 };
 
 struct LoraArgs {

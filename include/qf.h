@@ -217,7 +217,7 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
  * Merge (bit-exact): acc = 0; for k = 0..r-1 in order, acc = fl(acc + B[i,k] A[k,j])
  * (the products are exact in fp32); M[i,j] = bf16(fl(W[i,j] + acc)); no alpha/r
  * factor.  Gradients are fp32 sums in an unspecified but fixed order: the same
- * inputs always give the same bits. */
+ * inputs always give the same bits; with non-finite inputs they are unspecified. */
 #define QF_LORA_MAX_COLS 65536
 
 typedef struct qf_lora_desc {
