@@ -9,9 +9,11 @@
 // rounded to bf16 (RNE) once.
 //
 // Structure:
-//   - a workgroup of 256 lanes (4 waves, 2 x 2) owns a 256 x 256 tile of Y;
-//     each wave a 128 x 128 sub-tile = 4 x 4 v_mfma_f32_32x32x16_bf16 tiles
-//     (256 fp32 accumulators per lane);
+//   - a workgroup of 512 lanes (8 waves, 2 per SIMD, laid out 2 x 4) owns a 256 x 256
+//     tile of Y; each wave a 128 (X rows) x 64 (W rows) sub-tile = 4 x 2
+//     v_mfma_f32_32x32x16_bf16 tiles (128 fp32 accumulators per lane).  Two waves per
+//     SIMD let the hardware issue one wave's QDQ arithmetic, LDS traffic and waits
+//     while the other's MFMAs run (7% faster than 4 waves of 128 x 128);
 //   - K advances 64 at a time through two LDS stages of X and W slices
 //     (2 x 64 KiB).  16-byte chunks are XOR-swizzled by row so that the MFMA
 //     fragment reads (32 rows x 16 bytes per half-wave) hit distinct banks;
@@ -38,10 +40,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int GBM = 256, GBN = 256, GBK = 64;
-constexpr int G_THREADS = 256;
+constexpr int G_THREADS = 512;
 constexpr int G_CHUNKS = GBK / 8;                      // 16-byte chunks per row of a K slice
 constexpr int G_SLICE_BYTES = GBM * GBK * 2;           // one operand slice in LDS
-constexpr int G_LOADS = GBM * G_CHUNKS / G_THREADS;    // chunks per lane per operand per K step (8)
+constexpr int G_LOADS = GBM * G_CHUNKS / G_THREADS;    // chunks per lane per operand per K step (4)
 constexpr int G_GROUP_M = 8;                           // tile rows per group of the tile order
 
 // LDS byte offset of chunk c of row r in a slice (rows of 128 bytes).  Chunks are
@@ -97,12 +99,11 @@ __device__ __forceinline__ void store_chunk(uint8_t* lds, uint32_t r, uint32_t c
 #define QF_FENCE() __builtin_amdgcn_sched_barrier(0)
 
 template <bool QA, bool QW>
-__global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
-                                                             const uint16_t* __restrict__ W, int64_t ldw,
-                                                             uint16_t* __restrict__ Y, int64_t ldy,
-                                                             int M, int N, int K, int y_vec) {
+__global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
+                                                            const uint16_t* __restrict__ W, int64_t ldw,
+                                                            uint16_t* __restrict__ Y, int64_t ldy,
+                                                            int M, int N, int K, int y_vec) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];   // 128 KiB of the 160 KiB
-  // stage b holds the X slice at smem + 2b * G_SLICE_BYTES and the W slice right after it
 
   // ---- tile of this workgroup (XCD-aware grouped order) ----
   const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
@@ -118,78 +119,68 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
   const int m0 = tm * GBM, n0 = tn * GBN;
 
   const uint32_t lane = threadIdx.x & 63u;
-  const uint32_t wave = threadIdx.x >> 6;
-  const uint32_t wm = wave >> 1, wn = wave & 1u;          // 2 x 2 waves
-  const uint32_t frow = lane & 31u, fhalf = lane >> 5;    // MFMA fragment row, k half
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wm = wave >> 2, wn = wave & 3u;           // 2 x 4 waves: X rows wm*128, W rows wn*64
+  const uint32_t frow = lane & 31u, fhalf = lane >> 5;     // MFMA fragment row, k half
 
-  // global -> register loads: lane t takes chunk (t & 7) of rows (t >> 3) + 32 i
+  // global -> register loads: lane t takes chunk (t & 7) of rows (t >> 3) + 64 i
   const __amdgpu_buffer_rsrc_t rx = tile_rsrc(X + (int64_t)m0 * ldx, ldx, M - m0);
   const __amdgpu_buffer_rsrc_t rw = tile_rsrc(W + (int64_t)n0 * ldw, ldw, N - n0);
   const uint32_t lrow = threadIdx.x >> 3, lchunk = threadIdx.x & 7u;
-  const uint32_t xoff = (uint32_t)(lrow * ldx + lchunk * 8) * 2u, xstep = (uint32_t)(32 * ldx) * 2u;
-  const uint32_t woff = (uint32_t)(lrow * ldw + lchunk * 8) * 2u, wstep = (uint32_t)(32 * ldw) * 2u;
+  const uint32_t xoff = (uint32_t)(lrow * ldx + lchunk * 8) * 2u, xstep = (uint32_t)(64 * ldx) * 2u;
+  const uint32_t woff = (uint32_t)(lrow * ldw + lchunk * 8) * 2u, wstep = (uint32_t)(64 * ldw) * 2u;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  // Raw slices live in one register set, chunk by chunk: during K step k, chunk i holds
-  // step k+1's data (loaded during step k-1); right after it is QDQ'd and written to the
-  // other LDS stage, the same registers are refilled with step k+2's chunk i.  Every
-  // global load therefore has a whole K step of MFMA work to arrive in, and the QDQ
-  // arithmetic is spread between the MFMAs.
-  uint4 raw[2 * G_LOADS];                                  // 8 X chunks, then 8 W chunks
+  uint4 raw[2 * G_LOADS];                                 // 4 X chunks, then 4 W chunks
   auto issue_load = [&](int idx, uint32_t kbyte) {
     if (idx < G_LOADS) raw[idx] = load_chunk_buf(rx, xoff + idx * xstep + kbyte);
     else raw[idx] = load_chunk_buf(rw, woff + (idx - G_LOADS) * wstep + kbyte);
   };
   auto stage_chunk = [&](int idx, uint8_t* stage) {
-    if (idx < G_LOADS) store_chunk<QA>(stage, lrow + 32 * idx, lchunk, raw[idx]);
-    else store_chunk<QW>(stage + G_SLICE_BYTES, lrow + 32 * (idx - G_LOADS), lchunk, raw[idx]);
+    if (idx < G_LOADS) store_chunk<QA>(stage, lrow + 64 * idx, lchunk, raw[idx]);
+    else store_chunk<QW>(stage + G_SLICE_BYTES, lrow + 64 * (idx - G_LOADS), lchunk, raw[idx]);
   };
 
   const int nk = K / GBK;
-  // Chunks are staged and reloaded in "slot" order: slot j (0..11) handles chunk j, and
-  // slots 0..3 also chunk j + 12.  The prologue uses the same order as the loop, so the
-  // loads pending at the loop head are the same on entry and on the back edge and every
-  // wait counts exactly the loads issued after the one it needs.
+  // prologue: step 0's chunks into stage 0, then step 1's chunks into registers, in the
+  // loop's slot order (slot j stages and reloads chunk j)
 #pragma unroll
   for (int idx = 0; idx < 2 * G_LOADS; ++idx) issue_load(idx, 0);
   const uint32_t kb1 = (uint32_t)min(1, nk - 1) * GBK * 2u;
 #pragma unroll
-  for (int slot = 0; slot < 12; ++slot) {
+  for (int slot = 0; slot < 2 * G_LOADS; ++slot) {
     stage_chunk(slot, smem);
-    if (slot < 4) stage_chunk(slot + 12, smem);
     issue_load(slot, kb1);
-    if (slot < 4) issue_load(slot + 12, kb1);
     QF_FENCE();
   }
   __syncthreads();
 
-  // fragments of substep s: fx[i] = X rows wm*128 + 32i + frow, fw[j] = W rows wn*128 + 32j + frow,
+  // fragments of substep s: fx[i] = X rows wm*128 + 32i + frow, fw[j] = W rows wn*64 + 32j + frow,
   // k chunk 2s + fhalf; two register sets, so substep s+1's fragments load during substep s
-  bf16x8_t fx[2][4], fw[2][4];
+  bf16x8_t fx[2][4], fw[2][2];
   auto read_x = [&](int set, const uint8_t* base, int s, int i) {
     fx[set][i] = *reinterpret_cast<const bf16x8_t*>(base + lds_off(wm * 128 + i * 32 + frow, 2u * s + fhalf));
   };
   auto read_w = [&](int set, const uint8_t* base, int s, int j) {
-    fw[set][j] = *reinterpret_cast<const bf16x8_t*>(base + G_SLICE_BYTES + lds_off(wn * 128 + j * 32 + frow, 2u * s + fhalf));
+    fw[set][j] = *reinterpret_cast<const bf16x8_t*>(base + G_SLICE_BYTES + lds_off(wn * 64 + j * 32 + frow, 2u * s + fhalf));
   };
 #pragma unroll
   for (int i = 0; i < 4; ++i) read_x(0, smem, 0, i);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) read_w(0, smem, 0, j);
+  for (int j = 0; j < 2; ++j) read_w(0, smem, 0, j);
 
-  // The loop body has no branches, so the wait for chunk i's load can be exact (the 15
-  // loads issued after it may stay in flight): the last two steps reload the last K
-  // slice instead of skipping the load, and the last step stages into the idle LDS
-  // stage, which nothing reads afterwards.  The 16 chunks are staged during substeps
-  // 0-2 (two independent chunks in the first four slots), so the step's barrier can sit
-  // before substep 3 and the next step's first fragments load under its MFMAs.
+  // Substep s (16 of K) is 8 MFMAs in 4 pairs; pair q of substeps 0-2 also reads
+  // fragments for substep s+1 and stages/reloads chunk slots (3, 3, 2 per substep).
+  // Substep 3 follows the barrier and reads the next step's first fragments.  (Asking
+  // the scheduler for a finer MFMA/VALU interleave with sched_group_barrier measured
+  // 3% slower than these pair-sized groups.)
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
     const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
@@ -198,25 +189,24 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
 #pragma unroll
     for (int s = 0; s < GBK / 16; ++s) {
       const int fs = s & 1;
-      if (s == 3) {
-        __syncthreads();                                    // step ks+1's slice is in `next`
-      }
+      if (s == 3) __syncthreads();                          // step ks+1's slice is in `next`
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int slot = 4 * s + q;                         // 0..15
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
           acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fs][j], fx[fs][q], acc[q][j], 0, 0, 0);
+        const uint8_t* rb = (s < 3) ? base : next;
+        const int rs = (s < 3) ? s + 1 : 0;
+        const int rset = (s < 3) ? (fs ^ 1) : 0;
+        if (q < 2) { read_x(rset, rb, rs, 2 * q); read_x(rset, rb, rs, 2 * q + 1); }
+        else if (q == 2) { read_w(rset, rb, rs, 0); read_w(rset, rb, rs, 1); }
         if (s < 3) {
-          if (q < 2) { read_x(fs ^ 1, base, s + 1, 2 * q); read_x(fs ^ 1, base, s + 1, 2 * q + 1); }
-          else { read_w(fs ^ 1, base, s + 1, 2 * q - 4); read_w(fs ^ 1, base, s + 1, 2 * q - 3); }
-          stage_chunk(slot, next);                          // step ks+1's chunks (loaded during ks-1)
-          if (slot < 4) stage_chunk(slot + 12, next);
-          issue_load(slot, kb2);                            // step ks+2's chunks
-          if (slot < 4) issue_load(slot + 12, kb2);
-        } else {
-          if (q < 2) { read_x(0, next, 0, 2 * q); read_x(0, next, 0, 2 * q + 1); }
-          else { read_w(0, next, 0, 2 * q - 4); read_w(0, next, 0, 2 * q - 3); }
+          // slots: s=0 -> 0,1,2; s=1 -> 3,4,5; s=2 -> 6,7
+          const int slot = 3 * s + q;
+          if (q < 3 && slot < 2 * G_LOADS) {
+            stage_chunk(slot, next);                        // step ks+1's chunk (loaded during ks-1)
+            issue_load(slot, kb2);                          // step ks+2's chunk
+          }
         }
         QF_FENCE();
       }
@@ -230,10 +220,10 @@ __global__ __launch_bounds__(G_THREADS, 1) void k_gemm_mxfp4(const uint16_t* __r
     if (row >= M) continue;
     uint16_t* yr = Y + (int64_t)row * ldy;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = n0 + (int)(wn * 128 + j * 32 + 8 * g + 4 * fhalf);
+        const int col = n0 + (int)(wn * 64 + j * 32 + 8 * g + 4 * fhalf);
         const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
         const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
         if (y_vec && col + 3 < N) {
@@ -252,9 +242,9 @@ hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
                              int64_t ldy, int M, int N, int K, unsigned flags, hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
-  const dim3 g(tiles), b(G_THREADS);
   // 8-byte output stores need 8-byte aligned rows; otherwise the epilogue stores bf16 by bf16
   const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  const dim3 g(tiles), b(G_THREADS);
   if (qa && qw) hipLaunchKernelGGL((k_gemm_mxfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
   else if (qa) hipLaunchKernelGGL((k_gemm_mxfp4<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
   else if (qw) hipLaunchKernelGGL((k_gemm_mxfp4<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
