@@ -333,6 +333,7 @@ class Single256x512:
 
 
 MFMA_BF16_PEAK_TFS = 2516.6     # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (dense)
+MFMA_FP4_PEAK_TFS = 10100.0     # MI355X dense MXFP4 matrix throughput
 
 
 class W4A4GemmMXFP4:
@@ -363,11 +364,19 @@ class W4A4GemmMXFP4:
         t("gemm_mxfp4_fused", 1)
 
     def controls(self, reps=10):
-        """ms of the plain-BF16 run of the same kernel and of torch.matmul."""
+        """ms of the plain-BF16 run of the same kernel, of torch.matmul, and of the same
+        W4A4 product on the MXFP4 matrix cores (both operands quantized in the kernel, and
+        W pre-packed by qf_pack_mxfp4 with X quantized in the kernel; the pack is timed
+        on its own)."""
         torch = self.torch
+        fq = self.fq
         out = {}
-        for name, fn in (("gemm_bf16_same_kernel", lambda: self.fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
-                         ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y))):
+        Wc, Ws = fq.qf_pack_mxfp4(self.W)
+        for name, fn in (("gemm_bf16_same_kernel", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
+                         ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y)),
+                         ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
+                         ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
+                         ("pack_w_mxfp4", lambda: fq.qf_pack_mxfp4(self.W, Wc, Ws))):
             for _ in range(3):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -378,8 +387,13 @@ class W4A4GemmMXFP4:
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            out[name] = {"ms": round(ms, 4), "TFLOP/s": round(self.flop / ms / 1e9, 1),
-                         "frac_mfma": round(self.flop / ms / 1e9 / MFMA_BF16_PEAK_TFS, 4)}
+            if name == "pack_w_mxfp4":
+                out[name] = {"ms": round(ms, 4)}
+                continue
+            tf = self.flop / ms / 1e9
+            out[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)}
+            if "fp4_cores" in name:
+                out[name]["frac_mfma_fp4"] = round(tf / MFMA_FP4_PEAK_TFS, 4)
         return out
 
 
@@ -565,13 +579,24 @@ def main():
 
     ms_per_step, kern = measure(torch, wl, args.steps, args.warmup)
     dom = max(kern, key=lambda k: kern[k]["ms"])
-    achieved = kern[dom]["GB/s"]
-    traffic = traffic_from_profile(f"{wl.name}:{dom}", 1)
-    value = wl.bytes_per_step / (ms_per_step / 1e3) / 1e9
+    gemm = isinstance(wl, W4A4GemmMXFP4)
+    if gemm:
+        # a contraction: TFLOP/s against the dense BF16 MFMA peak
+        achieved = round(wl.flop / kern[dom]["ms"] / 1e9, 1)
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS,
+                    "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
+        value, unit = wl.flop / (ms_per_step / 1e3) / 1e12, "TFLOP/s"
+        for k in kern:
+            kern[k] = {"ms": kern[k]["ms"], "TFLOP/s": achieved, "launches_per_step": kern[k]["launches_per_step"]}
+    else:
+        achieved = kern[dom]["GB/s"]
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_from_profile(f"{wl.name}:{dom}", 1)}
+        value, unit = wl.bytes_per_step / (ms_per_step / 1e3) / 1e9, "GB/s"
     line = {
         "metric": METRIC,
         "value": round(value, 1),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -582,10 +607,11 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": wl.config,
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "roofline": roofline,
         "kernels": kern,
     }
+    if gemm:
+        line["controls"] = wl.controls()
     if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
         line["cpu_baseline"] = wl.cpu_baseline()
     if args.calibrate_copy:

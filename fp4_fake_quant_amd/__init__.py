@@ -16,7 +16,7 @@ import torch
 from ._lib import LoraDesc, TensorDesc, lib
 
 QF_OK = 0
-QF_QDQ_A, QF_QDQ_W = 1, 2
+QF_QDQ_A, QF_QDQ_W, QF_FP4_CORES = 1, 2, 4
 QF_FMT_NVFP4, QF_FMT_MXFP4, QF_FMT_Q4K = 0, 1, 2
 MAX_GROUPED = 16
 BLOCK = {QF_FMT_NVFP4: 16, QF_FMT_MXFP4: 32, QF_FMT_Q4K: 256}
@@ -306,6 +306,23 @@ def qf_gemm_mxfp4(X, W, Y=None, flags=QF_QDQ_A | QF_QDQ_W):
     _bf16(Y, "Y")
     _check(lib().qf_gemm_mxfp4(_p(X), ldx, _p(W), ldw, _p(Y), _mat(Y, "Y")[2], M, N, K, int(flags), _stream()),
            "qf_gemm_mxfp4")
+    return Y
+
+
+def qf_gemm_mxfp4_packed_w(X, Wc, Ws, Y=None):
+    """Y[M, N] = QDQ(X) . dequant(Wc, Ws)^T on the MXFP4 matrix cores; Wc [N, K/2] and
+    Ws [N, K/32] uint8 as qf_pack_mxfp4 writes them (contiguous)."""
+    M, K, ldx = _mat(_bf16(X, "X"), "X")
+    if Wc.dtype != torch.uint8 or Ws.dtype != torch.uint8 or not Wc.is_contiguous() or not Ws.is_contiguous():
+        raise ValueError("Wc and Ws must be contiguous uint8 tensors")
+    N = Wc.shape[0]
+    if tuple(Wc.shape) != (N, K // 2) or tuple(Ws.shape) != (N, K // 32):
+        raise ValueError(f"packed W shapes {tuple(Wc.shape)}, {tuple(Ws.shape)} do not fit K={K}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _bf16(Y, "Y")
+    _check(lib().qf_gemm_mxfp4_packed_w(_p(X), ldx, _p(Wc), _p(Ws), _p(Y), _mat(Y, "Y")[2], M, N, K, _stream()),
+           "qf_gemm_mxfp4_packed_w")
     return Y
 
 

@@ -448,15 +448,33 @@ qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, vo
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
                         int64_t M, int64_t N, int64_t K, unsigned flags, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
-  if (flags & ~(QF_QDQ_A | QF_QDQ_W)) return QF_ERR_ARG;
+  if (flags & ~(QF_QDQ_A | QF_QDQ_W | QF_FP4_CORES)) return QF_ERR_ARG;
+  if ((flags & QF_FP4_CORES) && (flags & (QF_QDQ_A | QF_QDQ_W)) != (QF_QDQ_A | QF_QDQ_W)) return QF_ERR_ARG;
   if (M == 0 || N == 0) return QF_OK;
   if (!X || !W || !Y) return QF_ERR_NULL;
   if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 2) || ldx % 8 || ldw % 8) return QF_ERR_ALIGN;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (flags & QF_FP4_CORES)
+    return hip_status(qf::launch_gemm_mx4(X, ldx, W, ldw, nullptr, nullptr, Y, ldy, (int)M, (int)N, (int)K,
+                                          (hipStream_t)stream));
   return hip_status(qf::launch_gemm_mxfp4(X, ldx, W, ldw, Y, ldy, (int)M, (int)N, (int)K, flags,
                                           (hipStream_t)stream));
+}
+
+qf_status qf_gemm_mxfp4_packed_w(const uint16_t* X, int64_t ldx, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
+                                 int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
+  if (M == 0 || N == 0) return QF_OK;
+  if (!X || !Wc || !Ws || !Y) return QF_ERR_NULL;
+  if (ldx < K || ldy < N) return QF_ERR_SHAPE;
+  if (!aligned(X, 16) || !aligned(Wc, 16) || !aligned(Ws, 2) || !aligned(Y, 2) || ldx % 8) return QF_ERR_ALIGN;
+  if ((N < 256 ? N : 256) * (K / 2) >= (1ll << 31)) return QF_ERR_SHAPE;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_gemm_mx4(X, ldx, nullptr, 0, Wc, Ws, Y, ldy, (int)M, (int)N, (int)K,
+                                        (hipStream_t)stream));
 }
 
 // ------------------------------------------------------ conformance test ---

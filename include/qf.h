@@ -269,9 +269,27 @@ qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, vo
  * operands. */
 #define QF_QDQ_A 1u
 #define QF_QDQ_W 2u
+/* QF_FP4_CORES (with QF_QDQ_A | QF_QDQ_W only, else QF_ERR_ARG): the same product
+ * formed on gfx950's MXFP4 matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4).  Each
+ * QDQ'd MXFP4 value is exactly E2M1(code) * 2^(E - 127), so the cores multiply the
+ * very values the BF16 path multiplies, exactly, and accumulate in fp32: the
+ * accuracy statement above holds unchanged.  The operands are quantized on the
+ * way into LDS (codes and exponents only; nothing is dequantized). */
+#define QF_FP4_CORES 4u
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
                         uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                         unsigned flags, void* stream);
+
+/* Y = QDQ(X) . dequant(Wc, Ws)^T on the MXFP4 matrix cores, with W already in the
+ * packed MXFP4 layout that qf_pack_mxfp4 writes (codes [N][K/2], two per byte,
+ * element 2i in the low nibble; E8M0 exponents [N][K/32]; both contiguous).  X is
+ * quantized on the way into LDS as in qf_gemm_mxfp4.  With Wc, Ws from
+ * qf_pack_mxfp4(W) the result is bit for bit that of qf_gemm_mxfp4(X, W, flags =
+ * QF_QDQ_A | QF_QDQ_W | QF_FP4_CORES) and obeys the same bound.  This is the
+ * deployment form: the engine-layout weights feed the matrix cores directly.
+ * Constraints as qf_gemm_mxfp4; Wc 16-byte aligned, Ws 2-byte aligned. */
+qf_status qf_gemm_mxfp4_packed_w(const uint16_t* X, int64_t ldx, const uint8_t* Wc, const uint8_t* Ws,
+                                 uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream);
 
 /* ---------------------------------------------------- conformance test ---- */
 /* Checks on the device that the gfx950 instructions and shortcuts the kernels

@@ -40,7 +40,7 @@ def _ops(M, N, K, scale_x=0.5, scale_w=0.02):
 
 
 @pytest.mark.parametrize("shape", [(256, 256, 64), (300, 200, 128), (33, 517, 192), (1, 1, 64), (513, 257, 256)])
-@pytest.mark.parametrize("flags", [3, 1, 2, 0])
+@pytest.mark.parametrize("flags", [3, 1, 2, 0, 7])
 def test_gemm_small_shapes(shape, flags):
     M, N, K = shape
     X, W = _ops(M, N, K)
@@ -48,6 +48,19 @@ def test_gemm_small_shapes(shape, flags):
     Xq = mxfp4.qdq(X) if flags & 1 else X
     Wq = mxfp4.qdq(W) if flags & 2 else W
     _check(host(Y), Xq, Wq, K, f"{shape} flags={flags}")
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 64), (300, 200, 128), (33, 517, 192), (513, 257, 256), (64, 96, 320)])
+def test_gemm_packed_w_matches_in_kernel_fp4_path(shape):
+    """W packed by qf_pack_mxfp4 feeds the FP4 cores directly: same bound, and the same
+    bits as quantizing W inside the GEMM (identical operands, identical MFMA order)."""
+    M, N, K = shape
+    X, W = _ops(M, N, K)
+    Wc, Ws = fq.qf_pack_mxfp4(dev(W))
+    Y = fq.qf_gemm_mxfp4_packed_w(dev(X), Wc, Ws)
+    _check(host(Y), mxfp4.qdq(X), mxfp4.qdq(W), K, f"packed W {shape}")
+    Y2 = fq.qf_gemm_mxfp4(dev(X), dev(W), flags=7)
+    assert np.array_equal(host(Y), host(Y2))
 
 
 def test_gemm_strided_operands_and_output():
@@ -58,9 +71,11 @@ def test_gemm_strided_operands_and_output():
     Wb = torch.zeros((N, K + 128), dtype=torch.bfloat16, device="cuda")
     Wb[:, :K] = dev(W)
     Yb = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device="cuda")
-    fq.qf_gemm_mxfp4(Xb[:, 32:32 + K], Wb[:, :K], Yb[:, 8:8 + N])
-    _check(host(Yb[:, 8:8 + N]), mxfp4.qdq(X), mxfp4.qdq(W), K, "strided")
-    assert torch.all(Yb[:, :8] == 7.0) and torch.all(Yb[:, 8 + N:] == 7.0)
+    for flags in (3, 7):
+        Yb.fill_(7.0)
+        fq.qf_gemm_mxfp4(Xb[:, 32:32 + K], Wb[:, :K], Yb[:, 8:8 + N], flags=flags)
+        _check(host(Yb[:, 8:8 + N]), mxfp4.qdq(X), mxfp4.qdq(W), K, f"strided flags={flags}")
+        assert torch.all(Yb[:, :8] == 7.0) and torch.all(Yb[:, 8 + N:] == 7.0)
 
 
 def test_gemm_outlier_columns_and_zero_rows():
@@ -70,9 +85,10 @@ def test_gemm_outlier_columns_and_zero_rows():
     X[7] = 0
     X[9] = 0x8000
     W[3] = 0
-    Y = fq.qf_gemm_mxfp4(dev(X), dev(W))
-    _check(host(Y), mxfp4.qdq(X), mxfp4.qdq(W), K, "outliers")
-    assert np.all(P.bf16_to_f32(host(Y))[7] == 0) and np.all(P.bf16_to_f32(host(Y))[:, 3] == 0)
+    for flags in (3, 7):
+        Y = fq.qf_gemm_mxfp4(dev(X), dev(W), flags=flags)
+        _check(host(Y), mxfp4.qdq(X), mxfp4.qdq(W), K, f"outliers flags={flags}")
+        assert np.all(P.bf16_to_f32(host(Y))[7] == 0) and np.all(P.bf16_to_f32(host(Y))[:, 3] == 0)
 
 
 def test_gemm_w4a4_full_size_sampled():
@@ -80,9 +96,14 @@ def test_gemm_w4a4_full_size_sampled():
     checks 64 sampled rows x 64 sampled columns (plus the first and last of each)."""
     g = workloads.w4a4_gemm()
     X, W = g["X"], g["W"]
-    Y = fq.qf_gemm_mxfp4(dev(X), dev(W))
     rows = sample_rows(X.shape[0], 64, seed=1)
     cols = sample_rows(W.shape[0], 64, seed=2)
-    Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
-    rel = _check(Ys, mxfp4.qdq(X[rows]), mxfp4.qdq(W[cols]), X.shape[1], "full size")
-    assert rel < 2e-3
+    Xq, Wq = mxfp4.qdq(X[rows]), mxfp4.qdq(W[cols])
+    Xd, Wd = dev(X), dev(W)
+    Wc, Ws = fq.qf_pack_mxfp4(Wd)
+    for name, Y in (("bf16 cores", fq.qf_gemm_mxfp4(Xd, Wd)), ("fp4 cores", fq.qf_gemm_mxfp4(Xd, Wd, flags=7)),
+                    ("packed W", fq.qf_gemm_mxfp4_packed_w(Xd, Wc, Ws))):
+        Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+        rel = _check(Ys, Xq, Wq, X.shape[1], f"full size, {name}")
+        assert rel < 2e-3
+        del Y
