@@ -35,9 +35,13 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 METRIC = "QDQ+pack GB/s (% HBM peak) per format; fused W4A4 QDQ-GEMM TFLOP/s (% MFMA)"
 
 
+# sources of the streaming QDQ / pack / STE kernels whose traffic profiles/traffic.json records
+TRAFFIC_SOURCES = ("qf_device.h", "qf_kernels.h", "qf_quant.hip", "qf_api.cpp")
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in sorted(os.listdir(os.path.join(ROOT, "fp4_fake_quant_amd", "csrc"))):
+    for f in TRAFFIC_SOURCES:
         with open(os.path.join(ROOT, "fp4_fake_quant_amd", "csrc", f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]
