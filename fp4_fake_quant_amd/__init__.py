@@ -326,6 +326,23 @@ def qf_gemm_mxfp4_packed_w(X, Wc, Ws, Y=None):
     return Y
 
 
+def qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, Y=None):
+    """Y[M, N] = dequant(Xc, Xs) . dequant(Wc, Ws)^T on the MXFP4 matrix cores; all four
+    arrays uint8 as qf_pack_mxfp4 writes them (contiguous), K a multiple of 128."""
+    for name, t in (("Xc", Xc), ("Xs", Xs), ("Wc", Wc), ("Ws", Ws)):
+        if t.dtype != torch.uint8 or not t.is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D uint8 tensor")
+    M, N, K = Xc.shape[0], Wc.shape[0], Xc.shape[1] * 2
+    if Wc.shape[1] * 2 != K or tuple(Xs.shape) != (M, K // 32) or tuple(Ws.shape) != (N, K // 32):
+        raise ValueError("packed operand shapes do not agree")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=Xc.device)
+    _bf16(Y, "Y")
+    _check(lib().qf_gemm_mxfp4_packed(_p(Xc), _p(Xs), _p(Wc), _p(Ws), _p(Y), _mat(Y, "Y")[2], M, N, K, _stream()),
+           "qf_gemm_mxfp4_packed")
+    return Y
+
+
 def qf_selftest_conversions(device="cuda"):
     counts = torch.zeros(8, dtype=torch.int64, device=device)
     _check(lib().qf_selftest_conversions(_p(counts), _stream()), "qf_selftest_conversions")

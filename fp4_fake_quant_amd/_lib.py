@@ -69,6 +69,7 @@ SIGNATURES = {
     "qf_lora_qdq_pack_nvfp4": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
     "qf_lora_adapter_grads": (c_int, [c_void_p, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "qf_gemm_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint, c_void_p]),
+    "qf_gemm_mxfp4_packed": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p]),
     "qf_gemm_mxfp4_packed_w": (c_int, [c_void_p, c_i64, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p]),
 }
 

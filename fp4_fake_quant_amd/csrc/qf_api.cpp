@@ -463,6 +463,19 @@ qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
                                           (hipStream_t)stream));
 }
 
+qf_status qf_gemm_mxfp4_packed(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
+                               int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
+  if (M == 0 || N == 0) return QF_OK;
+  if (!Xc || !Xs || !Wc || !Ws || !Y) return QF_ERR_NULL;
+  if (ldy < N) return QF_ERR_SHAPE;
+  if (!aligned(Xc, 16) || !aligned(Wc, 16) || !aligned(Xs, 4) || !aligned(Ws, 4) || !aligned(Y, 2)) return QF_ERR_ALIGN;
+  if (256 * (K / 2) >= (1ll << 31)) return QF_ERR_SHAPE;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_gemm_mx4pp(Xc, Xs, Wc, Ws, Y, ldy, (int)M, (int)N, (int)K, (hipStream_t)stream));
+}
+
 qf_status qf_gemm_mxfp4_packed_w(const uint16_t* X, int64_t ldx, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
                                  int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;

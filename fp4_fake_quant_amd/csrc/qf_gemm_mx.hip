@@ -326,6 +326,203 @@ __global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4(const uint16_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Both operands packed (codes [rows][K/2], exponents [rows][K/32], as qf_pack_mxfp4
+// writes them): no arithmetic before the MFMAs at all.  Operands go from memory
+// straight into LDS with buffer loads that write LDS (16 bytes per lane into a
+// 1 KiB window per wave instruction, 4 bytes per lane for the exponents), three
+// steps ahead through a four-stage ring (K = 128 per step, 34 KiB per stage).  Each
+// lane loads the global block that belongs at its place in the window, so the
+// bank-spreading rotation of the code rows costs nothing.  The barrier sits after
+// the first of the step's two MFMA substeps, so the next step's fragments are read
+// while the second substep's MFMAs run.
+constexpr int PP_BK = 128;
+constexpr int PP_STAGES = 4;
+constexpr int PP_AHEAD = PP_STAGES - 1;                   // steps of loads in flight
+constexpr int PP_LOADS = 5;                               // buffer-to-LDS loads per lane per step
+using PPL = MxLayout<PP_BK>;
+
+// s_waitcnt that waits until at most n vector-memory operations are outstanding (the
+// LDS and export counters left at their maximum)
+#define PP_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+// Workgroup barrier for the buffer-to-LDS ring: wait until at most n vector-memory
+// operations (this lane's later steps) are outstanding and all LDS reads are back, then
+// s_barrier.  A __syncthreads() here would wait for every load in flight (the compiler
+// cannot tell that only the oldest step's loads must have landed); the empty asm with a
+// memory clobber keeps the compiler from moving LDS accesses across the barrier.
+#define PP_BARRIER(n)                                                                       \
+  do {                                                                                      \
+    __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (0 << 8));      \
+    __builtin_amdgcn_s_barrier();                                                           \
+    asm volatile("" ::: "memory");                                                          \
+  } while (0)
+
+__global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4pp(const uint8_t* __restrict__ Xc, const uint8_t* __restrict__ Xs,
+                                                           const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
+                                                           uint16_t* __restrict__ Y, int64_t ldy, int M, int N, int K,
+                                                           int y_vec) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[PP_STAGES * PPL::STAGE];   // 136 KiB
+
+  // ---- tile of this workgroup (XCD-aware grouped order) ----
+  const int tiles_m = (M + MX_BM - 1) / MX_BM, tiles_n = (N + MX_BN - 1) / MX_BN;
+  const int total = tiles_m * tiles_n;
+  int t = blockIdx.x;
+  if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
+  const int group = t / (MX_GROUP_M * tiles_n);
+  const int first_m = group * MX_GROUP_M;
+  const int gsize = min(tiles_m - first_m, MX_GROUP_M);
+  const int in_group = t - group * MX_GROUP_M * tiles_n;
+  const int tm = first_m + in_group % gsize;
+  const int tn = in_group / gsize;
+  const int m0 = tm * MX_BM, n0 = tn * MX_BN;
+
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = tid & 63u;
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t wm = wave >> 2, wn = wave & 3u;
+  const uint32_t frow = lane & 31u, fblk = lane >> 5;
+
+  const int64_t kc = K / 2, ks32 = K / 32;
+  const __amdgpu_buffer_rsrc_t rxc = mx_rsrc(Xc + (int64_t)m0 * kc, kc, M - m0);
+  const __amdgpu_buffer_rsrc_t rwc = mx_rsrc(Wc + (int64_t)n0 * kc, kc, N - n0);
+  const __amdgpu_buffer_rsrc_t rxs = mx_rsrc(Xs + (int64_t)m0 * ks32, ks32, M - m0);
+  const __amdgpu_buffer_rsrc_t rws = mx_rsrc(Ws + (int64_t)n0 * ks32, ks32, N - n0);
+  // code windows: wave w fills windows 2w and 2w+1 (16 rows each) of both operands; lane l
+  // of window v holds row 16v + l/4 at slot l%4, which is K block (l%4) ^ rotation(row)
+  uint32_t coff[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t row = 16u * (2u * wave + i) + (lane >> 2);
+    const uint32_t kb = (lane & 3u) ^ ((row >> 2) & 3u);
+    coff[i] = row * (uint32_t)kc + kb * 16u;
+  }
+  // exponent windows: waves 0-3 copy X rows 64w + l, waves 4-7 W rows 64(w-4) + l (4 bytes each)
+  const bool sx_wave = wave < 4;
+  const uint32_t srow = 64u * (wave & 3u) + lane;
+  const uint32_t soff = srow * (uint32_t)ks32;
+
+  typedef __attribute__((address_space(3))) void* lds_ptr_t;
+  auto issue_step = [&](int step) {
+    const int k = min(step, K / PP_BK - 1);               // past the end: reload the last step
+    uint8_t* st = smem + (step % PP_STAGES) * PPL::STAGE;
+    const uint32_t kb = (uint32_t)k * (PP_BK / 2);          // code bytes into the row
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t win = 2u * wave + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rxc, (lds_ptr_t)(st + win * 1024u), 16, coff[i] + kb, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rwc, (lds_ptr_t)(st + PPL::OPER + win * 1024u), 16, coff[i] + kb, 0, 0, 0);
+    }
+    const uint32_t eb = (uint32_t)k * (PP_BK / 32);
+    if (sx_wave)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_ptr_t)(st + PPL::CODES + 256u * wave), 4, soff + eb, 0, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_ptr_t)(st + PPL::OPER + PPL::CODES + 256u * (wave - 4)), 4,
+                                               soff + eb, 0, 0, 0);
+  };
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  i32x4_t fx[2][4], fw[2][2];
+  uint32_t ex[2][4], ew[2][2];                               // exponent words of the step's rows
+  auto read_codes = [&](int set, const uint8_t* st, int sub) {
+    const uint32_t kb = 2u * sub + fblk;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      fx[set][i] = *reinterpret_cast<const i32x4_t*>(st + PPL::off(wm * 128u + 32u * i + frow, kb));
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      fw[set][j] = *reinterpret_cast<const i32x4_t*>(st + PPL::OPER + PPL::off(wn * 64u + 32u * j + frow, kb));
+  };
+  auto read_exps = [&](int set, const uint8_t* st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ex[set][i] = *reinterpret_cast<const uint32_t*>(st + PPL::CODES + (wm * 128u + 32u * i + frow) * 4u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      ew[set][j] = *reinterpret_cast<const uint32_t*>(st + PPL::OPER + PPL::CODES + (wn * 64u + 32u * j + frow) * 4u);
+  };
+
+  const int nk = K / PP_BK;
+  // prologue: steps 0 .. PP_AHEAD-1 in flight, step 0 landed and its first fragments read
+#pragma unroll
+  for (int s = 0; s < PP_AHEAD; ++s) issue_step(s);
+  PP_BARRIER((PP_AHEAD - 1) * PP_LOADS);
+  read_codes(0, smem, 0);
+  read_exps(0, smem);
+
+  // Step k: load step k+3; substep 0 on fragment set 0 while set 1 (substep 1) is read;
+  // wait for step k+1's loads and barrier; substep 1 on set 1 while step k+1's set 0 and
+  // exponents are read.  Exponent sets alternate with steps (unrolled by two).
+#pragma unroll 1
+  for (int k0 = 0; k0 < nk; k0 += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = k0 + h;
+      if (k >= nk) break;
+      const uint8_t* cur = smem + (k % PP_STAGES) * PPL::STAGE;
+      const uint8_t* nxt = smem + ((k + 1) % PP_STAGES) * PPL::STAGE;
+      issue_step(k + PP_AHEAD);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        if (sub == 1) PP_BARRIER((PP_AHEAD - 1) * PP_LOADS);   // step k+1 has landed (k+2, k+3 may fly)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int sh = 8 * (2 * sub) + 8 * (int)fblk;
+            acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                fp4_operand(fw[sub][j]), fp4_operand(fx[sub][q]), acc[q][j], 4, 4, 0, (int)(ew[h][j] >> sh), 0,
+                (int)(ex[h][q] >> sh));
+          }
+          if (q == 0) {
+            if (sub == 0) read_codes(1, cur, 1);
+            else { read_codes(0, nxt, 0); read_exps(h ^ 1, nxt); }
+          }
+          MX_FENCE();
+        }
+      }
+    }
+  }
+  PP_WAIT_VM(0);                                           // no load may still write LDS at exit
+
+  // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fblk + 0..3 ----
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = m0 + (int)(wm * 128 + i * 32 + frow);
+    if (row >= M) continue;
+    uint16_t* yr = Y + (int64_t)row * ldy;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = n0 + (int)(wn * 64 + j * 32 + 8 * g + 4 * fblk);
+        const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        if (y_vec && col + 3 < N) {
+          *reinterpret_cast<uint2*>(yr + col) = make_uint2(lo, hi);
+        } else {
+          const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+          for (int e = 0; e < 4; ++e)
+            if (col + e < N) yr[col + e] = v[e];
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gemm_mx4pp(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
+                             int64_t ldy, int M, int N, int K, hipStream_t s) {
+  const int tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
+  const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  hipLaunchKernelGGL(k_gemm_mx4pp, dim3(tiles), dim3(MX_THREADS), 0, s, Xc, Xs, Wc, Ws, Y, ldy, M, N, K, y_vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_mx4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, const uint8_t* Wc,
                            const uint8_t* Ws, uint16_t* Y, int64_t ldy, int M, int N, int K, hipStream_t s) {
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);

@@ -127,6 +127,8 @@ hipError_t launch_ste(const uint16_t* g, float* out, int64_t n, bool accumulate,
 hipError_t launch_selftest_conversions(unsigned long long* counts, hipStream_t s);
 hipError_t launch_gemm_mx4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, const uint8_t* Wc,
                            const uint8_t* Ws, uint16_t* Y, int64_t ldy, int M, int N, int K, hipStream_t s);
+hipError_t launch_gemm_mx4pp(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
+                             int64_t ldy, int M, int N, int K, hipStream_t s);
 hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
                              int64_t ldy, int M, int N, int K, unsigned flags, hipStream_t s);
 

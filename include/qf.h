@@ -291,6 +291,15 @@ qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
 qf_status qf_gemm_mxfp4_packed_w(const uint16_t* X, int64_t ldx, const uint8_t* Wc, const uint8_t* Ws,
                                  uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Y = dequant(Xc, Xs) . dequant(Wc, Ws)^T on the MXFP4 matrix cores, both operands in
+ * the packed layout of qf_pack_mxfp4 (codes [rows][K/2], exponents [rows][K/32],
+ * contiguous).  With the operands from qf_pack_mxfp4(X) and qf_pack_mxfp4(W) the result
+ * is bit for bit that of qf_gemm_mxfp4_packed_w(X, Wc, Ws) and obeys the same bound.
+ * Constraints: K a positive multiple of 128 (QF_ERR_SHAPE); code arrays 16-byte and
+ * exponent arrays 4-byte aligned (QF_ERR_ALIGN); ldy >= N; M, N < 2^30. */
+qf_status qf_gemm_mxfp4_packed(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws,
+                               uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* ---------------------------------------------------- conformance test ---- */
 /* Checks on the device that the gfx950 instructions and shortcuts the kernels
  * rely on agree bit for bit with the software definitions above, over their

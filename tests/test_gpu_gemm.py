@@ -63,6 +63,20 @@ def test_gemm_packed_w_matches_in_kernel_fp4_path(shape):
     assert np.array_equal(host(Y), host(Y2))
 
 
+@pytest.mark.parametrize("shape", [(256, 256, 128), (300, 200, 256), (33, 517, 384), (513, 257, 512), (1, 1, 128),
+                                   (64, 96, 896)])
+def test_gemm_both_packed_matches_packed_w(shape):
+    """X and W both packed by qf_pack_mxfp4: buffer-to-LDS path, same bound and the same
+    bits as the packed-W path (the same MFMAs in the same K order)."""
+    M, N, K = shape
+    X, W = _ops(M, N, K)
+    Xc, Xs = fq.qf_pack_mxfp4(dev(X))
+    Wc, Ws = fq.qf_pack_mxfp4(dev(W))
+    Y = fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws)
+    _check(host(Y), mxfp4.qdq(X), mxfp4.qdq(W), K, f"both packed {shape}")
+    assert np.array_equal(host(Y), host(fq.qf_gemm_mxfp4_packed_w(dev(X), Wc, Ws)))
+
+
 def test_gemm_strided_operands_and_output():
     M, N, K = 320, 288, 192
     X, W = _ops(M, N, K)
@@ -101,8 +115,10 @@ def test_gemm_w4a4_full_size_sampled():
     Xq, Wq = mxfp4.qdq(X[rows]), mxfp4.qdq(W[cols])
     Xd, Wd = dev(X), dev(W)
     Wc, Ws = fq.qf_pack_mxfp4(Wd)
+    Xc, Xs = fq.qf_pack_mxfp4(Xd)
     for name, Y in (("bf16 cores", fq.qf_gemm_mxfp4(Xd, Wd)), ("fp4 cores", fq.qf_gemm_mxfp4(Xd, Wd, flags=7)),
-                    ("packed W", fq.qf_gemm_mxfp4_packed_w(Xd, Wc, Ws))):
+                    ("packed W", fq.qf_gemm_mxfp4_packed_w(Xd, Wc, Ws)),
+                    ("both packed", fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws))):
         Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
         rel = _check(Ys, Xq, Wq, X.shape[1], f"full size, {name}")
         assert rel < 2e-3
