@@ -71,6 +71,18 @@ __device__ __forceinline__ uint32_t amax_bits8(uint4 w) {
   return m.x > m.y ? m.x : m.y;
 }
 
+// Largest bf16 exponent field of 8 bf16 values, in bits 7..14 of the result: the
+// exponent of max|x| (mantissas and signs masked off before the unsigned max).
+__device__ __forceinline__ uint32_t maxexp_bits8(uint4 w) {
+  const uint32_t M = 0x7F807F80u;
+  u16x2_t a = __builtin_bit_cast(u16x2_t, w.x & M);
+  u16x2_t b = __builtin_bit_cast(u16x2_t, w.y & M);
+  u16x2_t c = __builtin_bit_cast(u16x2_t, w.z & M);
+  u16x2_t d = __builtin_bit_cast(u16x2_t, w.w & M);
+  u16x2_t m = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return m.x > m.y ? m.x : m.y;
+}
+
 // ----------------------------------------------------------------- E4M3 ----
 // E4M3 ("FN": bias 7, max 448, no Inf) code of u >= 0: round to nearest even,
 // anything at or above 448 gives 448 (0x7E).  Below 2^-6 the step is 2^-9.

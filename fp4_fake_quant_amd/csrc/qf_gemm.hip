@@ -61,12 +61,13 @@ __device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
 // is the block maximum's bf16 exponent field minus 2, clamped at 0 (a saturating
 // subtract on the field moved to bits 23..30).
 __device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
-  uint32_t m = amax_bits8(w);
+  // only the exponent of the block maximum matters: E = its bf16 exponent field - 2
+  uint32_t m = maxexp_bits8(w);
   m = umax(m, dpp_xor1(m));
   m = umax(m, dpp_xor2(m));
-  const uint32_t ebits = __builtin_elementwise_sub_sat((m << 16) & 0x7F800000u, 0x01000000u);
+  const uint32_t ebits = __builtin_elementwise_sub_sat(m << 16, 0x01000000u);
   const float sc = __uint_as_float(ebits);
-  uint32_t codes = 0;
+  uint32_t codes = w.x;                        // every byte is overwritten below
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.y), sc, 1);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.z), sc, 2);
@@ -176,80 +177,12 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __rest
 #pragma unroll
   for (int j = 0; j < 2; ++j) read_w(0, smem, 0, j);
 
-#ifndef QF_GEMM_PIECES
-#define QF_GEMM_PIECES 1
-#endif
-#if QF_GEMM_PIECES
-  // Each of the 8 chunks a lane stages per K step is QDQ'd in three pieces (block
-  // maximum; exponent and E2M1 codes; values back to bf16, LDS write and reload), and
-  // each piece sits right after one MFMA of substeps 0-2 (24 MFMAs, 24 pieces), so that
-  // one wave's VALU work issues while its own MFMAs occupy the matrix pipe and the
-  // pieces of one chunk are an MFMA apart.  Substep 3 follows the barrier and reads the
-  // next step's first fragments.
-  uint32_t pmax[2 * G_LOADS], pcode[2 * G_LOADS];
-  float pscale[2 * G_LOADS];
-  auto piece = [&](int c, int p, uint8_t* stage, uint32_t kbyte) {
-    const bool q = c < G_LOADS ? QA : QW;
-    if (q && p == 0) pmax[c] = amax_bits8(raw[c]);
-    if (q && p == 1) {
-      uint32_t m = pmax[c];
-      m = umax(m, dpp_xor1(m));
-      m = umax(m, dpp_xor2(m));
-      const uint32_t ebits = __builtin_elementwise_sub_sat((m << 16) & 0x7F800000u, 0x01000000u);
-      const float sc = __uint_as_float(ebits);
-      const uint4 w = raw[c];
-      uint32_t codes = 0;
-      codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
-      codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.y), sc, 1);
-      codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.z), sc, 2);
-      codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.w), sc, 3);
-      pcode[c] = codes;
-      pscale[c] = sc;
-    }
-    if (p == 2) {
-      uint4 o = raw[c];
-      if (q) {
-        o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pcode[c], pscale[c], 0));
-        o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pcode[c], pscale[c], 1));
-        o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pcode[c], pscale[c], 2));
-        o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(pcode[c], pscale[c], 3));
-      }
-      if (c < G_LOADS) *reinterpret_cast<uint4*>(stage + lds_off(lrow + 64 * c, lchunk)) = o;
-      else *reinterpret_cast<uint4*>(stage + G_SLICE_BYTES + lds_off(lrow + 64 * (c - G_LOADS), lchunk)) = o;
-      issue_load(c, kbyte);
-    }
-  };
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
-    uint8_t* next = smem + 2 * (cur ^ 1) * G_SLICE_BYTES;
-    const uint32_t kb2 = (uint32_t)min(ks + 2, nk - 1) * GBK * 2u;
-#pragma unroll
-    for (int s = 0; s < GBK / 16; ++s) {
-      const int fs = s & 1;
-      if (s == 3) __syncthreads();                          // step ks+1's slice is in `next`
-      const uint8_t* rb = (s < 3) ? base : next;
-      const int rs = (s < 3) ? s + 1 : 0;
-      const int rset = (s < 3) ? (fs ^ 1) : 0;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        acc[m >> 1][m & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fs][m & 1], fx[fs][m >> 1], acc[m >> 1][m & 1], 0, 0, 0);
-        if (m < 4) read_x(rset, rb, rs, m);
-        else if (m < 6) read_w(rset, rb, rs, m - 4);
-        if (s < 3) {
-          const int slot = 8 * s + m;                       // 0..23: chunk slot / 3, piece slot % 3
-          piece(slot / 3, slot % 3, next, kb2);
-        }
-        QF_FENCE();
-      }
-    }
-  }
-#else
   // Substep s (16 of K) is 8 MFMAs in 4 pairs; pair q of substeps 0-2 also reads
   // fragments for substep s+1 and stages/reloads chunk slots (3, 3, 2 per substep).
-  // Substep 3 follows the barrier and reads the next step's first fragments.  (Asking
-  // the scheduler for a finer MFMA/VALU interleave with sched_group_barrier measured
-  // 3% slower than these pair-sized groups.)
+  // Substep 3 follows the barrier and reads the next step's first fragments.  Measured
+  // alternatives, all slower: a finer MFMA/VALU interleave asked of the scheduler with
+  // sched_group_barrier (-3%), one QDQ piece after every MFMA (-1%), staging spread
+  // over all four substeps with the barrier at the end of the step (-2%).
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
     const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
@@ -282,7 +215,6 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __rest
     }
   }
 
-#endif
 
   // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
 #pragma unroll

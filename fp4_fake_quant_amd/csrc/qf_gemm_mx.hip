@@ -79,13 +79,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const void* p, int64_t
 // E2M1 codes of one 16-byte bf16 chunk (lanes 4i..4i+3 hold one 32-element block) and
 // the block's E8M0 exponent E = max(floor(log2 amax) - 2 + 127, 0).
 __device__ __forceinline__ uint32_t mx_quant_chunk(uint4 w, uint32_t& e) {
-  uint32_t m = amax_bits8(w);
+  uint32_t m = maxexp_bits8(w);               // only the exponent of the block maximum matters
   m = umax(m, dpp_xor1(m));
   m = umax(m, dpp_xor2(m));
-  const uint32_t ebits = __builtin_elementwise_sub_sat((m << 16) & 0x7F800000u, 0x01000000u);
+  const uint32_t ebits = __builtin_elementwise_sub_sat(m << 16, 0x01000000u);
   e = ebits >> 23;
   const float sc = __uint_as_float(ebits);
-  uint32_t codes = 0;
+  uint32_t codes = w.x;                        // every byte is overwritten below
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.y), sc, 1);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.z), sc, 2);
