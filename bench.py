@@ -369,18 +369,21 @@ class W4A4GemmMXFP4:
 
     def controls(self, reps=10):
         """ms of the plain-BF16 run of the same kernel, of torch.matmul, and of the same
-        W4A4 product on the MXFP4 matrix cores (both operands quantized in the kernel, and
-        W pre-packed by qf_pack_mxfp4 with X quantized in the kernel; the pack is timed
-        on its own)."""
+        W4A4 product on the MXFP4 matrix cores: both operands quantized in the kernel; W
+        pre-packed by qf_pack_mxfp4 with X quantized in the kernel; both pre-packed (the
+        packs are timed on their own)."""
         torch = self.torch
         fq = self.fq
         out = {}
         Wc, Ws = fq.qf_pack_mxfp4(self.W)
+        Xc, Xs = fq.qf_pack_mxfp4(self.X)
         for name, fn in (("gemm_bf16_same_kernel", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
                          ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y)),
                          ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
                          ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
-                         ("pack_w_mxfp4", lambda: fq.qf_pack_mxfp4(self.W, Wc, Ws))):
+                         ("w4a4_fp4_cores_both_packed", lambda: fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)),
+                         ("pack_w_mxfp4", lambda: fq.qf_pack_mxfp4(self.W, Wc, Ws)),
+                         ("pack_x_mxfp4", lambda: fq.qf_pack_mxfp4(self.X, Xc, Xs))):
             for _ in range(3):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -391,7 +394,7 @@ class W4A4GemmMXFP4:
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            if name == "pack_w_mxfp4":
+            if name.startswith("pack_"):
                 out[name] = {"ms": round(ms, 4)}
                 continue
             tf = self.flop / ms / 1e9

@@ -339,7 +339,6 @@ __global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4(const uint16_t* __restr
 constexpr int PP_BK = 128;
 constexpr int PP_STAGES = 4;
 constexpr int PP_AHEAD = PP_STAGES - 1;                   // steps of loads in flight
-constexpr int PP_LOADS = 5;                               // buffer-to-LDS loads per lane per step
 using PPL = MxLayout<PP_BK>;
 
 // s_waitcnt that waits until at most n vector-memory operations are outstanding (the
@@ -357,10 +356,23 @@ using PPL = MxLayout<PP_BK>;
     asm volatile("" ::: "memory");                                                          \
   } while (0)
 
-__global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4pp(const uint8_t* __restrict__ Xc, const uint8_t* __restrict__ Xs,
+// 8 waves: 2 per SIMD laid out 2 x 4, each 128 rows of X by 64 of W (4 x 2 MFMA tiles).
+// (4 waves, one per SIMD with 128 x 128 wave tiles, would read a third fewer fragment
+// bytes from LDS per MFMA, but the compiler keeps its 256 accumulators in VGPRs and
+// spills; the code keeps the wave count as a parameter for that layout.)  What bounds this kernel: per
+// substep the 8 waves read 48 KiB of fragments and the loads write 17 KiB into LDS,
+// close to the LDS bandwidth the 16 MFMAs per SIMD take to run; timing without the
+// loads (stale data) still gives 1.07 ms against 1.45 ms with them.
+constexpr int WAVES = 8;
+__global__ __launch_bounds__(64 * WAVES) void k_gemm_mx4pp(const uint8_t* __restrict__ Xc, const uint8_t* __restrict__ Xs,
                                                            const uint8_t* __restrict__ Wc, const uint8_t* __restrict__ Ws,
                                                            uint16_t* __restrict__ Y, int64_t ldy, int M, int N, int K,
                                                            int y_vec) {
+  constexpr int NJ = WAVES == 8 ? 2 : 4;                   // 32-row W tiles per wave
+  constexpr int WN = 32 * NJ;                              // W rows per wave
+  constexpr int CW = 16 / WAVES;                           // code windows per wave per operand
+  constexpr int SW = 8 / WAVES;                            // exponent windows per wave
+  constexpr int LOADS = 2 * CW + SW;                       // buffer-to-LDS loads per lane per step
   __shared__ __attribute__((aligned(16))) uint8_t smem[PP_STAGES * PPL::STAGE];   // 136 KiB
 
   // ---- tile of this workgroup (XCD-aware grouped order) ----
@@ -379,7 +391,7 @@ __global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4pp(const uint8_t* __rest
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = tid & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t wm = wave >> 2, wn = wave & 3u;
+  const uint32_t wm = wave / (256 / WN), wn = wave % (256 / WN);
   const uint32_t frow = lane & 31u, fblk = lane >> 5;
 
   const int64_t kc = K / 2, ks32 = K / 32;
@@ -387,71 +399,71 @@ __global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4pp(const uint8_t* __rest
   const __amdgpu_buffer_rsrc_t rwc = mx_rsrc(Wc + (int64_t)n0 * kc, kc, N - n0);
   const __amdgpu_buffer_rsrc_t rxs = mx_rsrc(Xs + (int64_t)m0 * ks32, ks32, M - m0);
   const __amdgpu_buffer_rsrc_t rws = mx_rsrc(Ws + (int64_t)n0 * ks32, ks32, N - n0);
-  // code windows: wave w fills windows 2w and 2w+1 (16 rows each) of both operands; lane l
-  // of window v holds row 16v + l/4 at slot l%4, which is K block (l%4) ^ rotation(row)
-  uint32_t coff[2];
+  // code windows: wave w fills windows CW w .. CW w + CW-1 (16 rows each) of both operands;
+  // lane l of window v holds row 16v + l/4 at slot l%4, which is K block (l%4) ^ rotation(row)
+  uint32_t coff[CW];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t row = 16u * (2u * wave + i) + (lane >> 2);
+  for (int i = 0; i < CW; ++i) {
+    const uint32_t row = 16u * (CW * wave + i) + (lane >> 2);
     const uint32_t kb = (lane & 3u) ^ ((row >> 2) & 3u);
     coff[i] = row * (uint32_t)kc + kb * 16u;
   }
-  // exponent windows: waves 0-3 copy X rows 64w + l, waves 4-7 W rows 64(w-4) + l (4 bytes each)
-  const bool sx_wave = wave < 4;
-  const uint32_t srow = 64u * (wave & 3u) + lane;
-  const uint32_t soff = srow * (uint32_t)ks32;
-
+  // exponent windows (64 rows x 4 bytes): 8 of them, X rows 64v + l for v < 4, W rows
+  // 64(v-4) + l for v >= 4; wave w fills windows SW w .. SW w + SW-1
   typedef __attribute__((address_space(3))) void* lds_ptr_t;
   auto issue_step = [&](int step) {
     const int k = min(step, K / PP_BK - 1);               // past the end: reload the last step
     uint8_t* st = smem + (step % PP_STAGES) * PPL::STAGE;
     const uint32_t kb = (uint32_t)k * (PP_BK / 2);          // code bytes into the row
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const uint32_t win = 2u * wave + i;
+    for (int i = 0; i < CW; ++i) {
+      const uint32_t win = CW * wave + i;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rxc, (lds_ptr_t)(st + win * 1024u), 16, coff[i] + kb, 0, 0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rwc, (lds_ptr_t)(st + PPL::OPER + win * 1024u), 16, coff[i] + kb, 0, 0, 0);
     }
     const uint32_t eb = (uint32_t)k * (PP_BK / 32);
-    if (sx_wave)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_ptr_t)(st + PPL::CODES + 256u * wave), 4, soff + eb, 0, 0, 0);
-    else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_ptr_t)(st + PPL::OPER + PPL::CODES + 256u * (wave - 4)), 4,
-                                               soff + eb, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < SW; ++i) {
+      const uint32_t v = SW * wave + i;                     // uniform
+      const uint32_t off = (64u * (v & 3u) + lane) * (uint32_t)ks32 + eb;
+      if (v < 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rxs, (lds_ptr_t)(st + PPL::CODES + 256u * v), 4, off, 0, 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rws, (lds_ptr_t)(st + PPL::OPER + PPL::CODES + 256u * (v - 4)), 4, off,
+                                                    0, 0, 0);
+    }
   };
 
-  f32x16_t acc[4][2];
+  f32x16_t acc[4][NJ];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  i32x4_t fx[2][4], fw[2][2];
-  uint32_t ex[2][4], ew[2][2];                               // exponent words of the step's rows
+  i32x4_t fx[2][4], fw[2][NJ];
+  uint32_t ex[2][4], ew[2][NJ];                             // exponent words of the step's rows
   auto read_codes = [&](int set, const uint8_t* st, int sub) {
     const uint32_t kb = 2u * sub + fblk;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       fx[set][i] = *reinterpret_cast<const i32x4_t*>(st + PPL::off(wm * 128u + 32u * i + frow, kb));
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      fw[set][j] = *reinterpret_cast<const i32x4_t*>(st + PPL::OPER + PPL::off(wn * 64u + 32u * j + frow, kb));
+    for (int j = 0; j < NJ; ++j)
+      fw[set][j] = *reinterpret_cast<const i32x4_t*>(st + PPL::OPER + PPL::off(wn * WN + 32u * j + frow, kb));
   };
   auto read_exps = [&](int set, const uint8_t* st) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) ex[set][i] = *reinterpret_cast<const uint32_t*>(st + PPL::CODES + (wm * 128u + 32u * i + frow) * 4u);
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-      ew[set][j] = *reinterpret_cast<const uint32_t*>(st + PPL::OPER + PPL::CODES + (wn * 64u + 32u * j + frow) * 4u);
+    for (int j = 0; j < NJ; ++j)
+      ew[set][j] = *reinterpret_cast<const uint32_t*>(st + PPL::OPER + PPL::CODES + (wn * WN + 32u * j + frow) * 4u);
   };
 
   const int nk = K / PP_BK;
   // prologue: steps 0 .. PP_AHEAD-1 in flight, step 0 landed and its first fragments read
 #pragma unroll
   for (int s = 0; s < PP_AHEAD; ++s) issue_step(s);
-  PP_BARRIER((PP_AHEAD - 1) * PP_LOADS);
+  PP_BARRIER((PP_AHEAD - 1) * LOADS);
   read_codes(0, smem, 0);
   read_exps(0, smem);
 
@@ -469,16 +481,19 @@ __global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4pp(const uint8_t* __rest
       issue_step(k + PP_AHEAD);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        if (sub == 1) PP_BARRIER((PP_AHEAD - 1) * PP_LOADS);   // step k+1 has landed (k+2, k+3 may fly)
+        if (sub == 1) PP_BARRIER((PP_AHEAD - 1) * LOADS);   // step k+1 has landed (k+2, k+3 may fly)
+        const int sh = 8 * (2 * sub) + 8 * (int)fblk;
+        uint32_t sxs[4], sws[NJ];                           // the substep's exponent bytes in byte 0
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sxs[i] = ex[h][i] >> sh;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sws[j] = ew[h][j] >> sh;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
 #pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int sh = 8 * (2 * sub) + 8 * (int)fblk;
+          for (int j = 0; j < NJ; ++j)
             acc[q][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                fp4_operand(fw[sub][j]), fp4_operand(fx[sub][q]), acc[q][j], 4, 4, 0, (int)(ew[h][j] >> sh), 0,
-                (int)(ex[h][q] >> sh));
-          }
+                fp4_operand(fw[sub][j]), fp4_operand(fx[sub][q]), acc[q][j], 4, 4, 0, (int)sws[j], 0, (int)sxs[q]);
           if (q == 0) {
             if (sub == 0) read_codes(1, cur, 1);
             else { read_codes(0, nxt, 0); read_exps(h ^ 1, nxt); }
@@ -497,10 +512,10 @@ __global__ __launch_bounds__(MX_THREADS) void k_gemm_mx4pp(const uint8_t* __rest
     if (row >= M) continue;
     uint16_t* yr = Y + (int64_t)row * ldy;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < NJ; ++j) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = n0 + (int)(wn * 64 + j * 32 + 8 * g + 4 * fblk);
+        const int col = n0 + (int)(wn * WN + j * 32 + 8 * g + 4 * fblk);
         const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
         const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
         if (y_vec && col + 3 < N) {
@@ -519,7 +534,7 @@ hipError_t launch_gemm_mx4pp(const uint8_t* Xc, const uint8_t* Xs, const uint8_t
                              int64_t ldy, int M, int N, int K, hipStream_t s) {
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
   const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
-  hipLaunchKernelGGL(k_gemm_mx4pp, dim3(tiles), dim3(MX_THREADS), 0, s, Xc, Xs, Wc, Ws, Y, ldy, M, N, K, y_vec);
+  hipLaunchKernelGGL(k_gemm_mx4pp, dim3(tiles), dim3(64 * WAVES), 0, s, Xc, Xs, Wc, Ws, Y, ldy, M, N, K, y_vec);
   return hipGetLastError();
 }
 
