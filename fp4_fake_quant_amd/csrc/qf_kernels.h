@@ -81,8 +81,8 @@ struct ReduceArgs {
 // ------------------------------------------------------------------ LoRA ---
 constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
 constexpr int LORA_SLAB = 512;      // columns per wave: 64 lanes x 8
-constexpr int LORA_ROWS = 32;       // rows per merge unit
-constexpr int LORA_DA_ROWS = 256;   // rows per dA workgroup (one partial per workgroup)
+constexpr int LORA_ROWS = 32;       // rows per merge unit (at most; smaller for small launches)
+constexpr int LORA_DA_ROWS = 256;   // rows per dA workgroup, one partial each (at most)
 #ifndef QF_LORA_DB_ROWS
 #define QF_LORA_DB_ROWS 16
 #endif
@@ -112,6 +112,8 @@ struct LoraArgs {
   LoraTensor d[QF_MAX_GROUPED];
   int n;
   int n_groups;        // rows of merge partials
+  int merge_rows;      // rows per merge unit (32, 16 or 8)
+  int da_rows;         // rows per dA workgroup (LORA_DA_ROWS; a multiple of 4 * LORA_PREFETCH)
   uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
 };
 

@@ -19,7 +19,7 @@
 // scalar registers, where the FMAs read them.
 //
 // Kernels
-//   k_lora_merge     M = W + B.A for LORA_ROWS rows per unit; folds max|M| of the
+//   k_lora_merge     M = W + B.A for up to LORA_ROWS rows per unit; folds max|M| of the
 //                    workgroup into its tied group's partial (NVFP4 pass 1).
 //   k_lora_dB        dB = G . A^T on the 16x16x32 BF16 MFMA: a wave owns 16 rows
 //                    and walks all columns 32 at a time (G rows are the MFMA's A
@@ -124,8 +124,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int r = RK ? RK : T.r;
     const int rb = u / T.slabs;
     const int64_t cs = (int64_t)(u - rb * T.slabs) * LORA_SLAB;        // first column of the slab
-    const int64_t r0 = (int64_t)rb * LORA_ROWS;
-    const int rows = (int)min((int64_t)LORA_ROWS, T.rows - r0);
+    const int64_t r0 = (int64_t)rb * a.merge_rows;
+    const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);
     const bool active = cs + 8 * lane < cols;
     const uint32_t lo = active ? 16u * lane : BUF_OOR;                  // lane's byte offset in a row
     const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
@@ -270,7 +270,6 @@ __global__ __launch_bounds__(256) void k_lora_dB(LoraArgs a, int accumulate) {
 // take a quarter of the rows each (lane l: columns 8l .. 8l+7, 16 x 8 sums in
 // registers) and their sums are added in LDS in a fixed order (w0 + w2, w1 + w3,
 // then the two) before the workgroup writes its partial.
-constexpr int DA_WAVE_ROWS = LORA_DA_ROWS / 4;
 
 template <int RK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_dA(LoraArgs a) {
@@ -291,8 +290,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   for (int k = 0; k < LORA_MAX_R; ++k)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[k][e] = 0.0f;
-  const int64_t r0 = (int64_t)rb * LORA_DA_ROWS + (int64_t)wave * DA_WAVE_ROWS;
-  const int rows = (int)max((int64_t)0, min((int64_t)DA_WAVE_ROWS, T.rows - r0));
+  const int wave_rows = a.da_rows / 4;
+  const int64_t r0 = (int64_t)rb * a.da_rows + (int64_t)wave * wave_rows;
+  const int rows = (int)max((int64_t)0, min((int64_t)wave_rows, T.rows - r0));
   if (rows > 0) {
     const uint32_t lo = active ? 16u * lane : BUF_OOR;
     const uint32_t stride = (uint32_t)(cols * 2);
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumulate) {
   const LoraTensor& T = a.d[blockIdx.y];
   const int64_t n = (int64_t)T.r * T.cols;
-  const int nblk = (int)((T.rows + LORA_DA_ROWS - 1) / LORA_DA_ROWS);
+  const int nblk = (int)((T.rows + a.da_rows - 1) / a.da_rows);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t k = idx / T.cols, j = idx - k * T.cols;
     float s = 0.0f;
