@@ -127,3 +127,23 @@ def test_lora_validation():
     assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 17, q, None) == 7
     d[0].rows = d[1].rows = 0                                       # empty: nothing to do
     assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, 4, None) == 0
+
+
+def test_gemm_validation():
+    """GEMM entry points check flags, K and alignment before launching."""
+    L = _lib.lib()
+    p, q, y = _addr(0x10000000), _addr(0x10400000), _addr(0x10800000)
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 4, None) == 7        # FP4 cores need both QDQ flags
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 5, None) == 7
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 8, None) == 7        # unknown flag
+    assert L.qf_gemm_mxfp4(p, 96, q, 96, y, 64, 64, 64, 96, 3, None) == 2        # K not a multiple of 64
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 0, 64, 64, 7, None) == 0         # empty: no-op
+    xs, ws = _addr(0x10C00000), _addr(0x10E00000)
+    assert L.qf_gemm_mxfp4_packed(p, xs, q, ws, y, 64, 64, 64, 64, None) == 2    # K not a multiple of 128
+    assert L.qf_gemm_mxfp4_packed(p, _addr(0x10C00002), q, ws, y, 64, 64, 64, 128, None) == 3   # exponents 4-byte aligned
+    assert L.qf_gemm_mxfp4_packed(None, xs, q, ws, y, 64, 64, 64, 128, None) == 1
+    assert L.qf_gemm_mxfp4_packed(p, xs, q, ws, y, 32, 64, 64, 128, None) == 2   # ldy < N
+    assert L.qf_gemm_mxfp4_packed(p, xs, q, ws, y, 64, 64, 0, 128, None) == 0    # empty: no-op
+    assert L.qf_gemm_mxfp4_packed_w(p, 96, q, ws, y, 64, 64, 64, 96, None) == 2  # K not a multiple of 64
+    assert L.qf_gemm_mxfp4_packed_w(p, 64, _addr(0x10400008), ws, y, 64, 64, 64, 64, None) == 3  # codes 16-byte aligned
+    assert L.qf_gemm_mxfp4_packed_w(p, 64, q, None, y, 64, 64, 64, 64, None) == 1
