@@ -312,7 +312,7 @@ qf_status check_lora(const qf_lora_desc& d) {
 }
 
 struct LoraCounts {
-  int64_t merge_wg = 0, dB_waves = 0, dA_wg = 0, dA_part = 0;
+  int64_t merge_wg = 0, grad_wg = 0, dA_part = 0, dB_part = 0;
 };
 
 int64_t slabs_of(int64_t cols) { return (cols + qf::LORA_SLAB - 1) / qf::LORA_SLAB; }
@@ -336,19 +336,26 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da
       t.W = d[i].W; t.A = d[i].A; t.B = d[i].B; t.M = d[i].M; t.G = d[i].G;
       t.dA = d[i].dA; t.dB = d[i].dB;
       t.dA_partial = dA_part ? dA_part + c.dA_part : nullptr;
+      t.dB_partial = nullptr;
       t.rows = d[i].rows; t.cols = d[i].cols; t.ldw = d[i].ldw;
       t.r = d[i].r; t.group = d[i].group;
       t.slabs = (int32_t)slabs;
       t.merge_units = (int32_t)mu; t.merge_wg_begin = (int32_t)c.merge_wg;
-      t.dB_wave_begin = (int32_t)c.dB_waves;
-      t.dA_units = (int32_t)du; t.dA_wg_begin = (int32_t)c.dA_wg;
+      t.grad_wg_begin = (int32_t)c.grad_wg;
     }
     ++k;
     if (d[i].group + 1 > groups) groups = d[i].group + 1;
     c.merge_wg += ceil_div(mu, 4);
-    c.dB_waves += ceil_div(d[i].rows, qf::LORA_DB_ROWS);
-    c.dA_wg += du;
+    c.grad_wg += du;
     c.dA_part += dblk * qf::LORA_MAX_R * d[i].cols;
+  }
+  // dB partials follow all dA partials: [slabs][rows][LORA_MAX_R] per descriptor
+  int k2 = 0;
+  for (int i = 0; i < n; ++i) {
+    if (d[i].rows <= 0 || d[i].cols <= 0) continue;
+    if (a) a->d[k2].dB_partial = dA_part ? dA_part + c.dA_part + c.dB_part : nullptr;
+    ++k2;
+    c.dB_part += slabs_of(d[i].cols) * d[i].rows * qf::LORA_MAX_R;
   }
   if (a) {
     a->n = k;
@@ -389,7 +396,8 @@ size_t qf_lora_workspace(const qf_lora_desc* d, int n) {
     if (check_lora(d[i]) != QF_OK) return 0;
   const LoraCounts c = lora_layout(d, n, nullptr, nullptr);
   const int64_t merge_words = c.merge_wg * lora_groups(d, n);
-  const int64_t words = merge_words > c.dA_part ? merge_words : c.dA_part;
+  const int64_t grad_words = c.dA_part + c.dB_part;
+  const int64_t words = merge_words > grad_words ? merge_words : grad_words;
   return (size_t)(words > 0 ? words : 1) * 4;
 }
 
@@ -455,8 +463,8 @@ qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, vo
   if (!aligned(ws, 16)) return QF_ERR_ALIGN;
   qf::LoraArgs a;
   const LoraCounts c = lora_layout(d, n, &a, (float*)ws);
-  if (c.dB_waves >= (1ll << 31) || c.dA_wg >= (1ll << 31)) return QF_ERR_SHAPE;
-  return hip_status(qf::launch_lora_grads(a, (int)c.dB_waves, (int)c.dA_wg, accumulate != 0, (hipStream_t)stream));
+  if (c.grad_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_lora_grads(a, (int)c.grad_wg, accumulate != 0, (hipStream_t)stream));
 }
 
 }  // extern "C"

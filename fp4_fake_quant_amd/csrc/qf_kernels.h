@@ -82,11 +82,7 @@ struct ReduceArgs {
 constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
 constexpr int LORA_SLAB = 512;      // columns per wave: 64 lanes x 8
 constexpr int LORA_ROWS = 32;       // rows per merge unit (at most; smaller for small launches)
-constexpr int LORA_DA_ROWS = 256;   // rows per dA workgroup, one partial each (at most)
-#ifndef QF_LORA_DB_ROWS
-#define QF_LORA_DB_ROWS 16
-#endif
-constexpr int LORA_DB_ROWS = QF_LORA_DB_ROWS;   // rows per dB wave (a multiple of 16)
+constexpr int LORA_DA_ROWS = 256;   // rows per gradient workgroup, one dA partial each
 
 // A unit is one wave's work: a slab of LORA_SLAB columns of a run of rows.  Units
 // of a descriptor are numbered row block major, and every descriptor starts on a
@@ -100,12 +96,12 @@ struct LoraTensor {
   float* dA;
   float* dB;
   float* dA_partial;   // workspace: [row blocks][LORA_MAX_R][cols]
+  float* dB_partial;   // workspace: [slabs][rows][LORA_MAX_R]
   int64_t rows, cols, ldw;
   int32_t r, group;
   int32_t slabs;            // ceil(cols / LORA_SLAB)
   int32_t merge_units, merge_wg_begin;
-  int32_t dB_wave_begin;    // dB: one wave per LORA_DB_ROWS rows
-  int32_t dA_units, dA_wg_begin;   // dA: one workgroup per unit
+  int32_t grad_wg_begin;    // gradients: one workgroup per (row block, slab)
 };
 
 struct LoraArgs {
@@ -113,12 +109,12 @@ struct LoraArgs {
   int n;
   int n_groups;        // rows of merge partials
   int merge_rows;      // rows per merge unit (32, 16 or 8)
-  int da_rows;         // rows per dA workgroup (LORA_DA_ROWS; a multiple of 4 * LORA_PREFETCH)
+  int da_rows;         // rows per gradient workgroup (LORA_DA_ROWS, a multiple of 32)
   uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
 };
 
 hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s);
-hipError_t launch_lora_grads(const LoraArgs& a, int dB_waves, int dA_grid, int accumulate, hipStream_t s);
+hipError_t launch_lora_grads(const LoraArgs& a, int grid, int accumulate, hipStream_t s);
 
 // Workgroups of the amax pass for a launch with `tiles` tiles of 256 * L_AMAX chunks.
 inline int amax_grid(int tiles) { return tiles < AMAX_GRID ? tiles : AMAX_GRID; }

@@ -107,8 +107,8 @@ def test_lora_validation():
     assert need > 0 and need % 4 == 0
     # a launch this small shrinks its merge units to the minimum of 8 rows:
     # merge partials ceil(ceil(100/8) * 3 slabs / 4) = 10 workgroups per matrix x 2 groups;
-    # dA partials: one 256-row block x 16 x 1056 per matrix
-    assert need == 4 * max(20 * 2, 2 * 16 * 1056)
+    # gradient partials: dA one 256-row block x 16 x 1056, dB 3 slabs x 100 rows x 16, per matrix
+    assert need == 4 * max(20 * 2, 2 * (16 * 1056 + 3 * 100 * 16))
     assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need - 4, None) == 4
     assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 1, q, None, q, need, None) == 7   # group 1 >= 1
     assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, None, 0, None) == 4
