@@ -182,7 +182,9 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __rest
   // Substep 3 follows the barrier and reads the next step's first fragments.  Measured
   // alternatives, all slower: a finer MFMA/VALU interleave asked of the scheduler with
   // sched_group_barrier (-3%), one QDQ piece after every MFMA (-1%), staging spread
-  // over all four substeps with the barrier at the end of the step (-2%).
+  // over all four substeps with the barrier at the end of the step (-2%), and a
+  // ping-pong in which waves 0-3 run their MFMAs while waves 4-7 stage and then the
+  // reverse, with a barrier per phase (-26%).
   for (int ks = 0; ks < nk; ++ks) {
     const int cur = ks & 1;
     const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
