@@ -24,6 +24,8 @@
 //                    16x16x32 BF16 MFMA (G staged through LDS); per-slab dB partials and
 //                    per-row-block dA partials, added in a fixed order by
 //                    k_lora_dB_reduce and k_lora_dA_reduce (same inputs, same bits).
+#include <algorithm>
+
 #include "qf_device.h"
 #include "qf_kernels.h"
 
@@ -186,14 +188,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 }
 
 // dA[k][j] (+)= sum over row blocks, in block order.
+// Sum of count partials p[0], p[stride], ... added in index order from +0.  The loads
+// are issued LORA_RED_BATCH at a time before any add, so one element costs a few memory
+// latencies instead of one per partial; the order of the adds is unchanged.
+constexpr int LORA_RED_BATCH = 8;
+
+__device__ __forceinline__ float sum_partials(const float* p, int64_t stride, int count) {
+  float s = 0.0f;
+#pragma unroll 1
+  for (int q0 = 0; q0 < count; q0 += LORA_RED_BATCH) {
+    float v[LORA_RED_BATCH];
+#pragma unroll
+    for (int i = 0; i < LORA_RED_BATCH; ++i) v[i] = q0 + i < count ? p[(int64_t)(q0 + i) * stride] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < LORA_RED_BATCH; ++i)
+      if (q0 + i < count) s += v[i];
+  }
+  return s;
+}
+
 __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumulate) {
   const LoraTensor& T = a.d[blockIdx.y];
   const int64_t n = (int64_t)T.r * T.cols;
   const int nblk = (int)((T.rows + a.da_rows - 1) / a.da_rows);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t k = idx / T.cols, j = idx - k * T.cols;
-    float s = 0.0f;
-    for (int q = 0; q < nblk; ++q) s += T.dA_partial[((int64_t)q * LORA_MAX_R + k) * T.cols + j];
+    // partial q holds rows k = 0 .. 15 of cols columns; entry (k, j) of dA is at idx
+    const float s = sum_partials(T.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
     T.dA[idx] = accumulate ? T.dA[idx] + s : s;
   }
 }
@@ -346,8 +366,7 @@ __global__ __launch_bounds__(256) void k_lora_dB_reduce(LoraArgs a, int accumula
     const int64_t row = idx / LORA_MAX_R;
     const int k = (int)(idx - row * LORA_MAX_R);
     if (k >= T.r) continue;
-    float s = 0.0f;
-    for (int q = 0; q < T.slabs; ++q) s += T.dB_partial[((int64_t)q * T.rows + row) * LORA_MAX_R + k];
+    const float s = sum_partials(T.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
     float* dst = T.dB + row * T.r + k;
     *dst = accumulate ? *dst + s : s;
   }
@@ -374,10 +393,17 @@ hipError_t launch_lora_grads(const LoraArgs& a, int grid, int accumulate, hipStr
   hipLaunchKernelGGL(k_lora_grads, dim3(grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lora_dB_reduce, dim3(128, a.n), dim3(256), 0, s, a, accumulate);
+  // one thread per gradient entry (grid-stride past 8192 workgroups)
+  int64_t nB = 0, nA = 0;
+  for (int i = 0; i < a.n; ++i) {
+    nB = std::max<int64_t>(nB, a.d[i].rows * LORA_MAX_R);
+    nA = std::max<int64_t>(nA, (int64_t)a.d[i].r * a.d[i].cols);
+  }
+  const int gB = (int)std::min<int64_t>((nB + 255) / 256, 8192), gA = (int)std::min<int64_t>((nA + 255) / 256, 8192);
+  if (gB > 0) hipLaunchKernelGGL(k_lora_dB_reduce, dim3(gB, a.n), dim3(256), 0, s, a, accumulate);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_lora_dA_reduce, dim3(64, a.n), dim3(256), 0, s, a, accumulate);
+  if (gA > 0) hipLaunchKernelGGL(k_lora_dA_reduce, dim3(gA, a.n), dim3(256), 0, s, a, accumulate);
   return hipGetLastError();
 }
 
