@@ -414,10 +414,12 @@ class MoELoRANVFP4:
       3. the adapter gradients dA = B^T.G, dB = G.A^T from the upstream gradient G of
          the QDQ'd weight (identity STE).
     `experts_per_launch` experts share one launch of each call; the scratch holds that
-    many experts' merged and QDQ'd weights."""
+    many experts' merged and QDQ'd weights.  With merge_scratch=False there is no merged
+    weight in memory: step 1 only takes its maximum and step 2 merges again in registers
+    before the QDQ (same bits; W is read twice instead of M being written and read)."""
     name = "moe_lora_nvfp4"
 
-    def __init__(self, torch, fq, experts_per_launch=1):
+    def __init__(self, torch, fq, experts_per_launch=1, merge_scratch=True):
         import workloads
         self.torch, self.fq = torch, fq
         mo = workloads.MOE
@@ -428,7 +430,8 @@ class MoELoRANVFP4:
         dev = torch.device("cuda")
         mats = ("gate_up", "down")
         self.x = x
-        scratch = {m: (torch.empty((k,) + tuple(x[m]["W"].shape[1:]), dtype=torch.bfloat16, device=dev),
+        scratch = {m: (torch.empty((k,) + tuple(x[m]["W"].shape[1:]), dtype=torch.bfloat16, device=dev)
+                       if merge_scratch else None,
                        torch.empty((k,) + tuple(x[m]["W"].shape[1:]), dtype=torch.bfloat16, device=dev)) for m in mats}
         self.scratch = scratch
         self.codes, self.scl, self.dA, self.dB = {}, {}, {}, {}
@@ -445,7 +448,8 @@ class MoELoRANVFP4:
             for e in range(c0, c0 + k):
                 for j, m in enumerate(mats):
                     items.append(dict(W=x[m]["W"][e], A=x[m]["A"][e], B=x[m]["B"][e], G=x[m]["G"][e],
-                                      M=scratch[m][0][e - c0], y=scratch[m][1][e - c0],
+                                      M=scratch[m][0][e - c0] if merge_scratch else None,
+                                      y=scratch[m][1][e - c0],
                                       codes=self.codes[m][e], scales=self.scl[m][e],
                                       dA=self.dA[m][e], dB=self.dB[m][e], group=2 * (e - c0) + j))
             self.chunks.append((fq.LoraBatch(items), self.tscale[2 * c0: 2 * (c0 + k)]))
@@ -455,17 +459,20 @@ class MoELoRANVFP4:
         self.numel = n
         # algorithmic bytes: pass 1 reads W and the adapters, writes the merged bf16 weight
         # to scratch; pass 2 reads it back, writes the QDQ'd bf16 + E2M1 codes (0.5 B) + E4M3
-        # scales (1/16 B); the gradients read G and the adapters and write fp32 dA, dB
+        # scales (1/16 B); the gradients read G and the adapters and write fp32 dA, dB.
+        # Without the merge scratch, pass 1 writes nothing and pass 2 reads W and the
+        # adapters instead of M.
         self.kernels = {
-            "lora_merge_amax": n * 4 + adapters * 2,
-            "lora_qdq_pack": n * (2 + 2 + 0.5 + 1 / 16),
+            "lora_merge_amax": n * (4 if merge_scratch else 2) + adapters * 2,
+            "lora_qdq_pack": n * (2 + 2 + 0.5 + 1 / 16) + (0 if merge_scratch else adapters * 2),
             "lora_adapter_grads": n * 2 + adapters * (2 + 4),
         }
         self.bytes_per_step = sum(self.kernels.values())
         self.config = {"workload": self.name,
                        "experts": E, "matrices_per_expert": {m: list(x[m]["W"].shape[1:]) for m in mats},
                        "rank": r, "elements": n, "experts_per_launch": k,
-                       "scratch_bytes": sum(t.numel() * 2 for p in scratch.values() for t in p),
+                       "merge_scratch": merge_scratch,
+                       "scratch_bytes": sum(t.numel() * 2 for p in scratch.values() for t in p if t is not None),
                        "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale per expert per fused matrix)"}
 
     def step(self, mark=None):
@@ -519,11 +526,19 @@ class MoELoRANVFP4x8(MoELoRANVFP4):
         super().__init__(torch, fq, experts_per_launch=8)
 
 
+class MoELoRANVFP4x8Remerge(MoELoRANVFP4):
+    """8 experts per launch without the merged-weight scratch: the QDQ pass merges again."""
+    name = "moe_lora_nvfp4_x8_remerge"
+
+    def __init__(self, torch, fq):
+        super().__init__(torch, fq, experts_per_launch=8, merge_scratch=False)
+
+
 WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4,
-                                 MoELoRANVFP4, MoELoRANVFP4x8)}
+                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge)}
 # measured next to the headline workload in a default run (fewer steps each)
 SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
-             MoELoRANVFP4x8.name]
+             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name]
 
 
 def measure(torch, wl, steps, warmup):

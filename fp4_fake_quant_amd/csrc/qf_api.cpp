@@ -311,6 +311,12 @@ qf_status check_lora(const qf_lora_desc& d) {
   return QF_OK;
 }
 
+qf_status check_lora_merge_inputs(const qf_lora_desc& d) {
+  if (!d.W || !d.A || !d.B) return QF_ERR_NULL;
+  if (!aligned(d.W, 16) || !aligned(d.A, 16) || !aligned(d.B, 4) || d.ldw % 8) return QF_ERR_ALIGN;
+  return QF_OK;
+}
+
 struct LoraCounts {
   int64_t merge_wg = 0, grad_wg = 0, dA_part = 0, dB_part = 0;
 };
@@ -334,6 +340,7 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da
     if (a) {
       qf::LoraTensor& t = a->d[k];
       t.W = d[i].W; t.A = d[i].A; t.B = d[i].B; t.M = d[i].M; t.G = d[i].G;
+      t.y = d[i].y; t.codes = d[i].codes; t.scales = d[i].scales;
       t.dA = d[i].dA; t.dB = d[i].dB;
       t.dA_partial = dA_part ? dA_part + c.dA_part : nullptr;
       t.dB_partial = nullptr;
@@ -410,9 +417,9 @@ qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_g
     if (st != QF_OK) return st;
     if (d[i].rows == 0 || d[i].cols == 0) continue;
     if (d[i].group >= n_groups) return QF_ERR_ARG;
-    if (!d[i].W || !d[i].A || !d[i].B || !d[i].M) return QF_ERR_NULL;
-    if (!aligned(d[i].W, 16) || !aligned(d[i].A, 16) || !aligned(d[i].B, 4) || !aligned(d[i].M, 16) || d[i].ldw % 8)
-      return QF_ERR_ALIGN;
+    const qf_status sm = check_lora_merge_inputs(d[i]);
+    if (sm != QF_OK) return sm;
+    if (d[i].M && !aligned(d[i].M, 16)) return QF_ERR_ALIGN;
   }
   if (!ws || ws_bytes < qf_lora_workspace(d, n)) return QF_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return QF_ERR_ALIGN;
@@ -436,14 +443,42 @@ qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_g
 qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_scales, void* stream) {
   if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
   if (n > 0 && !d) return QF_ERR_NULL;
+  if (!d_scales) return QF_ERR_NULL;
+  // descriptors with M: QDQ + pack of M; without: merge again and QDQ in registers
   qf_tensor_desc t[QF_MAX_GROUPED];
+  qf_lora_desc fused[QF_MAX_GROUPED];
+  int nt = 0, nf = 0;
   for (int i = 0; i < n; ++i) {
     const qf_status st = check_lora(d[i]);
     if (st != QF_OK) return st;
-    t[i] = one(d[i].M, d[i].rows, d[i].cols, d[i].cols, d[i].y, d[i].cols, d[i].codes, d[i].scales);
-    t[i].group = d[i].group;
+    if (d[i].rows == 0 || d[i].cols == 0) continue;
+    if (d[i].group < 0) return QF_ERR_ARG;
+    const qf_tensor_desc q = one(d[i].M ? d[i].M : d[i].W, d[i].rows, d[i].cols, d[i].M ? d[i].cols : d[i].ldw,
+                                 d[i].y, d[i].cols, d[i].codes, d[i].scales);
+    const bool uy = d[i].y != nullptr, up = d[i].codes != nullptr;
+    if (!uy && !up) return QF_ERR_NULL;
+    const qf_status sq = check_desc(q, QF_FMT_NVFP4, uy, up);
+    if (sq != QF_OK) return sq;
+    if (d[i].M) {
+      t[nt] = q;
+      t[nt++].group = d[i].group;
+    } else {
+      const qf_status sm = check_lora_merge_inputs(d[i]);
+      if (sm != QF_OK) return sm;
+      fused[nf++] = d[i];
+    }
   }
-  return quant_grouped(QF_FMT_NVFP4, t, n, d_scales, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  if (nt > 0) {
+    const qf_status st = quant_grouped(QF_FMT_NVFP4, t, nt, d_scales, s);
+    if (st != QF_OK) return st;
+  }
+  if (nf == 0) return QF_OK;
+  qf::LoraArgs a;
+  const LoraCounts c = lora_layout(fused, nf, &a, nullptr);
+  if (c.merge_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  a.tscale = d_scales;
+  return hip_status(qf::launch_lora_merge_qdq(a, (int)c.merge_wg, s));
 }
 
 qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,

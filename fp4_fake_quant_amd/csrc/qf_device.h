@@ -42,6 +42,12 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t o
 __device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store1(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(v, r, (int)off, 0, 0);
+}
 
 // ----------------------------------------------------------------- bf16 ----
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -166,5 +172,61 @@ __device__ __forceinline__ uint32_t quad_bcast1(uint32_t v) { return (uint32_t)_
 
 __device__ __forceinline__ uint32_t umax(uint32_t a, uint32_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+// ------------------------------------------------------ NVFP4 QDQ chunk ----
+// NVFP4 QDQ of one lane's 8 bf16 elements (QATFactory project page, "Supported
+// formats" table: E2M1 elements, one E4M3 scale per 16-block, an FP32 tensor scale
+// s_t).  Lanes 2i and 2i+1 hold one 16-block and both must execute this together.
+// k = 6 s_t.  Block scale S = E4M3(amax / k) (RNE, saturating); with d = s S the
+// element code is E2M1(x / d) (RNE, saturating) and the QDQ'd value is
+// bf16((E2M1(code) s) s_t), each product rounded in fp32.
+struct Nvfp4Chunk {
+  uint32_t codes;   // nibble e holds element e's code
+  uint32_t S;       // the block's E4M3 scale byte
+  uint4 y;          // QDQ'd values, bf16
+};
+
+__device__ __forceinline__ Nvfp4Chunk nvfp4_qdq_chunk(uint4 w, float s_t, float k) {
+  uint32_t m = amax_bits8(w);
+  m = umax(m, dpp_xor1(m));
+  const float amax = __uint_as_float(m << 16);
+  Nvfp4Chunk o;
+  o.S = e4m3_encode(amax / k);
+  const float s = e4m3_value(o.S);
+  const float d = s * s_t;
+  const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    y[2 * e] = bf16_lo(wv[e]) * r;
+    y[2 * e + 1] = bf16_hi(wv[e]) * r;
+  }
+  if (__builtin_expect(r > __FLT_MAX__, 0)) {
+    // 1/d overflowed (the whole tied group lies below ~1e-35): 0 * inf must still
+    // give magnitude 0 with the element's own sign.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = bf16_lo(wv[e]), hi = bf16_hi(wv[e]);
+      if (lo == 0.0f) y[2 * e] = lo;
+      if (hi == 0.0f) y[2 * e + 1] = hi;
+    }
+  }
+  uint32_t codes = 0;
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[0], y[1], 1.0f, 0);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[4], y[5], 1.0f, 2);
+  codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[6], y[7], 1.0f, 3);
+  o.codes = codes;
+  const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  o.y.x = pack_bf16x2((v0.x * s) * s_t, (v0.y * s) * s_t);
+  o.y.y = pack_bf16x2((v1.x * s) * s_t, (v1.y * s) * s_t);
+  o.y.z = pack_bf16x2((v2.x * s) * s_t, (v2.y * s) * s_t);
+  o.y.w = pack_bf16x2((v3.x * s) * s_t, (v3.y * s) * s_t);
+  return o;
+}
 
 }  // namespace qf

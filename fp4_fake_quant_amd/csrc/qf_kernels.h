@@ -91,7 +91,10 @@ struct LoraTensor {
   const uint16_t* W;
   const uint16_t* A;
   const uint16_t* B;
-  uint16_t* M;
+  uint16_t* M;          // merged weight; null: not stored (the QDQ pass merges again)
+  uint16_t* y;          // merge-and-QDQ outputs (null: skipped)
+  uint8_t* codes;
+  uint8_t* scales;
   const uint16_t* G;
   float* dA;
   float* dB;
@@ -111,9 +114,11 @@ struct LoraArgs {
   int merge_rows;      // rows per merge unit (32, 16 or 8)
   int da_rows;         // rows per gradient workgroup (LORA_DA_ROWS, a multiple of 32)
   uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
+  const float* tscale; // merge-and-QDQ: NVFP4 tensor scale of every tied group
 };
 
 hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s);
+hipError_t launch_lora_merge_qdq(const LoraArgs& a, int grid, hipStream_t s);
 hipError_t launch_lora_grads(const LoraArgs& a, int grid, int accumulate, hipStream_t s);
 
 // Workgroups of the amax pass for a launch with `tiles` tiles of 256 * L_AMAX chunks.

@@ -18,8 +18,10 @@
 // loaded once per row through the scalar cache, where the FMAs read them.
 //
 // Kernels
-//   k_lora_merge     M = W + B.A for up to LORA_ROWS rows per unit; folds max|M| of the
-//                    workgroup into its tied group's partial (NVFP4 pass 1).
+//   k_lora_merge     M = W + B.A for up to LORA_ROWS rows per unit; either stores M
+//                    (or not) and folds max|M| of the workgroup into its tied group's
+//                    partial (NVFP4 pass 1), or merges again and NVFP4-QDQs and packs
+//                    the merged rows in registers (pass 2 without M in memory).
 //   k_lora_grads     dB = G . A^T and dA = B^T . G in one pass over G, both on the
 //                    16x16x32 BF16 MFMA (G staged through LDS); per-slab dB partials and
 //                    per-row-block dA partials, added in a fixed order by
@@ -110,7 +112,14 @@ __device__ __forceinline__ void b_row_values(const uint32_t (&w)[BW], int64_t ro
 // an out-of-range offset, and the rows of the last group past the end are computed on
 // zeros and dropped by the range check, so the compiler can keep every prefetched
 // load in flight across rows.
-template <int RK>
+//
+// QDQ = false: M is stored (unless T.M is null: the resource is then empty and every
+// store is dropped) and the workgroup's max|M| goes to its tied group's partial.
+// QDQ = true: the merged row stays in registers and is NVFP4-QDQ'd and packed with the
+// group's tensor scale (lanes 2i and 2i+1 hold one 16-block), so no M round trip
+// through memory is needed; the merge arithmetic is the same, so the values are the
+// same bits as QDQ of the stored M.
+template <int RK, bool QDQ>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_merge(LoraArgs a) {
   const int b = blockIdx.x;
   const LoraTensor& T = a.d[find_desc_wg(a, b)];
@@ -126,10 +135,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);
     const bool active = cs + 8 * lane < cols;
     const uint32_t lo = active ? 16u * lane : BUF_OOR;                  // lane's byte offset in a row
+    const int64_t e0 = r0 * cols + cs;                                  // first element of the unit
     const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
-    const __amdgpu_buffer_rsrc_t rm = make_buf(T.M + r0 * cols + cs, (int64_t)rows * cols * 2);
     const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
     const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
+    // outputs: M, or y / codes / scales (an empty resource drops the stores)
+    const bool wm = !QDQ && T.M, wy = QDQ && T.y, wp = QDQ && T.codes;
+    const __amdgpu_buffer_rsrc_t rm = make_buf(wm ? T.M + e0 : nullptr, wm ? (int64_t)rows * cols * 2 : 0);
+    const __amdgpu_buffer_rsrc_t ry = make_buf(wy ? T.y + e0 : nullptr, wy ? (int64_t)rows * cols * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rc = make_buf(wp ? T.codes + e0 / 2 : nullptr, wp ? (int64_t)rows * cols / 2 : 0);
+    const __amdgpu_buffer_rsrc_t rs = make_buf(wp ? T.scales + e0 / 16 : nullptr, wp ? (int64_t)rows * cols / 16 : 0);
+    const uint32_t clo = active ? 4u * lane : BUF_OOR;
+    const uint32_t slo = active && (lane & 1) == 0 ? (uint32_t)lane / 2u : BUF_OOR;
+    const uint32_t cstride = (uint32_t)(cols / 2), sstride = (uint32_t)(cols / 16);
+    const float s_t = QDQ ? a.tscale[T.group] : 0.0f, k6 = 6.0f * s_t;
     uint4 wv[LORA_PREFETCH];
 #pragma unroll
     for (int q = 0; q < LORA_PREFETCH; ++q) {
@@ -164,26 +183,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         o.y = pack_bf16x2(w[2] + acc[2], w[3] + acc[3]);
         o.z = pack_bf16x2(w[4] + acc[4], w[5] + acc[5]);
         o.w = pack_bf16x2(w[6] + acc[6], w[7] + acc[7]);
-        buf_store16(rm, lo + ii * mstride, o);                         // past the end: dropped
-        const uint32_t mo = amax_bits8(o);
-        m = umax(m, (active && ii < rows) ? mo : 0u);
+        if constexpr (QDQ) {                                           // rows past the end: dropped
+          const Nvfp4Chunk qc = nvfp4_qdq_chunk(o, s_t, k6);
+          buf_store16(ry, lo + ii * mstride, qc.y);
+          buf_store4(rc, clo + ii * cstride, qc.codes);
+          buf_store1(rs, slo + ii * sstride, (uint8_t)qc.S);
+        } else {
+          buf_store16(rm, lo + ii * mstride, o);                       // past the end: dropped
+          const uint32_t mo = amax_bits8(o);
+          m = umax(m, (active && ii < rows) ? mo : 0u);
+        }
         wv[q] = buf_load16(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
       }
     }
   }
-  // workgroup maximum -> partial[g * grid + b]: this descriptor's group, 0 for the others
-  m = umax(m, dpp_xor1(m));
-  m = umax(m, dpp_xor2(m));
-  m = umax(m, dpp_hmirror(m));
-  m = umax(m, dpp_mirror(m));
-  m = umax(m, swz_xor16(m));
-  m = umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
-  __shared__ uint32_t wm[4];
-  if (lane == 0) wm[wave] = m;
-  __syncthreads();
-  if ((int)threadIdx.x < a.n_groups) {
-    const uint32_t v = (int)threadIdx.x == T.group ? umax(umax(wm[0], wm[1]), umax(wm[2], wm[3])) : 0u;
-    a.partial[threadIdx.x * gridDim.x + b] = v;
+  if constexpr (!QDQ) {
+    // workgroup maximum -> partial[g * grid + b]: this descriptor's group, 0 for the others
+    m = umax(m, dpp_xor1(m));
+    m = umax(m, dpp_xor2(m));
+    m = umax(m, dpp_hmirror(m));
+    m = umax(m, dpp_mirror(m));
+    m = umax(m, swz_xor16(m));
+    m = umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
+    __shared__ uint32_t wm[4];
+    if (lane == 0) wm[wave] = m;
+    __syncthreads();
+    if ((int)threadIdx.x < a.n_groups) {
+      const uint32_t v = (int)threadIdx.x == T.group ? umax(umax(wm[0], wm[1]), umax(wm[2], wm[3])) : 0u;
+      a.partial[threadIdx.x * gridDim.x + b] = v;
+    }
   }
 }
 
@@ -232,7 +260,8 @@ __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumula
 //     the B operand read transposed from LDS (each lane gathers 8 rows of one column);
 //     wave w owns columns 128w .. 128w+127 of the slab and sums over all rows of the
 //     unit, giving one partial per unit (k_lora_dA_reduce adds the units in order).
-// One pass instead of one per gradient: 78 us instead of 149 us for 8 experts.
+// One pass instead of one per gradient: 149 us for 8 experts with a pass per gradient,
+// 73 us now (with both reduces, from cold caches).
 // Staged rows are 1040 bytes apart (16 B of padding) and rows 16..31 swap their 16-byte
 // chunks in pairs, so the natural reads (16 rows, one chunk) and the transposed reads
 // (4 groups of 8 rows, two chunks) both hit distinct banks.
@@ -291,26 +320,55 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   }
   // dA: B rows of the chunk transposed: lane l supplies adapter l%16, rows 8 (l/16) .. +7
   const __amdgpu_buffer_rsrc_t rbb = make_buf(T.B + r0 * r, (int64_t)rows * r * 2);
+  // dB partials of this unit's rows in this slab
+  const __amdgpu_buffer_rsrc_t rdbp =
+      make_buf(T.dB_partial + ((int64_t)slab * T.rows + r0) * LORA_MAX_R, (int64_t)rows * LORA_MAX_R * 4);
+
+  // a chunk's B values for dA (rows past the end and adapters past r read 0), loaded
+  // as 8 half words and packed into the MFMA operand only where it is used, so that
+  // nothing waits for these loads when they are issued
+  // (one 32-bit register per half word: packed 16-bit lanes would be merged, and
+  // waited for, right at the load)
+  auto load_bt = [&](int ci, uint32_t (&raw)[8]) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const uint32_t row = 32u * ci + 8u * lq + t;
+      const uint32_t off = ((int)l16 < r) ? (row * (uint32_t)r + l16) * 2u : BUF_OOR;
+      raw[t] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rbb, (int)off, 0, 0);
+    }
+  };
+  auto pack_bt = [&](const uint32_t (&raw)[8]) {
+    const uint4 w = make_uint4(raw[0] | (raw[1] << 16), raw[2] | (raw[3] << 16), raw[4] | (raw[5] << 16),
+                               raw[6] | (raw[7] << 16));
+    return __builtin_bit_cast(bf16x8_t, w);
+  };
 
   f32x4_t accA[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) accA[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Loads complete in issue order.  Each iteration computes chunk ci from LDS, stores
+  // its dB partials, then waits for chunk ci + 1 (B values requested before G rows),
+  // stages it into the other buffer and requests chunk ci + 2: the wait at the staging
+  // point covers exactly the oldest 16 loads, on the first iteration as on the others.
+  // Chunks past the unit's last row lie outside the resources and read zeros (no
+  // memory traffic).
+  uint32_t braw[8], braw_next[8];
+  load_bt(0, braw);
+  LORA_FENCE();
   load_chunk(0);
+  LORA_FENCE();
+  stage_chunk(gl);
+  bf16x8_t bt = pack_bt(braw);
+  LORA_FENCE();
+  load_bt(1, braw_next);
+  LORA_FENCE();
+  load_chunk(1);
+  LORA_FENCE();
 #pragma unroll 1
   for (int ci = 0; ci < nchunk; ++ci) {
     uint8_t* buf = gl + (ci & 1) * GR_BUF;
-    stage_chunk(buf);
-    load_chunk(min(ci + 1, nchunk - 1));                  // the last chunk reloads itself
-    // this chunk's B values for dA (rows past the end and adapters past r read 0)
-    bf16x8_t bt;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const uint32_t row = 32u * ci + 8u * lq + t;
-      const uint32_t off = ((int)l16 < r) ? (row * (uint32_t)r + l16) * 2u : BUF_OOR;
-      bt[t] = __builtin_bit_cast(__bf16, (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(rbb, (int)off, 0, 0));
-    }
-    __syncthreads();                                       // the chunk is in LDS
+    __syncthreads();                                       // chunk ci is in LDS
     // dB over this wave's 128 columns, both 16-row groups of the chunk
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
@@ -335,15 +393,27 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
       accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, gt, accA[j], 0, 0, 0);
     }
     __syncthreads();                                       // red is complete
-    // dB partial of this slab: lane t adds the 4 waves' sums for 2 of the 512 outputs
+    // dB partial of this slab: lane t adds the 4 waves' sums for 2 of the 512 outputs.
+    // The stores are unconditional (outputs past r or past the last row get an
+    // out-of-range offset), so every iteration issues the same number of memory
+    // operations and the next chunk's wait need not cover these stores.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t o = tid + 256u * h;                  // (group, row-in-group, adapter)
       const uint32_t g = o >> 8, rr = (o >> 4) & 15u, k = o & 15u;
       const float v = ((red[0][g][o & 255u] + red[1][g][o & 255u]) + red[2][g][o & 255u]) + red[3][g][o & 255u];
-      const int64_t row = r0 + 32 * ci + 16 * g + rr;
-      if ((int)k < r && row < T.rows) T.dB_partial[((int64_t)slab * T.rows + row) * LORA_MAX_R + k] = v;
+      const uint32_t row = 32u * ci + 16u * g + rr;        // within the unit
+      const uint32_t off = ((int)k < r && (int)row < rows) ? (row * LORA_MAX_R + k) * 4u : BUF_OOR;
+      buf_store4(rdbp, off, __float_as_uint(v));
     }
+    LORA_FENCE();
+    stage_chunk(gl + ((ci + 1) & 1) * GR_BUF);             // last read by chunk ci - 1
+    bt = pack_bt(braw_next);
+    LORA_FENCE();
+    load_bt(ci + 2, braw_next);
+    LORA_FENCE();
+    load_chunk(ci + 2);
+    LORA_FENCE();
   }
   // dA partial of this unit: lane holds adapters 4 (l/16) + e of columns 128 w + 16 j + l%16
   float* part = T.dA_partial + (int64_t)rb * LORA_MAX_R * cols + cs;
@@ -382,9 +452,18 @@ static bool all_rank16(const LoraArgs& a) {
 hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   if (all_rank16(a))
-    hipLaunchKernelGGL(k_lora_merge<LORA_MAX_R>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_lora_merge<LORA_MAX_R, false>), dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL(k_lora_merge<0>, dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_lora_merge<0, false>), dim3(grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_merge_qdq(const LoraArgs& a, int grid, hipStream_t s) {
+  if (grid == 0) return hipSuccess;
+  if (all_rank16(a))
+    hipLaunchKernelGGL((k_lora_merge<LORA_MAX_R, true>), dim3(grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_lora_merge<0, true>), dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

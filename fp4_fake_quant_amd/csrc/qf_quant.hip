@@ -133,51 +133,12 @@ __global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
 #pragma unroll
   for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
-    uint32_t m = amax_bits8(w[j]);
-    m = umax(m, dpp_xor1(m));
-    const float amax = __uint_as_float(m << 16);
-    const uint32_t S = e4m3_encode(amax / k);
-    const float s = e4m3_value(S);
-    const float d = s * s_t;
-    const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
-    const uint32_t wv[4] = {w[j].x, w[j].y, w[j].z, w[j].w};
-    float y[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      y[2 * e] = bf16_lo(wv[e]) * r;
-      y[2 * e + 1] = bf16_hi(wv[e]) * r;
-    }
-    if (__builtin_expect(r > FLT_MAX, 0)) {
-      // 1/d overflowed (the whole tied group lies below ~1e-35): 0 * inf must still
-      // give magnitude 0 with the element's own sign.
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf16_lo(wv[e]), hi = bf16_hi(wv[e]);
-        if (lo == 0.0f) y[2 * e] = lo;
-        if (hi == 0.0f) y[2 * e + 1] = hi;
-      }
-    }
-    uint32_t codes = 0;
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[0], y[1], 1.0f, 0);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[4], y[5], 1.0f, 2);
-    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[6], y[7], 1.0f, 3);
+    const Nvfp4Chunk q = nvfp4_qdq_chunk(w[j], s_t, k);
     if (c < T.nchunks) {
-      if (WY) {
-        f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-        f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-        f32x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-        f32x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-        uint4 o;
-        o.x = pack_bf16x2((v0.x * s) * s_t, (v0.y * s) * s_t);
-        o.y = pack_bf16x2((v1.x * s) * s_t, (v1.y * s) * s_t);
-        o.z = pack_bf16x2((v2.x * s) * s_t, (v2.y * s) * s_t);
-        o.w = pack_bf16x2((v3.x * s) * s_t, (v3.y * s) * s_t);
-        *reinterpret_cast<uint4*>(T.y + chunk_offset(c, T.cpr, T.ldy, T.contig_y)) = o;
-      }
+      if (WY) *reinterpret_cast<uint4*>(T.y + chunk_offset(c, T.cpr, T.ldy, T.contig_y)) = q.y;
       if (WP) {
-        reinterpret_cast<uint32_t*>(T.codes)[c] = codes;
-        if ((threadIdx.x & 1) == 0) T.scales[c >> 1] = (uint8_t)S;
+        reinterpret_cast<uint32_t*>(T.codes)[c] = q.codes;
+        if ((threadIdx.x & 1) == 0) T.scales[c >> 1] = (uint8_t)q.S;
       }
     }
   }

@@ -199,7 +199,10 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
  *   W  bf16 [rows, ldw] frozen base;  A bf16 [r, cols] and B bf16 [rows, r],
  *      both contiguous;  r in 1..16.
  *   M  bf16 [rows, cols] contiguous scratch for the merged weight (written by
- *      pass 1, read by pass 2; one expert's worth is the bounded scratch).
+ *      pass 1, read by pass 2; one expert's worth is the bounded scratch), or
+ *      NULL: pass 1 then only takes the maximum and pass 2 merges again from W,
+ *      A and B in registers (same bits, no scratch, one read of W instead of a
+ *      write and a read of M).
  *   y, codes, scales  pass-2 outputs as in qf_qdq_pack_nvfp4 (y contiguous,
  *      ldy = cols; y or codes may be NULL to skip it).
  *   G  bf16 [rows, cols] contiguous; dA fp32 [r, cols]; dB fp32 [rows, r].
@@ -239,11 +242,13 @@ typedef struct qf_lora_desc {
 /* Device workspace (bytes) the LoRA calls need for these descriptors (0 when a
  * descriptor is invalid). */
 size_t qf_lora_workspace(const qf_lora_desc* d, int n);
-/* Pass 1: merge into M and the NVFP4 tensor scale of every tied group
- * (d_scales[g] as in qf_nvfp4_tensor_scale_grouped, computed from M). */
+/* Pass 1: merge into M (skipped for M == NULL) and the NVFP4 tensor scale of
+ * every tied group (d_scales[g] as in qf_nvfp4_tensor_scale_grouped, computed
+ * from the merged values). */
 qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
                                            uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream);
-/* Pass 2: NVFP4 QDQ + pack of M (exactly qf_qdq_pack_nvfp4 on M with d_scales[group]). */
+/* Pass 2: NVFP4 QDQ + pack of the merged weight (exactly qf_qdq_pack_nvfp4 on M
+ * with d_scales[group]); descriptors with M == NULL merge again from W, A, B. */
 qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_scales, void* stream);
 /* STE to the adapters: dB = G . A^T, dA = B^T . G (fp32; accumulate != 0 adds). */
 qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,

@@ -122,8 +122,24 @@ def test_lora_validation():
     d[1].B = 0x10300002                                             # B must be 4-byte aligned
     assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 3
     d[1].B = 0x10300000
-    d[0].M = 0
+    d[0].W = 0                                                      # W is needed (M may be NULL)
     assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need, None) == 1
+    d[0].W = 0x10000000
+    # QDQ pass: an output is required; without M, W / A / B are read and checked
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 1            # no y and no codes
+    d[0].y, d[1].y = 0x10800000, 0x10900000
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, None, None) == 1         # no tensor scales
+    d[0].M = 0
+    d[0].W = 0x10000008                                             # W must be 16-byte aligned
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 3
+    d[0].W = 0x10000000
+    d[0].A = 0
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 1
+    d[0].A = 0x10200000
+    d[0].y = 0x10800008                                             # y must be 16-byte aligned
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 3
+    d[0].group = -1
+    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 7
     assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 17, q, None) == 7
     d[0].rows = d[1].rows = 0                                       # empty: nothing to do
     assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, 4, None) == 0
