@@ -375,14 +375,17 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da
 
 // Merge units shrink (32 -> 16 -> 8 rows) until a launch has at least two workgroups
 // per CU, so that one expert alone still fills the chip (one expert per launch: merge
-// 3.53 -> 3.08 ms per 128 experts).  dA keeps 256-row workgroups: smaller ones multiply
-// the fp32 partials, which cost more than the idle CUs (64 rows: grads 8.4 -> 10.1 ms).
+// 3.53 -> 3.08 ms per 128 experts).  Gradient workgroups take 512 rows when that still
+// gives one workgroup per CU, else 256: fewer fp32 partials and all workgroups resident
+// at once (8 experts per launch: 73.8 -> 69.0 us from cold caches); smaller ones multiply
+// the partials, which cost more than the idle CUs (64 rows: grads 8.4 -> 10.1 ms).
 // A function of the descriptors only, so the workspace size and the launches agree.
 LoraCounts lora_layout(const qf_lora_desc* d, int n, qf::LoraArgs* a, float* dA_part) {
   constexpr int64_t FILL = 2 * 256;
   int mr = qf::LORA_ROWS;
-  const int dr = qf::LORA_DA_ROWS;
+  int dr = qf::LORA_DA_ROWS_MAX;
   while (mr > 8 && lora_layout_with(d, n, mr, dr, nullptr, nullptr).merge_wg < FILL) mr /= 2;
+  if (lora_layout_with(d, n, mr, dr, nullptr, nullptr).grad_wg < 256) dr = qf::LORA_DA_ROWS;
   return lora_layout_with(d, n, mr, dr, a, dA_part);
 }
 

@@ -82,7 +82,8 @@ struct ReduceArgs {
 constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
 constexpr int LORA_SLAB = 512;      // columns per wave: 64 lanes x 8
 constexpr int LORA_ROWS = 32;       // rows per merge unit (at most; smaller for small launches)
-constexpr int LORA_DA_ROWS = 256;   // rows per gradient workgroup, one dA partial each
+constexpr int LORA_DA_ROWS = 256;       // rows per gradient workgroup (one dA partial each), or
+constexpr int LORA_DA_ROWS_MAX = 512;   // twice that when the launch still has a workgroup per CU
 
 // A unit is one wave's work: a slab of LORA_SLAB columns of a run of rows.  Units
 // of a descriptor are numbered row block major, and every descriptor starts on a
@@ -112,7 +113,7 @@ struct LoraArgs {
   int n;
   int n_groups;        // rows of merge partials
   int merge_rows;      // rows per merge unit (32, 16 or 8)
-  int da_rows;         // rows per gradient workgroup (LORA_DA_ROWS, a multiple of 32)
+  int da_rows;         // rows per gradient workgroup (LORA_DA_ROWS or LORA_DA_ROWS_MAX)
   uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
   const float* tscale; // merge-and-QDQ: NVFP4 tensor scale of every tied group
 };

@@ -247,8 +247,8 @@ __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumula
 }
 
 // --------------------------------------------- fused adapter gradients ---
-// One pass over G for both gradients.  A workgroup owns a unit of up to LORA_DA_ROWS
-// rows of one LORA_SLAB-column slab and walks it 32 rows at a time: the
+// One pass over G for both gradients.  A workgroup owns a unit of up to a.da_rows (256
+// or 512) rows of one LORA_SLAB-column slab and walks it 32 rows at a time: the
 // 32 x 512 chunk of G is loaded with 16-byte coalesced loads (a wave instruction covers
 // one row of the slab), the next chunk's loads are issued, and the chunk is written to
 // LDS, where both gradients read it on the 16x16x32 BF16 MFMA:

@@ -145,6 +145,20 @@ def test_lora_validation():
     assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, 4, None) == 0
 
 
+def test_lora_gradient_unit_rows():
+    """Gradient workgroups take 512 rows when that still gives 256 of them, else 256
+    (the workspace holds one dA partial per unit): 16 matrices of 600 x 4096 take 2 units
+    of 512 rows each, 2 such matrices take 3 of 256."""
+    L = _lib.lib()
+    d = (_lib.LoraDesc * 16)()
+    for i in range(16):
+        d[i].W, d[i].rows, d[i].cols, d[i].ldw = 0x10000000, 600, 4096, 4096
+        d[i].A, d[i].B, d[i].r, d[i].group = 0x10200000, 0x10300000, 16, i
+    dB = 8 * 600 * 16                                              # 8 slabs per matrix
+    assert L.qf_lora_workspace(ctypes.byref(d), 16) == 4 * 16 * (2 * 16 * 4096 + dB)
+    assert L.qf_lora_workspace(ctypes.byref(d), 2) == 4 * 2 * (3 * 16 * 4096 + dB)
+
+
 def test_gemm_validation():
     """GEMM entry points check flags, K and alignment before launching."""
     L = _lib.lib()

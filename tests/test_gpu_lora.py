@@ -228,3 +228,17 @@ def test_lora_without_scratch_full_size_expert():
         assert_same(host(it["y"])[rows_], nvfp4.dequantize(c, S, s_want[i]), f"y[{i}] sampled rows")
         assert_same(u8(it["codes"])[rows_], pc, f"codes[{i}] sampled rows")
         assert_same(u8(it["scales"])[rows_], ps, f"block scales[{i}] sampled rows")
+
+
+def test_lora_grads_512_row_units():
+    """16 descriptors of 600 x 4096 fill the chip with 512-row gradient units (ragged
+    second unit of 88 rows): dA and dB of every descriptor within the bound, mixed ranks."""
+    ranks = [16, 16, 7, 16, 1, 16, 16, 9, 16, 16, 16, 3, 16, 16, 16, 16]
+    cases = [make_case(600, 4096, r, seed=200 + i) for i, r in enumerate(ranks)]
+    items = [device_item(c, i) for i, c in enumerate(cases)]
+    b = fq.LoraBatch(items)
+    assert b.workspace_bytes == 4 * (16 * 2 * 16 * 4096 + 16 * 8 * 600 * 16)   # 2 dA blocks per matrix
+    fq.qf_lora_adapter_grads(b)
+    torch.cuda.synchronize()
+    for i, (c, it) in enumerate(zip(cases, items)):
+        check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"desc {i}")
