@@ -298,12 +298,11 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   const bool col_ok = cs + 8 * (int64_t)lane < cols;
   const uint32_t goff = col_ok ? ((tid >> 6) * (uint32_t)cols + 8u * lane) * 2u : BUF_OOR;
   const uint32_t gstep = (uint32_t)(4 * cols) * 2u, gchunk = (uint32_t)(GR_ROWS * cols) * 2u;
-  uint4 gv[8];
-  auto load_chunk = [&](int ci) {
+  auto load_chunk = [&](int ci, uint4 (&gv)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) gv[i] = buf_load16(rg, goff + i * gstep + (uint32_t)ci * gchunk);
   };
-  auto stage_chunk = [&](uint8_t* buf) {
+  auto stage_chunk = [&](uint8_t* buf, const uint4 (&gv)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(buf + gr_off((tid >> 6) + 4u * i, lane)) = gv[i];
   };
@@ -347,26 +346,14 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) accA[j] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // Loads complete in issue order.  Each iteration computes chunk ci from LDS, stores
-  // its dB partials, then waits for chunk ci + 1 (B values requested before G rows),
-  // stages it into the other buffer and requests chunk ci + 2: the wait at the staging
-  // point covers exactly the oldest 16 loads, on the first iteration as on the others.
-  // Chunks past the unit's last row lie outside the resources and read zeros (no
-  // memory traffic).
-  uint32_t braw[8], braw_next[8];
-  load_bt(0, braw);
-  LORA_FENCE();
-  load_chunk(0);
-  LORA_FENCE();
-  stage_chunk(gl);
-  bf16x8_t bt = pack_bt(braw);
-  LORA_FENCE();
-  load_bt(1, braw_next);
-  LORA_FENCE();
-  load_chunk(1);
-  LORA_FENCE();
-#pragma unroll 1
-  for (int ci = 0; ci < nchunk; ++ci) {
+  // Loads complete in issue order.  Each step computes chunk ci from LDS and stores its
+  // dB partials, then waits for chunk ci + 1, stages it into the other buffer and
+  // requests chunk ci + 2 into the registers it came from (B values before G rows), so
+  // the wait at the staging point covers exactly the oldest 16 loads, the same on every
+  // step.  (Two chunks in flight instead of one, in a second register set, measured
+  // the same.)  Chunks past the unit's last row lie outside the resources and read
+  // zeros, with no memory traffic.
+  auto compute_chunk = [&](int ci, const bf16x8_t& bt) {
     uint8_t* buf = gl + (ci & 1) * GR_BUF;
     __syncthreads();                                       // chunk ci is in LDS
     // dB over this wave's 128 columns, both 16-row groups of the chunk
@@ -395,8 +382,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
     __syncthreads();                                       // red is complete
     // dB partial of this slab: lane t adds the 4 waves' sums for 2 of the 512 outputs.
     // The stores are unconditional (outputs past r or past the last row get an
-    // out-of-range offset), so every iteration issues the same number of memory
-    // operations and the next chunk's wait need not cover these stores.
+    // out-of-range offset), so every step issues the same number of memory operations.
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t o = tid + 256u * h;                  // (group, row-in-group, adapter)
@@ -407,13 +393,35 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
       buf_store4(rdbp, off, __float_as_uint(v));
     }
     LORA_FENCE();
-    stage_chunk(gl + ((ci + 1) & 1) * GR_BUF);             // last read by chunk ci - 1
-    bt = pack_bt(braw_next);
+  };
+  // stage chunk ci + 1 (its buffer was last read by chunk ci - 1) and refill its registers
+  auto stage_and_refill = [&](int ci, uint4 (&gv)[8], uint32_t (&braw)[8], bf16x8_t& bt) {
+    stage_chunk(gl + ((ci + 1) & 1) * GR_BUF, gv);
+    bt = pack_bt(braw);
     LORA_FENCE();
-    load_bt(ci + 2, braw_next);
+    load_bt(ci + 2, braw);
     LORA_FENCE();
-    load_chunk(ci + 2);
+    load_chunk(ci + 2, gv);
     LORA_FENCE();
+  };
+  bf16x8_t bt;
+  uint4 gv[8];
+  uint32_t braw[8];
+  load_bt(0, braw);
+  LORA_FENCE();
+  load_chunk(0, gv);
+  LORA_FENCE();
+  stage_chunk(gl, gv);
+  bt = pack_bt(braw);
+  LORA_FENCE();
+  load_bt(1, braw);
+  LORA_FENCE();
+  load_chunk(1, gv);
+  LORA_FENCE();
+#pragma unroll 1
+  for (int ci = 0; ci < nchunk; ++ci) {
+    compute_chunk(ci, bt);
+    stage_and_refill(ci, gv, braw, bt);
   }
   // dA partial of this unit: lane holds adapters 4 (l/16) + e of columns 128 w + 16 j + l%16
   float* part = T.dA_partial + (int64_t)rb * LORA_MAX_R * cols + cs;
