@@ -368,16 +368,21 @@ class W4A4GemmMXFP4:
         t("gemm_mxfp4_fused", 1)
 
     def controls(self, reps=10):
-        """ms of the plain-BF16 run of the same kernel, of torch.matmul, and of the same
-        W4A4 product on the MXFP4 matrix cores: both operands quantized in the kernel; W
-        pre-packed by qf_pack_mxfp4 with X quantized in the kernel; both pre-packed (the
-        packs are timed on their own)."""
+        """ms of the plain-BF16 run of the same kernel, of torch.matmul, of the NVFP4 W4A4
+        form of the fused kernel (tensor scales of X and W from the tensor-scale pass, timed
+        on their own), and of the same MXFP4 W4A4 product on the MXFP4 matrix cores: both
+        operands quantized in the kernel; W pre-packed by qf_pack_mxfp4 with X quantized in
+        the kernel; both pre-packed (the packs are timed on their own)."""
         torch = self.torch
         fq = self.fq
         out = {}
         Wc, Ws = fq.qf_pack_mxfp4(self.W)
         Xc, Xs = fq.qf_pack_mxfp4(self.X)
+        sx, sw = fq.qf_nvfp4_tensor_scale(self.X), fq.qf_nvfp4_tensor_scale(self.W)
         for name, fn in (("gemm_bf16_same_kernel", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
+                         ("w4a4_nvfp4_fused", lambda: fq.qf_gemm_nvfp4(self.X, self.W, sx, sw, self.Y)),
+                         ("tensor_scales_nvfp4", lambda: (fq.qf_nvfp4_tensor_scale(self.X, sx),
+                                                          fq.qf_nvfp4_tensor_scale(self.W, sw))),
                          ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y)),
                          ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
                          ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
@@ -394,7 +399,7 @@ class W4A4GemmMXFP4:
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            if name.startswith("pack_"):
+            if name.startswith(("pack_", "tensor_scales")):
                 out[name] = {"ms": round(ms, 4)}
                 continue
             tf = self.flop / ms / 1e9

@@ -309,6 +309,24 @@ def qf_gemm_mxfp4(X, W, Y=None, flags=QF_QDQ_A | QF_QDQ_W):
     return Y
 
 
+def qf_gemm_nvfp4(X, W, d_scale_x, d_scale_w, Y=None, flags=QF_QDQ_A | QF_QDQ_W):
+    """Y[M, N] = QDQ(X) . QDQ(W)^T on the NVFP4 grid with the device fp32 tensor scales
+    d_scale_x, d_scale_w (one element each; None for an operand that is not quantized)."""
+    M, K, ldx = _mat(_bf16(X, "X"), "X")
+    N, K2, ldw = _mat(_bf16(W, "W"), "W")
+    if K2 != K:
+        raise ValueError(f"X has K={K} but W has K={K2}")
+    for t, name in ((d_scale_x, "d_scale_x"), (d_scale_w, "d_scale_w")):
+        if t is not None and (t.dtype != torch.float32 or t.device.type != "cuda"):
+            raise TypeError(f"{name} must be a float32 device tensor")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    _bf16(Y, "Y")
+    _check(lib().qf_gemm_nvfp4(_p(X), ldx, _p(W), ldw, _p(Y), _mat(Y, "Y")[2], M, N, K, int(flags), _p(d_scale_x),
+                               _p(d_scale_w), _stream()), "qf_gemm_nvfp4")
+    return Y
+
+
 def qf_gemm_mxfp4_packed_w(X, Wc, Ws, Y=None):
     """Y[M, N] = QDQ(X) . dequant(Wc, Ws)^T on the MXFP4 matrix cores; Wc [N, K/2] and
     Ws [N, K/32] uint8 as qf_pack_mxfp4 writes them (contiguous)."""

@@ -526,6 +526,23 @@ qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
                                           (hipStream_t)stream));
 }
 
+qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
+                        int64_t M, int64_t N, int64_t K, unsigned flags, const float* d_scale_x,
+                        const float* d_scale_w, void* stream) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
+  if ((flags & ~(QF_QDQ_A | QF_QDQ_W)) || flags == 0) return QF_ERR_ARG;
+  if (M == 0 || N == 0) return QF_OK;
+  if (!X || !W || !Y) return QF_ERR_NULL;
+  if (((flags & QF_QDQ_A) && !d_scale_x) || ((flags & QF_QDQ_W) && !d_scale_w)) return QF_ERR_NULL;
+  if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 2) || ldx % 8 || ldw % 8) return QF_ERR_ALIGN;
+  if ((d_scale_x && !aligned(d_scale_x, 4)) || (d_scale_w && !aligned(d_scale_w, 4))) return QF_ERR_ALIGN;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_gemm_nvfp4(X, ldx, W, ldw, Y, ldy, (int)M, (int)N, (int)K, flags, d_scale_x, d_scale_w,
+                                          (hipStream_t)stream));
+}
+
 qf_status qf_gemm_mxfp4_packed(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
                                int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;

@@ -91,20 +91,27 @@ __device__ __forceinline__ uint4 load_chunk_buf(__amdgpu_buffer_rsrc_t r, uint32
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
-template <bool QDQ>
-__device__ __forceinline__ void store_chunk(uint8_t* lds, uint32_t r, uint32_t c, uint4 v) {
-  const uint4 q = QDQ ? mxfp4_qdq_chunk(v) : v;
+// Grids of the in-kernel quantizer: MXFP4 (block 32 along K, E8M0 scale; lanes 4i..4i+3
+// hold one block) or NVFP4 (block 16 along K, E4M3 scale under the operand's FP32 tensor
+// scale s_t; lanes 2i and 2i+1 hold one block, the pairing nvfp4_qdq_chunk needs).
+enum { GRID_MX = 0, GRID_NV = 1 };
+
+template <int GRID, bool QDQ>
+__device__ __forceinline__ void store_chunk(uint8_t* lds, uint32_t r, uint32_t c, uint4 v, float s_t, float k6) {
+  uint4 q = v;
+  if constexpr (QDQ) q = GRID == GRID_MX ? mxfp4_qdq_chunk(v) : nvfp4_qdq_chunk(v, s_t, k6).y;
   *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = q;
 }
 
 #define QF_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-template <bool QA, bool QW>
-__global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
-                                                            const uint16_t* __restrict__ W, int64_t ldw,
-                                                            uint16_t* __restrict__ Y, int64_t ldy,
-                                                            int M, int N, int K, int y_vec) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];   // 128 KiB of the 160 KiB
+// The workgroup's 256 x 256 tile of Y; smem is the kernel's 128 KiB of LDS, sx / sw the
+// NVFP4 tensor scales of X and W (unused for MXFP4).
+template <int GRID, bool QA, bool QW>
+__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W,
+                                          int64_t ldw, uint16_t* __restrict__ Y, int64_t ldy, int M, int N, int K,
+                                          int y_vec, float sx, float sw, uint8_t* smem) {
+  const float kx = 6.0f * sx, kw = 6.0f * sw;
 
   // ---- tile of this workgroup (XCD-aware grouped order) ----
   const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
@@ -145,8 +152,8 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __rest
     else raw[idx] = load_chunk_buf(rw, woff + (idx - G_LOADS) * wstep + kbyte);
   };
   auto stage_chunk = [&](int idx, uint8_t* stage) {
-    if (idx < G_LOADS) store_chunk<QA>(stage, lrow + 64 * idx, lchunk, raw[idx]);
-    else store_chunk<QW>(stage + G_SLICE_BYTES, lrow + 64 * (idx - G_LOADS), lchunk, raw[idx]);
+    if (idx < G_LOADS) store_chunk<GRID, QA>(stage, lrow + 64 * idx, lchunk, raw[idx], sx, kx);
+    else store_chunk<GRID, QW>(stage + G_SLICE_BYTES, lrow + 64 * (idx - G_LOADS), lchunk, raw[idx], sw, kw);
   };
 
   const int nk = K / GBK;
@@ -241,6 +248,44 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __rest
       }
     }
   }
+}
+
+template <bool QA, bool QW>
+__global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
+                                                            const uint16_t* __restrict__ W, int64_t ldw,
+                                                            uint16_t* __restrict__ Y, int64_t ldy,
+                                                            int M, int N, int K, int y_vec) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];   // 128 KiB of the 160 KiB
+  gemm_tile<GRID_MX, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, 1.0f, 1.0f, smem);
+}
+
+// NVFP4 W4A4: the tensor scales come from device memory (computed by the tensor-scale
+// pass, or any fp32 the caller keeps there, e.g. a tracked activation maximum).
+template <bool QA, bool QW>
+__global__ __launch_bounds__(G_THREADS) void k_gemm_nvfp4(const uint16_t* __restrict__ X, int64_t ldx,
+                                                            const uint16_t* __restrict__ W, int64_t ldw,
+                                                            uint16_t* __restrict__ Y, int64_t ldy,
+                                                            int M, int N, int K, int y_vec,
+                                                            const float* __restrict__ d_sx,
+                                                            const float* __restrict__ d_sw) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];
+  gemm_tile<GRID_NV, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, QA ? *d_sx : 1.0f, QW ? *d_sw : 1.0f, smem);
+}
+
+hipError_t launch_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
+                             int64_t ldy, int M, int N, int K, unsigned flags, const float* d_sx, const float* d_sw,
+                             hipStream_t s) {
+  const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
+  const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
+  const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  const dim3 g(tiles), b(G_THREADS);
+  if (qa && qw)
+    hipLaunchKernelGGL((k_gemm_nvfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
+  else if (qa)
+    hipLaunchKernelGGL((k_gemm_nvfp4<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
+  else
+    hipLaunchKernelGGL((k_gemm_nvfp4<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,

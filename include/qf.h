@@ -305,6 +305,22 @@ qf_status qf_gemm_mxfp4_packed_w(const uint16_t* X, int64_t ldx, const uint8_t* 
 qf_status qf_gemm_mxfp4_packed(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws,
                                uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream);
 
+/* ------------------------------------------------- W4A4 NVFP4 GEMM ---- */
+/* Y = QDQ(X) . QDQ(W)^T on the NVFP4 grid, the same product as qf_gemm_mxfp4 with
+ * the NVFP4 rule of qf_qdq_nvfp4 along K ("Supported formats": E2M1 elements, an
+ * E4M3 scale per 16-block, an FP32 tensor scale; "Overview": activations may be
+ * quantized too).  X is quantized with the tensor scale *d_scale_x and W with
+ * *d_scale_w (device fp32 each, e.g. from qf_nvfp4_tensor_scale over the operand, or
+ * an activation scale the caller tracks across steps: the kernel reads whatever is
+ * there when it runs).  flags: QF_QDQ_A and/or QF_QDQ_W, not 0 (QF_ERR_ARG); the
+ * scale of each quantized operand must be given (QF_ERR_NULL).  Everything else as
+ * qf_gemm_mxfp4 (constraints, the BF16 matrix cores, the accuracy statement); a scale
+ * pointer that is given must be 4-byte aligned (QF_ERR_ALIGN).  There
+ * is no FP4-core form: the cores' block scales are E8M0, and NVFP4's are E4M3. */
+qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                        uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
+                        unsigned flags, const float* d_scale_x, const float* d_scale_w, void* stream);
+
 /* ---------------------------------------------------- conformance test ---- */
 /* Checks on the device that the gfx950 instructions and shortcuts the kernels
  * rely on agree bit for bit with the software definitions above, over their

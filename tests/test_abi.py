@@ -168,6 +168,14 @@ def test_gemm_validation():
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 8, None) == 7        # unknown flag
     assert L.qf_gemm_mxfp4(p, 96, q, 96, y, 64, 64, 64, 96, 3, None) == 2        # K not a multiple of 64
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 0, 64, 64, 7, None) == 0         # empty: no-op
+    s = _addr(0x10c00000)
+    assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 0, s, s, None) == 7   # no operand quantized
+    assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 7, s, s, None) == 7   # no FP4-core form
+    assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 3, None, s, None) == 1
+    assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 3, s, None, None) == 1
+    assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 2, _addr(0x10c00002), s, None) == 3   # unused, but misaligned
+    assert L.qf_gemm_nvfp4(p, 96, q, 96, y, 64, 64, 64, 96, 3, s, s, None) == 2   # K not a multiple of 64
+    assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 0, 64, 3, s, s, None) == 0    # empty: no-op
     xs, ws = _addr(0x10C00000), _addr(0x10E00000)
     assert L.qf_gemm_mxfp4_packed(p, xs, q, ws, y, 64, 64, 64, 64, None) == 2    # K not a multiple of 128
     assert L.qf_gemm_mxfp4_packed(p, _addr(0x10C00002), q, ws, y, 64, 64, 64, 128, None) == 3   # exponents 4-byte aligned

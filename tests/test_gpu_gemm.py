@@ -12,7 +12,7 @@ import torch
 
 import fp4_fake_quant_amd as fq
 import workloads
-from oracle import gemm, mxfp4
+from oracle import gemm, mxfp4, nvfp4
 from oracle import primitives as P
 from tests.gpu_util import dev, host, sample_rows
 
@@ -123,3 +123,79 @@ def test_gemm_w4a4_full_size_sampled():
         rel = _check(Ys, Xq, Wq, X.shape[1], f"full size, {name}")
         assert rel < 2e-3
         del Y
+
+
+# ----------------------------------------------------------- NVFP4 W4A4 ----
+def _nv_scale(bits):
+    """The operand's tensor scale on the device (qf_nvfp4_tensor_scale) after checking it
+    against the oracle's, so both sides quantize with the same fp32."""
+    s_dev = fq.qf_nvfp4_tensor_scale(dev(bits))
+    s_ref = nvfp4.tensor_scale([bits])
+    torch.cuda.synchronize()
+    assert np.float32(s_dev.cpu().numpy()[0]).view(np.uint32) == np.float32(s_ref).view(np.uint32)
+    return s_dev, s_ref
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 64), (300, 200, 128), (33, 517, 192), (1, 1, 64), (513, 257, 256)])
+@pytest.mark.parametrize("flags", [3, 1, 2])
+def test_gemm_nvfp4_small_shapes(shape, flags):
+    M, N, K = shape
+    X, W = _ops(M, N, K)
+    sx, sx_ref = _nv_scale(X)
+    sw, sw_ref = _nv_scale(W)
+    Y = fq.qf_gemm_nvfp4(dev(X), dev(W), sx if flags & 1 else None, sw if flags & 2 else None, flags=flags)
+    Xq = nvfp4.qdq(X, sx_ref) if flags & 1 else X
+    Wq = nvfp4.qdq(W, sw_ref) if flags & 2 else W
+    _check(host(Y), Xq, Wq, K, f"nvfp4 {shape} flags={flags}")
+
+
+def test_gemm_nvfp4_caller_scales():
+    """The kernel quantizes with whatever fp32 the scale pointers hold (a tracked activation
+    scale): one far below the data's (block scales saturate at 448, codes at 6) and one far
+    above it (many blocks round to zero)."""
+    M, N, K = 192, 320, 256
+    X, W = _ops(M, N, K)
+    for sx_val, sw_val in ((1e-5, 3e-6), (0.5, 0.01)):
+        sx = torch.tensor([sx_val], dtype=torch.float32, device="cuda")
+        sw = torch.tensor([sw_val], dtype=torch.float32, device="cuda")
+        Y = fq.qf_gemm_nvfp4(dev(X), dev(W), sx, sw)
+        _check(host(Y), nvfp4.qdq(X, np.float32(sx_val)), nvfp4.qdq(W, np.float32(sw_val)), K,
+               f"nvfp4 scales {sx_val}, {sw_val}")
+
+
+def test_gemm_nvfp4_strided_outliers_and_zero_rows():
+    M, N, K = 320, 288, 192
+    X, W = _ops(M, N, K)
+    X[:, 5] = P.f32_to_bf16(np.full(M, 300.0, np.float32))     # an outlier channel
+    X[7] = 0
+    X[9] = 0x8000
+    W[3] = 0
+    sx, sx_ref = _nv_scale(X)
+    sw, sw_ref = _nv_scale(W)
+    Xb = torch.zeros((M, K + 64), dtype=torch.bfloat16, device="cuda")
+    Xb[:, 32:32 + K] = dev(X)
+    Wb = torch.zeros((N, K + 128), dtype=torch.bfloat16, device="cuda")
+    Wb[:, :K] = dev(W)
+    Yb = torch.full((M, N + 40), 7.0, dtype=torch.bfloat16, device="cuda")
+    fq.qf_gemm_nvfp4(Xb[:, 32:32 + K], Wb[:, :K], sx, sw, Yb[:, 8:8 + N])
+    Y = host(Yb[:, 8:8 + N])
+    _check(Y, nvfp4.qdq(X, sx_ref), nvfp4.qdq(W, sw_ref), K, "nvfp4 strided")
+    assert torch.all(Yb[:, :8] == 7.0) and torch.all(Yb[:, 8 + N:] == 7.0)
+    assert np.all(P.bf16_to_f32(Y)[7] == 0) and np.all(P.bf16_to_f32(Y)[:, 3] == 0)
+
+
+def test_gemm_nvfp4_full_size_sampled():
+    """NVFP4 W4A4 at the 32768 x 14336 x 4096 shape, tensor scales from the tensor-scale
+    pass; 64 sampled rows x 64 sampled columns against the oracle."""
+    g = workloads.w4a4_gemm()
+    X, W = g["X"], g["W"]
+    rows = sample_rows(X.shape[0], 64, seed=3)
+    cols = sample_rows(W.shape[0], 64, seed=4)
+    sx_ref, sw_ref = nvfp4.tensor_scale([X]), nvfp4.tensor_scale([W])
+    Xd, Wd = dev(X), dev(W)
+    sx, sw = fq.qf_nvfp4_tensor_scale(Xd), fq.qf_nvfp4_tensor_scale(Wd)
+    Y = fq.qf_gemm_nvfp4(Xd, Wd, sx, sw)
+    assert np.float32(sx.cpu().numpy()[0]) == sx_ref and np.float32(sw.cpu().numpy()[0]) == sw_ref
+    Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
+    rel = _check(Ys, nvfp4.qdq(X[rows], sx_ref), nvfp4.qdq(W[cols], sw_ref), X.shape[1], "nvfp4 full size")
+    assert rel < 2e-3
