@@ -257,6 +257,86 @@ class Q4KSet:
                 "sample": f"the oracle's Q4_K QDQ + pack on the first {r} rows of the 4096x4096 matrix ({dt:.1f} s)"}
 
 
+class DequantDense:
+    """Dequant of the dense 8B layer's four matrices (218 M elements) from each packed
+    layout back to bf16: NVFP4 (per-matrix tensor scales), MXFP4 and Q4_K, four launches
+    per format.  The packed inputs are written once, before timing, by the pack calls."""
+    name = "dense_layer_8b_dequant"
+
+    def __init__(self, torch, fq):
+        import workloads
+        self.torch, self.fq = torch, fq
+        x = workloads.dense_layer_8b_device(seed=0)
+        dev = torch.device("cuda")
+        self.mats = []
+        n = 0
+        for w, _ in x.values():
+            rows, cols = w.shape
+            s = fq.qf_nvfp4_tensor_scale(w)
+            nc, ns = fq.qf_pack_nvfp4(w, s)
+            mc, ms = fq.qf_pack_mxfp4(w)
+            qb = fq.qf_pack_q4k(w)
+            self.mats.append(dict(rows=rows, cols=cols, s=s, nc=nc, ns=ns, mc=mc, ms=ms, qb=qb,
+                                  y=torch.empty((rows, cols), dtype=torch.bfloat16, device=dev)))
+            n += w.numel()
+        del x
+        torch.cuda.empty_cache()
+        self.numel = n
+        # algorithmic bytes: packed codes + scale bytes (or 144-byte blocks) in, bf16 out
+        self.kernels = {
+            "dequant_nvfp4": n * (0.5 + 1 / 16 + 2),
+            "dequant_mxfp4": n * (0.5 + 1 / 32 + 2),
+            "dequant_q4k": n * (144 / 256 + 2),
+        }
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {"workload": self.name, "elements": n,
+                       "formats": "NVFP4, MXFP4, Q4_K packed layouts -> bf16"}
+
+    def step(self, mark=None):
+        fq = self.fq
+        t = mark or _no_mark
+        t("dequant_nvfp4", 0)
+        for m in self.mats:
+            fq.qf_dequant_nvfp4(m["nc"], m["ns"], m["s"], m["y"])
+        t("dequant_nvfp4", 1)
+        t("dequant_mxfp4", 0)
+        for m in self.mats:
+            fq.qf_dequant_mxfp4(m["mc"], m["ms"], m["y"])
+        t("dequant_mxfp4", 1)
+        t("dequant_q4k", 0)
+        for m in self.mats:
+            fq.qf_dequant_q4k(m["qb"], m["rows"], m["cols"], m["y"])
+        t("dequant_q4k", 1)
+
+    def cpu_baseline(self, budget_s=10.0):
+        """The oracle's unpack + dequantize of all three layouts on the first rows of the
+        4096x4096 O projection, packed by the oracle."""
+        import workloads
+        from oracle import mxfp4, nvfp4, q4k
+        W = workloads.dense_layer_8b(names=["o"], with_grad=False)["o"][0]
+        s_t = nvfp4.tensor_scale([W])
+
+        def run(r):
+            x = W[:r]
+            pn = nvfp4.pack(*nvfp4.quantize(x, s_t))
+            pm = mxfp4.pack(*mxfp4.quantize(x))
+            pq = q4k.pack(q4k.quantize(x))
+            t0 = time.perf_counter()
+            nvfp4.dequantize(*nvfp4.unpack(*pn), s_t)
+            mxfp4.dequantize(*mxfp4.unpack(*pm))
+            q4k.dequantize(q4k.unpack(pq))
+            return time.perf_counter() - t0
+
+        r = 64
+        dt = run(r)
+        r = max(64, min(W.shape[0], int(r * budget_s / max(dt, 1e-3))))
+        dt = run(r)
+        nb = W[:r].size * ((0.5 + 1 / 16 + 2) + (0.5 + 1 / 32 + 2) + (144 / 256 + 2))
+        return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the oracle's unpack + dequantize of the three layouts on the first {r} rows of the "
+                          f"4096x4096 O projection ({dt:.1f} s)"}
+
+
 class MXFP4Operands:
     """MXFP4 QDQ + pack of the W4A4 GEMM operands, X 32768x4096 (activations, Student-t
     with outlier columns) and W 14336x4096, one grouped launch."""
@@ -540,10 +620,10 @@ class MoELoRANVFP4x8Remerge(MoELoRANVFP4):
 
 
 WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4,
-                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge)}
+                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge, DequantDense)}
 # measured next to the headline workload in a default run (fewer steps each)
 SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
-             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name]
+             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name]
 
 
 def measure(torch, wl, steps, warmup):

@@ -294,6 +294,50 @@ def qf_lora_adapter_grads(items, accumulate=False, ws=None):
                                        ws.numel() * ws.element_size(), _stream()), "qf_lora_adapter_grads")
 
 
+# ------------------------------------------------------------- dequant ----
+def _dequant_out(rows, cols, device, y):
+    if y is None:
+        y = torch.empty((rows, cols), dtype=torch.bfloat16, device=device)
+    _bf16(y, "y")
+    if tuple(y.shape) != (rows, cols):
+        raise ValueError(f"y has shape {tuple(y.shape)}, want {(rows, cols)}")
+    return y
+
+
+def _u8(t, name):
+    if t.dtype != torch.uint8 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous uint8 tensor")
+    return t
+
+
+def qf_dequant_nvfp4(codes, scales, d_scale, y=None):
+    """bf16 [rows, cols] from NVFP4 codes [rows, cols/2] and E4M3 scales [rows, cols/16]."""
+    rows, cols = _u8(codes, "codes").shape[0], codes.shape[1] * 2
+    y = _dequant_out(rows, cols, codes.device, y)
+    _check(lib().qf_dequant_nvfp4(_p(codes), _p(_u8(scales, "scales")), rows, cols, _p(d_scale), _p(y),
+                                  _mat(y, "y")[2], _stream()), "qf_dequant_nvfp4")
+    return y
+
+
+def qf_dequant_mxfp4(codes, scales, y=None):
+    """bf16 [rows, cols] from MXFP4 codes [rows, cols/2] and E8M0 scales [rows, cols/32]."""
+    rows, cols = _u8(codes, "codes").shape[0], codes.shape[1] * 2
+    y = _dequant_out(rows, cols, codes.device, y)
+    _check(lib().qf_dequant_mxfp4(_p(codes), _p(_u8(scales, "scales")), rows, cols, _p(y), _mat(y, "y")[2],
+                                  _stream()), "qf_dequant_mxfp4")
+    return y
+
+
+def qf_dequant_q4k(blocks, rows, cols, y=None):
+    """bf16 [rows, cols] from Q4_K blocks (rows * cols / 256 blocks of 144 bytes)."""
+    _u8(blocks, "blocks")
+    if blocks.numel() != rows * (cols // 256) * 144:
+        raise ValueError("blocks do not match rows x cols")
+    y = _dequant_out(rows, cols, blocks.device, y)
+    _check(lib().qf_dequant_q4k(_p(blocks), rows, cols, _p(y), _mat(y, "y")[2], _stream()), "qf_dequant_q4k")
+    return y
+
+
 # ---------------------------------------------------------------- GEMM ----
 def qf_gemm_mxfp4(X, W, Y=None, flags=QF_QDQ_A | QF_QDQ_W):
     """Y[M, N] = QDQ(X)[M, K] . QDQ(W)[N, K]^T (bf16 in, fp32 accumulate, bf16 out)."""

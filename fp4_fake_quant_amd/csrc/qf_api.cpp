@@ -155,6 +155,22 @@ qf_status single(int fmt, const qf_tensor_desc& d, const float* d_scale, void* s
 
 }  // namespace
 
+// ------------------------------------------------------------ dequant ----
+namespace {
+qf_status dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                  const float* d_scale, uint16_t* y, int64_t ldy, void* stream) {
+  const int blk = block_of(fmt);
+  if (rows < 0 || cols < 0 || cols % blk) return QF_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QF_OK;
+  if (!codes || !y || (fmt != QF_FMT_Q4K && !scales) || (fmt == QF_FMT_NVFP4 && !d_scale)) return QF_ERR_NULL;
+  if (ldy < cols) return QF_ERR_SHAPE;
+  if ((uint64_t)rows * (uint64_t)(cols / 8) >= (1ull << 32) - 4096) return QF_ERR_SHAPE;   // 32-bit chunk index
+  if (!aligned(y, 16) || ldy % 8 || !aligned(codes, fmt == QF_FMT_Q4K ? 16 : 4)) return QF_ERR_ALIGN;
+  if (fmt == QF_FMT_NVFP4 && !aligned(d_scale, 4)) return QF_ERR_ALIGN;
+  return hip_status(qf::launch_dequant(fmt, codes, scales, rows, cols, d_scale, y, ldy, (hipStream_t)stream));
+}
+}  // namespace
+
 extern "C" {
 
 uint32_t qf_version(void) { return (0u << 16) | (1u << 8) | 0u; }
@@ -508,6 +524,19 @@ qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, vo
 }  // extern "C"
 
 // ------------------------------------------------------------ W4A4 GEMM --
+
+qf_status qf_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           const float* d_scale, uint16_t* y, int64_t ldy, void* stream) {
+  return dequant(QF_FMT_NVFP4, codes, scales, rows, cols, d_scale, y, ldy, stream);
+}
+qf_status qf_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols, uint16_t* y,
+                           int64_t ldy, void* stream) {
+  return dequant(QF_FMT_MXFP4, codes, scales, rows, cols, nullptr, y, ldy, stream);
+}
+qf_status qf_dequant_q4k(const uint8_t* blocks, int64_t rows, int64_t cols, uint16_t* y, int64_t ldy, void* stream) {
+  return dequant(QF_FMT_Q4K, blocks, nullptr, rows, cols, nullptr, y, ldy, stream);
+}
+
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
                         int64_t M, int64_t N, int64_t K, unsigned flags, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;

@@ -254,6 +254,29 @@ qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_sc
 qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* ------------------------------------------------------------ dequant ---- */
+/* Packed engine layout -> BF16, the inverse direction of the pack calls ("Method":
+ * weights leave training in the engine's own format; "Supported formats" table for
+ * what each code and scale stands for).  Each call computes the dequant step of the
+ * matching QDQ from the stored bytes, so dequant(pack(x)) is bit for bit the QDQ'd
+ * bf16 of x:
+ *   NVFP4  y = sign | bf16(fl(fl(E2M1(code) * E4M3(scale)) * s_t)), s_t = *d_scale;
+ *   MXFP4  y = sign | bf16(E2M1(code) * 2^(E - 127))  (exact);
+ *   Q4_K   y = bf16(fl(D_j q - M_j)), D_j = f32(d) sc_j, M_j = f32(dmin) m_j (exact).
+ * Inputs are the contiguous arrays the pack calls write (codes [rows][cols/2], scales
+ * [rows][cols/16] or [rows][cols/32], Q4_K blocks [rows][cols/256][144]); y is bf16
+ * [rows, ldy], 16-byte aligned with ldy a multiple of 8 and >= cols.  Shapes as the pack
+ * calls (cols a multiple of 16 / 32 / 256, rows * cols / 8 < 2^32 - 4096, QF_ERR_SHAPE).  Codes 4-byte aligned, Q4_K
+ * blocks 16-byte aligned (QF_ERR_ALIGN).  Scale bytes must be ones a pack call can
+ * write (E4M3 0x00..0x7E, E8M0 0x00..0xFE; Q4_K d and dmin finite and >= 0); others
+ * give unspecified values. */
+qf_status qf_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           const float* d_scale, uint16_t* y, int64_t ldy, void* stream);
+qf_status qf_dequant_mxfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                           uint16_t* y, int64_t ldy, void* stream);
+qf_status qf_dequant_q4k(const uint8_t* blocks, int64_t rows, int64_t cols, uint16_t* y, int64_t ldy,
+                         void* stream);
+
 /* ------------------------------------------------- W4A4 MXFP4 GEMM ---- */
 /* Y = QDQ(X) . QDQ(W)^T with fp32 accumulation and one bf16 rounding of Y
  * ("Overview": weights and optionally activations rounded onto the grid, every

@@ -159,6 +159,22 @@ def test_lora_gradient_unit_rows():
     assert L.qf_lora_workspace(ctypes.byref(d), 2) == 4 * 2 * (3 * 16 * 4096 + dB)
 
 
+def test_dequant_validation():
+    """Dequant calls check shape, pointers and alignment before launching."""
+    L = _lib.lib()
+    c, s, y, f = _addr(0x10000000), _addr(0x10400000), _addr(0x10800000), _addr(0x10c00000)
+    assert L.qf_dequant_nvfp4(c, s, 4, 24, f, y, 24, None) == 2                 # cols not a multiple of 16
+    assert L.qf_dequant_mxfp4(c, s, 4, 48, y, 48, None) == 2                    # ... of 32
+    assert L.qf_dequant_q4k(c, 4, 384, y, 384, None) == 2                       # ... of 256
+    assert L.qf_dequant_nvfp4(c, s, 4, 32, None, y, 32, None) == 1              # NVFP4 needs the tensor scale
+    assert L.qf_dequant_mxfp4(c, None, 4, 64, y, 64, None) == 1
+    assert L.qf_dequant_nvfp4(c, s, 4, 32, f, y, 16, None) == 2                 # ldy < cols
+    assert L.qf_dequant_mxfp4(c, s, 4, 64, _addr(0x10800008), 64, None) == 3    # y 16-byte aligned
+    assert L.qf_dequant_mxfp4(c, s, 4, 64, y, 68, None) == 3                    # ldy a multiple of 8
+    assert L.qf_dequant_q4k(_addr(0x10000004), 4, 256, y, 256, None) == 3       # blocks 16-byte aligned
+    assert L.qf_dequant_q4k(c, 0, 256, y, 256, None) == 0                       # empty: no-op
+
+
 def test_gemm_validation():
     """GEMM entry points check flags, K and alignment before launching."""
     L = _lib.lib()
