@@ -16,7 +16,7 @@ import torch
 from ._lib import LoraDesc, TensorDesc, lib
 
 QF_OK = 0
-QF_QDQ_A, QF_QDQ_W, QF_FP4_CORES = 1, 2, 4
+QF_QDQ_A, QF_QDQ_W, QF_FP4_CORES, QF_MX_NOCLIP = 1, 2, 4, 8
 QF_FMT_NVFP4, QF_FMT_MXFP4, QF_FMT_Q4K = 0, 1, 2
 MAX_GROUPED = 16
 BLOCK = {QF_FMT_NVFP4: 16, QF_FMT_MXFP4: 32, QF_FMT_Q4K: 256}
@@ -201,6 +201,15 @@ def qf_qdq_pack_q4k(x, y=None, blocks=None):
     blocks, _ = _packed(QF_FMT_Q4K, rows, cols, x.device, blocks, None)
     _check(lib().qf_qdq_pack_q4k(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], _p(blocks), _stream()), "qf_qdq_pack_q4k")
     return y, blocks
+
+
+QF_MX_RULE_FLOOR, QF_MX_RULE_NOCLIP = 0, 1
+
+
+def qf_qdq_pack_mxfp4_rule(items, rule):
+    """qf_qdq_pack_mxfp4_grouped under shared-exponent rule QF_MX_RULE_FLOOR or QF_MX_RULE_NOCLIP."""
+    arr, n = _descs(items)
+    _check(lib().qf_qdq_pack_mxfp4_rule(ctypes.byref(arr), n, int(rule), _stream()), "qf_qdq_pack_mxfp4_rule")
 
 
 def qf_qdq_pack_q4k_grouped(items):

@@ -96,7 +96,8 @@ int partial_groups(const qf_tensor_desc* d, int n) {
 }
 
 // Grouped quantization; each descriptor's NULL outputs are skipped.
-qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_scales, hipStream_t s) {
+qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_scales, hipStream_t s,
+                        int mx_rule = QF_MX_RULE_FLOOR) {
   if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
   if (n > 0 && !d) return QF_ERR_NULL;
   if (fmt == QF_FMT_NVFP4 && !d_scales) return QF_ERR_NULL;
@@ -125,7 +126,7 @@ qf_status quant_grouped(int fmt, const qf_tensor_desc* d, int n, const float* d_
     qf::QArgs a;
     fill_args(a, sel, k, tile_chunks);
     a.tscale = d_scales;
-    const hipError_t e = qf::launch_quant(fmt, wy, wp, a, s);
+    const hipError_t e = qf::launch_quant(fmt, wy, wp, a, s, mx_rule);
     if (e != hipSuccess) return hip_status(e);
   }
   return QF_OK;
@@ -286,6 +287,10 @@ qf_status qf_qdq_pack_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64
 }
 qf_status qf_qdq_pack_mxfp4_grouped(const qf_tensor_desc* d, int n, void* stream) {
   return quant_grouped(QF_FMT_MXFP4, d, n, nullptr, (hipStream_t)stream);
+}
+qf_status qf_qdq_pack_mxfp4_rule(const qf_tensor_desc* d, int n, int rule, void* stream) {
+  if (rule != QF_MX_RULE_FLOOR && rule != QF_MX_RULE_NOCLIP) return QF_ERR_ARG;
+  return quant_grouped(QF_FMT_MXFP4, d, n, nullptr, (hipStream_t)stream, rule);
 }
 
 // --------------------------------------------------------------- Q4_K QDQ --
@@ -540,8 +545,9 @@ qf_status qf_dequant_q4k(const uint8_t* blocks, int64_t rows, int64_t cols, uint
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
                         int64_t M, int64_t N, int64_t K, unsigned flags, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
-  if (flags & ~(QF_QDQ_A | QF_QDQ_W | QF_FP4_CORES)) return QF_ERR_ARG;
+  if (flags & ~(QF_QDQ_A | QF_QDQ_W | QF_FP4_CORES | QF_MX_NOCLIP)) return QF_ERR_ARG;
   if ((flags & QF_FP4_CORES) && (flags & (QF_QDQ_A | QF_QDQ_W)) != (QF_QDQ_A | QF_QDQ_W)) return QF_ERR_ARG;
+  if ((flags & QF_MX_NOCLIP) && ((flags & QF_FP4_CORES) || !(flags & (QF_QDQ_A | QF_QDQ_W)))) return QF_ERR_ARG;
   if (M == 0 || N == 0) return QF_OK;
   if (!X || !W || !Y) return QF_ERR_NULL;
   if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;

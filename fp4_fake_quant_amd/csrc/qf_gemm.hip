@@ -60,12 +60,22 @@ __device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
 // The scale operand carries E in its exponent field: E = max(floor(log2 amax) - 2 + 127, 0)
 // is the block maximum's bf16 exponent field minus 2, clamped at 0 (a saturating
 // subtract on the field moved to bits 23..30).
+// NOCLIP: the noclip rule, E = max(that field - 2 + [significand > 1.5], 0).
+template <bool NOCLIP = false>
 __device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
-  // only the exponent of the block maximum matters: E = its bf16 exponent field - 2
-  uint32_t m = maxexp_bits8(w);
-  m = umax(m, dpp_xor1(m));
-  m = umax(m, dpp_xor2(m));
-  const uint32_t ebits = __builtin_elementwise_sub_sat(m << 16, 0x01000000u);
+  uint32_t ebits;
+  if constexpr (NOCLIP) {
+    uint32_t m = amax_bits8(w);
+    m = umax(m, dpp_xor1(m));
+    m = umax(m, dpp_xor2(m));
+    ebits = __builtin_elementwise_sub_sat((m & 0x7F80u) << 16, (m & 0x7Fu) > 0x40u ? 0x00800000u : 0x01000000u);
+  } else {
+    // only the exponent of the block maximum matters: E = its bf16 exponent field - 2
+    uint32_t m = maxexp_bits8(w);
+    m = umax(m, dpp_xor1(m));
+    m = umax(m, dpp_xor2(m));
+    ebits = __builtin_elementwise_sub_sat(m << 16, 0x01000000u);
+  }
   const float sc = __uint_as_float(ebits);
   uint32_t codes = w.x;                        // every byte is overwritten below
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
@@ -94,12 +104,15 @@ __device__ __forceinline__ uint4 load_chunk_buf(__amdgpu_buffer_rsrc_t r, uint32
 // Grids of the in-kernel quantizer: MXFP4 (block 32 along K, E8M0 scale; lanes 4i..4i+3
 // hold one block) or NVFP4 (block 16 along K, E4M3 scale under the operand's FP32 tensor
 // scale s_t; lanes 2i and 2i+1 hold one block, the pairing nvfp4_qdq_chunk needs).
-enum { GRID_MX = 0, GRID_NV = 1 };
+enum { GRID_MX = 0, GRID_NV = 1, GRID_MX_NOCLIP = 2 };
 
 template <int GRID, bool QDQ>
 __device__ __forceinline__ void store_chunk(uint8_t* lds, uint32_t r, uint32_t c, uint4 v, float s_t, float k6) {
   uint4 q = v;
-  if constexpr (QDQ) q = GRID == GRID_MX ? mxfp4_qdq_chunk(v) : nvfp4_qdq_chunk(v, s_t, k6).y;
+  if constexpr (QDQ) {
+    if constexpr (GRID == GRID_NV) q = nvfp4_qdq_chunk(v, s_t, k6).y;
+    else q = mxfp4_qdq_chunk<GRID == GRID_MX_NOCLIP>(v);
+  }
   *reinterpret_cast<uint4*>(lds + lds_off(r, c)) = q;
 }
 
@@ -259,6 +272,16 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __rest
   gemm_tile<GRID_MX, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, 1.0f, 1.0f, smem);
 }
 
+// MXFP4 under the noclip shared-exponent rule.
+template <bool QA, bool QW>
+__global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4_noclip(const uint16_t* __restrict__ X, int64_t ldx,
+                                                                   const uint16_t* __restrict__ W, int64_t ldw,
+                                                                   uint16_t* __restrict__ Y, int64_t ldy,
+                                                                   int M, int N, int K, int y_vec) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];
+  gemm_tile<GRID_MX_NOCLIP, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, 1.0f, 1.0f, smem);
+}
+
 // NVFP4 W4A4: the tensor scales come from device memory (computed by the tensor-scale
 // pass, or any fp32 the caller keeps there, e.g. a tracked activation maximum).
 template <bool QA, bool QW>
@@ -295,6 +318,15 @@ hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
   // 8-byte output stores need 8-byte aligned rows; otherwise the epilogue stores bf16 by bf16
   const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
   const dim3 g(tiles), b(G_THREADS);
+  if (flags & QF_MX_NOCLIP) {
+    if (qa && qw)
+      hipLaunchKernelGGL((k_gemm_mxfp4_noclip<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+    else if (qa)
+      hipLaunchKernelGGL((k_gemm_mxfp4_noclip<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+    else
+      hipLaunchKernelGGL((k_gemm_mxfp4_noclip<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+    return hipGetLastError();
+  }
   if (qa && qw) hipLaunchKernelGGL((k_gemm_mxfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
   else if (qa) hipLaunchKernelGGL((k_gemm_mxfp4<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
   else if (qw) hipLaunchKernelGGL((k_gemm_mxfp4<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);

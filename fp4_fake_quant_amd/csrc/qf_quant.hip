@@ -145,8 +145,8 @@ __global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
 }
 
 // ---------------------------------------------------------------- MXFP4 ----
-// Lanes 4i..4i+3 hold one 32-block.
-template <bool WY, bool WP, int L>
+// Lanes 4i..4i+3 hold one 32-block.  NOCLIP selects the noclip shared-exponent rule.
+template <bool WY, bool WP, int L, bool NOCLIP = false>
 __global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
   const int b = blockIdx.x;
   const int ti = find_tensor(a, b);
@@ -166,9 +166,12 @@ __global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
     m = umax(m, dpp_xor1(m));
     m = umax(m, dpp_xor2(m));
     // E = floor(log2 amax) - 2 + 127 clamped to [0, 254]: the bf16 exponent field minus 2
-    // (0 for zero and subnormal maxima, whose floor(log2) is below -126).
+    // (0 for zero and subnormal maxima, whose floor(log2) is below -126).  Noclip: the
+    // smallest E with amax <= 6 * 2^(E-127), one more than that when the maximum's
+    // significand exceeds 1.5 (mantissa field above 0x40).
     const int ef = (int)(m >> 7);
-    const uint32_t E = (uint32_t)(ef > 2 ? ef - 2 : 0);
+    const int e2 = NOCLIP ? ef - 2 + ((m & 0x7Fu) > 0x40u ? 1 : 0) : ef - 2;
+    const uint32_t E = (uint32_t)(e2 > 0 ? e2 : 0);
     const float sc = __uint_as_float(E << 23);
     uint32_t codes = 0;
     codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w[j].x), sc, 0);
@@ -400,16 +403,19 @@ hipError_t launch_nvfp4_scale_reduce(const ReduceArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s) {
+hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s, int mx_rule) {
   if (a.total_tiles == 0) return hipSuccess;
   const dim3 g(a.total_tiles), blk(WG);
-#define QF_DISPATCH(KERNEL, L)                                                     \
-  if (wy && wp) hipLaunchKernelGGL((KERNEL<true, true, L>), g, blk, 0, s, a);      \
-  else if (wy) hipLaunchKernelGGL((KERNEL<true, false, L>), g, blk, 0, s, a);      \
-  else hipLaunchKernelGGL((KERNEL<false, true, L>), g, blk, 0, s, a);
+#define QF_DISPATCH(KERNEL, ...)                                                              \
+  if (wy && wp) hipLaunchKernelGGL((KERNEL<true, true, __VA_ARGS__>), g, blk, 0, s, a);      \
+  else if (wy) hipLaunchKernelGGL((KERNEL<true, false, __VA_ARGS__>), g, blk, 0, s, a);      \
+  else hipLaunchKernelGGL((KERNEL<false, true, __VA_ARGS__>), g, blk, 0, s, a);
   switch (fmt) {
     case QF_FMT_NVFP4: QF_DISPATCH(k_nvfp4, L_NVFP4); break;
-    case QF_FMT_MXFP4: QF_DISPATCH(k_mxfp4, L_MXFP4); break;
+    case QF_FMT_MXFP4:
+      if (mx_rule == QF_MX_RULE_NOCLIP) { QF_DISPATCH(k_mxfp4, L_MXFP4, true); }
+      else { QF_DISPATCH(k_mxfp4, L_MXFP4); }
+      break;
     case QF_FMT_Q4K: QF_DISPATCH(k_q4k, L_Q4K); break;
     default: return hipErrorInvalidValue;
   }

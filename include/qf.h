@@ -69,6 +69,14 @@ typedef enum qf_status {
 
 enum qf_format { QF_FMT_NVFP4 = 0, QF_FMT_MXFP4 = 1, QF_FMT_Q4K = 2 };
 
+/* MXFP4 shared-exponent rules (the pages do not fix one).  FLOOR, the default of every
+ * MXFP4 call: E = clamp(floor(log2 amax) - 2 + 127, 0, 254), which clips block maxima in
+ * (6, 8) * 2^(E-127) to 6.  NOCLIP: the smallest E in [0, 254] with amax <= 6 *
+ * 2^(E-127) (ceil(log2(amax / 6)) + 127), one more than FLOOR exactly when the maximum's
+ * significand exceeds 1.5; nothing is clipped above E = 0.  amax == 0 gives E = 0. */
+#define QF_MX_RULE_FLOOR 0
+#define QF_MX_RULE_NOCLIP 1
+
 /* Most tensors one grouped call accepts. */
 #define QF_MAX_GROUPED 16
 /* Most tied groups one grouped tensor-scale call accepts. */
@@ -159,6 +167,10 @@ qf_status qf_qdq_pack_mxfp4(const uint16_t* x, int64_t rows, int64_t cols, int64
                             uint16_t* y, int64_t ldy, uint8_t* codes, uint8_t* scales,
                             void* stream);
 qf_status qf_qdq_pack_mxfp4_grouped(const qf_tensor_desc* d, int n, void* stream);
+/* qf_qdq_pack_mxfp4_grouped under a chosen shared-exponent rule (QF_MX_RULE_FLOOR or
+ * QF_MX_RULE_NOCLIP, else QF_ERR_ARG).  The packed bytes mean the same under either
+ * rule, so qf_dequant_mxfp4 and the packed GEMM inputs take them unchanged. */
+qf_status qf_qdq_pack_mxfp4_rule(const qf_tensor_desc* d, int n, int rule, void* stream);
 
 /* ------------------------------------------------------------ Q4_K QDQ ---- */
 /* Per 256 super-block of eight 32-sub-blocks j (min/max round-to-nearest):
@@ -304,6 +316,9 @@ qf_status qf_dequant_q4k(const uint8_t* blocks, int64_t rows, int64_t cols, uint
  * accuracy statement above holds unchanged.  The operands are quantized on the
  * way into LDS (codes and exponents only; nothing is dequantized). */
 #define QF_FP4_CORES 4u
+/* QF_MX_NOCLIP: quantize the operands under QF_MX_RULE_NOCLIP instead of the floor rule
+ * (BF16 cores only, with at least one of QF_QDQ_A / QF_QDQ_W; else QF_ERR_ARG). */
+#define QF_MX_NOCLIP 8u
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
                         uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                         unsigned flags, void* stream);

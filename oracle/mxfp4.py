@@ -13,6 +13,10 @@ Readings of what the page leaves open (stated choices):
   E = clamp(e - 2 + 127, 0, 254): the exponent of the largest element minus
   the largest E2M1 exponent (2), the usual microscaling rule.  Blocks whose
   amax lies in (6, 8) * 2^(E-127) therefore clip their top element to 6.
+* A second shared-exponent rule, "noclip", is kept as an option (the pages do not fix
+  the rule): E = the smallest value in [0, 254] with a <= 6 * 2^(E-127), i.e.
+  ceil(log2(a / 6)) + 127 clamped, so that no element is clipped (except when even
+  E = 254 is too small, which no finite bf16 reaches, or E = 0 is larger than needed).
 * X = 2^(E-127); y = |x| / X (exact unless it underflows far below 0.25);
   magnitude = E2M1 RNE-saturating(y); the code's sign bit is x's sign bit.
 * Dequant: o = sign * bf16(v * X), exact, including bf16 subnormals.
@@ -34,7 +38,25 @@ from .primitives import (F32, bf16_to_f32, f32_to_bf16, e2m1_encode_mag, E2M1_MA
 BLOCK = 32
 
 
-def quantize(x_bits):
+def shared_exponent(a, rule="floor"):
+    """E8M0 byte of blocks with maxima a (float32 >= 0) under the floor or noclip rule."""
+    a = np.asarray(a, dtype=np.float32)
+    pos = a > 0
+    e = np.where(pos, floor_log2(np.where(pos, a, 1.0)), 0)
+    if rule == "floor":
+        E = np.clip(e - 2 + 127, 0, 254)
+    elif rule == "noclip":
+        # the smallest E with a <= 6 * 2^(E - 127): a lies in [2^e, 2^(e+1)), so 6 * 2^(E-127)
+        # first reaches it at E - 127 = e - 2 or e - 1; test both exactly in float64
+        lo = e - 2 + 127
+        fits = a.astype(np.float64) <= np.ldexp(6.0, lo - 127)
+        E = np.clip(np.where(fits, lo, lo + 1), 0, 254)
+    else:
+        raise ValueError(rule)
+    return np.where(pos, E, 0).astype(np.int64)
+
+
+def quantize(x_bits, rule="floor"):
     """Codes (uint8 per element) and E8M0 scale bytes [rows, cols/32] for x [rows, cols]."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
@@ -42,9 +64,7 @@ def quantize(x_bits):
     x = bf16_to_f32(x_bits).reshape(rows, cols // BLOCK, BLOCK)
     ax = np.abs(x)
     a = np.max(ax, axis=-1) if cols else np.zeros((rows, 0), np.float32)
-    pos = a > 0
-    e = np.where(pos, floor_log2(np.where(pos, a, 1.0)), 0)
-    E = np.where(pos, np.clip(e - 2 + 127, 0, 254), 0).astype(np.int64)
+    E = shared_exponent(a, rule)
     X = e8m0_value(E)
     with np.errstate(under="ignore"):
         y = (ax / X[..., None]).astype(np.float32)
@@ -66,8 +86,8 @@ def dequantize(codes, E):
     return bits.reshape(rows, cols).astype(np.uint16)
 
 
-def qdq(x_bits):
-    codes, E = quantize(x_bits)
+def qdq(x_bits, rule="floor"):
+    codes, E = quantize(x_bits, rule)
     return dequantize(codes, E)
 
 

@@ -154,6 +154,49 @@ def check_mxfp4(x_bits):
     return bad
 
 
+def planted_mx_blocks():
+    """Block maxima on both sides of every decision of the noclip rule: 6 * 2^k exactly,
+    one bf16 step above and below, mantissas 1.5 and 1.5 + one step, the smallest and
+    largest normals, subnormals, zero."""
+    vals = []
+    for k in (-130, -126, -100, -3, 0, 1, 5, 100, 125):
+        base = np.float32(np.ldexp(6.0, k))
+        b = P.f32_to_bf16(np.array([base], np.float32))[0]
+        vals += [int(b), int(b) + 1, int(b) - 1]
+    for e in (1, 2, 3, 127, 254):
+        vals += [(e << 7) | 0x40, (e << 7) | 0x41, (e << 7) | 0x3F, (e << 7) | 0x7F, e << 7]
+    vals += [0x0001, 0x007F, 0x0000, 0x7F7F]
+    vals = [v for v in vals if 0 <= v < 0x7F80]
+    blocks = np.zeros((len(vals), 32), np.uint16)
+    rng = np.random.default_rng(5)
+    for i, v in enumerate(vals):
+        lo = P.bf16_to_f32(np.array([v], np.uint16))[0]
+        filler = P.f32_to_bf16((rng.uniform(-1, 1, 31) * lo).astype(np.float32))
+        blocks[i, :31] = filler
+        blocks[i, 31] = v | (0x8000 if i % 2 else 0)          # the block maximum, either sign
+    return blocks
+
+
+def check_mxfp4_noclip(x_bits):
+    """The noclip shared exponent by brute force over every E8M0 byte: the smallest E with
+    max|x| <= 6 * 2^(E-127) (exact in float64), then the same element rule as above."""
+    codes, E = mxfp4.quantize(x_bits, rule="noclip")
+    rows, cols = x_bits.shape
+    x = widen(x_bits).reshape(rows, cols // 32, 32)
+    a = np.abs(x).max(axis=-1)
+    E_ref = np.zeros(a.shape, np.int64)
+    for idx, ai in np.ndenumerate(a):
+        if ai > 0:
+            E_ref[idx] = next(k for k in range(255) if ai <= math.ldexp(6.0, k - 127) or k == 254)
+    bad = int(np.sum(E.astype(np.int64) != E_ref))
+    X = np.ldexp(1.0, E_ref - 127)[..., None]
+    y = np.abs(x) / X
+    c = codes.reshape(rows, cols // 32, 32)
+    bad += int(np.sum((c & 7) != best_codes(f32(y))))
+    bad += int(np.sum((c >> 3) != np.signbit(x)))
+    return bad
+
+
 # ---------------------------------------------------------------- Q4_K -----
 def check_q4k(x_bits):
     p = q4k.quantize(x_bits)

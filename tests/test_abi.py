@@ -159,6 +159,17 @@ def test_lora_gradient_unit_rows():
     assert L.qf_lora_workspace(ctypes.byref(d), 2) == 4 * 2 * (3 * 16 * 4096 + dB)
 
 
+def test_mxfp4_rule_validation():
+    L = _lib.lib()
+    d = (_lib.TensorDesc * 1)()
+    d[0].x, d[0].rows, d[0].cols, d[0].ldx = 0x10000000, 4, 64, 64
+    d[0].y, d[0].ldy = 0x10400000, 64
+    assert L.qf_qdq_pack_mxfp4_rule(ctypes.byref(d), 1, 2, None) == 7           # unknown rule
+    assert L.qf_qdq_pack_mxfp4_rule(ctypes.byref(d), 1, -1, None) == 7
+    d[0].cols = d[0].ldx = d[0].ldy = 48                                         # not a multiple of 32
+    assert L.qf_qdq_pack_mxfp4_rule(ctypes.byref(d), 1, 1, None) == 2
+
+
 def test_dequant_validation():
     """Dequant calls check shape, pointers and alignment before launching."""
     L = _lib.lib()
@@ -184,6 +195,9 @@ def test_gemm_validation():
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 8, None) == 7        # unknown flag
     assert L.qf_gemm_mxfp4(p, 96, q, 96, y, 64, 64, 64, 96, 3, None) == 2        # K not a multiple of 64
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 0, 64, 64, 7, None) == 0         # empty: no-op
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 8, None) == 7        # noclip needs a QDQ flag
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 15, None) == 7       # noclip is BF16-core only
+    assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 16, None) == 7       # unknown flag
     s = _addr(0x10c00000)
     assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 0, s, s, None) == 7   # no operand quantized
     assert L.qf_gemm_nvfp4(p, 64, q, 64, y, 64, 64, 64, 64, 7, s, s, None) == 7   # no FP4-core form

@@ -199,3 +199,15 @@ def test_gemm_nvfp4_full_size_sampled():
     Ys = host(Y[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()])
     rel = _check(Ys, nvfp4.qdq(X[rows], sx_ref), nvfp4.qdq(W[cols], sw_ref), X.shape[1], "nvfp4 full size")
     assert rel < 2e-3
+
+
+@pytest.mark.parametrize("shape", [(256, 256, 64), (300, 200, 128), (33, 517, 192)])
+@pytest.mark.parametrize("flags", [3, 1, 2])
+def test_gemm_mxfp4_noclip(shape, flags):
+    """QF_MX_NOCLIP: both operands quantized under the noclip exponent rule."""
+    M, N, K = shape
+    X, W = _ops(M, N, K)
+    Y = fq.qf_gemm_mxfp4(dev(X), dev(W), flags=flags | fq.QF_MX_NOCLIP)
+    Xq = mxfp4.qdq(X, rule="noclip") if flags & 1 else X
+    Wq = mxfp4.qdq(W, rule="noclip") if flags & 2 else W
+    _check(host(Y), Xq, Wq, K, f"noclip {shape} flags={flags}")

@@ -16,6 +16,7 @@ import fp4_fake_quant_amd as fq
 import workloads
 from oracle import nvfp4, mxfp4, q4k, ste
 from oracle import primitives as P
+from tests import pins
 from tests.gpu_util import dev, host, u8, f32bits, first_mismatch, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -323,3 +324,37 @@ def test_mxfp4_gemm_operands_full_size_sampled():
         assert_same(u8(c)[rows], pc, f"{name} codes")
         assert_same(u8(s)[rows], ps, f"{name} scales")
         del y, c, s
+
+
+# ------------------------------------------------- MXFP4 noclip exponent rule ----
+def _mx_rule_items(x_bits):
+    xd = dev(x_bits)
+    rows, cols = x_bits.shape
+    it = dict(x=xd, y=torch.empty_like(xd),
+              codes=torch.empty((rows, cols // 2), dtype=torch.uint8, device="cuda"),
+              scales=torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda"))
+    return it
+
+
+@pytest.mark.parametrize("which", ["single", "planted", "ragged"])
+def test_mxfp4_noclip_rule(single, which):
+    """QF_MX_RULE_NOCLIP against the oracle bit for bit (y, codes, E8M0 bytes); the floor
+    rule through the same entry point equals qf_qdq_pack_mxfp4."""
+    if which == "single":
+        x = single["W"]
+    elif which == "planted":
+        x = pins.planted_mx_blocks()
+    else:
+        x = workloads.to_bf16_bits(np.random.default_rng(3).standard_t(3, size=(37, 96)).astype(np.float32))
+    it = _mx_rule_items(x)
+    fq.qf_qdq_pack_mxfp4_rule([it], fq.QF_MX_RULE_NOCLIP)
+    c, E = mxfp4.quantize(x, rule="noclip")
+    pc, ps = mxfp4.pack(c, E)
+    assert_same(host(it["y"]), mxfp4.dequantize(c, E), "noclip y")
+    assert_same(u8(it["codes"]), pc, "noclip codes")
+    assert_same(u8(it["scales"]), ps, "noclip E")
+    assert_same(host(fq.qf_dequant_mxfp4(it["codes"], it["scales"])), host(it["y"]), "noclip dequant")
+    fq.qf_qdq_pack_mxfp4_rule([it], fq.QF_MX_RULE_FLOOR)
+    y, c2, s2 = fq.qf_qdq_pack_mxfp4(it["x"])
+    assert_same(host(it["y"]), host(y), "floor rule y")
+    assert_same(u8(it["scales"]), u8(s2), "floor rule E")

@@ -297,3 +297,29 @@ def test_block_codes_minimise_squared_error():
         emitted = np.where(np.signbit(y_b), -P.E2M1_MAG[mags], P.E2M1_MAG[mags])
         assert ((emitted - y_b) ** 2).sum() == err.min()
         assert np.allclose(np.abs(best), np.abs(emitted)) or ((best - y_b) ** 2).sum() == err.min()
+
+
+def test_mxfp4_noclip_rule_by_brute_force(single):
+    assert pins.check_mxfp4_noclip(single["W"]) == 0
+    assert pins.check_mxfp4_noclip(pins.planted_mx_blocks()) == 0
+
+
+def test_mxfp4_noclip_never_clips_and_is_minimal():
+    """Under noclip every |x| / X is at most 6 (no saturation), and one exponent lower
+    would put the block maximum above 6 unless E is already 0; E differs from the floor
+    rule exactly when the maximum's mantissa exceeds 1.5."""
+    b = pins.planted_mx_blocks()
+    x = P.bf16_to_f32(b).astype(np.float64)
+    a = np.abs(x).max(axis=-1)
+    _, E = mxfp4.quantize(b, rule="noclip")
+    _, Ef = mxfp4.quantize(b, rule="floor")
+    E, Ef = E.astype(np.int64)[:, 0], Ef.astype(np.int64)[:, 0]
+    X = np.ldexp(1.0, E - 127)
+    assert np.all(a / X <= 6.0)
+    low = np.ldexp(6.0, E - 1 - 127)
+    assert np.all((E == 0) | (a > low))
+    mant = (b[:, 31] & 0x7F).astype(np.int64)
+    normal = ((b[:, 31] >> 7) & 0xFF) >= 1
+    want = np.where(normal & (mant > 0x40) & (Ef + 1 <= 254) & (Ef > 0), Ef + 1, Ef)
+    ok = normal & (Ef > 0)                                    # above the clamp at E = 0
+    assert np.array_equal(E[ok], want[ok])

@@ -81,7 +81,7 @@ def test_mutation_e4m3_ties_up_is_caught(monkeypatch):
 
 
 def test_mutation_mxfp4_ceil_rule_is_caught(monkeypatch):
-    def ceil_rule(x_bits):
+    def ceil_rule(x_bits, rule="floor"):
         x_bits = np.asarray(x_bits, np.uint16)
         rows, cols = x_bits.shape
         x = P.bf16_to_f32(x_bits).reshape(rows, cols // 32, 32)
