@@ -49,10 +49,7 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int MX_BM = 256, MX_BN = 256;
 constexpr int MX_THREADS = 512;
-#ifndef QF_MX_GROUP_M
-#define QF_MX_GROUP_M 2                                      // tile rows per group of the tile order
-#endif
-constexpr int MX_GROUP_M = QF_MX_GROUP_M;
+constexpr int MX_GROUP_M = 2;                               // tile rows per group of the tile order
 
 // One operand slice of a K step of BK elements in LDS: codes [256 rows][BK/2 bytes]
 // (BK/32 16-byte K blocks per row), then the E8M0 exponents, 4 bytes per row (K
@@ -543,24 +540,11 @@ hipError_t launch_gemm_mx4(const uint16_t* X, int64_t ldx, const uint16_t* W, in
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
   const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
   const dim3 g(tiles), b(MX_THREADS);
-#ifndef QF_MX_BK_PACKED
-#define QF_MX_BK_PACKED 64
-#endif
-#ifndef QF_MX_BK_QDQ
-#define QF_MX_BK_QDQ 64
-#endif
-  const bool k128 = K % 128 == 0;
-  if (Wc) {
-    if (k128 && QF_MX_BK_PACKED == 128)
-      hipLaunchKernelGGL((k_gemm_mx4<true, 128>), g, b, 0, s, X, ldx, W, ldw, Wc, Ws, Y, ldy, M, N, K, y_vec);
-    else
-      hipLaunchKernelGGL((k_gemm_mx4<true, 64>), g, b, 0, s, X, ldx, W, ldw, Wc, Ws, Y, ldy, M, N, K, y_vec);
-  } else {
-    if (k128 && QF_MX_BK_QDQ == 128)
-      hipLaunchKernelGGL((k_gemm_mx4<false, 128>), g, b, 0, s, X, ldx, W, ldw, Wc, Ws, Y, ldy, M, N, K, y_vec);
-    else
-      hipLaunchKernelGGL((k_gemm_mx4<false, 64>), g, b, 0, s, X, ldx, W, ldw, Wc, Ws, Y, ldy, M, N, K, y_vec);
-  }
+  // K = 64 per step for both forms: 128 measured slower for each
+  if (Wc)
+    hipLaunchKernelGGL((k_gemm_mx4<true, 64>), g, b, 0, s, X, ldx, W, ldw, Wc, Ws, Y, ldy, M, N, K, y_vec);
+  else
+    hipLaunchKernelGGL((k_gemm_mx4<false, 64>), g, b, 0, s, X, ldx, W, ldw, Wc, Ws, Y, ldy, M, N, K, y_vec);
   return hipGetLastError();
 }
 

@@ -16,31 +16,10 @@ namespace qf {
 // tensors; a tensor's last tile may be partial.  L is chosen per kernel from
 // measurements (more, smaller workgroups stream writes better on gfx950).
 constexpr int WG = 256;
-#ifndef QF_L_AMAX
-#define QF_L_AMAX 2
-#endif
-#ifndef QF_L_NVFP4
-#define QF_L_NVFP4 1
-#endif
-#ifndef QF_L_MXFP4
-#define QF_L_MXFP4 1
-#endif
-#ifndef QF_L_Q4K
-#define QF_L_Q4K 2
-#endif
-#ifndef QF_L_STE
-#define QF_L_STE 1
-#endif
-#ifndef QF_REVERSE_PASS2
-#define QF_REVERSE_PASS2 1
-#endif
-#ifndef QF_AMAX_GRID
-#define QF_AMAX_GRID 2048
-#endif
-constexpr int L_AMAX = QF_L_AMAX, L_NVFP4 = QF_L_NVFP4, L_MXFP4 = QF_L_MXFP4, L_Q4K = QF_L_Q4K, L_STE = QF_L_STE;
+constexpr int L_AMAX = 2, L_NVFP4 = 1, L_MXFP4 = 1, L_Q4K = 2, L_STE = 1;
 // The amax pass runs a persistent grid of at most AMAX_GRID workgroups, each
 // keeping one maximum per tied group.
-constexpr int AMAX_GRID = QF_AMAX_GRID;
+constexpr int AMAX_GRID = 2048;
 
 inline int chunks_per_lane(int fmt) {
   return fmt == QF_FMT_NVFP4 ? L_NVFP4 : fmt == QF_FMT_MXFP4 ? L_MXFP4 : L_Q4K;

@@ -111,13 +111,9 @@ __global__ __launch_bounds__(RED_WG) void k_nvfp4_scale_reduce(ReduceArgs a) {
 // Lanes 2i and 2i+1 hold one 16-block.
 template <bool WY, bool WP, int L>
 __global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
-#if QF_REVERSE_PASS2
   // last tiles first: they are the ones the amax pass read last, so part of them
   // is still in the memory-side cache
   const int b = a.total_tiles - 1 - (int)blockIdx.x;
-#else
-  const int b = blockIdx.x;
-#endif
   const int ti = find_tensor(a, b);
   const QTensor& T = a.t[ti];
   const uint32_t base = (uint32_t)(b - T.tile_begin) * (WG * L);
