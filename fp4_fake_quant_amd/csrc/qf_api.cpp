@@ -325,7 +325,7 @@ namespace {
 qf_status check_lora(const qf_lora_desc& d) {
   if (d.rows < 0 || d.cols < 0) return QF_ERR_SHAPE;
   if (d.rows == 0 || d.cols == 0) return QF_OK;
-  if (d.cols % 32 != 0 || d.cols > QF_LORA_MAX_COLS || d.ldw < d.cols) return QF_ERR_SHAPE;
+  if (d.cols % 32 != 0 || d.cols > QF_LORA_MAX_COLS || d.ldw < d.cols || d.ldw >= (1ll << 24)) return QF_ERR_SHAPE;
   if (d.r < 1 || d.r > qf::LORA_MAX_R) return QF_ERR_ARG;
   if (d.group < 0) return QF_ERR_ARG;
   if ((uint64_t)d.rows * (uint64_t)(d.cols / 8) >= (1ull << 32)) return QF_ERR_SHAPE;
@@ -551,6 +551,7 @@ qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
   if (M == 0 || N == 0) return QF_OK;
   if (!X || !W || !Y) return QF_ERR_NULL;
   if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;
+  if (ldx >= (1ll << 22) || ldw >= (1ll << 22)) return QF_ERR_SHAPE;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 2) || ldx % 8 || ldw % 8) return QF_ERR_ALIGN;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
@@ -570,6 +571,7 @@ qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
   if (!X || !W || !Y) return QF_ERR_NULL;
   if (((flags & QF_QDQ_A) && !d_scale_x) || ((flags & QF_QDQ_W) && !d_scale_w)) return QF_ERR_NULL;
   if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;
+  if (ldx >= (1ll << 22) || ldw >= (1ll << 22)) return QF_ERR_SHAPE;
   if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 2) || ldx % 8 || ldw % 8) return QF_ERR_ALIGN;
   if ((d_scale_x && !aligned(d_scale_x, 4)) || (d_scale_w && !aligned(d_scale_w, 4))) return QF_ERR_ALIGN;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
@@ -597,6 +599,7 @@ qf_status qf_gemm_mxfp4_packed_w(const uint16_t* X, int64_t ldx, const uint8_t* 
   if (M == 0 || N == 0) return QF_OK;
   if (!X || !Wc || !Ws || !Y) return QF_ERR_NULL;
   if (ldx < K || ldy < N) return QF_ERR_SHAPE;
+  if (ldx >= (1ll << 22)) return QF_ERR_SHAPE;
   if (!aligned(X, 16) || !aligned(Wc, 16) || !aligned(Ws, 2) || !aligned(Y, 2) || ldx % 8) return QF_ERR_ALIGN;
   if ((N < 256 ? N : 256) * (K / 2) >= (1ll << 31)) return QF_ERR_SHAPE;
   const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);

@@ -221,7 +221,7 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
  *   group  tied-group index for the NVFP4 tensor scale (one per expert per
  *      fused matrix: experts never share a scale).
  * Shapes: cols a multiple of 32 and at most QF_LORA_MAX_COLS; rows >= 0; ldw a
- * multiple of 8.  W, A, M, G 16-byte aligned; B, dA, dB 4-byte aligned; the packed
+ * multiple of 8 and below 2^24.  W, A, M, G 16-byte aligned; B, dA, dB 4-byte aligned; the packed
  * arrays as in qf_qdq_pack_nvfp4.  With r odd, the row of B that ends the array
  * may be read as a whole 4-byte word (the 2 bytes after B, never used).
  * Empty descriptors (rows or cols 0) are skipped.  Errors: QF_ERR_SHAPE for a
@@ -301,8 +301,9 @@ qf_status qf_dequant_q4k(const uint8_t* blocks, int64_t rows, int64_t cols, uint
  * Constraints: M, N >= 0 (any value; a zero extent is a no-op), K a positive
  * multiple of 64 (QF_ERR_SHAPE), ldx, ldw >= K and ldy >= N; X and W 16-byte
  * aligned with ldx, ldw multiples of 8, Y 2-byte aligned (QF_ERR_ALIGN);
- * M, N < 2^30.  Output rows are written 8 bytes at a time when ldy is a
- * multiple of 4 and Y is 8-byte aligned, element by element otherwise.
+ * M, N < 2^30; ldx, ldw < 2^22 (a 256-row tile's byte offsets stay below 2^31).
+ * Output rows are written 8 bytes at a time when ldy is a multiple of 4 and Y is
+ * 8-byte aligned, element by element otherwise.
  * Accuracy: fp32 accumulation in an unspecified order; every element obeys
  * |y - y_ref| <= 2^-8 |y_ref| + (1 + 2^-8) gamma_K sum_k |xq_k wq_k|,
  * gamma_K = K 2^-24 / (1 - K 2^-24), against the exact product of the QDQ'd

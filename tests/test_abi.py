@@ -116,6 +116,8 @@ def test_lora_validation():
     assert L.qf_lora_workspace(ctypes.byref(d), 2) == 0
     assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need, None) == 7
     d[1].r = 16
+    d[1].ldw = 1 << 24                                              # row stride too large
+    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 2
     d[1].cols = d[1].ldw = 1048                                     # not a multiple of 32
     assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 2
     d[1].cols = d[1].ldw = 1056
@@ -195,6 +197,8 @@ def test_gemm_validation():
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 8, None) == 7        # unknown flag
     assert L.qf_gemm_mxfp4(p, 96, q, 96, y, 64, 64, 64, 96, 3, None) == 2        # K not a multiple of 64
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 0, 64, 64, 7, None) == 0         # empty: no-op
+    assert L.qf_gemm_mxfp4(p, 1 << 22, q, 64, y, 64, 64, 64, 64, 3, None) == 2   # a tile's offsets reach 2^31
+    assert L.qf_gemm_mxfp4(p, 64, q, 1 << 22, y, 64, 64, 64, 64, 3, None) == 2
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 8, None) == 7        # noclip needs a QDQ flag
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 15, None) == 7       # noclip is BF16-core only
     assert L.qf_gemm_mxfp4(p, 64, q, 64, y, 64, 64, 64, 64, 16, None) == 7       # unknown flag
