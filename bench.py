@@ -448,9 +448,10 @@ class W4A4GemmMXFP4:
         t("gemm_mxfp4_fused", 1)
 
     def controls(self, reps=10):
-        """ms of the plain-BF16 run of the same kernel, of torch.matmul, of the NVFP4 W4A4
-        form of the fused kernel (tensor scales of X and W from the tensor-scale pass, timed
-        on their own), and of the same MXFP4 W4A4 product on the MXFP4 matrix cores: both
+        """ms of the plain-BF16 run of the same kernel, of torch.matmul, of the layer's
+        backward (dX = dY . Wq and dW = dY^T . Xq with their three transposes; TFLOP/s over
+        both products), of the NVFP4 W4A4 form of the fused kernel (tensor scales of X and
+        W from the tensor-scale pass, timed on their own), and of the same MXFP4 W4A4 product on the MXFP4 matrix cores: both
         operands quantized in the kernel; W pre-packed by qf_pack_mxfp4 with X quantized in
         the kernel; both pre-packed (the packs are timed on their own)."""
         torch = self.torch
@@ -459,10 +460,19 @@ class W4A4GemmMXFP4:
         Wc, Ws = fq.qf_pack_mxfp4(self.W)
         Xc, Xs = fq.qf_pack_mxfp4(self.X)
         sx, sw = fq.qf_nvfp4_tensor_scale(self.X), fq.qf_nvfp4_tensor_scale(self.W)
+        # backward of the quantized linear: an N(0,1) upstream gradient of Y's shape
+        gen = torch.Generator(device="cuda").manual_seed(11)
+        dY = torch.randn((self.M, self.N), generator=gen, device="cuda").to(torch.bfloat16)
+        dX = torch.empty_like(self.X)
+        dW = torch.empty_like(self.W)
+        bws = torch.empty(fq.qf_linear_backward_workspace(self.M, self.N, self.K), dtype=torch.uint8,
+                          device="cuda")
         for name, fn in (("gemm_bf16_same_kernel", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
                          ("w4a4_nvfp4_fused", lambda: fq.qf_gemm_nvfp4(self.X, self.W, sx, sw, self.Y)),
                          ("tensor_scales_nvfp4", lambda: (fq.qf_nvfp4_tensor_scale(self.X, sx),
                                                           fq.qf_nvfp4_tensor_scale(self.W, sw))),
+                         ("backward_dx_dw_mxfp4", lambda: fq.qf_linear_backward_mxfp4(self.X, self.W, dY, dX, dW,
+                                                                                        ws=bws)),
                          ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y)),
                          ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
                          ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
@@ -482,7 +492,8 @@ class W4A4GemmMXFP4:
             if name.startswith(("pack_", "tensor_scales")):
                 out[name] = {"ms": round(ms, 4)}
                 continue
-            tf = self.flop / ms / 1e9
+            flop = 2 * self.flop if name.startswith("backward") else self.flop   # dX and dW: two products
+            tf = flop / ms / 1e9
             out[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)}
             if "fp4_cores" in name:
                 out[name]["frac_mfma_fp4"] = round(tf / MFMA_FP4_PEAK_TFS, 4)

@@ -380,6 +380,42 @@ def qf_gemm_nvfp4(X, W, d_scale_x, d_scale_w, Y=None, flags=QF_QDQ_A | QF_QDQ_W)
     return Y
 
 
+def qf_transpose_bf16(x, y=None, qdq_mxfp4=False):
+    """y [cols, rows] = x^T, MXFP4-QDQ'd along x's rows first when qdq_mxfp4."""
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    if y is None:
+        y = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
+    _bf16(y, "y")
+    _check(lib().qf_transpose_bf16(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], int(bool(qdq_mxfp4)), _stream()),
+           "qf_transpose_bf16")
+    return y
+
+
+def qf_linear_backward_workspace(M, N, K):
+    return lib().qf_linear_backward_workspace(M, N, K)
+
+
+def qf_linear_backward_mxfp4(X, W, dY, dX=None, dW=None, flags=QF_QDQ_A | QF_QDQ_W, ws=None, want=(True, True)):
+    """(dX, dW) of Y = Xq . Wq^T: dX = dY . Wq [M, K], dW = dY^T . Xq [N, K] (bf16)."""
+    M, K, ldx = _mat(_bf16(X, "X"), "X")
+    N, K2, ldw = _mat(_bf16(W, "W"), "W")
+    M2, N2, lddy = _mat(_bf16(dY, "dY"), "dY")
+    if K2 != K or M2 != M or N2 != N:
+        raise ValueError(f"shapes X {tuple(X.shape)}, W {tuple(W.shape)}, dY {tuple(dY.shape)} do not fit")
+    if dX is None and want[0]:
+        dX = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    if dW is None and want[1]:
+        dW = torch.empty((N, K), dtype=torch.bfloat16, device=X.device)
+    need = lib().qf_linear_backward_workspace(M, N, K)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=X.device)
+    _check(lib().qf_linear_backward_mxfp4(_p(X), ldx, _p(W), ldw, _p(dY), lddy, _p(dX),
+                                          _mat(dX, "dX")[2] if dX is not None else 0, _p(dW),
+                                          _mat(dW, "dW")[2] if dW is not None else 0, M, N, K, int(flags), _p(ws),
+                                          ws.numel(), _stream()), "qf_linear_backward_mxfp4")
+    return dX, dW
+
+
 def qf_gemm_mxfp4_packed_w(X, Wc, Ws, Y=None):
     """Y[M, N] = QDQ(X) . dequant(Wc, Ws)^T on the MXFP4 matrix cores; Wc [N, K/2] and
     Ws [N, K/32] uint8 as qf_pack_mxfp4 writes them (contiguous)."""

@@ -75,6 +75,11 @@ SIGNATURES = {
     "qf_dequant_nvfp4": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "qf_dequant_mxfp4": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i64, c_void_p]),
     "qf_dequant_q4k": (c_int, [c_void_p, c_i64, c_i64, c_void_p, c_i64, c_void_p]),
+    "qf_transpose_bf16": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_i64, c_int, c_void_p]),
+    "qf_linear_backward_workspace": (c_size_t, [c_i64, c_i64, c_i64]),
+    "qf_linear_backward_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64,
+                                         c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint, c_void_p, c_size_t,
+                                         c_void_p]),
     "qf_gemm_nvfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint,
                               c_void_p, c_void_p, c_void_p]),
 }

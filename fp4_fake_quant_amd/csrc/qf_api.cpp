@@ -580,6 +580,60 @@ qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
                                           (hipStream_t)stream));
 }
 
+qf_status qf_transpose_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                            int qdq_mxfp4, void* stream) {
+  if (rows < 0 || cols < 0 || rows % 8 || cols % (qdq_mxfp4 ? 32 : 8) || rows >= (1ll << 22) || cols >= (1ll << 31))
+    return QF_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QF_OK;
+  if (!x || !y) return QF_ERR_NULL;
+  if (ldx < cols || ldy < rows) return QF_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(y, 16) || ldx % 8 || ldy % 8) return QF_ERR_ALIGN;
+  return hip_status(qf::launch_transpose(x, ldx, (int)rows, (int)cols, y, ldy, qdq_mxfp4 != 0, (hipStream_t)stream));
+}
+
+namespace {
+int64_t round256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
+}  // namespace
+
+size_t qf_linear_backward_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return 0;
+  return (size_t)(round256(K * N * 2) + round256(N * M * 2) + round256(K * M * 2));
+}
+
+qf_status qf_linear_backward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, const uint16_t* dY,
+                                   int64_t lddy, uint16_t* dX, int64_t lddx, uint16_t* dW, int64_t lddw, int64_t M,
+                                   int64_t N, int64_t K, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
+  if (flags & ~(QF_QDQ_A | QF_QDQ_W)) return QF_ERR_ARG;
+  if (M < 0 || N < 0 || K < 0 || M % 64 || N % 64 || K % 32) return QF_ERR_SHAPE;
+  if (M >= (1ll << 22) || N >= (1ll << 22) || K >= (1ll << 22)) return QF_ERR_SHAPE;
+  if (M == 0 || N == 0 || K == 0 || (!dX && !dW)) return QF_OK;
+  if (!dY || (dX && !W) || (dW && !X)) return QF_ERR_NULL;
+  if (lddy < N || (dX && (ldw < K || lddx < K)) || (dW && (ldx < K || lddw < K))) return QF_ERR_SHAPE;
+  const int64_t big = 1ll << 22;                                            // tile offsets of the products
+  if (lddy >= big || (dX && (ldw >= big || lddx >= big)) || (dW && (ldx >= big || lddw >= big))) return QF_ERR_SHAPE;
+  if (!aligned(dY, 16) || lddy % 8) return QF_ERR_ALIGN;
+  if (dX && (!aligned(W, 16) || !aligned(dX, 16) || ldw % 8 || lddx % 8)) return QF_ERR_ALIGN;
+  if (dW && (!aligned(X, 16) || !aligned(dW, 16) || ldx % 8 || lddw % 8)) return QF_ERR_ALIGN;
+  if (!ws || ws_bytes < qf_linear_backward_workspace(M, N, K)) return QF_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return QF_ERR_ALIGN;
+  uint16_t* wqt = (uint16_t*)ws;                                           // Wq^T [K, N]
+  uint16_t* dyt = (uint16_t*)((char*)ws + round256(K * N * 2));             // dY^T [N, M]
+  uint16_t* xqt = (uint16_t*)((char*)dyt + round256(N * M * 2));            // Xq^T [K, M]
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipSuccess;
+  if (dX) {
+    e = qf::launch_transpose(W, ldw, (int)N, (int)K, wqt, N, (flags & QF_QDQ_W) != 0, s);
+    if (e == hipSuccess) e = qf::launch_gemm_mxfp4(dY, lddy, wqt, N, dX, lddx, (int)M, (int)K, (int)N, 0, s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  if (dW) {
+    e = qf::launch_transpose(dY, lddy, (int)M, (int)N, dyt, M, false, s);
+    if (e == hipSuccess) e = qf::launch_transpose(X, ldx, (int)M, (int)K, xqt, M, (flags & QF_QDQ_A) != 0, s);
+    if (e == hipSuccess) e = qf::launch_gemm_mxfp4(dyt, M, xqt, M, dW, lddw, (int)N, (int)K, (int)M, 0, s);
+  }
+  return hip_status(e);
+}
+
 qf_status qf_gemm_mxfp4_packed(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
                                int64_t ldy, int64_t M, int64_t N, int64_t K, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 128 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;

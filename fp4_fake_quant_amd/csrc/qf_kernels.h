@@ -118,6 +118,9 @@ hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
 // codes: NVFP4/MXFP4 code bytes (scales their scale bytes), or Q4_K blocks (scales unused)
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                           const float* d_scale, uint16_t* y, int64_t ldy, hipStream_t s);
+// dst [C, R] = src [R, C]^T, MXFP4-QDQ'd along C first when qdq
+hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint16_t* dst, int64_t ldd, bool qdq,
+                            hipStream_t s);
 hipError_t launch_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
                              int64_t ldy, int M, int N, int K, unsigned flags, const float* d_sx, const float* d_sw,
                              hipStream_t s);

@@ -360,6 +360,35 @@ qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
                         uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                         unsigned flags, const float* d_scale_x, const float* d_scale_w, void* stream);
 
+/* -------------------------------------- backward of the quantized linear ---- */
+/* "Method", "Framework overview": the backward pass reaches the latent weights through
+ * the STE, so the layer Y = Xq . Wq^T (Xq, Wq the MXFP4-QDQ'd operands, or the raw ones
+ * for an operand the forward did not quantize) has dX = dY . Wq and dWq = dY^T . Xq;
+ * qf_ste_backward then carries dWq to the fp32 latent weights.
+ *
+ * qf_transpose_bf16: y [cols, rows] = x [rows, cols]^T, MXFP4-QDQ'd along cols first
+ * (the rule of qf_qdq_mxfp4) when qdq_mxfp4 != 0.  rows and cols multiples of 8 (cols
+ * of 32 with qdq_mxfp4), rows < 2^22, ldx >= cols, ldy >= rows (QF_ERR_SHAPE); x, y
+ * 16-byte aligned with ldx, ldy multiples of 8 (QF_ERR_ALIGN); y must not overlap x.
+ * The result is exact (a copy, or QDQ values that are exactly those of qf_qdq_mxfp4). */
+qf_status qf_transpose_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
+                            int qdq_mxfp4, void* stream);
+
+/* dX [M, K] = dY [M, N] . Wq and dW [N, K] = dY^T . Xq for X [M, K], W [N, K], with Xq /
+ * Wq = QDQ(X) / QDQ(W) when flags has QF_QDQ_A / QF_QDQ_W (the forward's flags), else
+ * the operands themselves.  Five launches on `stream`: Wq^T, dY^T and Xq^T into the
+ * workspace (qf_transpose_bf16), then the two products on the BF16 matrix cores
+ * (qf_gemm_mxfp4 with flags 0).  dX or dW may be NULL to skip it.  Shapes: M and N
+ * multiples of 64 (the products' reduction lengths), K a multiple of 32, M, N, K and
+ * the leading dimensions < 2^22; leading dimensions >= the row lengths, multiples of 8;
+ * all arrays 16-byte aligned, the workspace 256-byte aligned.  Accuracy: each output element obeys the bound of qf_gemm_mxfp4 with the
+ * reduction length N (dX) or M (dW). */
+size_t qf_linear_backward_workspace(int64_t M, int64_t N, int64_t K);
+qf_status qf_linear_backward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                                   const uint16_t* dY, int64_t lddy, uint16_t* dX, int64_t lddx,
+                                   uint16_t* dW, int64_t lddw, int64_t M, int64_t N, int64_t K,
+                                   unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
 /* ---------------------------------------------------- conformance test ---- */
 /* Checks on the device that the gfx950 instructions and shortcuts the kernels
  * rely on agree bit for bit with the software definitions above, over their

@@ -172,6 +172,26 @@ def test_mxfp4_rule_validation():
     assert L.qf_qdq_pack_mxfp4_rule(ctypes.byref(d), 1, 1, None) == 2
 
 
+def test_transpose_and_backward_validation():
+    L = _lib.lib()
+    x, y, w, d = _addr(0x10000000), _addr(0x10400000), _addr(0x10800000), _addr(0x10c00000)
+    assert L.qf_transpose_bf16(x, 12, 64, 64, y, 16, 0, None) == 2             # rows not a multiple of 8
+    assert L.qf_transpose_bf16(x, 16, 48, 48, y, 16, 1, None) == 2             # QDQ needs 32-blocks
+    assert L.qf_transpose_bf16(x, 16, 48, 48, y, 8, 0, None) == 2              # ldy < rows
+    assert L.qf_transpose_bf16(_addr(0x10000008), 16, 48, 48, y, 16, 0, None) == 3
+    assert L.qf_transpose_bf16(x, 0, 48, 48, y, 16, 0, None) == 0              # empty: no-op
+    need = L.qf_linear_backward_workspace(128, 64, 96)
+    assert need == 96 * 64 * 2 + 64 * 128 * 2 + 96 * 128 * 2
+    args = (x, 96, w, 96, d, 64, y, 96, _addr(0x11000000), 96)
+    assert L.qf_linear_backward_mxfp4(*args, 100, 64, 96, 3, _addr(0x12000000), need, None) == 2   # M % 64
+    assert L.qf_linear_backward_mxfp4(*args, 128, 64, 80, 3, _addr(0x12000000), need, None) == 2   # K % 32
+    assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 4, _addr(0x12000000), need, None) == 7   # flags
+    assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 3, _addr(0x12000000), need - 2, None) == 4
+    assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 3, _addr(0x12000010), need, None) == 3   # ws alignment
+    assert L.qf_linear_backward_mxfp4(x, 96, None, 96, d, 64, y, 96, None, 0, 128, 64, 96, 3,
+                                      _addr(0x12000000), need, None) == 1                          # dX needs W
+
+
 def test_dequant_validation():
     """Dequant calls check shape, pointers and alignment before launching."""
     L = _lib.lib()
