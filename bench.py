@@ -422,9 +422,9 @@ MFMA_FP4_PEAK_TFS = 10100.0     # MI355X dense MXFP4 matrix throughput
 
 class W4A4GemmMXFP4:
     """Y = QDQ(X) . QDQ(W)^T, X 32768x4096 (Student-t activations with outlier columns),
-    W 14336x4096, MXFP4 QDQ of both operands fused into the BF16 MFMA GEMM; controls:
-    the same kernel without QDQ (flags = 0) and torch.matmul (hipBLASLt) on the raw
-    operands, each timed the same way."""
+    W 14336x4096, MXFP4 on both operands, through qf_linear_forward_mxfp4: the streaming
+    QDQ of X and of W into bf16 buffers, then the BF16 MFMA GEMM on them (bit for bit the
+    fused kernel's result, which is timed among the controls)."""
     name = "w4a4_mxfp4_gemm"
 
     def __init__(self, torch, fq):
@@ -435,25 +435,41 @@ class W4A4GemmMXFP4:
         self.M, self.K = self.X.shape
         self.N = self.W.shape[0]
         self.Y = torch.empty((self.M, self.N), dtype=torch.bfloat16, device="cuda")
+        self.Xq, self.Wq = torch.empty_like(self.X), torch.empty_like(self.W)
         self.flop = 2.0 * self.M * self.N * self.K
-        self.kernels = {"gemm_mxfp4_fused": self.flop}
+        # per kernel: algorithmic bytes of the QDQ passes (bf16 in, bf16 out), flop of the GEMM
+        self.kernels = {"mxfp4_qdq_x": 4.0 * self.M * self.K, "mxfp4_qdq_w": 4.0 * self.N * self.K,
+                        "gemm_bf16_on_qdq_operands": self.flop}
         self.bytes_per_step = self.flop
         self.config = {"workload": self.name, "M": self.M, "N": self.N, "K": self.K,
-                       "format": "MXFP4 W4A4 (E2M1, block 32, E8M0), BF16 MFMA, fp32 accumulate, bf16 out"}
+                       "format": "MXFP4 W4A4 (E2M1, block 32, E8M0): QDQ of X and W once each, then the "
+                                 "BF16 MFMA GEMM, fp32 accumulate, bf16 out"}
 
     def step(self, mark=None):
-        t = mark or _no_mark
-        t("gemm_mxfp4_fused", 0)
-        self.fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=3)
-        t("gemm_mxfp4_fused", 1)
+        fq = self.fq
+        if mark is None:
+            fq.qf_linear_forward_mxfp4(self.X, self.W, self.Y, Xq=self.Xq, Wq=self.Wq)
+            return
+        # the three launches the entry point makes, each bracketed on its own
+        mark("mxfp4_qdq_x", 0)
+        fq.qf_qdq_mxfp4(self.X, self.Xq)
+        mark("mxfp4_qdq_x", 1)
+        mark("mxfp4_qdq_w", 0)
+        fq.qf_qdq_mxfp4(self.W, self.Wq)
+        mark("mxfp4_qdq_w", 1)
+        mark("gemm_bf16_on_qdq_operands", 0)
+        fq.qf_gemm_mxfp4(self.Xq, self.Wq, self.Y, flags=0)
+        mark("gemm_bf16_on_qdq_operands", 1)
 
     def controls(self, reps=10):
-        """ms of the plain-BF16 run of the same kernel, of torch.matmul, of the layer's
-        backward (dX = dY . Wq and dW = dY^T . Xq with their three transposes; TFLOP/s over
-        both products), of the NVFP4 W4A4 form of the fused kernel (tensor scales of X and
-        W from the tensor-scale pass, timed on their own), and of the same MXFP4 W4A4 product on the MXFP4 matrix cores: both
-        operands quantized in the kernel; W pre-packed by qf_pack_mxfp4 with X quantized in
-        the kernel; both pre-packed (the packs are timed on their own)."""
+        """ms of: the fused kernel (QDQ inside the GEMM); the same kernel on the raw operands
+        (flags = 0); torch.matmul (hipBLASLt) on the raw operands; the NVFP4 W4A4 product,
+        fused and in two passes (tensor scales of X and W included in the two-pass time and
+        timed on their own); the layer's backward (dX = dY . Wq and dW = dY^T . Xq with
+        their three transposes; TFLOP/s over both products); the same MXFP4 W4A4 product on
+        the MXFP4 matrix cores: both operands quantized in the kernel, W pre-packed with X
+        quantized in the kernel, both pre-packed (the packs timed on their own), and both
+        packs followed by the packed GEMM."""
         torch = self.torch
         fq = self.fq
         out = {}
@@ -467,8 +483,22 @@ class W4A4GemmMXFP4:
         dW = torch.empty_like(self.W)
         bws = torch.empty(fq.qf_linear_backward_workspace(self.M, self.N, self.K), dtype=torch.uint8,
                           device="cuda")
-        for name, fn in (("gemm_bf16_same_kernel", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
+        Xq, Wq = self.Xq, self.Wq
+
+        def two_pass_nv():
+            fq.qf_nvfp4_tensor_scale(self.X, sx)
+            fq.qf_nvfp4_tensor_scale(self.W, sw)
+            fq.qf_linear_forward_nvfp4(self.X, self.W, sx, sw, self.Y, Xq=Xq, Wq=Wq)
+
+        def fp4_cores_pack_then_gemm():
+            fq.qf_pack_mxfp4(self.X, Xc, Xs)
+            fq.qf_pack_mxfp4(self.W, Wc, Ws)
+            fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)
+        for name, fn in (("w4a4_mxfp4_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=3)),
+                         ("gemm_bf16_same_kernel_raw_operands",
+                          lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
                          ("w4a4_nvfp4_fused", lambda: fq.qf_gemm_nvfp4(self.X, self.W, sx, sw, self.Y)),
+                         ("w4a4_nvfp4_two_pass", two_pass_nv),
                          ("tensor_scales_nvfp4", lambda: (fq.qf_nvfp4_tensor_scale(self.X, sx),
                                                           fq.qf_nvfp4_tensor_scale(self.W, sw))),
                          ("backward_dx_dw_mxfp4", lambda: fq.qf_linear_backward_mxfp4(self.X, self.W, dY, dX, dW,
@@ -477,6 +507,7 @@ class W4A4GemmMXFP4:
                          ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
                          ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
                          ("w4a4_fp4_cores_both_packed", lambda: fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)),
+                         ("w4a4_fp4_cores_pack_then_gemm", fp4_cores_pack_then_gemm),
                          ("pack_w_mxfp4", lambda: fq.qf_pack_mxfp4(self.W, Wc, Ws)),
                          ("pack_x_mxfp4", lambda: fq.qf_pack_mxfp4(self.X, Xc, Xs))):
             for _ in range(3):
@@ -669,6 +700,19 @@ def measure(torch, wl, steps, warmup):
     return ms_per_step, kern
 
 
+def gemm_kernel_figures(wl, kern):
+    """Per-kernel figures of the GEMM workload: TFLOP/s for the GEMM, GB/s for the QDQ passes."""
+    out = {}
+    for k, v in kern.items():
+        if k.startswith("gemm"):
+            tf = round(wl.flop / v["ms"] / 1e9, 1)
+            out[k] = {"ms": v["ms"], "TFLOP/s": tf, "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                      "launches_per_step": v["launches_per_step"]}
+        else:
+            out[k] = v
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -700,12 +744,11 @@ def main():
     gemm = isinstance(wl, W4A4GemmMXFP4)
     if gemm:
         # a contraction: TFLOP/s against the dense BF16 MFMA peak
-        achieved = round(wl.flop / kern[dom]["ms"] / 1e9, 1)
+        kern = gemm_kernel_figures(wl, kern)
+        achieved = kern[dom]["TFLOP/s"]
         roofline = {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": MFMA_BF16_PEAK_TFS,
                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFS, 4), "traffic": None}
         value, unit = wl.flop / (ms_per_step / 1e3) / 1e12, "TFLOP/s"
-        for k in kern:
-            kern[k] = {"ms": kern[k]["ms"], "TFLOP/s": achieved, "launches_per_step": kern[k]["launches_per_step"]}
     else:
         achieved = kern[dom]["GB/s"]
         roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -752,7 +795,8 @@ def main():
             if isinstance(w2, W4A4GemmMXFP4):
                 tf = w2.flop / ms2 / 1e9
                 other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5), "TFLOP/s": round(tf, 1),
-                               "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4), "controls": w2.controls()}
+                               "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4),
+                               "kernels": gemm_kernel_figures(w2, kern2), "controls": w2.controls()}
             else:
                 other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5),
                                "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1), "kernels": kern2}

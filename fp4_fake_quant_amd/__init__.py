@@ -380,6 +380,45 @@ def qf_gemm_nvfp4(X, W, d_scale_x, d_scale_w, Y=None, flags=QF_QDQ_A | QF_QDQ_W)
     return Y
 
 
+def _linear_forward_args(X, W, Y, Xq, Wq, flags):
+    M, K, ldx = _mat(_bf16(X, "X"), "X")
+    N, K2, ldw = _mat(_bf16(W, "W"), "W")
+    if K2 != K:
+        raise ValueError(f"X has K={K} but W has K={K2}")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=X.device)
+    if Xq is None and flags & QF_QDQ_A:
+        Xq = torch.empty((M, K), dtype=torch.bfloat16, device=X.device)
+    if Wq is None and flags & QF_QDQ_W:
+        Wq = torch.empty((N, K), dtype=torch.bfloat16, device=X.device)
+    _bf16(Y, "Y")
+    ldxq = _mat(_bf16(Xq, "Xq"), "Xq")[2] if Xq is not None else 0
+    ldwq = _mat(_bf16(Wq, "Wq"), "Wq")[2] if Wq is not None else 0
+    return M, N, K, ldx, ldw, Y, Xq, ldxq, Wq, ldwq
+
+
+def qf_linear_forward_mxfp4(X, W, Y=None, flags=QF_QDQ_A | QF_QDQ_W, Xq=None, Wq=None):
+    """(Y, Xq, Wq): Xq = QDQ(X), Wq = QDQ(W) (MXFP4, for the flagged operands), then
+    Y = Xq . Wq^T on the BF16 matrix cores; Y equals qf_gemm_mxfp4(X, W, flags) bit for bit."""
+    M, N, K, ldx, ldw, Y, Xq, ldxq, Wq, ldwq = _linear_forward_args(X, W, Y, Xq, Wq, flags)
+    _check(lib().qf_linear_forward_mxfp4(_p(X), ldx, _p(W), ldw, _p(Y), _mat(Y, "Y")[2], M, N, K, int(flags),
+                                         _p(Xq), ldxq, _p(Wq), ldwq, _stream()), "qf_linear_forward_mxfp4")
+    return Y, Xq, Wq
+
+
+def qf_linear_forward_nvfp4(X, W, d_scale_x, d_scale_w, Y=None, flags=QF_QDQ_A | QF_QDQ_W, Xq=None, Wq=None):
+    """(Y, Xq, Wq) as qf_linear_forward_mxfp4 on the NVFP4 grid with the device fp32 tensor
+    scales d_scale_x, d_scale_w; Y equals qf_gemm_nvfp4 with the same arguments bit for bit."""
+    for t, name in ((d_scale_x, "d_scale_x"), (d_scale_w, "d_scale_w")):
+        if t is not None and (t.dtype != torch.float32 or t.device.type != "cuda"):
+            raise TypeError(f"{name} must be a float32 device tensor")
+    M, N, K, ldx, ldw, Y, Xq, ldxq, Wq, ldwq = _linear_forward_args(X, W, Y, Xq, Wq, flags)
+    _check(lib().qf_linear_forward_nvfp4(_p(X), ldx, _p(W), ldw, _p(Y), _mat(Y, "Y")[2], M, N, K, int(flags),
+                                         _p(d_scale_x), _p(d_scale_w), _p(Xq), ldxq, _p(Wq), ldwq, _stream()),
+           "qf_linear_forward_nvfp4")
+    return Y, Xq, Wq
+
+
 def qf_transpose_bf16(x, y=None, qdq_mxfp4=False):
     """y [cols, rows] = x^T, MXFP4-QDQ'd along x's rows first when qdq_mxfp4."""
     rows, cols, ldx = _mat(_bf16(x, "x"), "x")

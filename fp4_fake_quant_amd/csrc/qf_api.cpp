@@ -542,6 +542,69 @@ qf_status qf_dequant_q4k(const uint8_t* blocks, int64_t rows, int64_t cols, uint
   return dequant(QF_FMT_Q4K, blocks, nullptr, rows, cols, nullptr, y, ldy, stream);
 }
 
+}  // extern "C"
+
+namespace {
+// Operand checks shared by the BF16-core GEMM entry points (flags are checked by each).
+qf_status check_gemm(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, const uint16_t* Y, int64_t ldy,
+                     int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;
+  if (M == 0 || N == 0) return QF_OK;
+  if (!X || !W || !Y) return QF_ERR_NULL;
+  if (ldx < K || ldw < K || ldy < N) return QF_ERR_SHAPE;
+  if (ldx >= (1ll << 22) || ldw >= (1ll << 22)) return QF_ERR_SHAPE;
+  if (!aligned(X, 16) || !aligned(W, 16) || !aligned(Y, 2) || ldx % 8 || ldw % 8) return QF_ERR_ALIGN;
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  return QF_OK;
+}
+
+// Two-pass forward: QDQ of each flagged operand into its caller buffer, then the BF16
+// GEMM with no QDQ on what the matrix cores should see.  Every argument is checked
+// before the first launch.
+qf_status linear_forward(int fmt, const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
+                         int64_t ldy, int64_t M, int64_t N, int64_t K, unsigned flags, const float* d_sx,
+                         const float* d_sw, uint16_t* Xq, int64_t ldxq, uint16_t* Wq, int64_t ldwq, hipStream_t s) {
+  const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
+  qf_status st = check_gemm(X, ldx, W, ldw, Y, ldy, M, N, K);
+  if (st != QF_OK || M == 0 || N == 0) return st;
+  // the GEMM then reads the QDQ'd copies: the same constraints apply to them
+  st = check_gemm(qa ? Xq : X, qa ? ldxq : ldx, qw ? Wq : W, qw ? ldwq : ldw, Y, ldy, M, N, K);
+  if (st != QF_OK) return st;
+  if (fmt == QF_FMT_NVFP4 && ((qa && !d_sx) || (qw && !d_sw))) return QF_ERR_NULL;
+  if ((d_sx && !aligned(d_sx, 4)) || (d_sw && !aligned(d_sw, 4))) return QF_ERR_ALIGN;
+  const qf_tensor_desc dx = one(X, M, K, ldx, Xq, ldxq, nullptr, nullptr);
+  const qf_tensor_desc dw = one(W, N, K, ldw, Wq, ldwq, nullptr, nullptr);
+  if (qa && (st = check_desc(dx, fmt, true, false)) != QF_OK) return st;
+  if (qw && (st = check_desc(dw, fmt, true, false)) != QF_OK) return st;
+  const int rule = (flags & QF_MX_NOCLIP) ? QF_MX_RULE_NOCLIP : QF_MX_RULE_FLOOR;
+  if (qa && (st = quant_grouped(fmt, &dx, 1, d_sx, s, rule)) != QF_OK) return st;
+  if (qw && (st = quant_grouped(fmt, &dw, 1, d_sw, s, rule)) != QF_OK) return st;
+  return hip_status(qf::launch_gemm_mxfp4(qa ? Xq : X, qa ? ldxq : ldx, qw ? Wq : W, qw ? ldwq : ldw, Y, ldy, (int)M,
+                                          (int)N, (int)K, 0, s));
+}
+}  // namespace
+
+extern "C" {
+
+qf_status qf_linear_forward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
+                                  int64_t ldy, int64_t M, int64_t N, int64_t K, unsigned flags, uint16_t* Xq,
+                                  int64_t ldxq, uint16_t* Wq, int64_t ldwq, void* stream) {
+  if (flags & ~(QF_QDQ_A | QF_QDQ_W | QF_MX_NOCLIP)) return QF_ERR_ARG;
+  if ((flags & QF_MX_NOCLIP) && !(flags & (QF_QDQ_A | QF_QDQ_W))) return QF_ERR_ARG;
+  return linear_forward(QF_FMT_MXFP4, X, ldx, W, ldw, Y, ldy, M, N, K, flags, nullptr, nullptr, Xq, ldxq, Wq, ldwq,
+                        (hipStream_t)stream);
+}
+
+qf_status qf_linear_forward_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
+                                  int64_t ldy, int64_t M, int64_t N, int64_t K, unsigned flags,
+                                  const float* d_scale_x, const float* d_scale_w, uint16_t* Xq, int64_t ldxq,
+                                  uint16_t* Wq, int64_t ldwq, void* stream) {
+  if ((flags & ~(QF_QDQ_A | QF_QDQ_W)) || flags == 0) return QF_ERR_ARG;
+  return linear_forward(QF_FMT_NVFP4, X, ldx, W, ldw, Y, ldy, M, N, K, flags, d_scale_x, d_scale_w, Xq, ldxq, Wq,
+                        ldwq, (hipStream_t)stream);
+}
+
 qf_status qf_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y, int64_t ldy,
                         int64_t M, int64_t N, int64_t K, unsigned flags, void* stream) {
   if (M < 0 || N < 0 || K <= 0 || K % 64 != 0 || M >= (1ll << 30) || N >= (1ll << 30)) return QF_ERR_SHAPE;

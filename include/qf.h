@@ -360,6 +360,36 @@ qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
                         uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K,
                         unsigned flags, const float* d_scale_x, const float* d_scale_w, void* stream);
 
+/* ---------------------------------------- forward of the quantized linear ---- */
+/* Y = QDQ(X) . QDQ(W)^T, the product of qf_gemm_mxfp4 / qf_gemm_nvfp4, in two passes
+ * ("Overview": weights and optionally activations rounded onto the grid, every matmul
+ * in BF16; "Method", "Framework overview": the forward applies the QDQ transform):
+ *   1. Xq = QDQ(X) when flags has QF_QDQ_A and Wq = QDQ(W) when flags has QF_QDQ_W,
+ *      written to the caller's bf16 buffers Xq [M, ldxq] and Wq [N, ldwq] by the
+ *      streaming QDQ kernels (the rules of qf_qdq_mxfp4, or qf_qdq_nvfp4 with the
+ *      tensor scales *d_scale_x / *d_scale_w);
+ *   2. Y = Xq . Wq^T on the BF16 matrix cores (the kernel of qf_gemm_mxfp4 with
+ *      flags 0; an operand that is not flagged is read as given).
+ * Y is bit for bit that of qf_gemm_mxfp4 (qf_gemm_nvfp4) with the same flags and
+ * obeys the same bound.  On MI355X this order is faster than quantizing inside the
+ * GEMM: the fused kernel re-quantizes every operand tile for each tile of Y that
+ * reads it, while here each element is quantized once, and Xq / Wq stay available
+ * for the backward products (qf_linear_backward_mxfp4 with flags 0 on them).
+ * Arguments: as qf_gemm_mxfp4 (flags QF_QDQ_A, QF_QDQ_W, QF_MX_NOCLIP there) or
+ * qf_gemm_nvfp4 (flags QF_QDQ_A and/or QF_QDQ_W, not 0, and the flagged operands'
+ * scales, 4-byte aligned); a flagged operand's buffer is required (QF_ERR_NULL),
+ * 16-byte aligned with its leading dimension a multiple of 8 and >= K, < 2^22; an
+ * unflagged one's buffer is ignored.  Xq may be X (ldxq == ldx: X is overwritten by
+ * its QDQ), likewise Wq and W; no other overlap is allowed.  Every argument is
+ * checked before the first of the three launches on `stream`. */
+qf_status qf_linear_forward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                                  uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, unsigned flags,
+                                  uint16_t* Xq, int64_t ldxq, uint16_t* Wq, int64_t ldwq, void* stream);
+qf_status qf_linear_forward_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                                  uint16_t* Y, int64_t ldy, int64_t M, int64_t N, int64_t K, unsigned flags,
+                                  const float* d_scale_x, const float* d_scale_w,
+                                  uint16_t* Xq, int64_t ldxq, uint16_t* Wq, int64_t ldwq, void* stream);
+
 /* -------------------------------------- backward of the quantized linear ---- */
 /* "Method", "Framework overview": the backward pass reaches the latent weights through
  * the STE, so the layer Y = Xq . Wq^T (Xq, Wq the MXFP4-QDQ'd operands, or the raw ones

@@ -192,6 +192,26 @@ def test_transpose_and_backward_validation():
                                       _addr(0x12000000), need, None) == 1                          # dX needs W
 
 
+def test_linear_forward_validation():
+    """The two-pass forward checks every argument before its first launch."""
+    L = _lib.lib()
+    x, w, y, xq, wq, f = (_addr(a) for a in (0x10000000, 0x10400000, 0x10800000, 0x10c00000, 0x11000000, 0x11400000))
+    mx = lambda *a: L.qf_linear_forward_mxfp4(*a, None)
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 96, 3, xq, 128, wq, 128) == 2            # K % 64
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 16, xq, 128, wq, 128) == 7          # unknown flag
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 8, xq, 128, wq, 128) == 7           # noclip with no operand
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 3, None, 128, wq, 128) == 1         # Xq needed
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 3, xq, 120, wq, 128) == 2           # ldxq < K
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 3, _addr(0x10c00008), 128, wq, 128) == 3
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 3, xq, 132, wq, 128) == 3           # ldxq % 8
+    assert mx(x, 128, w, 128, y, 64, 64, 64, 128, 3, xq, 1 << 22, wq, 128) == 2       # ldxq >= 2^22
+    assert mx(x, 128, w, 128, y, 64, 0, 64, 128, 3, None, 0, None, 0) == 0            # empty: no-op
+    nv = lambda *a: L.qf_linear_forward_nvfp4(*a, None)
+    assert nv(x, 128, w, 128, y, 64, 64, 64, 128, 0, f, f, xq, 128, wq, 128) == 7     # flags 0
+    assert nv(x, 128, w, 128, y, 64, 64, 64, 128, 3, None, f, xq, 128, wq, 128) == 1  # scale of X
+    assert nv(x, 128, w, 128, y, 64, 64, 64, 128, 3, _addr(0x11400002), f, xq, 128, wq, 128) == 3
+
+
 def test_dequant_validation():
     """Dequant calls check shape, pointers and alignment before launching."""
     L = _lib.lib()
