@@ -463,7 +463,7 @@ class W4A4GemmMXFP4:
 
     def controls(self, reps=10):
         """ms of: the fused kernel (QDQ inside the GEMM); the same kernel on the raw operands
-        (flags = 0); torch.matmul (hipBLASLt) on the raw operands; the NVFP4 W4A4 product,
+        (flags = 0); torch.matmul (hipBLASLt) on the raw and on the QDQ'd operands; the NVFP4 W4A4 product,
         fused and in two passes (tensor scales of X and W included in the two-pass time and
         timed on their own); the layer's backward (dX = dY . Wq and dW = dY^T . Xq with
         their three transposes; TFLOP/s over both products); the same MXFP4 W4A4 product on
@@ -483,12 +483,13 @@ class W4A4GemmMXFP4:
         dW = torch.empty_like(self.W)
         bws = torch.empty(fq.qf_linear_backward_workspace(self.M, self.N, self.K), dtype=torch.uint8,
                           device="cuda")
-        Xq, Wq = self.Xq, self.Wq
+        Xq, Wq = self.Xq, self.Wq                         # MXFP4 QDQ'd by the workload's steps
+        Xq_nv, Wq_nv = torch.empty_like(self.X), torch.empty_like(self.W)
 
         def two_pass_nv():
             fq.qf_nvfp4_tensor_scale(self.X, sx)
             fq.qf_nvfp4_tensor_scale(self.W, sw)
-            fq.qf_linear_forward_nvfp4(self.X, self.W, sx, sw, self.Y, Xq=Xq, Wq=Wq)
+            fq.qf_linear_forward_nvfp4(self.X, self.W, sx, sw, self.Y, Xq=Xq_nv, Wq=Wq_nv)
 
         def fp4_cores_pack_then_gemm():
             fq.qf_pack_mxfp4(self.X, Xc, Xs)
@@ -504,6 +505,7 @@ class W4A4GemmMXFP4:
                          ("backward_dx_dw_mxfp4", lambda: fq.qf_linear_backward_mxfp4(self.X, self.W, dY, dX, dW,
                                                                                         ws=bws)),
                          ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y)),
+                         ("torch_matmul_hipblaslt_qdq_operands", lambda: torch.matmul(Xq, Wq.t(), out=self.Y)),
                          ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
                          ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
                          ("w4a4_fp4_cores_both_packed", lambda: fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)),
