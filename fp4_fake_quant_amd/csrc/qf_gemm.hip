@@ -32,6 +32,7 @@
 //     tile order (8 tile rows at a time) and its concurrently running
 //     workgroups share X and W panels in its L2.
 #include "qf_device.h"
+#include "qf_gemm_epilogue.h"
 #include "qf_kernels.h"
 
 namespace qf {
@@ -239,6 +240,10 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X, int64_
 
 
   // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
+  if (y_vec == 2) {                                          // 16-byte aligned rows: through LDS
+    store_tile_lds(acc, smem, Y, ldy, m0, n0, M, N);
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = m0 + (int)(wm * 128 + i * 32 + frow);
@@ -300,7 +305,7 @@ hipError_t launch_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
                              hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
-  const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  const int y_vec = y_store_mode(Y, ldy);
   const dim3 g(tiles), b(G_THREADS);
   if (qa && qw)
     hipLaunchKernelGGL((k_gemm_nvfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
@@ -316,7 +321,7 @@ hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
   // 8-byte output stores need 8-byte aligned rows; otherwise the epilogue stores bf16 by bf16
-  const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  const int y_vec = y_store_mode(Y, ldy);
   const dim3 g(tiles), b(G_THREADS);
   if (flags & QF_MX_NOCLIP) {
     if (qa && qw)

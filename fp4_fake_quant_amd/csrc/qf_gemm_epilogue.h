@@ -1,0 +1,67 @@
+// Output of a 256 x 256 tile of Y from the GEMM kernels whose 8 waves (2 x 4) each hold a
+// 128 x 64 sub-tile as 4 x 2 MFMA 32 x 32 accumulator tiles: lane (frow, fhalf) of wave
+// (wm, wn) holds row wm*128 + 32i + frow, columns wn*64 + 32j + 8g + 4 fhalf + 0..3 in
+// elements 4g .. 4g+3 of acc[i][j].
+//
+// Stored straight from the accumulators, each store instruction covers 32 rows with 16
+// bytes each: 32 partial cache lines, and the address unit takes that many cycles.  Here
+// the tile is converted to bf16 into LDS instead (256 rows x 512 bytes, 16-byte chunks
+// XOR-swizzled by the row's low 5 bits, so the 32 rows of one write instruction spread
+// over all banks and a row's 32 chunks read back conflict-free), then leaves in 16-byte
+// stores: one instruction writes two whole 512-byte row segments.  The bf16 values are
+// the same (RNE of the same fp32), only the store pattern changes.
+#pragma once
+#include "qf_device.h"
+
+namespace qf {
+
+__device__ __forceinline__ uint32_t epi_off(uint32_t r, uint32_t c) { return r * 512u + ((c ^ (r & 31u)) << 4); }
+
+// lds: 128 KiB that no wave reads any more once every wave has arrived here (the
+// function starts with a barrier).  Y rows 16-byte aligned (Y and ldy * 2).
+template <typename AccT>
+__device__ __forceinline__ void store_tile_lds(const AccT (&acc)[4][2], uint8_t* lds, uint16_t* __restrict__ Y,
+                                               int64_t ldy, int m0, int n0, int M, int N) {
+  const uint32_t lane = threadIdx.x & 63u, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t wm = wave >> 2, wn = wave & 3u, frow = lane & 31u, fhalf = lane >> 5;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t r = wm * 128u + 32u * i + frow;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t c = 8u * wn + 4u * j + g;
+        const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<uint2*>(lds + epi_off(r, c) + 8u * fhalf) = make_uint2(lo, hi);
+      }
+  }
+  __syncthreads();
+  // wave w stores rows 32w .. 32w+31, two rows per instruction, lane l chunk l & 31
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const uint32_t r = 32u * wave + 2u * t + (lane >> 5), c = lane & 31u;
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + epi_off(r, c));
+    const int row = m0 + (int)r, col = n0 + 8 * (int)c;
+    if (row >= M || col >= N) continue;
+    uint16_t* yp = Y + (int64_t)row * ldy + col;
+    if (col + 8 <= N) {
+      *reinterpret_cast<uint4*>(yp) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int e = 0; e < N - col; ++e) yp[e] = (uint16_t)(w[e >> 1] >> (16 * (e & 1)));
+    }
+  }
+}
+
+// Store mode of Y for the launchers: 2 when rows are 16-byte aligned (store_tile_lds),
+// 1 when they are 8-byte aligned (8-byte stores from the accumulators), 0 otherwise
+// (element stores).
+inline int y_store_mode(const uint16_t* Y, int64_t ldy) {
+  if (ldy % 8 == 0 && (uintptr_t)Y % 16 == 0) return 2;
+  return (ldy % 4 == 0 && (uintptr_t)Y % 8 == 0) ? 1 : 0;
+}
+
+}  // namespace qf

@@ -35,6 +35,7 @@
 //   - K = 64 per step: the 128 variant is written but needs more registers than
 //     two waves per SIMD allow (it spills), so it is not the default.
 #include "qf_device.h"
+#include "qf_gemm_epilogue.h"
 #include "qf_kernels.h"
 
 namespace qf {
@@ -501,6 +502,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mx4pp(const uint8_t* __rest
     }
   }
   PP_WAIT_VM(0);                                           // no load may still write LDS at exit
+  if (y_vec == 2) {                                          // 16-byte aligned rows: through LDS
+    store_tile_lds(acc, smem, Y, ldy, m0, n0, M, N);
+    return;
+  }
 
   // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fblk + 0..3 ----
 #pragma unroll
@@ -530,7 +535,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mx4pp(const uint8_t* __rest
 hipError_t launch_gemm_mx4pp(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
                              int64_t ldy, int M, int N, int K, hipStream_t s) {
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
-  const int y_vec = (ldy % 4 == 0) && ((uintptr_t)Y % 8 == 0);
+  const int y_vec = y_store_mode(Y, ldy);
   hipLaunchKernelGGL(k_gemm_mx4pp, dim3(tiles), dim3(64 * WAVES), 0, s, Xc, Xs, Wc, Ws, Y, ldy, M, N, K, y_vec);
   return hipGetLastError();
 }
