@@ -5,19 +5,22 @@
 // with both operands contiguous along the reduction axis, so dX takes Wq^T [K, N] and
 // dWq takes dY^T [N, M] and Xq^T [K, M]; these come from one pass here.
 //
-// A workgroup of 256 lanes moves a 64 x 64 tile through LDS.  Reads: lane t takes the
-// 16-byte chunks (t & 7) of rows (t >> 3) + 32 i, so an MXFP4 block of 32 source
-// elements sits in 4 adjacent lanes and is quantized in registers exactly as k_mxfp4
-// does it.  Writes: lane t builds the 8 elements of output row (t & 63), columns
-// 8 (t >> 6) + 32 i .. +7, from 8 LDS half-word reads (a wave's reads cover 64
-// consecutive columns of one LDS row: no bank conflicts), and stores them as 16 bytes.
+// A workgroup of 256 lanes moves a 64-row x 128-column tile through LDS.  Reads: lane t
+// takes the 16-byte chunks (t & 15) of rows (t >> 4) + 16 i (4 loads in flight), so an
+// MXFP4 block of 32 source elements sits in 4 adjacent lanes and is quantized in
+// registers exactly as k_mxfp4 does it; the chunk goes to LDS as four 32-bit words.
+// Writes: lane t builds the 8 elements of output row (t >> 3) + 32 i, columns
+// 8 (t & 7) .. +7, from 8 LDS half-word reads, and stores them as 16 bytes, so 8
+// consecutive lanes write one whole 128-byte output row segment.  The LDS row pitch of
+// 130 elements (65 words) puts the 8 source rows 8 apart that one read instruction
+// touches on 8 different bank groups.
 #include "qf_device.h"
 #include "qf_kernels.h"
 
 namespace qf {
 
-constexpr int TR_TILE = 64;
-constexpr int TR_PITCH = TR_TILE + 8;                      // elements; rows stay 16-byte aligned
+constexpr int TR_ROWS = 64, TR_COLS = 128;               // source tile
+constexpr int TR_PITCH = TR_COLS + 2;                      // elements (65 words): rows 4-byte aligned
 
 // MXFP4 QDQ of one 16-byte chunk; lanes 4i..4i+3 hold one 32-element block (the rule of
 // qf_qdq_mxfp4: E = max(bf16 exponent field of the block maximum - 2, 0)).
@@ -46,26 +49,33 @@ __device__ __forceinline__ uint4 tr_mxfp4_qdq(uint4 w) {
 template <bool QDQ>
 __global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ src, int64_t lds, int R, int C,
                                                    uint16_t* __restrict__ dst, int64_t ldd) {
-  __shared__ __attribute__((aligned(16))) uint16_t t[TR_TILE * TR_PITCH];
-  const int r0 = blockIdx.y * TR_TILE, c0 = blockIdx.x * TR_TILE;
+  __shared__ __attribute__((aligned(16))) uint16_t t[TR_ROWS * TR_PITCH];
+  uint32_t* tw = reinterpret_cast<uint32_t*>(t);
+  const int r0 = blockIdx.y * TR_ROWS, c0 = blockIdx.x * TR_COLS;
   const uint32_t tid = threadIdx.x;
-  uint4 v[2];
+  constexpr int NL = TR_ROWS * TR_COLS / 8 / 256;          // 16-byte chunks per lane (4)
+  uint4 v[NL];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (int)(tid >> 3) + 32 * i, c = 8 * (int)(tid & 7u);
+  for (int i = 0; i < NL; ++i) {
+    const int r = (int)(tid >> 4) + 16 * i, c = 8 * (int)(tid & 15u);
     v[i] = make_uint4(0, 0, 0, 0);
     if (r0 + r < R && c0 + c < C) v[i] = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * lds + c0 + c);
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (int)(tid >> 3) + 32 * i, c = 8 * (int)(tid & 7u);
-    *reinterpret_cast<uint4*>(t + r * TR_PITCH + c) = QDQ ? tr_mxfp4_qdq(v[i]) : v[i];
+  for (int i = 0; i < NL; ++i) {
+    const int r = (int)(tid >> 4) + 16 * i, c = 8 * (int)(tid & 15u);
+    const uint4 q = QDQ ? tr_mxfp4_qdq(v[i]) : v[i];
+    uint32_t* row = tw + (r * TR_PITCH + c) / 2;
+    row[0] = q.x;
+    row[1] = q.y;
+    row[2] = q.z;
+    row[3] = q.w;
   }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int j = (int)(tid & 63u);                        // output row = source column c0 + j
-    const int q = 8 * ((int)(tid >> 6) + 4 * i);           // output columns = source rows r0 + q ..
+  for (int i = 0; i < TR_COLS / 32; ++i) {
+    const int j = (int)(tid >> 3) + 32 * i;                // output row = source column c0 + j
+    const int q = 8 * (int)(tid & 7u);                     // output columns = source rows r0 + q ..
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -78,10 +88,19 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ 
 hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint16_t* dst, int64_t ldd, bool qdq,
                             hipStream_t s) {
   if (R == 0 || C == 0) return hipSuccess;
-  const dim3 g((unsigned)((C + TR_TILE - 1) / TR_TILE), (unsigned)((R + TR_TILE - 1) / TR_TILE)), b(256);
-  if (qdq) hipLaunchKernelGGL(k_transpose<true>, g, b, 0, s, src, lds, R, C, dst, ldd);
-  else hipLaunchKernelGGL(k_transpose<false>, g, b, 0, s, src, lds, R, C, dst, ldd);
-  return hipGetLastError();
+  // grid y is limited to 65535 row tiles: taller sources go in row bands of that many
+  constexpr int BAND = 65535 * TR_ROWS;
+  for (int rb = 0; rb < R; rb += BAND) {
+    const int rn = R - rb < BAND ? R - rb : BAND;
+    const dim3 g((unsigned)((C + TR_COLS - 1) / TR_COLS), (unsigned)((rn + TR_ROWS - 1) / TR_ROWS)), b(256);
+    const uint16_t* sp = src + (int64_t)rb * lds;
+    uint16_t* dp = dst + rb;                                 // the band's rows are output columns rb ..
+    if (qdq) hipLaunchKernelGGL(k_transpose<true>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
+    else hipLaunchKernelGGL(k_transpose<false>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qf

@@ -52,6 +52,15 @@ def test_transpose_bit_exact(shape, qdq):
     assert np.array_equal(y, want), first_mismatch(y, want)
 
 
+def test_transpose_tallest_source():
+    """The largest row count the call takes (rows < 2^22, a multiple of 8) spans more
+    row tiles than one launch grid holds; the launcher splits it into bands."""
+    rows, cols = (1 << 22) - 8, 8
+    x = RNG.integers(0, 1 << 16, size=(rows, cols), dtype=np.uint64).astype(np.uint16)
+    y = host(fq.qf_transpose_bf16(dev(x)))
+    assert np.array_equal(y, x.T), first_mismatch(y, x.T)
+
+
 def test_transpose_strided():
     rows, cols = 72, 96
     x = _bits(RNG.standard_normal((rows, cols)))
