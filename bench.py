@@ -723,6 +723,7 @@ def main():
     ap.add_argument("--workload", default=DenseLayerNVFP4.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads of a default run")
+    ap.add_argument("--no-controls", action="store_true", help="skip the GEMM workload's control timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one 1 GiB device copy (the counter reference of a rocprofv3 --pmc run)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -773,7 +774,7 @@ def main():
         "roofline": roofline,
         "kernels": kern,
     }
-    if gemm:
+    if gemm and not args.no_controls:
         line["controls"] = wl.controls()
     if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
         line["cpu_baseline"] = wl.cpu_baseline()
