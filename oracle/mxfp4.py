@@ -74,6 +74,22 @@ def quantize(x_bits, rule="floor"):
     return codes.reshape(rows, cols), E.astype(np.uint8)
 
 
+def saturated(x_bits, rule="floor"):
+    """Elements the quantizer saturates: y = |x| / 2^(E-127) (exact) exceeds 6, the largest
+    E2M1 magnitude (bool [rows, cols]).  Under the floor rule these are the elements in
+    (6, 8) * 2^(E-127) of blocks whose maximum has a significand above 1.5; under the
+    noclip rule there are none."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    rows, cols = x_bits.shape
+    x = bf16_to_f32(x_bits).reshape(rows, cols // BLOCK, BLOCK)
+    ax = np.abs(x)
+    a = np.max(ax, axis=-1) if cols else np.zeros((rows, 0), np.float32)
+    X = e8m0_value(shared_exponent(a, rule))
+    with np.errstate(under="ignore"):
+        y = (ax / X[..., None]).astype(np.float32)
+    return (y > F32(6.0)).reshape(rows, cols)
+
+
 def dequantize(codes, E):
     """BF16 bits of sign * bf16(v * 2^(E-127))."""
     codes = np.asarray(codes, dtype=np.uint8)

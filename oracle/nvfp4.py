@@ -72,8 +72,9 @@ def tensor_scale(tensors):
     return F32(A) / TENSOR_DIV
 
 
-def quantize(x_bits, s_t):
-    """Codes (uint8 per element, 0..15) and E4M3 block-scale codes for x [rows, cols]."""
+def _scaled(x_bits, s_t):
+    """The quantizer's intermediate values for x [rows, cols]: (x as float32 blocks
+    [rows, cols/16, 16], y = fl(|x| r) per element, the E4M3 codes S, d == 0 per block)."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
     assert cols % BLOCK == 0
@@ -91,11 +92,29 @@ def quantize(x_bits, s_t):
         r = np.where(zero, F32(0.0), F32(1.0) / np.where(zero, F32(1.0), d)).astype(np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
         y = (ax * r[..., None]).astype(np.float32)
+    return x, y, S, zero
+
+
+def quantize(x_bits, s_t):
+    """Codes (uint8 per element, 0..15) and E4M3 block-scale codes for x [rows, cols]."""
+    rows, cols = np.shape(x_bits)
+    x, y, S, zero = _scaled(x_bits, s_t)
     mag = e2m1_encode_mag(y)
     mag[np.broadcast_to(zero[..., None], mag.shape)] = 0
     sign = np.signbit(x).astype(np.uint8)
     codes = (sign << 3) | mag
     return codes.reshape(rows, cols), S
+
+
+def saturated(x_bits, s_t):
+    """Elements the quantizer saturates: the scaled magnitude y = fl(|x| r) exceeds 6, the
+    largest E2M1 magnitude (bool [rows, cols]).  Blocks with d == 0 have none; a zero
+    element has none even where r overflowed (0 * inf is no magnitude)."""
+    rows, cols = np.shape(x_bits)
+    x, y, S, zero = _scaled(x_bits, s_t)
+    with np.errstate(invalid="ignore"):
+        sat = (y > F32(6.0)) & ~zero[..., None] & (x != 0)
+    return sat.reshape(rows, cols)
 
 
 def dequantize(codes, S, s_t):
