@@ -257,6 +257,43 @@ class Q4KSet:
                 "sample": f"the oracle's Q4_K QDQ + pack on the first {r} rows of the 4096x4096 matrix ({dt:.1f} s)"}
 
 
+class SteClippedDense:
+    """The clipped STE over the dense 8B layer's four matrices (218 M elements): the
+    gradient of each latent weight, or +0.0 where the quantizer saturated it, from the
+    weight x, the upstream gradient g (N(0,1)) and, for NVFP4, the matrix's tensor scale
+    (computed once, before timing).  NVFP4 and MXFP4 (floor rule), four launches each."""
+    name = "dense_layer_8b_ste_clipped"
+
+    def __init__(self, torch, fq):
+        import workloads
+        self.torch, self.fq = torch, fq
+        x = workloads.dense_layer_8b_device(seed=0)
+        self.mats = []
+        n = 0
+        for w, g in x.values():
+            self.mats.append(dict(x=w, g=g, s=fq.qf_nvfp4_tensor_scale(w),
+                                  out=torch.empty(w.shape, dtype=torch.float32, device="cuda")))
+            n += w.numel()
+        self.numel = n
+        # algorithmic bytes: x and g in (bf16), fp32 out
+        self.kernels = {"ste_clipped_nvfp4": n * 8.0, "ste_clipped_mxfp4": n * 8.0}
+        self.bytes_per_step = sum(self.kernels.values())
+        self.config = {"workload": self.name, "elements": n,
+                       "formats": "NVFP4 (per-matrix tensor scale), MXFP4 floor rule"}
+
+    def step(self, mark=None):
+        fq = self.fq
+        t = mark or _no_mark
+        t("ste_clipped_nvfp4", 0)
+        for m in self.mats:
+            fq.qf_ste_backward_clipped_nvfp4(m["g"], m["x"], m["s"], m["out"])
+        t("ste_clipped_nvfp4", 1)
+        t("ste_clipped_mxfp4", 0)
+        for m in self.mats:
+            fq.qf_ste_backward_clipped_mxfp4(m["g"], m["x"], m["out"])
+        t("ste_clipped_mxfp4", 1)
+
+
 class DequantDense:
     """Dequant of the dense 8B layer's four matrices (218 M elements) from each packed
     layout back to bf16: NVFP4 (per-matrix tensor scales), MXFP4 and Q4_K, four launches
@@ -664,10 +701,11 @@ class MoELoRANVFP4x8Remerge(MoELoRANVFP4):
 
 
 WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4,
-                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge, DequantDense)}
+                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge, DequantDense,
+                                 SteClippedDense)}
 # measured next to the headline workload in a default run (fewer steps each)
 SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
-             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name]
+             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name, SteClippedDense.name]
 
 
 def measure(torch, wl, steps, warmup):

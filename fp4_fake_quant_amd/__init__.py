@@ -230,6 +230,36 @@ def qf_ste_backward(g_q, g_latent=None, accumulate=False):
     return g_latent
 
 
+def _ste_clip_args(g_q, x, g_latent):
+    rows, cols, ldx = _mat(_bf16(x, "x"), "x")
+    _bf16(g_q, "g_q")
+    if tuple(g_q.shape) != (rows, cols) or not g_q.is_contiguous():
+        raise ValueError("g_q must be a contiguous tensor of x's shape")
+    if g_latent is None:
+        g_latent = torch.empty((rows, cols), dtype=torch.float32, device=x.device)
+    if g_latent.dtype != torch.float32 or tuple(g_latent.shape) != (rows, cols) or not g_latent.is_contiguous():
+        raise ValueError("g_latent must be a contiguous float32 tensor of x's shape")
+    return rows, cols, ldx, g_latent
+
+
+def qf_ste_backward_clipped_nvfp4(g_q, x, d_scale, g_latent=None, accumulate=False):
+    """g_latent = f32(g_q), or +0.0 where the NVFP4 quantizer (tensor scale d_scale)
+    saturated x; added to g_latent when accumulate."""
+    rows, cols, ldx, g_latent = _ste_clip_args(g_q, x, g_latent)
+    _check(lib().qf_ste_backward_clipped_nvfp4(_p(g_q), _p(x), rows, cols, ldx, _p(d_scale), _p(g_latent),
+                                               int(bool(accumulate)), _stream()), "qf_ste_backward_clipped_nvfp4")
+    return g_latent
+
+
+def qf_ste_backward_clipped_mxfp4(g_q, x, g_latent=None, accumulate=False, rule=QF_MX_RULE_FLOOR):
+    """g_latent = f32(g_q), or +0.0 where the MXFP4 quantizer (shared-exponent rule `rule`)
+    saturated x; added to g_latent when accumulate."""
+    rows, cols, ldx, g_latent = _ste_clip_args(g_q, x, g_latent)
+    _check(lib().qf_ste_backward_clipped_mxfp4(_p(g_q), _p(x), rows, cols, ldx, int(rule), _p(g_latent),
+                                               int(bool(accumulate)), _stream()), "qf_ste_backward_clipped_mxfp4")
+    return g_latent
+
+
 # ---------------------------------------------------------------- LoRA ----
 class LoraBatch:
     """Descriptor array for the qf_lora_* calls, built once and reusable.

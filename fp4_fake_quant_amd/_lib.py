@@ -82,6 +82,10 @@ SIGNATURES = {
                                          c_void_p]),
     "qf_gemm_nvfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint,
                               c_void_p, c_void_p, c_void_p]),
+    "qf_ste_backward_clipped_nvfp4": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_int,
+                                              c_void_p]),
+    "qf_ste_backward_clipped_mxfp4": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_i64, c_int, c_void_p, c_int,
+                                              c_void_p]),
     "qf_linear_forward_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64,
                                         ctypes.c_uint, c_void_p, c_i64, c_void_p, c_i64, c_void_p]),
     "qf_linear_forward_nvfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64,

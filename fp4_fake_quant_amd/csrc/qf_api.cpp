@@ -319,6 +319,34 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
   return hip_status(qf::launch_ste(g_q, g_latent, n, accumulate != 0, (hipStream_t)stream));
 }
 
+namespace {
+qf_status ste_clipped(int fmt, int rule, const uint16_t* g_q, const uint16_t* x, int64_t rows, int64_t cols,
+                      int64_t ldx, const float* d_scale, float* g_latent, int accumulate, void* stream) {
+  if (rows < 0 || cols < 0 || cols % block_of(fmt)) return QF_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return QF_OK;
+  if (!g_q || !x || !g_latent || (fmt == QF_FMT_NVFP4 && !d_scale)) return QF_ERR_NULL;
+  if (ldx < cols) return QF_ERR_SHAPE;
+  if ((uint64_t)rows * (uint64_t)(cols / 8) >= (1ull << 32) - 4096) return QF_ERR_SHAPE;   // 32-bit chunk index
+  if (!aligned(g_q, 16) || !aligned(x, 16) || !aligned(g_latent, 16) || ldx % 8) return QF_ERR_ALIGN;
+  if (fmt == QF_FMT_NVFP4 && !aligned(d_scale, 4)) return QF_ERR_ALIGN;
+  return hip_status(qf::launch_ste_clip(fmt, rule, g_q, x, rows, cols, ldx, d_scale, g_latent, accumulate != 0,
+                                        (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" {
+qf_status qf_ste_backward_clipped_nvfp4(const uint16_t* g_q, const uint16_t* x, int64_t rows, int64_t cols,
+                                        int64_t ldx, const float* d_scale, float* g_latent, int accumulate,
+                                        void* stream) {
+  return ste_clipped(QF_FMT_NVFP4, QF_MX_RULE_FLOOR, g_q, x, rows, cols, ldx, d_scale, g_latent, accumulate, stream);
+}
+qf_status qf_ste_backward_clipped_mxfp4(const uint16_t* g_q, const uint16_t* x, int64_t rows, int64_t cols,
+                                        int64_t ldx, int rule, float* g_latent, int accumulate, void* stream) {
+  if (rule != QF_MX_RULE_FLOOR && rule != QF_MX_RULE_NOCLIP) return QF_ERR_ARG;
+  return ste_clipped(QF_FMT_MXFP4, rule, g_q, x, rows, cols, ldx, nullptr, g_latent, accumulate, stream);
+}
+}  // extern "C"
+
 // ------------------------------------------------------------------ LoRA --
 namespace {
 

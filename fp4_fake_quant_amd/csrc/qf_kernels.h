@@ -108,6 +108,8 @@ hipError_t launch_nvfp4_scale_reduce(const ReduceArgs& a, hipStream_t s);
 hipError_t launch_quant(int fmt, bool write_y, bool write_packed, const QArgs& a, hipStream_t s,
                         int mx_rule = QF_MX_RULE_FLOOR);
 hipError_t launch_ste(const uint16_t* g, float* out, int64_t n, bool accumulate, hipStream_t s);
+hipError_t launch_ste_clip(int fmt, int mx_rule, const uint16_t* g, const uint16_t* x, int64_t rows, int64_t cols,
+                           int64_t ldx, const float* d_scale, float* out, bool acc, hipStream_t s);
 hipError_t launch_selftest_conversions(unsigned long long* counts, hipStream_t s);
 hipError_t launch_gemm_mx4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, const uint8_t* Wc,
                            const uint8_t* Ws, uint16_t* Y, int64_t ldy, int M, int N, int K, hipStream_t s);

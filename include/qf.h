@@ -200,6 +200,26 @@ qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream);
 qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int accumulate,
                           void* stream);
 
+/* Clipped STE on the FP4 grids (the second reading of the "Method", "Framework overview"
+ * STE: the gradient reaches the latent weight only where the quantizer kept the element
+ * inside the E2M1 grid of the "Supported formats" table).  For x [rows, ldx] (the latent
+ * weight the forward quantized) an element saturates when its scaled magnitude exceeds 6:
+ *   NVFP4: fl(|x| r) > 6 with the block's r = fl(1/d), d = fl(s s_t), s_t = *d_scale (the
+ *          tensor scale the forward used); blocks with d = 0 and zero elements never do;
+ *   MXFP4: |x| > 6 * 2^(E-127) with the block's shared exponent E under `rule`
+ *          (QF_MX_RULE_FLOOR or QF_MX_RULE_NOCLIP; none saturates under the latter).
+ * g_latent[i] = f32(g_q[i]), or +0.0 where x[i] saturated; with accumulate != 0 that value
+ * is added (one fp32 rounding).  g_q bf16 and g_latent fp32 are contiguous [rows, cols],
+ * 16-byte aligned; x 16-byte aligned with ldx a multiple of 8 and >= cols (QF_ERR_ALIGN /
+ * QF_ERR_SHAPE); cols a multiple of 16 (NVFP4) or 32 (MXFP4), rows * cols / 8 < 2^32 - 4096
+ * (QF_ERR_SHAPE); d_scale 4-byte aligned (QF_ERR_NULL if missing); an unknown rule gives
+ * QF_ERR_ARG.  The masks are bit for bit the quantizers' own decisions. */
+qf_status qf_ste_backward_clipped_nvfp4(const uint16_t* g_q, const uint16_t* x, int64_t rows, int64_t cols,
+                                        int64_t ldx, const float* d_scale, float* g_latent, int accumulate,
+                                        void* stream);
+qf_status qf_ste_backward_clipped_mxfp4(const uint16_t* g_q, const uint16_t* x, int64_t rows, int64_t cols,
+                                        int64_t ldx, int rule, float* g_latent, int accumulate, void* stream);
+
 /* ---------------------------------------------- LoRA, one expert at a time */
 /* "Method" section, "Quantization-aware distillation": LoRA keeps one frozen
  * base W, trains only the adapters A (r x cols) and B (rows x r), and quantizes

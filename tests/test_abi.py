@@ -212,6 +212,20 @@ def test_linear_forward_validation():
     assert nv(x, 128, w, 128, y, 64, 64, 64, 128, 3, _addr(0x11400002), f, xq, 128, wq, 128) == 3
 
 
+def test_ste_clipped_validation():
+    L = _lib.lib()
+    g, x, o, f = _addr(0x10000000), _addr(0x10400000), _addr(0x10800000), _addr(0x10c00000)
+    assert L.qf_ste_backward_clipped_mxfp4(g, x, 4, 48, 48, 0, o, 0, None) == 2        # cols % 32
+    assert L.qf_ste_backward_clipped_nvfp4(g, x, 4, 24, 24, f, o, 0, None) == 2        # cols % 16
+    assert L.qf_ste_backward_clipped_mxfp4(g, x, 4, 64, 64, 5, o, 0, None) == 7        # rule
+    assert L.qf_ste_backward_clipped_nvfp4(g, x, 4, 32, 32, None, o, 0, None) == 1     # tensor scale
+    assert L.qf_ste_backward_clipped_mxfp4(g, x, 4, 64, 32, 0, o, 0, None) == 2        # ldx < cols
+    assert L.qf_ste_backward_clipped_mxfp4(g, _addr(0x10400008), 4, 64, 64, 0, o, 0, None) == 3
+    assert L.qf_ste_backward_clipped_mxfp4(g, x, 4, 64, 68, 0, o, 0, None) == 3        # ldx % 8
+    assert L.qf_ste_backward_clipped_nvfp4(g, x, 4, 32, 32, _addr(0x10c00002), o, 0, None) == 3
+    assert L.qf_ste_backward_clipped_mxfp4(g, x, 0, 64, 64, 0, o, 0, None) == 0        # empty: no-op
+
+
 def test_dequant_validation():
     """Dequant calls check shape, pointers and alignment before launching."""
     L = _lib.lib()
