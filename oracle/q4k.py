@@ -31,9 +31,22 @@ bytes 0-1 d (fp16, little endian), 2-3 dmin, 4-15 a 96-bit little-endian bit
 stream with sc_j at bits 6j..6j+5 and m_j at bits 48+6j..48+6j+5, bytes
 16-143 the codes, byte i holding element 2i (low nibble) and 2i+1 (high).
 
+A second sub-block scale rule, "mse", is kept as an option (a search of our own; the
+page names an MSE-optimal quantizer only as a PTQ baseline and gives no rule): step 2's
+scale_j is replaced by the best of 8 shrunken candidates, judged by the squared error of
+the sub-block quantized with that scale and the offset off_j, before the two-level
+(d, sc_j) quantization:
+  base = fl(fl(mx_j - mn_j) / 15); for k = 0..7: s_k = fl(base * (1 - k/16));
+  r = 0 if s_k == 0 else fl(1 / s_k); q_e = clamp(rint(fl(fl(x_e - mn_j) * r)), 0, 15);
+  e_e = fl(fl(fl(q_e * s_k) + mn_j) - x_e); err_k = the sum of fl(e_e * e_e) in a fixed
+  order: over the 8 elements of each quarter of the sub-block in index order, then
+  (quarter 0 + quarter 1) + (quarter 2 + quarter 3), each addition rounded to float32;
+  scale_j = s_k for the first k with the smallest err_k (k = 0 is the min/max rule).
+Steps 3-7 are unchanged.
+
 Pins: closed-form packed size, brute-force per-element q and rint steps,
 on-grid outputs, QDQ == dequant(unpack(pack)), planted exact round trip and
-idempotence, tests/test_oracle_formats.py.
+idempotence, tests/test_oracle_formats.py; the mse rule in tests/test_oracle_q4k_mse.py.
 """
 
 import numpy as np
@@ -46,9 +59,46 @@ NSUB = SUPER // SUB
 BLOCK_BYTES = 144
 
 
-def quantize(x_bits):
+MSE_CANDIDATES = 8
+
+
+def mse_scale(x, mn, mx):
+    """Sub-block scales under the mse rule.  x: float32 [..., NSUB, SUB]; mn, mx: the
+    sub-blocks' (normalized) extremes [..., NSUB].  Returns (scale [..., NSUB] float32,
+    err [..., NSUB, MSE_CANDIDATES] float32, the chosen candidate index)."""
+    base = ((mx - mn).astype(np.float32) / F32(15.0)).astype(np.float32)
+    t = (x - mn[..., None]).astype(np.float32)                        # >= 0
+    errs, scales = [], []
+    for k in range(MSE_CANDIDATES):
+        s = (base * F32(1.0 - k / 16.0)).astype(np.float32)
+        zero = s == 0
+        with np.errstate(divide="ignore"):
+            r = np.where(zero, F32(0.0), F32(1.0) / np.where(zero, F32(1.0), s)).astype(np.float32)
+        q = np.clip(rint((t * r[..., None]).astype(np.float32)), 0, 15).astype(np.float32)
+        xh = ((q * s[..., None]).astype(np.float32) + mn[..., None]).astype(np.float32)
+        e = (xh - x).astype(np.float32)
+        sq = (e * e).astype(np.float32).reshape(e.shape[:-1] + (4, SUB // 4))
+        part = sq[..., 0]
+        for i in range(1, SUB // 4):                                    # in index order
+            part = (part + sq[..., i]).astype(np.float32)
+        err = ((part[..., 0] + part[..., 1]).astype(np.float32) +
+               (part[..., 2] + part[..., 3]).astype(np.float32)).astype(np.float32)
+        errs.append(err)
+        scales.append(s)
+    err = np.stack(errs, axis=-1)
+    best = np.zeros(err.shape[:-1], np.int64)
+    best_err = err[..., 0]
+    for k in range(1, MSE_CANDIDATES):                                 # first strict minimum
+        better = err[..., k] < best_err
+        best = np.where(better, k, best)
+        best_err = np.where(better, err[..., k], best_err)
+    scale = np.take_along_axis(np.stack(scales, axis=-1), best[..., None], axis=-1)[..., 0]
+    return scale.astype(np.float32), err, best
+
+
+def quantize(x_bits, rule="minmax"):
     """Returns dict with d, dmin (fp16 bits [rows, nsb]), sc, m ([rows, nsb, 8] uint8),
-    q ([rows, cols] uint8)."""
+    q ([rows, cols] uint8).  rule: "minmax" (the default) or "mse" (see the module notes)."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
     assert cols % SUPER == 0
@@ -63,7 +113,12 @@ def quantize(x_bits):
     mn = np.where(mn == 0, F32(0.0), mn).astype(np.float32)
     mx = np.max(x, axis=-1)
     mx = np.where(mx == 0, F32(0.0), mx).astype(np.float32)
-    scale = ((mx - mn).astype(np.float32) / F32(15.0)).astype(np.float32)
+    if rule == "minmax":
+        scale = ((mx - mn).astype(np.float32) / F32(15.0)).astype(np.float32)
+    elif rule == "mse":
+        scale = mse_scale(x, mn, mx)[0]
+    else:
+        raise ValueError(rule)
     off = (F32(0.0) - mn).astype(np.float32)
     d_bits = f32_to_f16_bits((np.max(scale, axis=-1) / F32(63.0)).astype(np.float32))
     dmin_bits = f32_to_f16_bits((np.max(off, axis=-1) / F32(63.0)).astype(np.float32))
@@ -98,8 +153,8 @@ def dequantize(p):
     return f32_to_bf16(o).reshape(rows, cols).astype(np.uint16)
 
 
-def qdq(x_bits):
-    return dequantize(quantize(x_bits))
+def qdq(x_bits, rule="minmax"):
+    return dequantize(quantize(x_bits, rule))
 
 
 def pack(p):

@@ -1,0 +1,81 @@
+"""Pins of the oracle's Q4_K "mse" sub-block scale rule (CPU).
+
+Independent of the rule's float32 code, they check what it must achieve and its special cases:
+- the chosen candidate minimizes the sub-block's squared error recomputed in float64 from the
+  candidate scales (within float32 summation noise), so a wrong index, a reversed comparison or
+  a dropped term fails;
+- k = 0 is the min/max rule, so the chosen error is never above the min/max scale's;
+- sub-blocks that already sit on the min/max grid (error 0 at k = 0) and constant sub-blocks
+  keep the min/max scale;
+- with every sub-block on k = 0 the whole quantizer equals the min/max rule.
+"""
+
+import numpy as np
+
+import workloads
+from oracle import q4k
+from oracle import primitives as P
+
+RNG = np.random.default_rng(2718)
+
+
+def _extremes(x):
+    mn = np.minimum(np.min(x, axis=-1), np.float32(0.0))
+    mn = np.where(mn == 0, np.float32(0.0), mn).astype(np.float32)
+    mx = np.max(x, axis=-1)
+    mx = np.where(mx == 0, np.float32(0.0), mx).astype(np.float32)
+    return mn, mx
+
+
+def _err64(x, mn, s):
+    """Squared error of the sub-blocks under scale s (float64 arithmetic, ties to even)."""
+    x64, mn64, s64 = x.astype(np.float64), mn.astype(np.float64)[..., None], s.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s64 == 0, 0.0, np.clip(np.rint((x64 - mn64) / np.where(s64 == 0, 1.0, s64)), 0, 15))
+    return ((q * s64 + mn64 - x64) ** 2).sum(axis=-1)
+
+
+def _subblocks(bits):
+    rows, cols = bits.shape
+    return P.bf16_to_f32(bits).reshape(rows, cols // 256, 8, 32)
+
+
+def test_choice_minimizes_float64_error():
+    for bits in (workloads.single_256x512()["W"],
+                 P.f32_to_bf16((RNG.standard_t(2, size=(64, 512)) * 0.02 + 0.001).astype(np.float32))):
+        x = _subblocks(bits)
+        mn, mx = _extremes(x)
+        scale, err32, best = q4k.mse_scale(x, mn, mx)
+        base = ((mx - mn).astype(np.float32) / np.float32(15.0)).astype(np.float32)
+        e64 = np.stack([_err64(x, mn, (base * np.float32(1 - k / 16)).astype(np.float32)) for k in range(8)], -1)
+        chosen = np.take_along_axis(e64, best[..., None], -1)[..., 0]
+        tol = 1e-5 * e64.min(-1) + 1e-30
+        assert np.all(chosen <= e64.min(-1) + tol)
+        assert np.all(chosen <= e64[..., 0] + tol)                     # never worse than min/max
+        assert (best > 0).mean() > 0.05                                # the search does act
+        assert np.allclose(err32, e64, rtol=1e-5, atol=1e-30)
+
+
+def test_special_cases():
+    x = np.zeros((1, 1, 8, 32), np.float32)
+    base = np.float32(0.25)
+    x[0, 0, 0] = (np.float32(-1.0) + base * np.arange(16, dtype=np.float32).repeat(2)).astype(np.float32)  # on the grid
+    x[0, 0, 1] = 0.5                                                    # constant (mn clamps to 0)
+    x[0, 0, 2] = 0.0                                                    # all zero
+    mn, mx = _extremes(x)
+    scale, _, best = q4k.mse_scale(x, mn, mx)
+    assert best[0, 0, 0] == 0 and best[0, 0, 1] == 0 and best[0, 0, 2] == 0
+
+
+def test_equal_to_minmax_when_nothing_shrinks():
+    # every sub-block on its own min/max grid: the mse rule reproduces the min/max quantizer
+    rows = 8
+    lo = -(RNG.integers(1, 8, size=(rows, 2, 8, 1)).astype(np.float32) * np.float32(0.125))
+    step = RNG.integers(1, 4, size=(rows, 2, 8, 1)).astype(np.float32) * np.float32(0.0625)
+    lvl = np.stack([RNG.permutation(np.arange(16).repeat(2)) for _ in range(rows * 16)]).reshape(rows, 2, 8, 32)
+    x = (lo + step * lvl.astype(np.float32)).astype(np.float32).reshape(rows, 512)
+    bits = P.f32_to_bf16(x)
+    assert np.array_equal(P.bf16_to_f32(bits), x)                        # exactly representable
+    a, b = q4k.quantize(bits), q4k.quantize(bits, "mse")
+    for key in ("d", "dmin", "sc", "m", "q"):
+        assert np.array_equal(a[key], b[key]), key
