@@ -99,9 +99,9 @@ def test_mutation_mxfp4_ceil_rule_is_caught(monkeypatch):
 def test_mutation_q4k_unclamped_min_is_caught(monkeypatch):
     orig = q4k.quantize
 
-    def unclamped(x_bits):
+    def unclamped(x_bits, rule="minmax"):
         # shift every input up so a block is all-positive, then quantize as if min were not clamped
-        p = orig(x_bits)
+        p = orig(x_bits, rule)
         x = P.bf16_to_f32(x_bits).reshape(p["sc"].shape + (32,))
         allpos = (x.min(axis=-1) > 0)
         p["m"] = np.where(allpos, 1, p["m"]).astype(np.uint8)
