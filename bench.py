@@ -239,6 +239,8 @@ class Q4KSet:
         self.fq.qf_qdq_pack_q4k_grouped(self.items)
         t("q4k_qdq_pack", 1)
 
+    rule = "minmax"
+
     def cpu_baseline(self, budget_s=10.0):
         import numpy as np
         import workloads
@@ -246,15 +248,16 @@ class Q4KSet:
         W = workloads.q4k_set(names=["o"])["o"]
         t0 = time.perf_counter()
         r = 64
-        p = q4k.quantize(W[:r]); q4k.dequantize(p); q4k.pack(p)
+        p = q4k.quantize(W[:r], self.rule); q4k.dequantize(p); q4k.pack(p)
         dt = time.perf_counter() - t0
         r = max(64, min(W.shape[0], int(64 * budget_s / max(dt, 1e-3))))
         t0 = time.perf_counter()
-        p = q4k.quantize(W[:r]); q4k.dequantize(p); q4k.pack(p)
+        p = q4k.quantize(W[:r], self.rule); q4k.dequantize(p); q4k.pack(p)
         dt = time.perf_counter() - t0
         nb = W[:r].size * (2 + 2 + 144 / 256)
         return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-                "sample": f"the oracle's Q4_K QDQ + pack on the first {r} rows of the 4096x4096 matrix ({dt:.1f} s)"}
+                "sample": f"the oracle's Q4_K QDQ + pack ({self.rule} rule) on the first {r} rows of the "
+                          f"4096x4096 matrix ({dt:.1f} s)"}
 
 
 class SteClippedDense:
@@ -292,6 +295,24 @@ class SteClippedDense:
         for m in self.mats:
             fq.qf_ste_backward_clipped_mxfp4(m["g"], m["x"], m["out"])
         t("ste_clipped_mxfp4", 1)
+
+
+class Q4KSetMSE(Q4KSet):
+    """The Q4_K set under the mse sub-block scale rule (8 candidate scales per sub-block,
+    each judged by the sub-block's squared error), one grouped launch."""
+    name = "q4k_set_qdq_pack_mse"
+    rule = "mse"
+
+    def __init__(self, torch, fq):
+        super().__init__(torch, fq)
+        self.kernels = {"q4k_qdq_pack_mse": self.kernels["q4k_qdq_pack"]}
+        self.config = dict(self.config, workload=self.name, rule="mse (8 candidate scales per sub-block)")
+
+    def step(self, mark=None):
+        t = mark or _no_mark
+        t("q4k_qdq_pack_mse", 0)
+        self.fq.qf_qdq_pack_q4k_rule(self.items, self.fq.QF_Q4K_RULE_MSE)
+        t("q4k_qdq_pack_mse", 1)
 
 
 class DequantDense:
@@ -702,10 +723,11 @@ class MoELoRANVFP4x8Remerge(MoELoRANVFP4):
 
 WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4,
                                  MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge, DequantDense,
-                                 SteClippedDense)}
+                                 SteClippedDense, Q4KSetMSE)}
 # measured next to the headline workload in a default run (fewer steps each)
 SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
-             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name, SteClippedDense.name]
+             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name, SteClippedDense.name,
+             Q4KSetMSE.name]
 
 
 def measure(torch, wl, steps, warmup):

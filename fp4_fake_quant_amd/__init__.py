@@ -212,6 +212,15 @@ def qf_qdq_pack_mxfp4_rule(items, rule):
     _check(lib().qf_qdq_pack_mxfp4_rule(ctypes.byref(arr), n, int(rule), _stream()), "qf_qdq_pack_mxfp4_rule")
 
 
+QF_Q4K_RULE_MINMAX, QF_Q4K_RULE_MSE = 0, 1
+
+
+def qf_qdq_pack_q4k_rule(items, rule):
+    """qf_qdq_pack_q4k_grouped under sub-block scale rule QF_Q4K_RULE_MINMAX or QF_Q4K_RULE_MSE."""
+    arr, n = _descs(items)
+    _check(lib().qf_qdq_pack_q4k_rule(ctypes.byref(arr), n, int(rule), _stream()), "qf_qdq_pack_q4k_rule")
+
+
 def qf_qdq_pack_q4k_grouped(items):
     arr, n = _descs(items)
     _check(lib().qf_qdq_pack_q4k_grouped(ctypes.byref(arr), n, _stream()), "qf_qdq_pack_q4k_grouped")

@@ -72,6 +72,7 @@ SIGNATURES = {
     "qf_gemm_mxfp4_packed": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p]),
     "qf_gemm_mxfp4_packed_w": (c_int, [c_void_p, c_i64, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p]),
     "qf_qdq_pack_mxfp4_rule": (c_int, [c_void_p, c_int, c_int, c_void_p]),
+    "qf_qdq_pack_q4k_rule": (c_int, [c_void_p, c_int, c_int, c_void_p]),
     "qf_dequant_nvfp4": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "qf_dequant_mxfp4": (c_int, [c_void_p, c_void_p, c_i64, c_i64, c_void_p, c_i64, c_void_p]),
     "qf_dequant_q4k": (c_int, [c_void_p, c_i64, c_i64, c_void_p, c_i64, c_void_p]),

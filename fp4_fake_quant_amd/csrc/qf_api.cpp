@@ -308,6 +308,10 @@ qf_status qf_qdq_pack_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t
 qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream) {
   return quant_grouped(QF_FMT_Q4K, d, n, nullptr, (hipStream_t)stream);
 }
+qf_status qf_qdq_pack_q4k_rule(const qf_tensor_desc* d, int n, int rule, void* stream) {
+  if (rule != QF_Q4K_RULE_MINMAX && rule != QF_Q4K_RULE_MSE) return QF_ERR_ARG;
+  return quant_grouped(QF_FMT_Q4K, d, n, nullptr, (hipStream_t)stream, rule);
+}
 
 // -------------------------------------------------------------------- STE --
 qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int accumulate, void* stream) {

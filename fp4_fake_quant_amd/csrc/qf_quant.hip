@@ -196,7 +196,13 @@ __global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
 __device__ __forceinline__ float fbits(uint32_t u) { return __uint_as_float(u); }
 __device__ __forceinline__ uint32_t ubits(float f) { return __float_as_uint(f); }
 
-template <bool WY, bool WP, int L>
+// MSE: the sub-block scale is the best of 8 shrunken min/max scales, base (1 - k/16) for
+// k = 0..7, by the squared error of the sub-block quantized with it and the offset -mn:
+// each lane sums its 8 elements' squared errors in index order, the quad adds the four
+// partials as (lane 0 + lane 1) + (lane 2 + lane 3) (DPP xor 1, then xor 2; every lane
+// gets the same total), and the first smallest total wins.  All steps are single fp32
+// operations, so the choice is bit for bit the oracle's.
+template <bool WY, bool WP, int L, bool MSE = false>
 __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
   const int b = blockIdx.x;
   const int ti = find_tensor(a, b);
@@ -234,7 +240,32 @@ __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
     mn = fminf(mn, 0.0f);
     if (mn == 0.0f) mn = 0.0f;        // a zero extreme counts as +0
     if (mx == 0.0f) mx = 0.0f;
-    const float scale = div15(mx - mn);
+    float scale = div15(mx - mn);
+    if constexpr (MSE) {
+      const float base = scale;
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) t[e] = xv[e] - mn;
+      float best = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float sk = base * (1.0f - (float)k / 16.0f);
+        const float rk = (sk == 0.0f) ? 0.0f : 1.0f / sk;
+        float p = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float qe = fminf(fmaxf(__builtin_rintf(t[e] * rk), 0.0f), 15.0f);
+          const float de = (qe * sk + mn) - xv[e];           // two roundings: no contraction
+          p = e == 0 ? de * de : p + de * de;
+        }
+        float tot = p + fbits(dpp_xor1(ubits(p)));
+        tot = tot + fbits(dpp_xor2(ubits(tot)));
+        if (k == 0 || tot < best) {
+          best = tot;
+          scale = sk;
+        }
+      }
+    }
     const float off = 0.0f - mn;
     // super-block maxima of the (non-negative) scales and offsets: unsigned max on bits
     uint32_t sb = ubits(scale), ob = ubits(off);
@@ -400,6 +431,7 @@ hipError_t launch_nvfp4_scale_reduce(const ReduceArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s, int mx_rule) {
+  // mx_rule: QF_MX_RULE_* for MXFP4, QF_Q4K_RULE_* for Q4_K
   if (a.total_tiles == 0) return hipSuccess;
   const dim3 g(a.total_tiles), blk(WG);
 #define QF_DISPATCH(KERNEL, ...)                                                              \
@@ -412,7 +444,10 @@ hipError_t launch_quant(int fmt, bool wy, bool wp, const QArgs& a, hipStream_t s
       if (mx_rule == QF_MX_RULE_NOCLIP) { QF_DISPATCH(k_mxfp4, L_MXFP4, true); }
       else { QF_DISPATCH(k_mxfp4, L_MXFP4); }
       break;
-    case QF_FMT_Q4K: QF_DISPATCH(k_q4k, L_Q4K); break;
+    case QF_FMT_Q4K:
+      if (mx_rule == QF_Q4K_RULE_MSE) { QF_DISPATCH(k_q4k, L_Q4K, true); }
+      else { QF_DISPATCH(k_q4k, L_Q4K); }
+      break;
     default: return hipErrorInvalidValue;
   }
 #undef QF_DISPATCH

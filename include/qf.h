@@ -192,6 +192,19 @@ qf_status qf_qdq_pack_q4k(const uint16_t* x, int64_t rows, int64_t cols, int64_t
                           uint16_t* y, int64_t ldy, uint8_t* blocks, void* stream);
 qf_status qf_qdq_pack_q4k_grouped(const qf_tensor_desc* d, int n, void* stream);
 
+/* qf_qdq_pack_q4k_grouped under a sub-block scale rule: QF_Q4K_RULE_MINMAX (the rule above)
+ * or QF_Q4K_RULE_MSE, a search of our own (the pages name an MSE-optimal quantizer only as a
+ * PTQ baseline): each sub-block's scale is the best of the 8 candidates
+ * s_k = fl(base (1 - k/16)), base = fl(fl(mx - mn)/15), by the squared error of the
+ * sub-block quantized with s_k and the offset -mn (q = clamp(rint(fl(fl(x - mn) fl(1/s_k))),
+ * 0, 15), error fl(fl(fl(q s_k) + mn) - x)), summed in float32 over each quarter of the
+ * sub-block in index order and then as (quarter 0 + quarter 1) + (quarter 2 + quarter 3);
+ * the first smallest sum wins.  The offsets, the two-level d / sc_j and dmin / m_j
+ * quantization, the codes and the layout are as above.  Unknown rules give QF_ERR_ARG. */
+#define QF_Q4K_RULE_MINMAX 0
+#define QF_Q4K_RULE_MSE 1
+qf_status qf_qdq_pack_q4k_rule(const qf_tensor_desc* d, int n, int rule, void* stream);
+
 /* ---------------------------------------------------------------- STE ---- */
 /* Identity straight-through estimator ("Method", "Framework overview"):
  * g_latent[i] = f32(g_q[i]) (accumulate == 0) or g_latent[i] += f32(g_q[i])

@@ -172,6 +172,17 @@ def test_mxfp4_rule_validation():
     assert L.qf_qdq_pack_mxfp4_rule(ctypes.byref(d), 1, 1, None) == 2
 
 
+def test_q4k_rule_validation():
+    L = _lib.lib()
+    d = (_lib.TensorDesc * 1)()
+    d[0].x, d[0].rows, d[0].cols, d[0].ldx = 0x10000000, 4, 512, 512
+    d[0].y, d[0].ldy = 0x10400000, 512
+    assert L.qf_qdq_pack_q4k_rule(ctypes.byref(d), 1, 2, None) == 7             # unknown rule
+    assert L.qf_qdq_pack_q4k_rule(ctypes.byref(d), 1, -1, None) == 7
+    d[0].cols = d[0].ldx = d[0].ldy = 384                                        # not a multiple of 256
+    assert L.qf_qdq_pack_q4k_rule(ctypes.byref(d), 1, 1, None) == 2
+
+
 def test_transpose_and_backward_validation():
     L = _lib.lib()
     x, y, w, d = _addr(0x10000000), _addr(0x10400000), _addr(0x10800000), _addr(0x10c00000)

@@ -358,3 +358,57 @@ def test_mxfp4_noclip_rule(single, which):
     y, c2, s2 = fq.qf_qdq_pack_mxfp4(it["x"])
     assert_same(host(it["y"]), host(y), "floor rule y")
     assert_same(u8(it["scales"]), u8(s2), "floor rule E")
+
+
+# --------------------------------------------------- Q4_K mse scale rule ----
+def _q4k_rule_items(x_bits):
+    xd = dev(x_bits)
+    rows, cols = x_bits.shape
+    return dict(x=xd, y=torch.empty_like(xd),
+                codes=torch.empty((rows, cols // 256, 144), dtype=torch.uint8, device="cuda"))
+
+
+@pytest.mark.parametrize("which", ["single", "asymmetric", "ragged", "on_grid"])
+def test_q4k_mse_rule(single, which):
+    """QF_Q4K_RULE_MSE against the oracle bit for bit (y and the 144-byte blocks), dequant of
+    the blocks equal to y, and the min/max rule through the same entry point equal to
+    qf_qdq_pack_q4k."""
+    rng = np.random.default_rng(11)
+    if which == "single":
+        x = single["W"]
+    elif which == "asymmetric":                      # the Q4_K set's recipe: mean 0.001, row offsets
+        x = workloads.to_bf16_bits((np.float32(0.001) + np.float32(0.02) * rng.standard_normal((64, 1024))
+                                    + rng.uniform(-0.01, 0.01, (64, 1)).astype(np.float32)).astype(np.float32))
+    elif which == "ragged":
+        x = workloads.to_bf16_bits(rng.standard_t(3, size=(37, 768)).astype(np.float32))
+    else:                                            # every sub-block on its own min/max grid
+        lvl = np.stack([rng.permutation(np.arange(16).repeat(2)) for _ in range(16 * 16)]).reshape(16, 512)
+        x = workloads.to_bf16_bits((np.float32(-0.5) + np.float32(0.0625) * lvl).astype(np.float32))
+    it = _q4k_rule_items(x)
+    fq.qf_qdq_pack_q4k_rule([it], fq.QF_Q4K_RULE_MSE)
+    p = q4k.quantize(x, "mse")
+    assert_same(host(it["y"]), q4k.dequantize(p), f"mse y ({which})")
+    assert_same(u8(it["codes"]), q4k.pack(p), f"mse blocks ({which})")
+    assert_same(host(fq.qf_dequant_q4k(it["codes"], *x.shape)), host(it["y"]), f"mse dequant ({which})")
+    fq.qf_qdq_pack_q4k_rule([it], fq.QF_Q4K_RULE_MINMAX)
+    y, b = fq.qf_qdq_pack_q4k(it["x"])
+    assert_same(host(it["y"]), host(y), "minmax rule y")
+    assert_same(u8(it["codes"]), u8(b), "minmax rule blocks")
+
+
+def test_q4k_mse_rule_full_size_sampled():
+    """The Q4_K set's gate/up and vocabulary matrices at full size under the mse rule, one
+    grouped launch; the oracle checks sampled rows bit for bit."""
+    names = ["gate_up", "vocab"]
+    tens = workloads.q4k_set(names=names)
+    items = [_q4k_rule_items(tens[n]) for n in names]
+    fq.qf_qdq_pack_q4k_rule(items, fq.QF_Q4K_RULE_MSE)
+    for n, it in zip(names, items):
+        x = tens[n]
+        rows = sample_rows(x.shape[0], 24, seed=len(n))
+        ri = torch.from_numpy(rows).cuda()
+        p = q4k.quantize(x[rows], "mse")
+        assert_same(host(it["y"][ri]), q4k.dequantize(p), f"{n} mse y")
+        assert_same(u8(it["codes"][ri]), q4k.pack(p), f"{n} mse blocks")
+    del items
+    torch.cuda.empty_cache()
