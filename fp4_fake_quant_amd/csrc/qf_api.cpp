@@ -5,6 +5,7 @@
 #include "qf_kernels.h"
 
 namespace {
+int64_t round256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
 
 thread_local int g_last_hip_error = 0;
 
@@ -323,6 +324,8 @@ qf_status qf_ste_backward(const uint16_t* g_q, float* g_latent, int64_t n, int a
   return hip_status(qf::launch_ste(g_q, g_latent, n, accumulate != 0, (hipStream_t)stream));
 }
 
+}  // extern "C"
+
 namespace {
 qf_status ste_clipped(int fmt, int rule, const uint16_t* g_q, const uint16_t* x, int64_t rows, int64_t cols,
                       int64_t ldx, const float* d_scale, float* g_latent, int accumulate, void* stream) {
@@ -558,8 +561,6 @@ qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, vo
   return hip_status(qf::launch_lora_grads(a, (int)c.grad_wg, accumulate != 0, (hipStream_t)stream));
 }
 
-}  // extern "C"
-
 // ------------------------------------------------------------ W4A4 GEMM --
 
 qf_status qf_dequant_nvfp4(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
@@ -685,10 +686,6 @@ qf_status qf_transpose_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64
   if (!aligned(x, 16) || !aligned(y, 16) || ldx % 8 || ldy % 8) return QF_ERR_ALIGN;
   return hip_status(qf::launch_transpose(x, ldx, (int)rows, (int)cols, y, ldy, qdq_mxfp4 != 0, (hipStream_t)stream));
 }
-
-namespace {
-int64_t round256(int64_t bytes) { return (bytes + 255) / 256 * 256; }
-}  // namespace
 
 size_t qf_linear_backward_workspace(int64_t M, int64_t N, int64_t K) {
   if (M < 0 || N < 0 || K < 0) return 0;
