@@ -50,7 +50,7 @@ __global__ __launch_bounds__(DQ_WG) void k_dequant_fp4(const uint8_t* __restrict
     w[j] = 0;
     sb[j] = 0;
     if (c < nchunks) {
-      w[j] = reinterpret_cast<const uint32_t*>(codes)[c];
+      w[j] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(codes) + c);   // read once
       sb[j] = scales[NV ? c >> 1 : c >> 2];
     }
   }

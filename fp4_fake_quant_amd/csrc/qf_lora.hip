@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     uint4 wv[LORA_PREFETCH];
 #pragma unroll
     for (int q = 0; q < LORA_PREFETCH; ++q) {
-      wv[q] = buf_load16(rw, lo + q * wstride);
+      wv[q] = buf_load16_nt(rw, lo + q * wstride);
       LORA_FENCE();
     }
     uint32_t bw[BW];
@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
           const uint32_t mo = amax_bits8(o);
           m = umax(m, (active && ii < rows) ? mo : 0u);
         }
-        wv[q] = buf_load16(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
+        wv[q] = buf_load16_nt(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
       }
     }
   }
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   const uint32_t gstep = (uint32_t)(4 * cols) * 2u, gchunk = (uint32_t)(GR_ROWS * cols) * 2u;
   auto load_chunk = [&](int ci, uint4 (&gv)[8]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) gv[i] = buf_load16(rg, goff + i * gstep + (uint32_t)ci * gchunk);
+    for (int i = 0; i < 8; ++i) gv[i] = buf_load16_nt(rg, goff + i * gstep + (uint32_t)ci * gchunk);
   };
   auto stage_chunk = [&](uint8_t* buf, const uint4 (&gv)[8]) {
 #pragma unroll

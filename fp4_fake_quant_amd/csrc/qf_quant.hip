@@ -37,6 +37,15 @@ __device__ __forceinline__ uint64_t chunk_offset(uint32_t c, uint32_t cpr, int64
 }
 
 __device__ __forceinline__ uint4 load_chunk(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+// Non-temporal, for the NVFP4 step's kernels (amax, QDQ+pack, STE; every input is read
+// once).  Measured on the dense 8B step: 0.481 -> 0.456 ms; with plain loads the amax pass
+// paid for writing back the previous kernel's dirty lines (121 us against 77 us now).  The
+// MXFP4 and Q4_K kernels keep plain loads: nt measured 2-3% slower on their workloads.
+__device__ __forceinline__ uint4 load_chunk_nt(const uint16_t* p) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 // -------------------------------------------------- NVFP4 pass 1: amax -----
 // Persistent grid: workgroup w walks tiles w, w + grid, ...; every wave folds
@@ -65,7 +74,7 @@ __global__ __launch_bounds__(WG) void k_nvfp4_amax(QArgs a) {
     for (int j = 0; j < L; ++j) {
       const uint32_t c = base + j * WG + threadIdx.x;
       w[j] = make_uint4(0, 0, 0, 0);
-      if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+      if (c < T.nchunks) w[j] = load_chunk_nt(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
     }
     uint32_t m = 0;
 #pragma unroll
@@ -124,7 +133,7 @@ __global__ __launch_bounds__(WG) void k_nvfp4(QArgs a) {
   for (int j = 0; j < L; ++j) {
     const uint32_t c = base + j * WG + threadIdx.x;
     w[j] = make_uint4(0, 0, 0, 0);
-    if (c < T.nchunks) w[j] = load_chunk(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
+    if (c < T.nchunks) w[j] = load_chunk_nt(T.x + chunk_offset(c, T.cpr, T.ldx, T.contig_x));
   }
 #pragma unroll
   for (int j = 0; j < L; ++j) {
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(WG) void k_ste(const uint16_t* __restrict__ g, floa
   for (int j = 0; j < L; ++j) {
     const int64_t i = base + j * WG + threadIdx.x;
     if (i < nv) {
-      const uint4 w = load_chunk(g + i * 8);
+      const uint4 w = load_chunk_nt(g + i * 8);
       float4 lo = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
       float4 hi = make_float4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w));
       float4* o = reinterpret_cast<float4*>(out + i * 8);

@@ -33,8 +33,10 @@ __global__ __launch_bounds__(SC_WG) void k_ste_clip(const uint16_t* __restrict__
     const uint32_t c = base + j * SC_WG;
     if (c >= nchunks) break;                               // uniform over a block's lanes
     const uint32_t row = c / cpr, c8 = c - row * cpr;
-    const uint4 w = *reinterpret_cast<const uint4*>(x + (int64_t)row * ldx + 8 * c8);
-    const uint4 gv = *reinterpret_cast<const uint4*>(g + (int64_t)c * 8);
+    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // both read once: non-temporal
+    const u32x4_t wn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + (int64_t)row * ldx + 8 * c8));
+    const u32x4_t gn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(g + (int64_t)c * 8));
+    const uint4 w = make_uint4(wn.x, wn.y, wn.z, wn.w), gv = make_uint4(gn.x, gn.y, gn.z, gn.w);
     uint32_t m = amax_bits8(w);
     m = umax(m, dpp_xor1(m));
     const uint32_t wv[4] = {w.x, w.y, w.z, w.w};

@@ -59,7 +59,11 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ 
   for (int i = 0; i < NL; ++i) {
     const int r = (int)(tid >> 4) + 16 * i, c = 8 * (int)(tid & 15u);
     v[i] = make_uint4(0, 0, 0, 0);
-    if (r0 + r < R && c0 + c < C) v[i] = *reinterpret_cast<const uint4*>(src + (int64_t)(r0 + r) * lds + c0 + c);
+    if (r0 + r < R && c0 + c < C) {                        // read once: non-temporal
+      typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+      const u32x4_t n = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(src + (int64_t)(r0 + r) * lds + c0 + c));
+      v[i] = make_uint4(n.x, n.y, n.z, n.w);
+    }
   }
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
