@@ -473,6 +473,32 @@ class Single256x512:
         fq.qf_ste_backward(self.G, self.g)
         t("ste_backward", 1)
 
+    def controls(self, reps=500):
+        """The same step captured once in a HIP graph and replayed: the GPU-side time of its
+        six launches without the per-call host overhead."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            self.step()
+        for _ in range(10):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1000.0 / reps
+        return {"graph_replay": {"us_per_step": round(us, 2), "replays": reps,
+                                 "GB/s": round(self.bytes_per_step / us / 1e3, 1)}}
+
 
 MFMA_BF16_PEAK_TFS = 2516.6     # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (dense)
 MFMA_FP4_PEAK_TFS = 10100.0     # MI355X dense MXFP4 matrix throughput
@@ -783,7 +809,7 @@ def main():
     ap.add_argument("--workload", default=DenseLayerNVFP4.name, choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the other workloads of a default run")
-    ap.add_argument("--no-controls", action="store_true", help="skip the GEMM workload's control timings")
+    ap.add_argument("--no-controls", action="store_true", help="skip the control timings (GEMM workload; graph replay of the 256x512 case)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one 1 GiB device copy (the counter reference of a rocprofv3 --pmc run)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -834,7 +860,7 @@ def main():
         "roofline": roofline,
         "kernels": kern,
     }
-    if gemm and not args.no_controls:
+    if (gemm or isinstance(wl, Single256x512)) and not args.no_controls:
         line["controls"] = wl.controls()
     if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
         line["cpu_baseline"] = wl.cpu_baseline()
@@ -863,6 +889,8 @@ def main():
             else:
                 other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5),
                                "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1), "kernels": kern2}
+                if isinstance(w2, Single256x512):
+                    other[name]["controls"] = w2.controls()
             del w2
             torch.cuda.empty_cache()
         line["per_workload"] = other
