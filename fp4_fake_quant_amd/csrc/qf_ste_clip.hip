@@ -31,7 +31,7 @@ __global__ __launch_bounds__(SC_WG) void k_ste_clip(const uint16_t* __restrict__
 #pragma unroll
   for (int j = 0; j < SC_L; ++j) {
     const uint32_t c = base + j * SC_WG;
-    if (c >= nchunks) break;                               // uniform over a block's lanes
+    if (c >= nchunks) break;                               // the same for all lanes of a quantization block
     const uint32_t row = c / cpr, c8 = c - row * cpr;
     typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // both read once: non-temporal
     const u32x4_t wn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + (int64_t)row * ldx + 8 * c8));
