@@ -423,6 +423,23 @@ class MXFP4Operands:
         t("mxfp4_qdq_pack", 1)
 
 
+class MXFP4OperandsNoclip(MXFP4Operands):
+    """The same operands under the noclip shared-exponent rule (the block maximum is never
+    clipped onto 6 X), one grouped launch."""
+    name = "mxfp4_gemm_operands_qdq_pack_noclip"
+
+    def __init__(self, torch, fq):
+        super().__init__(torch, fq)
+        self.kernels = {"mxfp4_qdq_pack_noclip": self.kernels["mxfp4_qdq_pack"]}
+        self.config = dict(self.config, workload=self.name, rule="noclip (E = ceil(log2(amax / 6)))")
+
+    def step(self, mark=None):
+        t = mark or _no_mark
+        t("mxfp4_qdq_pack_noclip", 0)
+        self.fq.qf_qdq_pack_mxfp4_rule(self.items, self.fq.QF_MX_RULE_NOCLIP)
+        t("mxfp4_qdq_pack_noclip", 1)
+
+
 class Single256x512:
     """The 256x512 matrix (N(0, 0.02^2) with 131 N(0, 0.5^2) outliers) under each format:
     launch-latency bound, reported in microseconds per call."""
@@ -547,7 +564,8 @@ class W4A4GemmMXFP4:
 
     def controls(self, reps=10):
         """ms of: the fused kernel (QDQ inside the GEMM); the same kernel on the raw operands
-        (flags = 0); torch.matmul (hipBLASLt) on the raw and on the QDQ'd operands; the NVFP4 W4A4 product,
+        (flags = 0); the same forward under the MXFP4 noclip rule, in two passes and fused; torch.matmul
+        (hipBLASLt) on the raw and on the QDQ'd operands; the NVFP4 W4A4 product,
         fused and in two passes (tensor scales of X and W included in the two-pass time and
         timed on their own); the layer's backward (dX = dY . Wq and dW = dY^T . Xq with
         their three transposes; TFLOP/s over both products); the same MXFP4 W4A4 product on
@@ -579,7 +597,11 @@ class W4A4GemmMXFP4:
             fq.qf_pack_mxfp4(self.X, Xc, Xs)
             fq.qf_pack_mxfp4(self.W, Wc, Ws)
             fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)
+        noclip = fq.QF_QDQ_A | fq.QF_QDQ_W | fq.QF_MX_NOCLIP
         for name, fn in (("w4a4_mxfp4_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=3)),
+                         ("w4a4_mxfp4_noclip_two_pass",
+                          lambda: fq.qf_linear_forward_mxfp4(self.X, self.W, self.Y, flags=noclip, Xq=Xq_nv, Wq=Wq_nv)),
+                         ("w4a4_mxfp4_noclip_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=noclip)),
                          ("gemm_bf16_same_kernel_raw_operands",
                           lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=0)),
                          ("w4a4_nvfp4_fused", lambda: fq.qf_gemm_nvfp4(self.X, self.W, sx, sw, self.Y)),
@@ -747,11 +769,12 @@ class MoELoRANVFP4x8Remerge(MoELoRANVFP4):
         super().__init__(torch, fq, experts_per_launch=8, merge_scratch=False)
 
 
-WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, Single256x512, W4A4GemmMXFP4,
+WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, MXFP4OperandsNoclip, Single256x512,
+                                 W4A4GemmMXFP4,
                                  MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge, DequantDense,
                                  SteClippedDense, Q4KSetMSE)}
 # measured next to the headline workload in a default run (fewer steps each)
-SECONDARY = [MXFP4Operands.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
+SECONDARY = [MXFP4Operands.name, MXFP4OperandsNoclip.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
              MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name, SteClippedDense.name,
              Q4KSetMSE.name]
 
