@@ -330,31 +330,36 @@ __global__ __launch_bounds__(WG) void k_q4k(QArgs a) {
 }
 
 // ------------------------------------------------------------------ STE ----
-// Identity STE: 8 bf16 gradients per lane -> 8 fp32, optionally accumulated.
+// Identity STE: bf16 gradients -> fp32, optionally accumulated.  A wave owns 512
+// consecutive elements; lane l takes elements 4l..4l+3 and 256+4l..256+4l+3 of them (two
+// 8-byte loads, two 16-byte stores), so each store instruction writes 1 KiB of contiguous
+// output.  With 8 elements per lane (one 16-byte load, two 16-byte stores 32 bytes apart)
+// every store instruction covered half of each of 16 lines: 222 -> 208 us on the dense 8B
+// layer (218 M elements).  The launcher gives each workgroup WG * 8 elements.
 template <bool ACC, int L>
 __global__ __launch_bounds__(WG) void k_ste(const uint16_t* __restrict__ g, float* __restrict__ out, int64_t n) {
-  const int64_t nv = n >> 3;
-  const int64_t base = (int64_t)blockIdx.x * (WG * L);
+  static_assert(L == 1, "one 512-element segment per wave");
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const int64_t ne = (n >> 3) << 3;                        // elements in whole 8-element chunks
+  const uint32_t lane = threadIdx.x & 63u;
+  const int64_t wbase = ((int64_t)blockIdx.x * WG + (threadIdx.x & ~63u)) * 8;
 #pragma unroll
-  for (int j = 0; j < L; ++j) {
-    const int64_t i = base + j * WG + threadIdx.x;
-    if (i < nv) {
-      const uint4 w = load_chunk_nt(g + i * 8);
-      float4 lo = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
-      float4 hi = make_float4(bf16_lo(w.z), bf16_hi(w.z), bf16_lo(w.w), bf16_hi(w.w));
-      float4* o = reinterpret_cast<float4*>(out + i * 8);
+  for (int h = 0; h < 2; ++h) {
+    const int64_t e = wbase + 256 * h + 4 * lane;
+    if (e < ne) {                                         // e + 4 <= ne: e and ne are multiples of 4
+      const u32x2_t w = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(g + e));   // read once
+      float4 v = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+      float4* o = reinterpret_cast<float4*>(out + e);
       if (ACC) {
-        const float4 p = o[0], q = o[1];
-        lo.x += p.x; lo.y += p.y; lo.z += p.z; lo.w += p.w;
-        hi.x += q.x; hi.y += q.y; hi.z += q.z; hi.w += q.w;
+        const float4 p = o[0];
+        v.x += p.x; v.y += p.y; v.z += p.z; v.w += p.w;
       }
-      o[0] = lo;
-      o[1] = hi;
+      o[0] = v;
     }
   }
   // ragged tail (n % 8 elements) handled by the first lanes of the first workgroup
   if (blockIdx.x == 0 && threadIdx.x < (n & 7)) {
-    const int64_t i = nv * 8 + threadIdx.x;
+    const int64_t i = ne + threadIdx.x;
     const float v = __uint_as_float((uint32_t)g[i] << 16);
     out[i] = ACC ? out[i] + v : v;
   }

@@ -10,78 +10,77 @@
 //   MXFP4: |x| > 6 * 2^(E-127) with the block's shared exponent E under the floor or the
 //          noclip rule (y = |x| / 2^(E-127) is exact, so this is the QDQ's own decision).
 //
-// A lane takes 8 elements at a time: one 16-byte chunk of x (row stride ldx) and of g_q,
-// two 16-byte stores of fp32.  Consecutive lanes take consecutive chunks of a row, so an
-// MXFP4 block sits in 4 adjacent lanes and an NVFP4 block in 2, and the block maximum is
-// one or two DPP steps.
+// A wave takes 64 consecutive 8-element chunks (512 elements of the row-major [rows, cols]
+// numbering) at a time, in two halves: in half h lane l takes elements 256h + 4l .. +3 of
+// them (8-byte loads of x, row stride ldx, and of g_q; one 16-byte fp32 store), so every
+// store instruction writes 1 KiB of contiguous output (8 elements per lane with two stores
+// 32 bytes apart measured slower on the STE).  An NVFP4 block then sits in 4 adjacent
+// lanes and an MXFP4 block in 8, and the block maximum is two or three DPP steps.
 #include "qf_device.h"
 #include "qf_kernels.h"
 
 namespace qf {
 
 constexpr int SC_WG = 256;
-constexpr int SC_L = 2;                                    // chunks per lane
+constexpr int SC_L = 2;                                    // 64-chunk segments per wave
 
 template <int FMT, bool ACC, bool NOCLIP>
 __global__ __launch_bounds__(SC_WG) void k_ste_clip(const uint16_t* __restrict__ g, const uint16_t* __restrict__ x,
                                                     int64_t ldx, uint32_t nchunks, uint32_t cpr,
                                                     const float* __restrict__ d_scale, float* __restrict__ out) {
-  const uint32_t base = blockIdx.x * (SC_WG * SC_L) + threadIdx.x;
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wbase = blockIdx.x * (SC_WG * SC_L) + (threadIdx.x & ~63u);   // the wave's first chunk
   const float s_t = FMT == QF_FMT_NVFP4 ? *d_scale : 0.0f, k6 = 6.0f * s_t;
 #pragma unroll
   for (int j = 0; j < SC_L; ++j) {
-    const uint32_t c = base + j * SC_WG;
-    if (c >= nchunks) break;                               // the same for all lanes of a quantization block
-    const uint32_t row = c / cpr, c8 = c - row * cpr;
-    typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));   // both read once: non-temporal
-    const u32x4_t wn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(x + (int64_t)row * ldx + 8 * c8));
-    const u32x4_t gn = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(g + (int64_t)c * 8));
-    const uint4 w = make_uint4(wn.x, wn.y, wn.z, wn.w), gv = make_uint4(gn.x, gn.y, gn.z, gn.w);
-    uint32_t m = amax_bits8(w);
-    m = umax(m, dpp_xor1(m));
-    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-    bool sat[8];
-    if constexpr (FMT == QF_FMT_NVFP4) {
-      const float s = e4m3_value(e4m3_encode(__uint_as_float(m << 16) / k6));
-      const float d = s * s_t;
-      const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = fabsf(bf16_lo(wv[e])), hi = fabsf(bf16_hi(wv[e]));
-        sat[2 * e] = d != 0.0f && lo != 0.0f && lo * r > 6.0f;
-        sat[2 * e + 1] = d != 0.0f && hi != 0.0f && hi * r > 6.0f;
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t c = wbase + j * SC_WG + 32 * h + (lane >> 1), half = lane & 1u;
+      if (c >= nchunks) break;                             // the same for all lanes of a quantization block
+      const uint32_t row = c / cpr, c8 = c - row * cpr;
+      // both read once: non-temporal
+      const u32x2_t wn = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(x + (int64_t)row * ldx + 8 * c8 + 4 * half));
+      const u32x2_t gn = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t*>(g + (int64_t)c * 8 + 4 * half));
+      const uint32_t wv[2] = {wn.x, wn.y};
+      uint32_t m = amax_bits8(make_uint4(wn.x, wn.y, 0u, 0u));
+      m = umax(m, dpp_xor1(m));
+      m = umax(m, dpp_xor2(m));                            // NVFP4 block: 4 lanes
+      bool sat[4];
+      if constexpr (FMT == QF_FMT_NVFP4) {
+        const float s = e4m3_value(e4m3_encode(__uint_as_float(m << 16) / k6));
+        const float d = s * s_t;
+        const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const float lo = fabsf(bf16_lo(wv[e])), hi = fabsf(bf16_hi(wv[e]));
+          sat[2 * e] = d != 0.0f && lo != 0.0f && lo * r > 6.0f;
+          sat[2 * e + 1] = d != 0.0f && hi != 0.0f && hi * r > 6.0f;
+        }
+      } else {
+        m = umax(m, dpp_hmirror(m));                       // MXFP4 block: 8 lanes
+        // E = max(bf16 exponent field of the block maximum - 2 (+1 under noclip when its
+        // significand exceeds 1.5), 0); the limit 6 * 2^(E-127) = 1.5 * 2^(E-125) is exact
+        // for E <= 252 and beyond every finite bf16 above that
+        const int ef = (int)(m >> 7);
+        int E = ef - 2 + (NOCLIP && (m & 0x7Fu) > 0x40u ? 1 : 0);
+        E = E < 0 ? 0 : E;
+        const float lim = E + 2 >= 255 ? __builtin_inff() : __uint_as_float(((uint32_t)(E + 2) << 23) | 0x400000u);
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          sat[2 * e] = fabsf(bf16_lo(wv[e])) > lim;
+          sat[2 * e + 1] = fabsf(bf16_hi(wv[e])) > lim;
+        }
       }
-    } else {
-      m = umax(m, dpp_xor2(m));
-      // E = max(bf16 exponent field of the block maximum - 2 (+1 under noclip when its
-      // significand exceeds 1.5), 0); the limit 6 * 2^(E-127) = 1.5 * 2^(E-125) is exact
-      // for E <= 252 and beyond every finite bf16 above that
-      const int ef = (int)(m >> 7);
-      int E = ef - 2 + (NOCLIP && (m & 0x7Fu) > 0x40u ? 1 : 0);
-      E = E < 0 ? 0 : E;
-      const float lim = E + 2 >= 255 ? __builtin_inff() : __uint_as_float(((uint32_t)(E + 2) << 23) | 0x400000u);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sat[2 * e] = fabsf(bf16_lo(wv[e])) > lim;
-        sat[2 * e + 1] = fabsf(bf16_hi(wv[e])) > lim;
+      float4 a = make_float4(sat[0] ? 0.0f : bf16_lo(gn.x), sat[1] ? 0.0f : bf16_hi(gn.x),
+                             sat[2] ? 0.0f : bf16_lo(gn.y), sat[3] ? 0.0f : bf16_hi(gn.y));
+      float4* o = reinterpret_cast<float4*>(out + (int64_t)c * 8 + 4 * half);
+      if constexpr (ACC) {
+        const float4 p = o[0];
+        a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
       }
+      o[0] = a;
     }
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      v[2 * e] = sat[2 * e] ? 0.0f : bf16_lo(gw[e]);
-      v[2 * e + 1] = sat[2 * e + 1] ? 0.0f : bf16_hi(gw[e]);
-    }
-    float4* o = reinterpret_cast<float4*>(out + (int64_t)c * 8);
-    float4 a = make_float4(v[0], v[1], v[2], v[3]), b = make_float4(v[4], v[5], v[6], v[7]);
-    if constexpr (ACC) {
-      const float4 p = o[0], q = o[1];
-      a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
-      b.x += q.x; b.y += q.y; b.z += q.z; b.w += q.w;
-    }
-    o[0] = a;
-    o[1] = b;
   }
 }
 
