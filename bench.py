@@ -715,13 +715,13 @@ class MoELoRANVFP4:
         t = mark or _no_mark
         for items, sc in self.chunks:
             t("lora_merge_amax", 0)
-            fq.qf_lora_merge_tensor_scale_nvfp4(items, items.n, sc, None, ws)
+            fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
             t("lora_merge_amax", 1)
             t("lora_qdq_pack", 0)
-            fq.qf_lora_qdq_pack_nvfp4(items, sc)
+            fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
             t("lora_qdq_pack", 1)
             t("lora_adapter_grads", 0)
-            fq.qf_lora_adapter_grads(items, ws=ws)
+            fq.qf_lora_adapter_grads_grouped(items, ws=ws)
             t("lora_adapter_grads", 1)
 
     def cpu_baseline(self, budget_s=15.0):

@@ -13,11 +13,12 @@ import ctypes
 
 import torch
 
-from ._lib import LoraDesc, TensorDesc, lib
+from ._lib import GgufTensor, LoraDesc, StTensor, TensorDesc, lib
 
 QF_OK = 0
 QF_QDQ_A, QF_QDQ_W, QF_FP4_CORES, QF_MX_NOCLIP = 1, 2, 4, 8
 QF_FMT_NVFP4, QF_FMT_MXFP4, QF_FMT_Q4K = 0, 1, 2
+QF_OP_NVFP4_TENSOR_SCALE, QF_OP_LORA, QF_OP_LINEAR_BACKWARD = 0, 1, 2
 MAX_GROUPED = 16
 BLOCK = {QF_FMT_NVFP4: 16, QF_FMT_MXFP4: 32, QF_FMT_Q4K: 256}
 
@@ -119,8 +120,46 @@ def qf_nvfp4_tensor_scale_grouped(items, n_groups, d_scales=None, d_nonfinite=No
     return d_scales
 
 
+def qf_nvfp4_tensor_scale_tracked(items, n_groups, d_amax, d_scales=None, d_nonfinite=None, ws=None):
+    """Tensor scales from the running maximum d_amax (device float32 [n_groups], updated in
+    place: max(d_amax, this call's group maxima)); items as qf_nvfp4_tensor_scale_grouped."""
+    if d_amax.dtype != torch.float32 or d_amax.device.type != "cuda" or d_amax.numel() < n_groups:
+        raise TypeError("d_amax must be a float32 device tensor with a value per group")
+    dev = items[0]["x"].device if items else d_amax.device
+    arr, n = _descs(items)
+    need = lib().qf_nvfp4_tensor_scale_workspace(ctypes.byref(arr), n)
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    if d_scales is None:
+        d_scales = torch.empty(n_groups, dtype=torch.float32, device=dev)
+    _check(lib().qf_nvfp4_tensor_scale_tracked(ctypes.byref(arr), n, n_groups, _p(d_amax), _p(d_scales),
+                                                _p(d_nonfinite), _p(ws), ws.numel() * ws.element_size(), _stream()),
+           "qf_nvfp4_tensor_scale_tracked")
+    return d_scales
+
+
+def qf_workspace_size(op, rows, cols, n):
+    return lib().qf_workspace_size(int(op), int(rows), int(cols), int(n))
+
+
 def qf_nvfp4_tensor_scale(x, d_scale=None, d_nonfinite=None, ws=None):
-    return qf_nvfp4_tensor_scale_grouped([dict(x=x, group=0)], 1, d_scale, d_nonfinite, ws)
+    """Tensor scale of one tied group: x is a bf16 tensor or a list of them (e.g. Q, K, V).
+    Contiguous members go through the pointer-array call, strided ones through the grouped
+    call (same arithmetic).  Returns the device float32 scale (shape [1])."""
+    xs = list(x) if isinstance(x, (list, tuple)) else [x]
+    if not all(t.is_contiguous() for t in xs):
+        return qf_nvfp4_tensor_scale_grouped([dict(x=t, group=0) for t in xs], 1, d_scale, d_nonfinite, ws)
+    dev = xs[0].device if xs else torch.device("cuda")
+    ptrs = (ctypes.c_void_p * max(len(xs), 1))(*[_bf16(t, "x").data_ptr() for t in xs])
+    numel = (ctypes.c_int64 * max(len(xs), 1))(*[t.numel() for t in xs])
+    need = lib().qf_workspace_size(QF_OP_NVFP4_TENSOR_SCALE, 1, max([t.numel() for t in xs] + [0]), len(xs))
+    if ws is None:
+        ws = torch.empty(max(need, 4), dtype=torch.uint8, device=dev)
+    if d_scale is None:
+        d_scale = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(lib().qf_nvfp4_tensor_scale(ptrs, numel, len(xs), _p(d_scale), _p(d_nonfinite), _p(ws),
+                                       ws.numel() * ws.element_size(), _stream()), "qf_nvfp4_tensor_scale")
+    return d_scale
 
 
 # ------------------------------------------------------------ QDQ/pack ----
@@ -319,27 +358,89 @@ def qf_lora_workspace(items):
     return _batch(items).workspace_bytes
 
 
-def qf_lora_merge_tensor_scale_nvfp4(items, n_groups, d_scales=None, d_nonfinite=None, ws=None):
+def qf_lora_layout(items):
+    """(rows per merge unit, merge workgroups, rows per gradient workgroup, gradient workgroups)
+    the LoRA calls choose for these descriptors (a host query)."""
+    b = _batch(items)
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().qf_lora_layout(b.ref, b.n, out), "qf_lora_layout")
+    return tuple(out)
+
+
+def qf_lora_merge_tensor_scale_nvfp4_grouped(items, n_groups, d_scales=None, d_nonfinite=None, ws=None):
     b = _batch(items)
     ws = _lora_ws(b, ws)
     if d_scales is None:
         d_scales = torch.empty(n_groups, dtype=torch.float32, device=b.device)
-    _check(lib().qf_lora_merge_tensor_scale_nvfp4(b.ref, b.n, n_groups, _p(d_scales), _p(d_nonfinite),
-                                                   _p(ws), ws.numel() * ws.element_size(), _stream()),
-           "qf_lora_merge_tensor_scale_nvfp4")
+    _check(lib().qf_lora_merge_tensor_scale_nvfp4_grouped(b.ref, b.n, n_groups, _p(d_scales), _p(d_nonfinite),
+                                                           _p(ws), ws.numel() * ws.element_size(), _stream()),
+           "qf_lora_merge_tensor_scale_nvfp4_grouped")
     return d_scales
 
 
-def qf_lora_qdq_pack_nvfp4(items, d_scales):
+def qf_lora_merge_qdq_pack_nvfp4_grouped(items, d_scales):
     b = _batch(items)
-    _check(lib().qf_lora_qdq_pack_nvfp4(b.ref, b.n, _p(d_scales), _stream()), "qf_lora_qdq_pack_nvfp4")
+    _check(lib().qf_lora_merge_qdq_pack_nvfp4_grouped(b.ref, b.n, _p(d_scales), _stream()),
+           "qf_lora_merge_qdq_pack_nvfp4_grouped")
 
 
-def qf_lora_adapter_grads(items, accumulate=False, ws=None):
+def qf_lora_adapter_grads_grouped(items, accumulate=False, ws=None):
     b = _batch(items)
     ws = _lora_ws(b, ws)
-    _check(lib().qf_lora_adapter_grads(b.ref, b.n, int(bool(accumulate)), _p(ws),
-                                       ws.numel() * ws.element_size(), _stream()), "qf_lora_adapter_grads")
+    _check(lib().qf_lora_adapter_grads_grouped(b.ref, b.n, int(bool(accumulate)), _p(ws),
+                                               ws.numel() * ws.element_size(), _stream()),
+           "qf_lora_adapter_grads_grouped")
+
+
+def _lora_single(W, A, B):
+    for t, name in ((W, "W"), (A, "A"), (B, "B")):
+        if not _bf16(t, name).is_contiguous() or t.dim() != 2:
+            raise ValueError(f"{name} must be a contiguous 2-D bf16 tensor")
+    rows, cols = W.shape
+    r = A.shape[0]
+    if A.shape[1] != cols or tuple(B.shape) != (rows, r):
+        raise ValueError(f"adapter shapes {tuple(A.shape)}, {tuple(B.shape)} do not fit W {rows}x{cols}")
+    return rows, cols, r
+
+
+def _lora_single_ws(rows, cols, device, ws):
+    if ws is None:
+        ws = torch.empty(max(lib().qf_workspace_size(QF_OP_LORA, rows, cols, 1), 4), dtype=torch.uint8,
+                         device=device)
+    return ws
+
+
+def qf_lora_merge_tensor_scale_nvfp4(W, A, B, d_scale=None, ws=None):
+    """NVFP4 tensor scale of M = W + B.A for one contiguous matrix, merged in registers."""
+    rows, cols, r = _lora_single(W, A, B)
+    ws = _lora_single_ws(rows, cols, W.device, ws)
+    if d_scale is None:
+        d_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    _check(lib().qf_lora_merge_tensor_scale_nvfp4(_p(W), _p(A), _p(B), rows, cols, r, _p(d_scale), _p(ws),
+                                                   ws.numel() * ws.element_size(), _stream()),
+           "qf_lora_merge_tensor_scale_nvfp4")
+    return d_scale
+
+
+def qf_lora_merge_qdq_pack_nvfp4(W, A, B, d_scale, y=None, codes=None, scales=None):
+    """(y, codes, scales): NVFP4 QDQ + pack of M = W + B.A (merged again in registers)."""
+    rows, cols, r = _lora_single(W, A, B)
+    y = torch.empty((rows, cols), dtype=torch.bfloat16, device=W.device) if y is None else y
+    codes, scales = _packed(QF_FMT_NVFP4, rows, cols, W.device, codes, scales)
+    _check(lib().qf_lora_merge_qdq_pack_nvfp4(_p(W), _p(A), _p(B), rows, cols, r, _p(d_scale), _p(y), _p(codes),
+                                               _p(scales), _stream()), "qf_lora_merge_qdq_pack_nvfp4")
+    return y, codes, scales
+
+
+def qf_lora_adapter_grads(G, A, B, dA=None, dB=None, accumulate=False, ws=None):
+    """(dA [r, cols], dB [rows, r]) fp32 = (B^T . G, G . A^T) for one contiguous matrix."""
+    rows, cols, r = _lora_single(G, A, B)
+    ws = _lora_single_ws(rows, cols, G.device, ws)
+    dA = torch.empty((r, cols), dtype=torch.float32, device=G.device) if dA is None else dA
+    dB = torch.empty((rows, r), dtype=torch.float32, device=G.device) if dB is None else dB
+    _check(lib().qf_lora_adapter_grads(_p(G), _p(A), _p(B), rows, cols, r, _p(dA), _p(dB), int(bool(accumulate)),
+                                       _p(ws), ws.numel() * ws.element_size(), _stream()), "qf_lora_adapter_grads")
+    return dA, dB
 
 
 # ------------------------------------------------------------- dequant ----
@@ -458,13 +559,13 @@ def qf_linear_forward_nvfp4(X, W, d_scale_x, d_scale_w, Y=None, flags=QF_QDQ_A |
     return Y, Xq, Wq
 
 
-def qf_transpose_bf16(x, y=None, qdq_mxfp4=False):
-    """y [cols, rows] = x^T, MXFP4-QDQ'd along x's rows first when qdq_mxfp4."""
+def qf_transpose_bf16(x, y=None, qdq_mxfp4=False, rule=QF_MX_RULE_FLOOR):
+    """y [cols, rows] = x^T, MXFP4-QDQ'd along x's rows first (under `rule`) when qdq_mxfp4."""
     rows, cols, ldx = _mat(_bf16(x, "x"), "x")
     if y is None:
         y = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
     _bf16(y, "y")
-    _check(lib().qf_transpose_bf16(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], int(bool(qdq_mxfp4)), _stream()),
+    _check(lib().qf_transpose_bf16(_p(x), rows, cols, ldx, _p(y), _mat(y, "y")[2], (1 + int(rule == QF_MX_RULE_NOCLIP)) if qdq_mxfp4 else 0, _stream()),
            "qf_transpose_bf16")
     return y
 
@@ -532,3 +633,91 @@ def qf_selftest_conversions(device="cuda"):
     counts = torch.zeros(8, dtype=torch.int64, device=device)
     _check(lib().qf_selftest_conversions(_p(counts), _stream()), "qf_selftest_conversions")
     return counts
+
+
+# ------------------------------------------------- checkpoint containers ----
+_ST_DTYPE = {torch.uint8: "U8", torch.int8: "I8", torch.bool: "BOOL", torch.float8_e4m3fn: "F8_E4M3",
+             torch.float8_e5m2: "F8_E5M2", torch.float8_e8m0fnu: "F8_E8M0", torch.int16: "I16",
+             torch.float16: "F16", torch.bfloat16: "BF16", torch.int32: "I32", torch.float32: "F32",
+             torch.int64: "I64", torch.float64: "F64"}
+_ST_SIZE = {"U8": 1, "I8": 1, "BOOL": 1, "F8_E4M3": 1, "F8_E5M2": 1, "F8_E8M0": 1, "U16": 2, "I16": 2, "F16": 2,
+            "BF16": 2, "U32": 4, "I32": 4, "F32": 4, "U64": 8, "I64": 8, "F64": 8}
+
+
+def _host_bytes(t):
+    return t.detach().contiguous().cpu()
+
+
+def _cstrings(strs):
+    arr = (ctypes.c_char_p * max(len(strs), 1))(*[x.encode() for x in strs])
+    return arr
+
+
+def qf_write_safetensors(path, tensors, metadata=None):
+    """Write a safetensors file.  tensors: list of (name, tensor, dtype) with tensor on any
+    device and dtype a safetensors dtype string or None (taken from the tensor); a uint8
+    tensor of E4M3 / E8M0 scale bytes is written as "F8_E4M3" / "F8_E8M0" by naming that
+    dtype.  metadata: dict of str -> str."""
+    keep = []
+    arr = (StTensor * max(len(tensors), 1))()
+    for i, (name, t, dt) in enumerate(tensors):
+        h = _host_bytes(t)
+        dt = dt or _ST_DTYPE.get(h.dtype)
+        if dt is None or _ST_SIZE.get(dt) != h.element_size():
+            raise TypeError(f"{name}: cannot write a {h.dtype} tensor as {dt}")
+        shape = (ctypes.c_int64 * max(h.dim(), 1))(*h.shape)
+        keep += [h, shape, name.encode(), dt.encode()]
+        arr[i].name, arr[i].dtype, arr[i].ndim = keep[-2], keep[-1], h.dim()
+        arr[i].shape = ctypes.cast(shape, ctypes.POINTER(ctypes.c_int64))
+        arr[i].data = h.data_ptr() if h.numel() else None
+    meta = metadata or {}
+    keys, vals = _cstrings(list(meta)), _cstrings([str(v) for v in meta.values()])
+    _check(lib().qf_write_safetensors(str(path).encode(), ctypes.byref(arr), len(tensors), keys, vals, len(meta)),
+           "qf_write_safetensors")
+
+
+def qf_write_gguf(path, tensors, kv=None):
+    """Write a GGUF-style file.  tensors: list of (name, tensor of raw bytes, dims innermost
+    first, type code); kv: dict of str -> str."""
+    keep = []
+    arr = (GgufTensor * max(len(tensors), 1))()
+    for i, (name, t, dims, typ) in enumerate(tensors):
+        h = _host_bytes(t)
+        d = (ctypes.c_int64 * len(dims))(*dims)
+        keep += [h, d, name.encode()]
+        arr[i].name, arr[i].ndim = keep[-1], len(dims)
+        arr[i].dims = ctypes.cast(d, ctypes.POINTER(ctypes.c_int64))
+        arr[i].type, arr[i].data = int(typ), (h.data_ptr() if h.numel() else None)
+        arr[i].nbytes = h.numel() * h.element_size()
+    kv = kv or {}
+    keys, vals = _cstrings(list(kv)), _cstrings([str(v) for v in kv.values()])
+    _check(lib().qf_write_gguf(str(path).encode(), ctypes.byref(arr), len(tensors), keys, vals, len(kv)),
+           "qf_write_gguf")
+
+
+GGUF_TYPE_Q4_K = 12
+Q4K_BLOCK_LAYOUT = ("144-byte blocks per 256 weights along a row: d (fp16 LE), dmin (fp16 LE), a 96-bit "
+                    "little-endian stream with the 6-bit sub-block scale j at bits 6j and min j at bits 48+6j, "
+                    "128 code bytes with element 2i in the low nibble and 2i+1 in the high nibble; "
+                    "w = d*sc_j*q - dmin*m_j")
+
+
+def export_fp4_tensors(prefix, fmt, codes, scales, d_scale=None, d_input_scale=None):
+    """The (name, tensor, dtype) list of one packed NVFP4 / MXFP4 layer in the names this
+    library uses ("compressed-tensors-style"): weight_packed, weight_scale (E4M3 or E8M0
+    bytes), and for NVFP4 weight_global_scale (the layer group's dequant multiplier s_t)
+    and, when given, input_global_scale (the tracked activation s_t)."""
+    out = [(f"{prefix}.weight_packed", codes, "U8"),
+           (f"{prefix}.weight_scale", scales, "F8_E4M3" if fmt == QF_FMT_NVFP4 else "F8_E8M0")]
+    if fmt == QF_FMT_NVFP4:
+        if d_scale is None:
+            raise ValueError("NVFP4 needs the tensor scale")
+        out.append((f"{prefix}.weight_global_scale", d_scale.reshape(-1)[:1], "F32"))
+        if d_input_scale is not None:
+            out.append((f"{prefix}.input_global_scale", d_input_scale.reshape(-1)[:1], "F32"))
+    return out
+
+
+def export_q4k_tensor(name, blocks, rows, cols):
+    """The (name, bytes, dims, type) entry of one Q4_K matrix for qf_write_gguf."""
+    return (name, blocks, (cols, rows), GGUF_TYPE_Q4_K)

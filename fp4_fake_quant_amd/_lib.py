@@ -41,6 +41,18 @@ class LoraDesc(ctypes.Structure):
     ]
 
 
+class StTensor(ctypes.Structure):
+    """Mirror of qf_st_tensor in include/qf.h."""
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_char_p), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.POINTER(c_i64)), ("data", c_void_p)]
+
+
+class GgufTensor(ctypes.Structure):
+    """Mirror of qf_gguf_tensor in include/qf.h."""
+    _fields_ = [("name", ctypes.c_char_p), ("ndim", ctypes.c_int32), ("dims", ctypes.POINTER(c_i64)),
+                ("type", ctypes.c_uint32), ("data", c_void_p), ("nbytes", ctypes.c_uint64)]
+
+
 # name -> (restype, argtypes); every entry point declared in include/qf.h
 SIGNATURES = {
     "qf_version": (c_u32, []),
@@ -49,7 +61,10 @@ SIGNATURES = {
     "qf_packed_bytes": (c_size_t, [c_int, c_i64, c_i64]),
     "qf_nvfp4_tensor_scale_workspace": (c_size_t, [c_void_p, c_int]),
     "qf_nvfp4_tensor_scale_grouped": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-    "qf_nvfp4_tensor_scale": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qf_nvfp4_tensor_scale_tracked": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                              c_size_t, c_void_p]),
+    "qf_nvfp4_tensor_scale": (c_int, [c_void_p, c_void_p, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "qf_workspace_size": (c_size_t, [c_int, c_i64, c_i64, c_int]),
     "qf_qdq_nvfp4": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p]),
     "qf_pack_nvfp4": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_void_p, c_void_p]),
     "qf_qdq_pack_nvfp4": (c_int, [c_void_p, c_i64, c_i64, c_i64, c_void_p, c_void_p, c_i64, c_void_p, c_void_p, c_void_p]),
@@ -65,9 +80,17 @@ SIGNATURES = {
     "qf_ste_backward": (c_int, [c_void_p, c_void_p, c_i64, c_int, c_void_p]),
     "qf_selftest_conversions": (c_int, [c_void_p, c_void_p]),
     "qf_lora_workspace": (c_size_t, [c_void_p, c_int]),
-    "qf_lora_merge_tensor_scale_nvfp4": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
-    "qf_lora_qdq_pack_nvfp4": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
-    "qf_lora_adapter_grads": (c_int, [c_void_p, c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "qf_lora_layout": (c_int, [c_void_p, c_int, c_void_p]),
+    "qf_lora_merge_tensor_scale_nvfp4_grouped": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                                         c_size_t, c_void_p]),
+    "qf_lora_merge_qdq_pack_nvfp4_grouped": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
+    "qf_lora_adapter_grads_grouped": (c_int, [c_void_p, c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "qf_lora_merge_tensor_scale_nvfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_int, c_void_p,
+                                                 c_void_p, c_size_t, c_void_p]),
+    "qf_lora_merge_qdq_pack_nvfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_int, c_void_p, c_void_p,
+                                             c_void_p, c_void_p, c_void_p]),
+    "qf_lora_adapter_grads": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_int, c_void_p, c_void_p, c_int,
+                                      c_void_p, c_size_t, c_void_p]),
     "qf_gemm_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64, ctypes.c_uint, c_void_p]),
     "qf_gemm_mxfp4_packed": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p]),
     "qf_gemm_mxfp4_packed_w": (c_int, [c_void_p, c_i64, c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_i64, c_i64, c_void_p]),
@@ -89,6 +112,8 @@ SIGNATURES = {
                                               c_void_p]),
     "qf_linear_forward_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64,
                                         ctypes.c_uint, c_void_p, c_i64, c_void_p, c_i64, c_void_p]),
+    "qf_write_safetensors": (c_int, [ctypes.c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_int]),
+    "qf_write_gguf": (c_int, [ctypes.c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_int]),
     "qf_linear_forward_nvfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64,
                                         ctypes.c_uint, c_void_p, c_void_p, c_void_p, c_i64, c_void_p, c_i64,
                                         c_void_p]),

@@ -16,6 +16,11 @@ qf_status hip_status(hipError_t e) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+}  // namespace
+
+qf_status qf::status_of(hipError_t e) { return hip_status(e); }
+
+namespace {
 
 int block_of(int fmt) {
   switch (fmt) {
@@ -187,6 +192,7 @@ const char* qf_status_str(qf_status s) {
     case QF_ERR_HIP: return "HIP launch failed";
     case QF_ERR_NOT_IMPLEMENTED: return "not implemented";
     case QF_ERR_ARG: return "invalid argument";
+    case QF_ERR_IO: return "file could not be written";
   }
   return "unknown status";
 }
@@ -216,6 +222,13 @@ size_t qf_nvfp4_tensor_scale_workspace(const qf_tensor_desc* d, int n) {
 
 qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_groups, float* d_scales,
                                         uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+  return qf_nvfp4_tensor_scale_tracked(d, n, n_groups, nullptr, d_scales, d_nonfinite, ws, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+// Every argument check of the tensor-scale calls except the workspace.
+qf_status qf::check_tensor_scale(const qf_tensor_desc* d, int n, int n_groups, const float* d_scales) {
   if (n < 0 || n > QF_MAX_GROUPED || n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
   if ((n > 0 && !d) || !d_scales) return QF_ERR_NULL;
   int64_t tiles = 0;
@@ -226,6 +239,17 @@ qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_gr
     tiles += tiles_of(d[i], AMAX_TILE);
   }
   if (tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  return QF_OK;
+}
+
+extern "C" {
+
+qf_status qf_nvfp4_tensor_scale_tracked(const qf_tensor_desc* d, int n, int n_groups, float* d_amax,
+                                        float* d_scales, uint32_t* d_nonfinite, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  if (d_amax && !aligned(d_amax, 4)) return QF_ERR_ALIGN;
+  const qf_status chk = qf::check_tensor_scale(d, n, n_groups, d_scales);
+  if (chk != QF_OK) return chk;
   const size_t need = qf_nvfp4_tensor_scale_workspace(d, n);
   if (!ws || ws_bytes < need) return QF_ERR_WORKSPACE;
   if (!aligned(ws, 4)) return QF_ERR_ALIGN;
@@ -241,15 +265,23 @@ qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_gr
   r.partial = (const uint32_t*)ws;
   r.tscale = d_scales;
   r.nonfinite = d_nonfinite;
+  r.tracked = d_amax;
   hipError_t e = qf::launch_nvfp4_amax(a, s);
   if (e != hipSuccess) return hip_status(e);
   return hip_status(qf::launch_nvfp4_scale_reduce(r, s));
 }
 
-qf_status qf_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, float* d_scale,
+qf_status qf_nvfp4_tensor_scale(const uint16_t* const* x, const int64_t* numel, int n_tensors, float* d_scale,
                                 uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
-  const qf_tensor_desc d = one(x, rows, cols, ldx, nullptr, 0, nullptr, nullptr);
-  return qf_nvfp4_tensor_scale_grouped(&d, 1, 1, d_scale, d_nonfinite, ws, ws_bytes, stream);
+  if (n_tensors < 0 || n_tensors > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n_tensors > 0 && (!x || !numel)) return QF_ERR_NULL;
+  // each tensor is one contiguous row of numel elements, all in tied group 0
+  qf_tensor_desc d[QF_MAX_GROUPED];
+  for (int i = 0; i < n_tensors; ++i) {
+    if (numel[i] < 0 || numel[i] % 16) return QF_ERR_SHAPE;
+    d[i] = one(x[i], numel[i] ? 1 : 0, numel[i], numel[i], nullptr, 0, nullptr, nullptr);
+  }
+  return qf_nvfp4_tensor_scale_grouped(d, n_tensors, 1, d_scale, d_nonfinite, ws, ws_bytes, stream);
 }
 
 // -------------------------------------------------------------- NVFP4 QDQ --
@@ -467,8 +499,24 @@ size_t qf_lora_workspace(const qf_lora_desc* d, int n) {
   return (size_t)(words > 0 ? words : 1) * 4;
 }
 
-qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
-                                           uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if ((n > 0 && !d) || !out) return QF_ERR_NULL;
+  for (int i = 0; i < n; ++i) {
+    const qf_status st = check_lora(d[i]);
+    if (st != QF_OK) return st;
+  }
+  qf::LoraArgs a;
+  const LoraCounts c = lora_layout(d, n, &a, nullptr);
+  out[0] = a.merge_rows;
+  out[1] = (int32_t)c.merge_wg;
+  out[2] = a.da_rows;
+  out[3] = (int32_t)c.grad_wg;
+  return QF_OK;
+}
+
+qf_status qf_lora_merge_tensor_scale_nvfp4_grouped(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
+                                                   uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
   if (n < 0 || n > QF_MAX_GROUPED || n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
   if ((n > 0 && !d) || !d_scales) return QF_ERR_NULL;
   for (int i = 0; i < n; ++i) {
@@ -496,10 +544,11 @@ qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_g
   r.partial = (const uint32_t*)ws;
   r.tscale = d_scales;
   r.nonfinite = d_nonfinite;
+  r.tracked = nullptr;
   return hip_status(qf::launch_nvfp4_scale_reduce(r, s));
 }
 
-qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_scales, void* stream) {
+qf_status qf_lora_merge_qdq_pack_nvfp4_grouped(const qf_lora_desc* d, int n, const float* d_scales, void* stream) {
   if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
   if (n > 0 && !d) return QF_ERR_NULL;
   if (!d_scales) return QF_ERR_NULL;
@@ -540,8 +589,8 @@ qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_sc
   return hip_status(qf::launch_lora_merge_qdq(a, (int)c.merge_wg, s));
 }
 
-qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
-                                void* stream) {
+qf_status qf_lora_adapter_grads_grouped(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
+                                        void* stream) {
   if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
   if (n > 0 && !d) return QF_ERR_NULL;
   for (int i = 0; i < n; ++i) {
@@ -559,6 +608,54 @@ qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, vo
   const LoraCounts c = lora_layout(d, n, &a, (float*)ws);
   if (c.grad_wg >= (1ll << 31)) return QF_ERR_SHAPE;
   return hip_status(qf::launch_lora_grads(a, (int)c.grad_wg, accumulate != 0, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+// One contiguous matrix (ldw = cols) as a LoRA descriptor of tied group 0.
+namespace {
+qf_lora_desc lora_one(const uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t rows, int64_t cols, int r) {
+  qf_lora_desc d;
+  memset(&d, 0, sizeof(d));
+  d.W = W;
+  d.A = A;
+  d.B = B;
+  d.rows = rows;
+  d.cols = cols;
+  d.ldw = cols;
+  d.r = r;
+  d.group = 0;
+  return d;
+}
+}  // namespace
+
+extern "C" {
+
+qf_status qf_lora_merge_tensor_scale_nvfp4(const uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t rows,
+                                           int64_t cols, int r, float* d_scale, void* ws, size_t ws_bytes,
+                                           void* stream) {
+  const qf_lora_desc d = lora_one(W, A, B, rows, cols, r);
+  return qf_lora_merge_tensor_scale_nvfp4_grouped(&d, 1, 1, d_scale, nullptr, ws, ws_bytes, stream);
+}
+
+qf_status qf_lora_merge_qdq_pack_nvfp4(const uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t rows,
+                                       int64_t cols, int r, const float* d_scale, uint16_t* y_scratch,
+                                       uint8_t* codes, uint8_t* scales, void* stream) {
+  qf_lora_desc d = lora_one(W, A, B, rows, cols, r);
+  d.y = y_scratch;
+  d.codes = codes;
+  d.scales = scales;
+  return qf_lora_merge_qdq_pack_nvfp4_grouped(&d, 1, d_scale, stream);
+}
+
+qf_status qf_lora_adapter_grads(const uint16_t* G, const uint16_t* A, const uint16_t* B, int64_t rows, int64_t cols,
+                                int r, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes,
+                                void* stream) {
+  qf_lora_desc d = lora_one(nullptr, A, B, rows, cols, r);
+  d.G = G;
+  d.dA = dA;
+  d.dB = dB;
+  return qf_lora_adapter_grads_grouped(&d, 1, accumulate, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------ W4A4 GEMM --
@@ -678,13 +775,14 @@ qf_status qf_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64
 
 qf_status qf_transpose_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
                             int qdq_mxfp4, void* stream) {
+  if (qdq_mxfp4 < 0 || qdq_mxfp4 > 2) return QF_ERR_ARG;
   if (rows < 0 || cols < 0 || rows % 8 || cols % (qdq_mxfp4 ? 32 : 8) || rows >= (1ll << 22) || cols >= (1ll << 31))
     return QF_ERR_SHAPE;
   if (rows == 0 || cols == 0) return QF_OK;
   if (!x || !y) return QF_ERR_NULL;
   if (ldx < cols || ldy < rows) return QF_ERR_SHAPE;
   if (!aligned(x, 16) || !aligned(y, 16) || ldx % 8 || ldy % 8) return QF_ERR_ALIGN;
-  return hip_status(qf::launch_transpose(x, ldx, (int)rows, (int)cols, y, ldy, qdq_mxfp4 != 0, (hipStream_t)stream));
+  return hip_status(qf::launch_transpose(x, ldx, (int)rows, (int)cols, y, ldy, qdq_mxfp4, (hipStream_t)stream));
 }
 
 size_t qf_linear_backward_workspace(int64_t M, int64_t N, int64_t K) {
@@ -695,7 +793,8 @@ size_t qf_linear_backward_workspace(int64_t M, int64_t N, int64_t K) {
 qf_status qf_linear_backward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, const uint16_t* dY,
                                    int64_t lddy, uint16_t* dX, int64_t lddx, uint16_t* dW, int64_t lddw, int64_t M,
                                    int64_t N, int64_t K, unsigned flags, void* ws, size_t ws_bytes, void* stream) {
-  if (flags & ~(QF_QDQ_A | QF_QDQ_W)) return QF_ERR_ARG;
+  if (flags & ~(QF_QDQ_A | QF_QDQ_W | QF_MX_NOCLIP)) return QF_ERR_ARG;
+  if ((flags & QF_MX_NOCLIP) && !(flags & (QF_QDQ_A | QF_QDQ_W))) return QF_ERR_ARG;
   if (M < 0 || N < 0 || K < 0 || M % 64 || N % 64 || K % 32) return QF_ERR_SHAPE;
   if (M >= (1ll << 22) || N >= (1ll << 22) || K >= (1ll << 22)) return QF_ERR_SHAPE;
   if (M == 0 || N == 0 || K == 0 || (!dX && !dW)) return QF_OK;
@@ -713,14 +812,15 @@ qf_status qf_linear_backward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_
   uint16_t* xqt = (uint16_t*)((char*)dyt + round256(N * M * 2));            // Xq^T [K, M]
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = hipSuccess;
+  const int qdq = (flags & QF_MX_NOCLIP) ? qf::TR_QDQ_NOCLIP : qf::TR_QDQ_FLOOR;
   if (dX) {
-    e = qf::launch_transpose(W, ldw, (int)N, (int)K, wqt, N, (flags & QF_QDQ_W) != 0, s);
+    e = qf::launch_transpose(W, ldw, (int)N, (int)K, wqt, N, (flags & QF_QDQ_W) ? qdq : qf::TR_COPY, s);
     if (e == hipSuccess) e = qf::launch_gemm_mxfp4(dY, lddy, wqt, N, dX, lddx, (int)M, (int)K, (int)N, 0, s);
     if (e != hipSuccess) return hip_status(e);
   }
   if (dW) {
-    e = qf::launch_transpose(dY, lddy, (int)M, (int)N, dyt, M, false, s);
-    if (e == hipSuccess) e = qf::launch_transpose(X, ldx, (int)M, (int)K, xqt, M, (flags & QF_QDQ_A) != 0, s);
+    e = qf::launch_transpose(dY, lddy, (int)M, (int)N, dyt, M, qf::TR_COPY, s);
+    if (e == hipSuccess) e = qf::launch_transpose(X, ldx, (int)M, (int)K, xqt, M, (flags & QF_QDQ_A) ? qdq : qf::TR_COPY, s);
     if (e == hipSuccess) e = qf::launch_gemm_mxfp4(dyt, M, xqt, M, dW, lddw, (int)N, (int)K, (int)M, 0, s);
   }
   return hip_status(e);
@@ -759,6 +859,41 @@ qf_status qf_selftest_conversions(unsigned long long* d_counts, void* stream) {
   if (!d_counts) return QF_ERR_NULL;
   if (!aligned(d_counts, 8)) return QF_ERR_ALIGN;
   return hip_status(qf::launch_selftest_conversions(d_counts, (hipStream_t)stream));
+}
+
+}  // extern "C"
+
+extern "C" {
+
+// --------------------------------------------------------- workspace query --
+size_t qf_workspace_size(int op, int64_t rows, int64_t cols, int n) {
+  if (rows < 0 || cols < 0 || n < 0) return 0;
+  switch (op) {
+    case QF_OP_NVFP4_TENSOR_SCALE: {
+      if (n > QF_MAX_GROUPED) return 0;
+      // partials: min(tiles, AMAX_GRID) per group with a tensor, group indices below QF_MAX_GROUPS
+      const uint64_t chunks = (uint64_t)rows * (uint64_t)cols / 8;
+      const uint64_t tiles = (uint64_t)n * ((chunks + AMAX_TILE - 1) / AMAX_TILE);
+      const uint64_t grid = tiles < (uint64_t)qf::AMAX_GRID ? tiles : (uint64_t)qf::AMAX_GRID;
+      const uint64_t words = grid * QF_MAX_GROUPS;
+      return (size_t)(words > 0 ? words : 1) * sizeof(uint32_t);
+    }
+    case QF_OP_LORA: {
+      if (n > QF_MAX_GROUPED || cols > QF_LORA_MAX_COLS) return 0;
+      // the most any layout asks for: 8-row merge units, 256-row gradient blocks, 64 groups
+      const int64_t slabs = slabs_of(cols);
+      const int64_t merge_wg = (int64_t)n * ceil_div(ceil_div(rows, 8) * slabs, 4);
+      const int64_t merge_words = merge_wg * QF_MAX_GROUPS;
+      const int64_t grad_words = (int64_t)n * (ceil_div(rows, qf::LORA_DA_ROWS) * qf::LORA_MAX_R * cols +
+                                               slabs * rows * qf::LORA_MAX_R);
+      const int64_t words = merge_words > grad_words ? merge_words : grad_words;
+      return (size_t)(words > 0 ? words : 1) * 4;
+    }
+    case QF_OP_LINEAR_BACKWARD:
+      return qf_linear_backward_workspace(rows, cols, n);
+    default:
+      return 0;
+  }
 }
 
 }  // extern "C"

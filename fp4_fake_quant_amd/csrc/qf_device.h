@@ -21,6 +21,10 @@
 
 namespace qf {
 
+// Largest MXFP4 shared exponent of the noclip rule: 6 * 2^(252-127) = 1.5 * 2^127 is the
+// top of the last E2M1 grid that bf16 can hold (6 * 2^126 is beyond its range).
+constexpr int MX_NOCLIP_E_MAX = 252;
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));

@@ -61,7 +61,7 @@ __device__ __forceinline__ uint32_t lds_off(uint32_t r, uint32_t c) {
 // The scale operand carries E in its exponent field: E = max(floor(log2 amax) - 2 + 127, 0)
 // is the block maximum's bf16 exponent field minus 2, clamped at 0 (a saturating
 // subtract on the field moved to bits 23..30).
-// NOCLIP: the noclip rule, E = max(that field - 2 + [significand > 1.5], 0).
+// NOCLIP: the noclip rule, E = min(max(that field - 2 + [significand > 1.5], 0), 252).
 template <bool NOCLIP = false>
 __device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
   uint32_t ebits;
@@ -70,6 +70,7 @@ __device__ __forceinline__ uint4 mxfp4_qdq_chunk(uint4 w) {
     m = umax(m, dpp_xor1(m));
     m = umax(m, dpp_xor2(m));
     ebits = __builtin_elementwise_sub_sat((m & 0x7F80u) << 16, (m & 0x7Fu) > 0x40u ? 0x00800000u : 0x01000000u);
+    ebits = ebits < ((uint32_t)MX_NOCLIP_E_MAX << 23) ? ebits : ((uint32_t)MX_NOCLIP_E_MAX << 23);
   } else {
     // only the exponent of the block maximum matters: E = its bf16 exponent field - 2
     uint32_t m = maxexp_bits8(w);

@@ -9,6 +9,12 @@
 
 namespace qf {
 
+// QF_OK for hipSuccess; otherwise records e as the calling thread's last HIP error
+// (qf_last_hip_error) and returns QF_ERR_HIP.
+qf_status status_of(hipError_t e);
+// Every argument check of the NVFP4 tensor-scale calls except the workspace.
+qf_status check_tensor_scale(const qf_tensor_desc* d, int n, int n_groups, const float* d_scales);
+
 // A quantization launch works on "chunks" of 8 consecutive bf16 (16 bytes):
 // one 128-bit load per lane.  A workgroup of 256 lanes handles a tile of
 // 256 * L chunks (L per lane, at stride 256 so that every load instruction of
@@ -55,6 +61,7 @@ struct ReduceArgs {
   const uint32_t* partial;
   float* tscale;
   uint32_t* nonfinite;
+  float* tracked;       // running maximum |x| per group, folded in and updated (null: none)
 };
 
 // ------------------------------------------------------------------ LoRA ---
@@ -120,8 +127,9 @@ hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
 // codes: NVFP4/MXFP4 code bytes (scales their scale bytes), or Q4_K blocks (scales unused)
 hipError_t launch_dequant(int fmt, const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
                           const float* d_scale, uint16_t* y, int64_t ldy, hipStream_t s);
-// dst [C, R] = src [R, C]^T, MXFP4-QDQ'd along C first when qdq
-hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint16_t* dst, int64_t ldd, bool qdq,
+// dst [C, R] = src [R, C]^T, MXFP4-QDQ'd along C first (floor or noclip rule) unless mode is TR_COPY
+enum { TR_COPY = 0, TR_QDQ_FLOOR = 1, TR_QDQ_NOCLIP = 2 };
+hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint16_t* dst, int64_t ldd, int mode,
                             hipStream_t s);
 hipError_t launch_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
                              int64_t ldy, int M, int N, int K, unsigned flags, const float* d_sx, const float* d_sw,

@@ -111,7 +111,15 @@ __global__ __launch_bounds__(RED_WG) void k_nvfp4_scale_reduce(ReduceArgs a) {
   for (int g = threadIdx.x; g < a.n_groups; g += RED_WG) {
     const uint32_t bits = gmax[g];
     if (bits >= 0x7F80u && a.nonfinite) *a.nonfinite = 1u;
-    const float A = __uint_as_float(bits << 16);
+    uint32_t abits = bits << 16;                           // |x| max as fp32 bits (exact)
+    if (a.tracked) {
+      // running maximum over calls: the integer max of non-negative fp32 bit patterns is
+      // their numeric max (a NaN pattern wins and stays, which the flag reports)
+      const uint32_t prev = __float_as_uint(a.tracked[g]) & 0x7FFFFFFFu;
+      abits = abits > prev ? abits : prev;
+      a.tracked[g] = __uint_as_float(abits);
+    }
+    const float A = __uint_as_float(abits);
     a.tscale[g] = (A == 0.0f) ? 1.0f : A / 2688.0f;
   }
 }
@@ -173,9 +181,11 @@ __global__ __launch_bounds__(WG) void k_mxfp4(QArgs a) {
     // E = floor(log2 amax) - 2 + 127 clamped to [0, 254]: the bf16 exponent field minus 2
     // (0 for zero and subnormal maxima, whose floor(log2) is below -126).  Noclip: the
     // smallest E with amax <= 6 * 2^(E-127), one more than that when the maximum's
-    // significand exceeds 1.5 (mantissa field above 0x40).
+    // significand exceeds 1.5 (mantissa field above 0x40), at most 252 (the last E whose
+    // grid top 6 * 2^(E-127) is a finite bf16).
     const int ef = (int)(m >> 7);
-    const int e2 = NOCLIP ? ef - 2 + ((m & 0x7Fu) > 0x40u ? 1 : 0) : ef - 2;
+    int e2 = NOCLIP ? ef - 2 + ((m & 0x7Fu) > 0x40u ? 1 : 0) : ef - 2;
+    if (NOCLIP) e2 = e2 < MX_NOCLIP_E_MAX ? e2 : MX_NOCLIP_E_MAX;
     const uint32_t E = (uint32_t)(e2 > 0 ? e2 : 0);
     const float sc = __uint_as_float(E << 23);
     uint32_t codes = 0;

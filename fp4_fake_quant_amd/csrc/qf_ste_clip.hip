@@ -60,10 +60,11 @@ __global__ __launch_bounds__(SC_WG) void k_ste_clip(const uint16_t* __restrict__
       } else {
         m = umax(m, dpp_hmirror(m));                       // MXFP4 block: 8 lanes
         // E = max(bf16 exponent field of the block maximum - 2 (+1 under noclip when its
-        // significand exceeds 1.5), 0); the limit 6 * 2^(E-127) = 1.5 * 2^(E-125) is exact
-        // for E <= 252 and beyond every finite bf16 above that
+        // significand exceeds 1.5, capped at 252), 0); the limit 6 * 2^(E-127) =
+        // 1.5 * 2^(E-125) is exact for E <= 252 and beyond every finite bf16 above that
         const int ef = (int)(m >> 7);
         int E = ef - 2 + (NOCLIP && (m & 0x7Fu) > 0x40u ? 1 : 0);
+        if (NOCLIP) E = E < MX_NOCLIP_E_MAX ? E : MX_NOCLIP_E_MAX;
         E = E < 0 ? 0 : E;
         const float lim = E + 2 >= 255 ? __builtin_inff() : __uint_as_float(((uint32_t)(E + 2) << 23) | 0x400000u);
 #pragma unroll

@@ -22,14 +22,18 @@ namespace qf {
 constexpr int TR_ROWS = 64, TR_COLS = 128;               // source tile
 constexpr int TR_PITCH = TR_COLS + 2;                      // elements (65 words): rows 4-byte aligned
 
-// MXFP4 QDQ of one 16-byte chunk; lanes 4i..4i+3 hold one 32-element block (the rule of
-// qf_qdq_mxfp4: E = max(bf16 exponent field of the block maximum - 2, 0)).
+// MXFP4 QDQ of one 16-byte chunk; lanes 4i..4i+3 hold one 32-element block (the rules of
+// qf_qdq_mxfp4: E = max(bf16 exponent field of the block maximum - 2, 0); under NOCLIP one
+// more when the maximum's significand exceeds 1.5, at most MX_NOCLIP_E_MAX).
+template <bool NOCLIP>
 __device__ __forceinline__ uint4 tr_mxfp4_qdq(uint4 w) {
   uint32_t m = amax_bits8(w);
   m = umax(m, dpp_xor1(m));
   m = umax(m, dpp_xor2(m));
   const int ef = (int)(m >> 7);
-  const uint32_t E = (uint32_t)(ef > 2 ? ef - 2 : 0);
+  int e2 = ef - 2 + (NOCLIP && (m & 0x7Fu) > 0x40u ? 1 : 0);
+  if (NOCLIP) e2 = e2 < MX_NOCLIP_E_MAX ? e2 : MX_NOCLIP_E_MAX;
+  const uint32_t E = (uint32_t)(e2 > 0 ? e2 : 0);
   const float sc = __uint_as_float(E << 23);
   uint32_t codes = 0;
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(codes, __builtin_bit_cast(bf16x2_t, w.x), sc, 0);
@@ -45,8 +49,8 @@ __device__ __forceinline__ uint4 tr_mxfp4_qdq(uint4 w) {
 }
 
 // dst [C, R] (row stride ldd) = src [R, C] (row stride lds) transposed, QDQ'd along C
-// first when QDQ.  Grid: x over column tiles of src, y over row tiles.
-template <bool QDQ>
+// first unless MODE is TR_COPY.  Grid: x over column tiles of src, y over row tiles.
+template <int MODE>
 __global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ src, int64_t lds, int R, int C,
                                                    uint16_t* __restrict__ dst, int64_t ldd) {
   __shared__ __attribute__((aligned(16))) uint16_t t[TR_ROWS * TR_PITCH];
@@ -68,7 +72,7 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ 
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
     const int r = (int)(tid >> 4) + 16 * i, c = 8 * (int)(tid & 15u);
-    const uint4 q = QDQ ? tr_mxfp4_qdq(v[i]) : v[i];
+    const uint4 q = MODE == TR_COPY ? v[i] : tr_mxfp4_qdq<MODE == TR_QDQ_NOCLIP>(v[i]);
     uint32_t* row = tw + (r * TR_PITCH + c) / 2;
     row[0] = q.x;
     row[1] = q.y;
@@ -89,7 +93,7 @@ __global__ __launch_bounds__(256) void k_transpose(const uint16_t* __restrict__ 
   }
 }
 
-hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint16_t* dst, int64_t ldd, bool qdq,
+hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint16_t* dst, int64_t ldd, int mode,
                             hipStream_t s) {
   if (R == 0 || C == 0) return hipSuccess;
   // grid y is limited to 65535 row tiles: taller sources go in row bands of that many
@@ -99,8 +103,9 @@ hipError_t launch_transpose(const uint16_t* src, int64_t lds, int R, int C, uint
     const dim3 g((unsigned)((C + TR_COLS - 1) / TR_COLS), (unsigned)((rn + TR_ROWS - 1) / TR_ROWS)), b(256);
     const uint16_t* sp = src + (int64_t)rb * lds;
     uint16_t* dp = dst + rb;                                 // the band's rows are output columns rb ..
-    if (qdq) hipLaunchKernelGGL(k_transpose<true>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
-    else hipLaunchKernelGGL(k_transpose<false>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
+    if (mode == TR_QDQ_FLOOR) hipLaunchKernelGGL(k_transpose<TR_QDQ_FLOOR>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
+    else if (mode == TR_QDQ_NOCLIP) hipLaunchKernelGGL(k_transpose<TR_QDQ_NOCLIP>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
+    else hipLaunchKernelGGL(k_transpose<TR_COPY>, g, b, 0, s, sp, lds, rn, C, dp, ldd);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

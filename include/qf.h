@@ -64,16 +64,21 @@ typedef enum qf_status {
   QF_ERR_WORKSPACE = 4,       /* workspace missing or smaller than required         */
   QF_ERR_HIP = 5,             /* a HIP launch failed; see qf_last_hip_error()       */
   QF_ERR_NOT_IMPLEMENTED = 6, /* reserved                                           */
-  QF_ERR_ARG = 7              /* other invalid argument (count, flag, group index)  */
+  QF_ERR_ARG = 7,             /* other invalid argument (count, flag, group index)  */
+  QF_ERR_IO = 8               /* a file could not be created or written             */
 } qf_status;
 
 enum qf_format { QF_FMT_NVFP4 = 0, QF_FMT_MXFP4 = 1, QF_FMT_Q4K = 2 };
 
 /* MXFP4 shared-exponent rules (the pages do not fix one).  FLOOR, the default of every
  * MXFP4 call: E = clamp(floor(log2 amax) - 2 + 127, 0, 254), which clips block maxima in
- * (6, 8) * 2^(E-127) to 6.  NOCLIP: the smallest E in [0, 254] with amax <= 6 *
- * 2^(E-127) (ceil(log2(amax / 6)) + 127), one more than FLOOR exactly when the maximum's
- * significand exceeds 1.5; nothing is clipped above E = 0.  amax == 0 gives E = 0. */
+ * (6, 8) * 2^(E-127) to 6 (finite inputs never get past E = 252).  NOCLIP: the smallest
+ * E in [0, 252] with amax <= 6 * 2^(E-127) (ceil(log2(amax / 6)) + 127), one more than
+ * FLOOR exactly when the maximum's significand exceeds 1.5 and FLOOR's E is below 252;
+ * nothing is clipped except block maxima above 6 * 2^125 = 1.5 * 2^127.  252 is the last
+ * exponent whose whole grid (up to 6 * 2^(E-127)) bf16 can hold: at 253 a maximum in
+ * [1.75, 2) * 2^127 would round to the code 4 and dequantize to 2^128 = Inf.  So every
+ * finite input gives finite QDQ'd values under both rules.  amax == 0 gives E = 0. */
 #define QF_MX_RULE_FLOOR 0
 #define QF_MX_RULE_NOCLIP 1
 
@@ -86,6 +91,19 @@ enum qf_format { QF_FMT_NVFP4 = 0, QF_FMT_MXFP4 = 1, QF_FMT_Q4K = 2 };
 uint32_t qf_version(void);                 /* (major << 16) | (minor << 8) | patch */
 const char* qf_status_str(qf_status s);
 int qf_last_hip_error(void);               /* hipError_t of this thread's last failed launch */
+
+/* Device workspace (bytes) that suffices for any call of operation `op` over at most n
+ * tensors of at most rows x cols elements each (0 for an unknown op or invalid sizes):
+ *   QF_OP_NVFP4_TENSOR_SCALE  the tensor-scale calls (any grouping below QF_MAX_GROUPS);
+ *   QF_OP_LORA                the LoRA merge / tensor-scale and adapter-gradient calls
+ *                             (n matrices, any rank 1..16, any grouping);
+ *   QF_OP_LINEAR_BACKWARD     qf_linear_backward_mxfp4 with M = rows, N = cols, K = n.
+ * The per-call queries (qf_nvfp4_tensor_scale_workspace, qf_lora_workspace,
+ * qf_linear_backward_workspace) give the exact size for given descriptors. */
+#define QF_OP_NVFP4_TENSOR_SCALE 0
+#define QF_OP_LORA 1
+#define QF_OP_LINEAR_BACKWARD 2
+size_t qf_workspace_size(int op, int64_t rows, int64_t cols, int n);
 
 /* Packed bytes of one [rows, cols] tensor (codes + block scales; Q4_K blocks).
  * NVFP4: rows*cols/2 + rows*cols/16 (the 4-byte FP32 tensor scale per group is
@@ -129,8 +147,25 @@ size_t qf_nvfp4_tensor_scale_workspace(const qf_tensor_desc* d, int n);
 qf_status qf_nvfp4_tensor_scale_grouped(const qf_tensor_desc* d, int n, int n_groups,
                                         float* d_scales, uint32_t* d_nonfinite,
                                         void* ws, size_t ws_bytes, void* stream);
-/* Single tensor (a group of one). ws sized by qf_nvfp4_tensor_scale_workspace. */
-qf_status qf_nvfp4_tensor_scale(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx,
+/* The same pass with a TRACKED scale ("Method", "Export": NVFP4 activation scales are
+ * tracked during training and saved, so no calibration pass is needed).  The reading
+ * taken: the tracked amax of group g is the running maximum of |x| over every call so far.
+ * d_amax: device float[n_groups], 4-byte aligned, the state (the caller zeroes it to start
+ * tracking and saves it with the checkpoint; non-negative finite values).  Each call sets
+ * d_amax[g] = max(d_amax[g], A_g) with A_g this call's group maximum (a group with no
+ * tensor keeps its value), then d_scales[g] = (d_amax[g] == 0) ? 1.0f :
+ * fl(d_amax[g] / 2688.0f).  d_amax == NULL is qf_nvfp4_tensor_scale_grouped.  Everything
+ * else as qf_nvfp4_tensor_scale_grouped. */
+qf_status qf_nvfp4_tensor_scale_tracked(const qf_tensor_desc* d, int n, int n_groups, float* d_amax,
+                                        float* d_scales, uint32_t* d_nonfinite,
+                                        void* ws, size_t ws_bytes, void* stream);
+/* One tied group given as a host array of n_tensors (<= QF_MAX_GROUPED, else QF_ERR_ARG)
+ * device pointers to contiguous bf16 tensors of numel[i] elements each (the members the
+ * engines fuse, e.g. Q, K and V): *d_scale = the group's tensor scale as above.  numel[i]
+ * must be a non-negative multiple of 16 (the NVFP4 block; QF_ERR_SHAPE) below 2^35, each
+ * x[i] 16-byte aligned (QF_ERR_ALIGN).  ws: at least
+ * qf_workspace_size(QF_OP_NVFP4_TENSOR_SCALE, 1, max numel, n_tensors) bytes. */
+qf_status qf_nvfp4_tensor_scale(const uint16_t* const* x, const int64_t* numel, int n_tensors,
                                 float* d_scale, uint32_t* d_nonfinite,
                                 void* ws, size_t ws_bytes, void* stream);
 
@@ -287,16 +322,40 @@ typedef struct qf_lora_desc {
 /* Device workspace (bytes) the LoRA calls need for these descriptors (0 when a
  * descriptor is invalid). */
 size_t qf_lora_workspace(const qf_lora_desc* d, int n);
+/* Host query of the launch layout the LoRA calls choose for these descriptors (nothing
+ * is launched; only shapes, ranks and groups are read): out[0] rows per merge unit (32,
+ * 16 or 8: units shrink until a launch has at least 512 merge workgroups), out[1] merge
+ * workgroups, out[2] rows per gradient workgroup (512 when that still gives 256
+ * workgroups, else 256), out[3] gradient workgroups.  out is host int32[4].  Errors as
+ * the LoRA calls' shape and argument checks. */
+qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out);
 /* Pass 1: merge into M (skipped for M == NULL) and the NVFP4 tensor scale of
  * every tied group (d_scales[g] as in qf_nvfp4_tensor_scale_grouped, computed
  * from the merged values). */
-qf_status qf_lora_merge_tensor_scale_nvfp4(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
-                                           uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream);
+qf_status qf_lora_merge_tensor_scale_nvfp4_grouped(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
+                                                   uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream);
 /* Pass 2: NVFP4 QDQ + pack of the merged weight (exactly qf_qdq_pack_nvfp4 on M
  * with d_scales[group]); descriptors with M == NULL merge again from W, A, B. */
-qf_status qf_lora_qdq_pack_nvfp4(const qf_lora_desc* d, int n, const float* d_scales, void* stream);
+qf_status qf_lora_merge_qdq_pack_nvfp4_grouped(const qf_lora_desc* d, int n, const float* d_scales, void* stream);
 /* STE to the adapters: dB = G . A^T, dA = B^T . G (fp32; accumulate != 0 adds). */
-qf_status qf_lora_adapter_grads(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
+qf_status qf_lora_adapter_grads_grouped(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
+                                        void* stream);
+
+/* The same three steps for one contiguous matrix (W [rows, cols], A [r, cols], B [rows, r],
+ * G [rows, cols]; ldw = cols) with no merge scratch: pass 1 merges in registers and only
+ * takes the maximum (*d_scale = the matrix's NVFP4 tensor scale, a tied group of one);
+ * pass 2 merges again and writes the QDQ'd bf16 to y_scratch [rows, cols] (NULL: skipped)
+ * and the packed codes [rows, cols/2] and E4M3 scales [rows, cols/16] (NULL: skipped; not
+ * both NULL).  Bits, shapes, alignment and errors as the grouped calls with one descriptor
+ * and M = NULL; ws of at least qf_workspace_size(QF_OP_LORA, rows, cols, 1) bytes. */
+qf_status qf_lora_merge_tensor_scale_nvfp4(const uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t rows,
+                                           int64_t cols, int r, float* d_scale, void* ws, size_t ws_bytes,
+                                           void* stream);
+qf_status qf_lora_merge_qdq_pack_nvfp4(const uint16_t* W, const uint16_t* A, const uint16_t* B, int64_t rows,
+                                       int64_t cols, int r, const float* d_scale, uint16_t* y_scratch,
+                                       uint8_t* codes, uint8_t* scales, void* stream);
+qf_status qf_lora_adapter_grads(const uint16_t* G, const uint16_t* A, const uint16_t* B, int64_t rows, int64_t cols,
+                                int r, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes,
                                 void* stream);
 
 /* ------------------------------------------------------------ dequant ---- */
@@ -430,10 +489,11 @@ qf_status qf_linear_forward_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t
  * qf_ste_backward then carries dWq to the fp32 latent weights.
  *
  * qf_transpose_bf16: y [cols, rows] = x [rows, cols]^T, MXFP4-QDQ'd along cols first
- * (the rule of qf_qdq_mxfp4) when qdq_mxfp4 != 0.  rows and cols multiples of 8 (cols
- * of 32 with qdq_mxfp4), rows < 2^22, ldx >= cols, ldy >= rows (QF_ERR_SHAPE); x, y
- * 16-byte aligned with ldx, ldy multiples of 8 (QF_ERR_ALIGN); y must not overlap x.
- * The result is exact (a copy, or QDQ values that are exactly those of qf_qdq_mxfp4). */
+ * when qdq_mxfp4 is 1 (the floor rule of qf_qdq_mxfp4) or 2 (QF_MX_RULE_NOCLIP); 0 copies,
+ * other values give QF_ERR_ARG.  rows and cols multiples of 8 (cols of 32 with
+ * qdq_mxfp4), rows < 2^22, ldx >= cols, ldy >= rows (QF_ERR_SHAPE); x, y 16-byte aligned
+ * with ldx, ldy multiples of 8 (QF_ERR_ALIGN); y must not overlap x.  The result is exact
+ * (a copy, or QDQ values that are exactly those of qf_qdq_pack_mxfp4_rule). */
 qf_status qf_transpose_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ldx, uint16_t* y, int64_t ldy,
                             int qdq_mxfp4, void* stream);
 
@@ -441,7 +501,9 @@ qf_status qf_transpose_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64
  * Wq = QDQ(X) / QDQ(W) when flags has QF_QDQ_A / QF_QDQ_W (the forward's flags), else
  * the operands themselves.  Five launches on `stream`: Wq^T, dY^T and Xq^T into the
  * workspace (qf_transpose_bf16), then the two products on the BF16 matrix cores
- * (qf_gemm_mxfp4 with flags 0).  dX or dW may be NULL to skip it.  Shapes: M and N
+ * (qf_gemm_mxfp4 with flags 0).  QF_MX_NOCLIP (with QF_QDQ_A and/or QF_QDQ_W, else
+ * QF_ERR_ARG) quantizes under the noclip rule, matching a forward run with that flag.
+ * dX or dW may be NULL to skip it.  Shapes: M and N
  * multiples of 64 (the products' reduction lengths), K a multiple of 32, M, N, K and
  * the leading dimensions < 2^22; leading dimensions >= the row lengths, multiples of 8;
  * all arrays 16-byte aligned, the workspace 256-byte aligned.  Accuracy: each output element obeys the bound of qf_gemm_mxfp4 with the
@@ -451,6 +513,63 @@ qf_status qf_linear_backward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_
                                    const uint16_t* dY, int64_t lddy, uint16_t* dX, int64_t lddx,
                                    uint16_t* dW, int64_t lddw, int64_t M, int64_t N, int64_t K,
                                    unsigned flags, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------ checkpoint containers ---- */
+/* "Method", "Export" on the project page: NVFP4 / MXFP4 checkpoints go to vLLM in the
+ * compressed-tensors layout and Q4_K to llama.cpp as GGUF, so that the engine loads the
+ * trained codes and scales with no extra lossy conversion (and the saved NVFP4 activation
+ * scales need no calibration pass).  The pages fix neither container; these writers take
+ * HOST buffers (copy the packed device arrays first) and write plain files.
+ *
+ * qf_write_safetensors: the safetensors container -- an 8-byte little-endian header
+ * length N, N bytes of JSON {name: {"dtype", "shape", "data_offsets": [begin, end]}, ...,
+ * "__metadata__": {key: value}} padded with spaces to a multiple of 8, then each tensor's
+ * bytes in the order given (offsets relative to the end of the header).  dtype is a
+ * safetensors dtype string: "U8", "I8", "BOOL", "F8_E4M3", "F8_E5M2", "F8_E8M0", "U16",
+ * "I16", "F16", "BF16", "U32", "I32", "F32", "U64", "I64", "F64"; the data holds
+ * product(shape) elements of it.  The metadata map (n_meta pairs, may be 0) holds strings.
+ * Errors: QF_ERR_NULL (path, a name, dtype, key, value, or data of a non-empty tensor
+ * missing), QF_ERR_ARG (unknown dtype, empty or repeated name, the name "__metadata__",
+ * negative counts), QF_ERR_SHAPE (ndim outside 0..8, a negative extent), QF_ERR_IO (the file
+ * cannot be written).  The file is only created once the arguments are checked.
+ *
+ * Names and the scale convention of the NVFP4 / MXFP4 tensors this library's binding
+ * writes ("compressed-tensors-style"; byte compatibility with an engine's loader is
+ * unpinned): <layer>.weight_packed U8 [rows, cols/2] (codes as qf_pack_*), <layer>.
+ * weight_scale F8_E4M3 [rows, cols/16] or F8_E8M0 [rows, cols/32], <layer>.
+ * weight_global_scale F32 [1] = the dequant multiplier s_t of the layer's tied group,
+ * <layer>.input_global_scale F32 [1] = the tracked activation s_t (W4A4). */
+typedef struct qf_st_tensor {
+  const char* name;      /* UTF-8, unique within the file                   */
+  const char* dtype;     /* safetensors dtype string                        */
+  int32_t ndim;          /* 0..8                                            */
+  const int64_t* shape;  /* host int64[ndim], row-major, outermost first    */
+  const void* data;      /* HOST bytes, product(shape) * dtype size         */
+} qf_st_tensor;
+qf_status qf_write_safetensors(const char* path, const qf_st_tensor* t, int n, const char* const* meta_keys,
+                               const char* const* meta_values, int n_meta);
+
+/* qf_write_gguf: a GGUF-style container -- uint32 magic 0x46554747 ("GGUF"), uint32
+ * version 3, uint64 tensor count, uint64 key-value count; each key-value pair as a string
+ * key (uint64 length + bytes), uint32 type 8 (string) and a string value; each tensor info
+ * as a string name, uint32 ndim (1..4), uint64 extents innermost first, uint32 type,
+ * uint64 offset of its data; zero padding to a multiple of 32 bytes; then each tensor's
+ * nbytes at its offset (multiples of 32, zero padded).  For this library's Q4_K blocks
+ * (qf_pack_q4k, [rows, cols/256, 144]) the binding writes type 12 with extents {cols, rows}
+ * and a key "qf.q4k.block_layout" describing the 144-byte block (d, dmin, the 96-bit
+ * sc/m stream, element 2i in the low nibble): whether an engine reads these blocks the
+ * same way is unpinned.  Errors as qf_write_safetensors (QF_ERR_SHAPE for ndim outside
+ * 1..4 or a negative extent). */
+typedef struct qf_gguf_tensor {
+  const char* name;
+  int32_t ndim;          /* 1..4                                            */
+  const int64_t* dims;   /* host int64[ndim], innermost (contiguous) first  */
+  uint32_t type;         /* the file's tensor type code                     */
+  const void* data;      /* HOST bytes                                      */
+  uint64_t nbytes;
+} qf_gguf_tensor;
+qf_status qf_write_gguf(const char* path, const qf_gguf_tensor* t, int n, const char* const* kv_keys,
+                        const char* const* kv_values, int n_kv);
 
 /* ---------------------------------------------------- conformance test ---- */
 /* Checks on the device that the gfx950 instructions and shortcuts the kernels

@@ -14,9 +14,13 @@ Readings of what the page leaves open (stated choices):
   the largest E2M1 exponent (2), the usual microscaling rule.  Blocks whose
   amax lies in (6, 8) * 2^(E-127) therefore clip their top element to 6.
 * A second shared-exponent rule, "noclip", is kept as an option (the pages do not fix
-  the rule): E = the smallest value in [0, 254] with a <= 6 * 2^(E-127), i.e.
-  ceil(log2(a / 6)) + 127 clamped, so that no element is clipped (except when even
-  E = 254 is too small, which no finite bf16 reaches, or E = 0 is larger than needed).
+  the rule): E = the smallest value in [0, 252] with a <= 6 * 2^(E-127), i.e.
+  ceil(log2(a / 6)) + 127 clamped to [0, 252], so that no element is clipped unless
+  a > 6 * 2^125.  The upper end 252 is the largest exponent whose grid top 6 * 2^(E-127)
+  is a finite bf16: at E = 253 a block maximum in [1.75, 2) * 2^127 would round to the
+  code 4 and dequantize to 2^128, which bf16 cannot hold.  So blocks with maxima above
+  1.5 * 2^127 take E = 252 and clip to 6 * 2^125, as under the floor rule (which never
+  goes above 252 for finite inputs).
 * X = 2^(E-127); y = |x| / X (exact unless it underflows far below 0.25);
   magnitude = E2M1 RNE-saturating(y); the code's sign bit is x's sign bit.
 * Dequant: o = sign * bf16(v * X), exact, including bf16 subnormals.
@@ -25,9 +29,10 @@ Packing: codes[r][c/2] (element 2i low nibble, 2i+1 high nibble) and
 scales[r][c/32] E8M0 bytes: 17 bytes per 32 elements = 4.25 bits per weight.
 Engine compatibility is parity unpinned.
 
-Pins: closed-form packed size, brute-force codes, on-grid outputs,
-QDQ == dequant(unpack(pack)), exact idempotence on all finite inputs,
-exact-representable round trip; tests/test_oracle_formats.py.
+Pins: closed-form packed size, brute-force codes and exponents, on-grid outputs,
+finite outputs for every finite input under both rules, QDQ == dequant(unpack(pack)),
+exact idempotence on all finite inputs, exact-representable round trip;
+tests/test_oracle_formats.py.
 """
 
 import numpy as np
@@ -36,6 +41,9 @@ from .primitives import (F32, bf16_to_f32, f32_to_bf16, e2m1_encode_mag, E2M1_MA
                          e8m0_value, floor_log2)
 
 BLOCK = 32
+# the largest shared exponent of the noclip rule: 6 * 2^(252-127) = 1.5 * 2^127 is the
+# top of the E2M1 grid that bf16 still holds; 6 * 2^126 is beyond the bf16 range
+NOCLIP_E_MAX = 252
 
 
 def shared_exponent(a, rule="floor"):
@@ -50,7 +58,7 @@ def shared_exponent(a, rule="floor"):
         # first reaches it at E - 127 = e - 2 or e - 1; test both exactly in float64
         lo = e - 2 + 127
         fits = a.astype(np.float64) <= np.ldexp(6.0, lo - 127)
-        E = np.clip(np.where(fits, lo, lo + 1), 0, 254)
+        E = np.clip(np.where(fits, lo, lo + 1), 0, NOCLIP_E_MAX)
     else:
         raise ValueError(rule)
     return np.where(pos, E, 0).astype(np.int64)
@@ -78,7 +86,7 @@ def saturated(x_bits, rule="floor"):
     """Elements the quantizer saturates: y = |x| / 2^(E-127) (exact) exceeds 6, the largest
     E2M1 magnitude (bool [rows, cols]).  Under the floor rule these are the elements in
     (6, 8) * 2^(E-127) of blocks whose maximum has a significand above 1.5; under the
-    noclip rule there are none."""
+    noclip rule only the elements above 6 * 2^125 = 1.5 * 2^127 (blocks capped at E = 252)."""
     x_bits = np.asarray(x_bits, dtype=np.uint16)
     rows, cols = x_bits.shape
     x = bf16_to_f32(x_bits).reshape(rows, cols // BLOCK, BLOCK)

@@ -30,10 +30,14 @@ scales[r][c/16] holds E4M3 bytes; the fp32 tensor scale s_t travels separately
 (per tied group).  9 bytes per 16 elements plus 4 bytes per group, i.e. 4.50
 bits per weight, as the table states.
 
+Tracked scale (activations): the running maximum of |x| over the batches seen so far,
+then the rule above; see tracked_scale.
+
 Pins: closed-form packed size (bits per weight from the table), brute-force
 element codes, on-grid outputs, QDQ == dequant(unpack(pack)), idempotence for
 normal block scales, exact-representable round trip, tying equals fusing,
-tests/test_oracle_formats.py.
+tests/test_oracle_formats.py; the tracked scale equals the scale of all batches
+seen so far taken together, in any order, tests/test_oracle_misc.py.
 """
 
 import numpy as np
@@ -70,6 +74,17 @@ def tensor_scale(tensors):
     if A == 0:
         return F32(1.0)
     return F32(A) / TENSOR_DIV
+
+
+def tracked_scale(amax_prev, tensors):
+    """Tracked tensor scale ("Method", "Export" on the project page: NVFP4 activation
+    scales are tracked during training and saved, so no calibration pass runs).  Reading:
+    the tracked amax is the running maximum of |x| over every batch seen so far.
+    Returns (amax, s_t): amax = max(amax_prev, A of this batch's tied group) as float32,
+    s_t = 1 if amax == 0 else fl(amax / 2688) (the rule of tensor_scale)."""
+    A, _ = group_amax(tensors)
+    amax = max(F32(amax_prev), F32(A))
+    return F32(amax), (F32(1.0) if amax == 0 else F32(amax) / TENSOR_DIV)
 
 
 def _scaled(x_bits, s_t):

@@ -177,17 +177,29 @@ def planted_mx_blocks():
     return blocks
 
 
+# the largest finite bf16, (2 - 2^-7) * 2^127, read from its bit pattern
+BF16_MAX = struct.unpack("<f", struct.pack("<I", 0x7F7F0000))[0]
+
+
+def noclip_exponents():
+    """E8M0 bytes the noclip rule may use: those whose whole E2M1 grid, up to 6 * 2^(E-127),
+    is a finite bf16 (so a QDQ'd value can never become Inf)."""
+    return [k for k in range(255) if math.ldexp(6.0, k - 127) <= BF16_MAX]
+
+
 def check_mxfp4_noclip(x_bits):
-    """The noclip shared exponent by brute force over every E8M0 byte: the smallest E with
-    max|x| <= 6 * 2^(E-127) (exact in float64), then the same element rule as above."""
+    """The noclip shared exponent by brute force over the usable E8M0 bytes: the smallest E
+    with max|x| <= 6 * 2^(E-127) (exact in float64), or the largest usable one when none
+    fits; then the same element rule as above."""
     codes, E = mxfp4.quantize(x_bits, rule="noclip")
     rows, cols = x_bits.shape
     x = widen(x_bits).reshape(rows, cols // 32, 32)
     a = np.abs(x).max(axis=-1)
+    usable = noclip_exponents()
     E_ref = np.zeros(a.shape, np.int64)
     for idx, ai in np.ndenumerate(a):
         if ai > 0:
-            E_ref[idx] = next(k for k in range(255) if ai <= math.ldexp(6.0, k - 127) or k == 254)
+            E_ref[idx] = next((k for k in usable if ai <= math.ldexp(6.0, k - 127)), usable[-1])
     bad = int(np.sum(E.astype(np.int64) != E_ref))
     X = np.ldexp(1.0, E_ref - 127)[..., None]
     y = np.abs(x) / X

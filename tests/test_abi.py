@@ -109,42 +109,42 @@ def test_lora_validation():
     # merge partials ceil(ceil(100/8) * 3 slabs / 4) = 10 workgroups per matrix x 2 groups;
     # gradient partials: dA one 256-row block x 16 x 1056, dB 3 slabs x 100 rows x 16, per matrix
     assert need == 4 * max(20 * 2, 2 * (16 * 1056 + 3 * 100 * 16))
-    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need - 4, None) == 4
-    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 1, q, None, q, need, None) == 7   # group 1 >= 1
-    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, None, 0, None) == 4
+    assert L.qf_lora_merge_tensor_scale_nvfp4_grouped(ctypes.byref(d), 2, 2, q, None, q, need - 4, None) == 4
+    assert L.qf_lora_merge_tensor_scale_nvfp4_grouped(ctypes.byref(d), 2, 1, q, None, q, need, None) == 7   # group 1 >= 1
+    assert L.qf_lora_adapter_grads_grouped(ctypes.byref(d), 2, 0, None, 0, None) == 4
     d[1].r = 17
     assert L.qf_lora_workspace(ctypes.byref(d), 2) == 0
-    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need, None) == 7
+    assert L.qf_lora_merge_tensor_scale_nvfp4_grouped(ctypes.byref(d), 2, 2, q, None, q, need, None) == 7
     d[1].r = 16
     d[1].ldw = 1 << 24                                              # row stride too large
-    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 2
+    assert L.qf_lora_adapter_grads_grouped(ctypes.byref(d), 2, 0, q, need, None) == 2
     d[1].cols = d[1].ldw = 1048                                     # not a multiple of 32
-    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 2
+    assert L.qf_lora_adapter_grads_grouped(ctypes.byref(d), 2, 0, q, need, None) == 2
     d[1].cols = d[1].ldw = 1056
     d[1].B = 0x10300002                                             # B must be 4-byte aligned
-    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, need, None) == 3
+    assert L.qf_lora_adapter_grads_grouped(ctypes.byref(d), 2, 0, q, need, None) == 3
     d[1].B = 0x10300000
     d[0].W = 0                                                      # W is needed (M may be NULL)
-    assert L.qf_lora_merge_tensor_scale_nvfp4(ctypes.byref(d), 2, 2, q, None, q, need, None) == 1
+    assert L.qf_lora_merge_tensor_scale_nvfp4_grouped(ctypes.byref(d), 2, 2, q, None, q, need, None) == 1
     d[0].W = 0x10000000
     # QDQ pass: an output is required; without M, W / A / B are read and checked
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 1            # no y and no codes
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 2, q, None) == 1            # no y and no codes
     d[0].y, d[1].y = 0x10800000, 0x10900000
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, None, None) == 1         # no tensor scales
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 2, None, None) == 1         # no tensor scales
     d[0].M = 0
     d[0].W = 0x10000008                                             # W must be 16-byte aligned
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 3
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 2, q, None) == 3
     d[0].W = 0x10000000
     d[0].A = 0
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 1
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 2, q, None) == 1
     d[0].A = 0x10200000
     d[0].y = 0x10800008                                             # y must be 16-byte aligned
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 3
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 2, q, None) == 3
     d[0].group = -1
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 2, q, None) == 7
-    assert L.qf_lora_qdq_pack_nvfp4(ctypes.byref(d), 17, q, None) == 7
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 2, q, None) == 7
+    assert L.qf_lora_merge_qdq_pack_nvfp4_grouped(ctypes.byref(d), 17, q, None) == 7
     d[0].rows = d[1].rows = 0                                       # empty: nothing to do
-    assert L.qf_lora_adapter_grads(ctypes.byref(d), 2, 0, q, 4, None) == 0
+    assert L.qf_lora_adapter_grads_grouped(ctypes.byref(d), 2, 0, q, 4, None) == 0
 
 
 def test_lora_gradient_unit_rows():
@@ -191,12 +191,15 @@ def test_transpose_and_backward_validation():
     assert L.qf_transpose_bf16(x, 16, 48, 48, y, 8, 0, None) == 2              # ldy < rows
     assert L.qf_transpose_bf16(_addr(0x10000008), 16, 48, 48, y, 16, 0, None) == 3
     assert L.qf_transpose_bf16(x, 0, 48, 48, y, 16, 0, None) == 0              # empty: no-op
+    assert L.qf_transpose_bf16(x, 16, 64, 64, y, 16, 3, None) == 7             # unknown QDQ mode
+    assert L.qf_transpose_bf16(x, 16, 64, 64, y, 16, -1, None) == 7
     need = L.qf_linear_backward_workspace(128, 64, 96)
     assert need == 96 * 64 * 2 + 64 * 128 * 2 + 96 * 128 * 2
     args = (x, 96, w, 96, d, 64, y, 96, _addr(0x11000000), 96)
     assert L.qf_linear_backward_mxfp4(*args, 100, 64, 96, 3, _addr(0x12000000), need, None) == 2   # M % 64
     assert L.qf_linear_backward_mxfp4(*args, 128, 64, 80, 3, _addr(0x12000000), need, None) == 2   # K % 32
     assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 4, _addr(0x12000000), need, None) == 7   # flags
+    assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 8, _addr(0x12000000), need, None) == 7   # noclip alone
     assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 3, _addr(0x12000000), need - 2, None) == 4
     assert L.qf_linear_backward_mxfp4(*args, 128, 64, 96, 3, _addr(0x12000010), need, None) == 3   # ws alignment
     assert L.qf_linear_backward_mxfp4(x, 96, None, 96, d, 64, y, 96, None, 0, 128, 64, 96, 3,
@@ -284,3 +287,108 @@ def test_gemm_validation():
     assert L.qf_gemm_mxfp4_packed_w(p, 96, q, ws, y, 64, 64, 64, 96, None) == 2  # K not a multiple of 64
     assert L.qf_gemm_mxfp4_packed_w(p, 64, _addr(0x10400008), ws, y, 64, 64, 64, 64, None) == 3  # codes 16-byte aligned
     assert L.qf_gemm_mxfp4_packed_w(p, 64, q, None, y, 64, 64, 64, 64, None) == 1
+
+
+# the calls of the boundary as the survey's contract lists them
+SURVEY_BOUNDARY = [
+    "qf_nvfp4_tensor_scale", "qf_qdq_nvfp4", "qf_qdq_mxfp4", "qf_qdq_q4k",
+    "qf_pack_nvfp4", "qf_pack_mxfp4", "qf_pack_q4k",
+    "qf_qdq_pack_nvfp4", "qf_qdq_pack_mxfp4", "qf_qdq_pack_q4k",
+    "qf_nvfp4_tensor_scale_grouped", "qf_qdq_pack_nvfp4_grouped", "qf_qdq_pack_mxfp4_grouped",
+    "qf_qdq_pack_q4k_grouped", "qf_ste_backward", "qf_gemm_mxfp4",
+    "qf_lora_merge_tensor_scale_nvfp4", "qf_lora_merge_qdq_pack_nvfp4", "qf_lora_adapter_grads",
+    "qf_packed_bytes", "qf_workspace_size", "qf_status_str", "qf_last_hip_error", "qf_version",
+]
+
+
+def test_survey_boundary_names_are_exported():
+    L = _lib.lib()
+    declared = declared_functions()
+    for n in SURVEY_BOUNDARY:
+        assert n in declared and hasattr(L, n), n
+
+
+def test_pointer_array_tensor_scale_validation():
+    """qf_nvfp4_tensor_scale over a host array of device pointers (one tied group)."""
+    L = _lib.lib()
+    q = _addr(0x10100000)
+    ptrs = (ctypes.c_void_p * 3)(0x10000000, 0x10200000, 0x10400000)
+    numel = (ctypes.c_int64 * 3)(6144 * 4096 // 3, 6144 * 4096 // 6, 6144 * 4096 // 6)
+    need = L.qf_workspace_size(0, 1, numel[0], 3)
+    assert need == 4 * 2048 * 64                                   # the persistent grid, 64 groups
+    assert L.qf_nvfp4_tensor_scale(ptrs, numel, 3, q, None, None, 0, None) == 4
+    assert L.qf_nvfp4_tensor_scale(ptrs, numel, 17, q, None, q, need, None) == 7
+    assert L.qf_nvfp4_tensor_scale(ptrs, numel, 3, None, None, q, need, None) == 1
+    assert L.qf_nvfp4_tensor_scale(None, numel, 3, q, None, q, need, None) == 1
+    bad = (ctypes.c_int64 * 3)(4096, 4100, 16)                    # 4100 is not a multiple of 16
+    assert L.qf_nvfp4_tensor_scale(ptrs, bad, 3, q, None, q, need, None) == 2
+    odd = (ctypes.c_void_p * 3)(0x10000000, 0x10200008, 0x10400000)
+    assert L.qf_nvfp4_tensor_scale(odd, numel, 3, q, None, q, need, None) == 3
+
+
+def test_single_matrix_lora_validation():
+    L = _lib.lib()
+    W, A, B, G = (_addr(0x10000000 + 0x1000000 * i) for i in range(4))
+    q = _addr(0x14000000)
+    need = L.qf_workspace_size(1, 3072, 3072, 1)
+    assert L.qf_lora_merge_tensor_scale_nvfp4(W, A, B, 3072, 3072, 16, q, q, need - 4, None) == 4
+    assert L.qf_lora_merge_tensor_scale_nvfp4(W, A, B, 3072, 3072, 17, q, q, need, None) == 7   # rank
+    assert L.qf_lora_merge_tensor_scale_nvfp4(W, A, B, 3072, 3000, 16, q, q, need, None) == 2   # cols % 32
+    assert L.qf_lora_merge_tensor_scale_nvfp4(None, A, B, 3072, 3072, 16, q, q, need, None) == 1
+    assert L.qf_lora_merge_qdq_pack_nvfp4(W, A, B, 3072, 3072, 16, q, None, None, None, None) == 1   # no output
+    assert L.qf_lora_merge_qdq_pack_nvfp4(W, A, B, 3072, 3072, 16, None, q, None, None, None) == 1   # no scale
+    assert L.qf_lora_merge_qdq_pack_nvfp4(W, A, B, 3072, 3072, 16, q, _addr(0x14000008), None, None, None) == 3
+    assert L.qf_lora_adapter_grads(G, A, B, 3072, 3072, 16, q, q, 0, q, need - 4, None) == 4
+    assert L.qf_lora_adapter_grads(G, A, B, 3072, 3072, 16, None, q, 0, q, need, None) == 1
+    assert L.qf_lora_adapter_grads(G, A, B, 0, 3072, 16, q, q, 0, q, need, None) == 0          # empty
+
+
+def test_workspace_size_bounds_every_layout():
+    """qf_workspace_size is at least what each concrete call asks for, over ragged shapes,
+    ranks and descriptor counts (the layout changes with the launch size)."""
+    L = _lib.lib()
+    assert L.qf_workspace_size(9, 10, 10, 1) == 0
+    assert L.qf_workspace_size(2, 256, 512, 64) == L.qf_linear_backward_workspace(256, 512, 64)
+    rng = __import__("numpy").random.default_rng(1)
+    for _ in range(200):
+        n = int(rng.integers(1, 17))
+        rows = int(rng.integers(1, 12000))
+        cols = 32 * int(rng.integers(1, 300))
+        d = (_lib.LoraDesc * n)()
+        for i in range(n):
+            d[i].rows = int(rng.integers(0, rows + 1))
+            d[i].cols = 32 * int(rng.integers(1, cols // 32 + 1))
+            d[i].ldw = d[i].cols
+            d[i].r = int(rng.integers(1, 17))
+            d[i].group = int(rng.integers(0, 64))
+        assert L.qf_lora_workspace(ctypes.byref(d), n) <= L.qf_workspace_size(1, rows, cols, n)
+        t = (_lib.TensorDesc * n)()
+        for i in range(n):
+            t[i].rows, t[i].cols = d[i].rows, 16 * int(rng.integers(1, cols // 16 + 1))
+            t[i].ldx, t[i].group = t[i].cols, int(rng.integers(0, 64))
+        assert L.qf_nvfp4_tensor_scale_workspace(ctypes.byref(t), n) <= L.qf_workspace_size(0, rows, cols, n)
+
+
+def _moe_descs(experts):
+    d = (_lib.LoraDesc * (2 * experts))()
+    for e in range(experts):
+        for j, (rows, cols) in enumerate(((3072, 3072), (3072, 1536))):
+            k = 2 * e + j
+            d[k].rows, d[k].cols, d[k].ldw, d[k].r, d[k].group = rows, cols, cols, 16, k
+    return d
+
+
+def test_lora_layout_of_the_moe_launches():
+    """The MoE share's launches: 8 experts per launch (16 matrices) take 32-row merge units
+    (1,728 workgroups) and 512-row gradient blocks; 2 experts take 16-row units; one expert
+    8-row units and 256-row gradient blocks."""
+    L = _lib.lib()
+    out = (ctypes.c_int32 * 4)()
+    assert L.qf_lora_layout(ctypes.byref(_moe_descs(8)), 16, out) == 0
+    assert tuple(out) == (32, 8 * (144 + 72), 512, 8 * (6 * 6 + 6 * 3))
+    assert L.qf_lora_layout(ctypes.byref(_moe_descs(2)), 4, out) == 0
+    assert tuple(out)[:2] == (16, 2 * (288 + 144))
+    assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, out) == 0
+    assert tuple(out) == (8, 576 + 288, 256, 12 * 6 + 12 * 3)
+    assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, None) == 1
+

@@ -40,16 +40,32 @@ def _check(got_bits, A_bits, B_bits, n, what):
     return rel
 
 
-@pytest.mark.parametrize("shape", [(64, 64), (200, 96), (8, 32), (520, 1056), (64, 8)])
-@pytest.mark.parametrize("qdq", [False, True])
-def test_transpose_bit_exact(shape, qdq):
+_TR_CASES = [(shape, mode) for shape in [(64, 64), (200, 96), (8, 32), (520, 1056), (64, 8)]
+             for mode in ("copy", "floor", "noclip") if mode == "copy" or shape[1] % 32 == 0]
+
+
+@pytest.mark.parametrize("shape,mode", _TR_CASES)
+def test_transpose_bit_exact(shape, mode):
     rows, cols = shape
-    if qdq and cols % 32:
-        pytest.skip("QDQ needs whole 32-blocks")
     x = _bits(RNG.standard_t(3, size=(rows, cols)) * 0.3)
-    y = host(fq.qf_transpose_bf16(dev(x), qdq_mxfp4=qdq))
-    want = (mxfp4.qdq(x) if qdq else x).T
+    rule = fq.QF_MX_RULE_NOCLIP if mode == "noclip" else fq.QF_MX_RULE_FLOOR
+    y = host(fq.qf_transpose_bf16(dev(x), qdq_mxfp4=mode != "copy", rule=rule))
+    want = (x if mode == "copy" else mxfp4.qdq(x, rule=mode)).T
     assert np.array_equal(y, want), first_mismatch(y, want)
+
+
+@pytest.mark.parametrize("rule", ["floor", "noclip"])
+def test_transpose_planted_maxima(rule):
+    """Block maxima at every decision of both exponent rules, up to the largest finite bf16
+    (which must not become Inf under noclip)."""
+    from tests import pins
+    b = pins.planted_mx_blocks()
+    b = np.ascontiguousarray(b[: b.shape[0] // 8 * 8])
+    r = fq.QF_MX_RULE_NOCLIP if rule == "noclip" else fq.QF_MX_RULE_FLOOR
+    y = host(fq.qf_transpose_bf16(dev(b), qdq_mxfp4=True, rule=r))
+    want = mxfp4.qdq(b, rule=rule).T
+    assert np.array_equal(y, want), first_mismatch(y, want)
+    assert not np.any((y & 0x7F80) == 0x7F80)
 
 
 def test_transpose_tallest_source():
@@ -73,15 +89,17 @@ def test_transpose_strided():
 
 
 @pytest.mark.parametrize("shape", [(64, 64, 32), (128, 192, 96), (320, 256, 160)])
-@pytest.mark.parametrize("flags", [3, 0, 1, 2])
+@pytest.mark.parametrize("flags", [3, 0, 1, 2, 11, 9, 10])
 def test_linear_backward_small(shape, flags):
+    """flags 8 | ...: QF_MX_NOCLIP, the backward of a forward run under the noclip rule."""
     M, N, K = shape
     X = _bits(RNG.standard_t(3, size=(M, K)) * 0.5)
     W = _bits(RNG.standard_normal((N, K)) * 0.02)
     dY = _bits(RNG.standard_normal((M, N)))
     dX, dW = fq.qf_linear_backward_mxfp4(dev(X), dev(W), dev(dY), flags=flags)
-    Xq = mxfp4.qdq(X) if flags & 1 else X
-    Wq = mxfp4.qdq(W) if flags & 2 else W
+    rule = "noclip" if flags & 8 else "floor"
+    Xq = mxfp4.qdq(X, rule=rule) if flags & 1 else X
+    Wq = mxfp4.qdq(W, rule=rule) if flags & 2 else W
     _check(host(dX), dY, np.ascontiguousarray(Wq.T), N, f"dX {shape} flags={flags}")
     _check(host(dW), np.ascontiguousarray(dY.T), np.ascontiguousarray(Xq.T), M, f"dW {shape} flags={flags}")
 

@@ -136,3 +136,38 @@ def test_forward_full_size():
     Xq_ref, Wq_ref = nvfp4.qdq(X[rows], sx_ref), nvfp4.qdq(W[cols], sw_ref)
     assert np.array_equal(host(Xq[ri]), Xq_ref) and np.array_equal(host(Wq[ci]), Wq_ref)
     assert _check(host(Y[ri][:, ci]), Xq_ref, Wq_ref, K, "full size nvfp4") < 2e-3
+
+
+def test_forward_nvfp4_tracked_activation_scale():
+    """NVFP4 W4A4 training steps with a tracked activation scale: each step's activations
+    update the running amax on the device (qf_nvfp4_tensor_scale_tracked), and the forward
+    quantizes X with the tracked scale.  State, scale, Xq and Y checked against the oracle
+    after every step; one step with an outlier raises the state, later smaller batches keep
+    it; the state is per group (two tied groups, Q/K/V-like activations tied)."""
+    M, N, K = 200, 160, 128
+    W = P.f32_to_bf16((RNG.standard_normal((N, K)) * 0.02).astype(np.float32))
+    Wd = dev(W)
+    sw = fq.qf_nvfp4_tensor_scale(Wd)
+    sw_ref = nvfp4.tensor_scale([W])
+    amax_d = torch.zeros(2, dtype=torch.float32, device="cuda")
+    amax_ref = [np.float32(0.0), np.float32(0.0)]
+    for step in range(5):
+        X = (RNG.standard_t(3, size=(M, K)) * 0.5).astype(np.float32)
+        if step == 1:
+            X[3, 7] = 900.0                                          # an outlier the state keeps
+        X = P.f32_to_bf16(X)
+        X2 = P.f32_to_bf16((RNG.standard_normal((64, K)) * (step + 1)).astype(np.float32))
+        Xd, X2d = dev(X), dev(X2)
+        sc = fq.qf_nvfp4_tensor_scale_tracked([dict(x=Xd, group=0), dict(x=X2d, group=1)], 2, amax_d)
+        s_ref = []
+        for g, t in ((0, X), (1, X2)):
+            amax_ref[g], s = nvfp4.tracked_scale(amax_ref[g], [t])
+            s_ref.append(s)
+        got_amax, got_s = amax_d.cpu().numpy(), sc.cpu().numpy()
+        assert np.array_equal(got_amax.view(np.uint32), np.array(amax_ref, np.float32).view(np.uint32)), step
+        assert np.array_equal(got_s.view(np.uint32), np.array(s_ref, np.float32).view(np.uint32)), step
+        Y, Xq, Wq = fq.qf_linear_forward_nvfp4(Xd, Wd, sc[0:1], sw, flags=3)
+        Xq_ref, Wq_ref = nvfp4.qdq(X, s_ref[0]), nvfp4.qdq(W, sw_ref)
+        assert np.array_equal(host(Xq), Xq_ref), f"step {step}: {first_mismatch(host(Xq), Xq_ref)}"
+        _check(host(Y), Xq_ref, Wq_ref, K, f"tracked step {step}")
+    assert amax_ref[0] == np.float32(900.0)

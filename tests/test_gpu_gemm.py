@@ -211,3 +211,27 @@ def test_gemm_mxfp4_noclip(shape, flags):
     Xq = mxfp4.qdq(X, rule="noclip") if flags & 1 else X
     Wq = mxfp4.qdq(W, rule="noclip") if flags & 2 else W
     _check(host(Y), Xq, Wq, K, f"noclip {shape} flags={flags}")
+
+
+def test_gemm_mxfp4_noclip_top_binade():
+    """W rows whose 32-blocks have maxima up to the largest finite bf16 (the planted maxima
+    of the noclip pins, two blocks per row), X scaled by 2^-120 so the products stay finite:
+    the fused noclip QDQ must cap the exponent at 252 as the oracle does (a block maximum in
+    [1.75, 2) * 2^127 would otherwise dequantize to 2^128 and turn the row into Inf)."""
+    from tests import pins
+    b = pins.planted_mx_blocks()
+    b = b[(b[:, 31] & 0x7F80) >= (191 << 7)]                 # maxima of 2^64 and above: no fp32 underflow
+    assert b.shape[0] >= 8 and np.any((b[:, 31] & 0x7FFF) == 0x7F7F)
+    b = np.ascontiguousarray(b[: b.shape[0] // 2 * 2].reshape(-1, 64))
+    N, K = b.shape
+    M = 96
+    X = P.f32_to_bf16((RNG.standard_t(3, size=(M, K)) * np.ldexp(1.0, -120)).astype(np.float32))
+    for flags in (2, 3):
+        Y = fq.qf_gemm_mxfp4(dev(X), dev(b), flags=flags | fq.QF_MX_NOCLIP)
+        Xq = mxfp4.qdq(X, rule="noclip") if flags & 1 else X
+        Wq = mxfp4.qdq(b, rule="noclip")
+        assert np.all(np.isfinite(P.bf16_to_f32(Wq)))
+        _check(host(Y), Xq, Wq, K, f"noclip top binade flags={flags}")
+        Y2, _, Wq_d = fq.qf_linear_forward_mxfp4(dev(X), dev(b), flags=flags | fq.QF_MX_NOCLIP)
+        assert np.array_equal(host(Wq_d), Wq)
+        assert np.array_equal(host(Y2), host(Y))

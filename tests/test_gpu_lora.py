@@ -80,8 +80,8 @@ def check_grads(c, dA, dB, what, extra_terms=0):
 
 
 def run_merge_quant(items, n_groups):
-    scales = fq.qf_lora_merge_tensor_scale_nvfp4(items, n_groups)
-    fq.qf_lora_qdq_pack_nvfp4(items, scales)
+    scales = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, n_groups)
+    fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, scales)
     torch.cuda.synchronize()
     return scales.cpu().numpy()
 
@@ -112,7 +112,7 @@ def test_lora_single_descriptor(rows, cols, r):
     it = device_item(c, 0)
     s = run_merge_quant([it], 1)
     check_merge_quant([c], [0], [it], s, 1)
-    fq.qf_lora_adapter_grads([it])
+    fq.qf_lora_adapter_grads_grouped([it])
     torch.cuda.synchronize()
     check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"{rows}x{cols} r{r}")
 
@@ -126,7 +126,7 @@ def test_lora_grouped_strided_and_large_adapters():
     items = [device_item(c, g, ldw_pad=(64 if i == 2 else 0)) for i, (c, g) in enumerate(zip(cases, groups))]
     s = run_merge_quant(items, 4)                                 # group 3 has no member: scale 1
     check_merge_quant(cases, groups, items, s, 4)
-    fq.qf_lora_adapter_grads(items)
+    fq.qf_lora_adapter_grads_grouped(items)
     torch.cuda.synchronize()
     for i, (c, it) in enumerate(zip(cases, items)):
         check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"desc {i}")
@@ -147,9 +147,9 @@ def test_lora_zero_adapter_is_identity():
 def test_lora_accumulate_adds():
     c = make_case(80, 544, 16, seed=9)
     it = device_item(c, 0)
-    fq.qf_lora_adapter_grads([it])
+    fq.qf_lora_adapter_grads_grouped([it])
     dA1, dB1 = it["dA"].clone(), it["dB"].clone()
-    fq.qf_lora_adapter_grads([it], accumulate=True)
+    fq.qf_lora_adapter_grads_grouped([it], accumulate=True)
     torch.cuda.synchronize()
     assert_same(f32bits(it["dA"].cpu().numpy()), f32bits((dA1 + dA1).cpu().numpy()), "dA accumulate")
     assert_same(f32bits(it["dB"].cpu().numpy()), f32bits((dB1 + dB1).cpu().numpy()), "dB accumulate")
@@ -177,7 +177,7 @@ def test_lora_full_size_expert():
         assert_same(host(it["y"])[rows_], nvfp4.dequantize(c, S, s_want[i]), f"y[{i}] sampled rows")
         assert_same(u8(it["codes"])[rows_], pc, f"codes[{i}] sampled rows")
         assert_same(u8(it["scales"])[rows_], ps, f"block scales[{i}] sampled rows")
-    fq.qf_lora_adapter_grads(items)
+    fq.qf_lora_adapter_grads_grouped(items)
     torch.cuda.synchronize()
     for i, (c, it) in enumerate(zip(cases, items)):
         check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"expert 3 matrix {i}")
@@ -238,7 +238,89 @@ def test_lora_grads_512_row_units():
     items = [device_item(c, i) for i, c in enumerate(cases)]
     b = fq.LoraBatch(items)
     assert b.workspace_bytes == 4 * (16 * 2 * 16 * 4096 + 16 * 8 * 600 * 16)   # 2 dA blocks per matrix
-    fq.qf_lora_adapter_grads(b)
+    fq.qf_lora_adapter_grads_grouped(b)
     torch.cuda.synchronize()
     for i, (c, it) in enumerate(zip(cases, items)):
         check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"desc {i}")
+
+
+# ------------------------------------------------ the MoE share's launch layouts ----
+_EXPERT_CACHE = {}
+
+
+def _expert_oracle(e):
+    """Host bits of expert e (both matrices), its merged weights and their tensor scales."""
+    if e not in _EXPERT_CACHE:
+        ex = workloads.moe_expert(e)
+        mats = []
+        for name in ("gate_up", "down"):
+            W, A, B, G = ex[name]
+            M = lora.merge(W, A, B)
+            mats.append(dict(W=W, A=A, B=B, G=G, M=M, s=nvfp4.tensor_scale([M])))
+        _EXPERT_CACHE[e] = mats
+    return _EXPERT_CACHE[e]
+
+
+@pytest.mark.parametrize("experts,merge_rows", [(8, 32), (2, 16)])
+@pytest.mark.parametrize("with_M", [True, False])
+def test_moe_launch_layout(experts, merge_rows, with_M):
+    """The layout the MoE step runs: `experts` full-size experts (gate/up 3072x3072 and
+    down 3072x1536, rank 16) per launch, one tied group per matrix (2 x experts groups),
+    with and without the merge scratch.  8 experts per launch is the benchmark's
+    layout (32-row merge units, 512-row gradient blocks); 2 experts take 16-row units.
+    Every tensor scale and every merged weight bit for bit; y, codes and block scales on
+    sampled rows of every matrix; dA and dB of every matrix within Higham's bound."""
+    ids = list(range(11, 11 + experts))
+    mats = [m for e in ids for m in _expert_oracle(e)]
+    items = []
+    for k, m in enumerate(mats):
+        c = dict(W=m["W"], A=m["A"], B=m["B"], G=m["G"])
+        items.append(device_item(c, k, with_M=with_M))
+    batch = fq.LoraBatch(items)
+    layout = fq.qf_lora_layout(batch)
+    assert layout[0] == merge_rows, layout
+    if experts == 8:
+        assert layout[2] == 512, layout
+    s = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(batch, len(items))
+    fq.qf_lora_merge_qdq_pack_nvfp4_grouped(batch, s)
+    torch.cuda.synchronize()
+    s = s.cpu().numpy()
+    assert_same(f32bits(s), f32bits([m["s"] for m in mats]), "tensor scales of all groups")
+    for k, (m, it) in enumerate(zip(mats, items)):
+        if with_M:
+            assert_same(host(it["M"]), m["M"], f"M[{k}]")
+        rows_ = sample_rows(m["M"].shape[0], 24, seed=100 + k)
+        c, S = nvfp4.quantize(m["M"][rows_], m["s"])
+        pc, ps = nvfp4.pack(c, S)
+        assert_same(host(it["y"])[rows_], nvfp4.dequantize(c, S, m["s"]), f"y[{k}] sampled rows")
+        assert_same(u8(it["codes"])[rows_], pc, f"codes[{k}] sampled rows")
+        assert_same(u8(it["scales"])[rows_], ps, f"block scales[{k}] sampled rows")
+    if with_M:
+        fq.qf_lora_adapter_grads_grouped(batch)
+        torch.cuda.synchronize()
+        for k, (m, it) in enumerate(zip(mats, items)):
+            check_grads(m, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"matrix {k}")
+
+
+def test_single_matrix_calls_equal_the_grouped_form():
+    """The single-matrix calls (merge in registers, no scratch) give the bits of a grouped
+    launch of one descriptor, for a full-size gate/up matrix and a ragged one."""
+    e = _expert_oracle(11)[0]
+    for c in (dict(W=e["W"], A=e["A"], B=e["B"], G=e["G"]), make_case(37, 544, 7, seed=3)):
+        Wd, Ad, Bd, Gd = dev(c["W"]), dev(c["A"]), dev(c["B"]), dev(c["G"])
+        s = fq.qf_lora_merge_tensor_scale_nvfp4(Wd, Ad, Bd)
+        y, codes, scales = fq.qf_lora_merge_qdq_pack_nvfp4(Wd, Ad, Bd, s)
+        dA, dB = fq.qf_lora_adapter_grads(Gd, Ad, Bd)
+        it = device_item(c, 0, with_M=False)
+        s2 = fq.qf_lora_merge_tensor_scale_nvfp4_grouped([it], 1)
+        fq.qf_lora_merge_qdq_pack_nvfp4_grouped([it], s2)
+        fq.qf_lora_adapter_grads_grouped([it])
+        torch.cuda.synchronize()
+        M = lora.merge(c["W"], c["A"], c["B"])
+        assert_same(f32bits(s.cpu().numpy()), f32bits([nvfp4.tensor_scale([M])]), "single tensor scale")
+        assert_same(f32bits(s.cpu().numpy()), f32bits(s2.cpu().numpy()), "single vs grouped scale")
+        assert torch.equal(y.view(torch.int16), it["y"].view(torch.int16))
+        assert torch.equal(codes, it["codes"]) and torch.equal(scales, it["scales"])
+        assert_same(f32bits(dA.cpu().numpy()), f32bits(it["dA"].cpu().numpy()), "dA")
+        assert_same(f32bits(dB.cpu().numpy()), f32bits(it["dB"].cpu().numpy()), "dB")
+        check_grads(c, dA.cpu().numpy(), dB.cpu().numpy(), "single-matrix grads")

@@ -229,6 +229,24 @@ def test_ste_ragged_lengths():
 
 
 # ------------------------------------------------------ tying / grouping ----
+def test_nvfp4_pointer_array_tensor_scale():
+    """qf_nvfp4_tensor_scale over a host array of pointers (Q, K, V as separate contiguous
+    tensors, one tied group) gives the fused matrix's scale; also with a single tensor, an
+    empty member, and a member whose length is a multiple of 16 but not of a row."""
+    q = _bits(RNG.standard_normal((512, 256)) * 0.02)
+    k = _bits(RNG.standard_normal((128, 256)) * 0.05)
+    v = _bits(RNG.standard_normal((128, 256)) * 0.01)
+    ts = [dev(t) for t in (q, k, v)]
+    got = fq.qf_nvfp4_tensor_scale(ts)
+    assert f32bits(got.cpu().numpy()[0]) == f32bits(nvfp4.tensor_scale([np.concatenate([q, k, v])]))
+    assert f32bits(fq.qf_nvfp4_tensor_scale(ts[1]).cpu().numpy()[0]) == f32bits(nvfp4.tensor_scale([k]))
+    flat = dev(q).reshape(-1)[: 16 * 1001]
+    empty = dev(q).reshape(-1)[:0]
+    got = fq.qf_nvfp4_tensor_scale([flat, empty, ts[2]])
+    want = nvfp4.tensor_scale([q.reshape(-1)[: 16 * 1001].reshape(1001, 16), v])
+    assert f32bits(got.cpu().numpy()[0]) == f32bits(want)
+
+
 def test_nvfp4_tied_qkv_equals_fused():
     q = _bits(RNG.standard_normal((512, 256)) * 0.02)
     k = _bits(RNG.standard_normal((128, 256)) * 0.05)
@@ -311,6 +329,31 @@ def test_q4k_set_full_size_sampled():
         y_ref, b_ref = oracle_q4k(W[rows])
         assert_same(host(outs[n][1])[rows], y_ref, f"{n} y")
         assert_same(u8(outs[n][2])[rows], b_ref, f"{n} blocks")
+
+
+def test_q4k_set_all_six_one_launch():
+    """The benchmark's Q4_K launch: all six tensors of the Q4_K set (256 x 512, QKV,
+    gate/up, down, O and the 151936 x 4096 vocabulary) in one grouped call, drawn on the
+    device with the same recipe; sampled rows of every tensor, copied to the host, against
+    the oracle bit for bit (y and 144-byte blocks)."""
+    tens = workloads.q4k_set_device()
+    names = list(tens)
+    assert len(names) == 6
+    items, outs = [], {}
+    for n in names:
+        Wd = tens[n]
+        r, c = Wd.shape
+        outs[n] = (torch.empty_like(Wd), torch.empty((r, c // 256, 144), dtype=torch.uint8, device="cuda"))
+        items.append(dict(x=Wd, y=outs[n][0], codes=outs[n][1]))
+    fq.qf_qdq_pack_q4k_grouped(items)
+    torch.cuda.synchronize()
+    for i, n in enumerate(names):
+        rows = sample_rows(tens[n].shape[0], 24, seed=40 + i)
+        ri = torch.from_numpy(rows).cuda()
+        W = host(tens[n][ri])
+        y_ref, b_ref = oracle_q4k(W)
+        assert_same(host(outs[n][0][ri]), y_ref, f"{n} y")
+        assert_same(u8(outs[n][1][ri]), b_ref, f"{n} blocks")
 
 
 def test_mxfp4_gemm_operands_full_size_sampled():

@@ -72,20 +72,48 @@ def test_mxfp4_workload(rule):
     same_bits(f32(acc), ste.ste_backward_clipped(g, mask, acc0, accumulate=True), f"mxfp4 acc {r}")
 
 
-@pytest.mark.parametrize("shape", [(37, 768), (5, 32), (1, 64), (300, 96)])
-def test_ragged_and_strided(shape):
+# (1, 384) and (3, 160) leave 48 and 60 chunks in the last wave: its second half of lanes
+# (4 elements each, two halves of 64 chunks per wave segment) is only partly filled
+@pytest.mark.parametrize("shape", [(37, 768), (5, 32), (1, 64), (300, 96), (1, 384), (3, 160)])
+@pytest.mark.parametrize("accumulate", [False, True])
+def test_ragged_and_strided(shape, accumulate):
     rows, cols = shape
     x = P.f32_to_bf16((RNG.standard_t(3, size=(rows, cols)) * 0.3).astype(np.float32))
     g = _g((rows, cols))
     xb = torch.zeros((rows, cols + 40), dtype=torch.bfloat16, device="cuda")
     xb[:, 24:24 + cols] = dev(x)
     xs = xb[:, 24:24 + cols]
-    got = f32(fq.qf_ste_backward_clipped_mxfp4(dev(g), xs))
-    same_bits(got, ste.ste_backward_clipped(g, mxfp4.saturated(x)), f"mxfp4 {shape}")
+    acc0 = RNG.standard_normal((rows, cols)).astype(np.float32)
+
+    def run(call, mask, what):
+        if accumulate:
+            out = torch.from_numpy(acc0.copy()).cuda()
+            call(out)
+            same_bits(f32(out), ste.ste_backward_clipped(g, mask, acc0, accumulate=True), what)
+        else:
+            same_bits(f32(call(None)), ste.ste_backward_clipped(g, mask), what)
+
+    for rule, r in ((fq.QF_MX_RULE_FLOOR, "floor"), (fq.QF_MX_RULE_NOCLIP, "noclip")):
+        run(lambda o: fq.qf_ste_backward_clipped_mxfp4(dev(g), xs, o, accumulate=accumulate, rule=rule),
+            mxfp4.saturated(x, r), f"mxfp4 {r} {shape} acc={accumulate}")
     s_t = nvfp4.tensor_scale([x])
     sd = torch.tensor([float(s_t)], dtype=torch.float32, device="cuda")
-    got = f32(fq.qf_ste_backward_clipped_nvfp4(dev(g), xs, sd))
-    same_bits(got, ste.ste_backward_clipped(g, nvfp4.saturated(x, s_t)), f"nvfp4 {shape}")
+    run(lambda o: fq.qf_ste_backward_clipped_nvfp4(dev(g), xs, sd, o, accumulate=accumulate),
+        nvfp4.saturated(x, s_t), f"nvfp4 {shape} acc={accumulate}")
+
+
+@pytest.mark.parametrize("rule", [fq.QF_MX_RULE_FLOOR, fq.QF_MX_RULE_NOCLIP])
+def test_mxfp4_top_binade(rule):
+    """Block maxima up to the largest finite bf16: under both rules the blocks in the top
+    binade take E = 252 and elements above 6 * 2^125 saturate (the mask is the oracle's)."""
+    from tests import pins
+    x = pins.planted_mx_blocks()
+    r = "noclip" if rule == fq.QF_MX_RULE_NOCLIP else "floor"
+    mask = mxfp4.saturated(x, r)
+    assert mask[x[:, 31] & 0x7FFF == 0x7F7F].any()
+    g = _g(x.shape)
+    same_bits(f32(fq.qf_ste_backward_clipped_mxfp4(dev(g), dev(x), rule=rule)), ste.ste_backward_clipped(g, mask),
+              f"mxfp4 {r} planted maxima")
 
 
 def test_empty():

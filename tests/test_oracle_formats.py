@@ -305,9 +305,10 @@ def test_mxfp4_noclip_rule_by_brute_force(single):
 
 
 def test_mxfp4_noclip_never_clips_and_is_minimal():
-    """Under noclip every |x| / X is at most 6 (no saturation), and one exponent lower
-    would put the block maximum above 6 unless E is already 0; E differs from the floor
-    rule exactly when the maximum's mantissa exceeds 1.5."""
+    """Under noclip every |x| / X is at most 6 (no saturation) unless the block maximum is
+    above 6 * 2^125, the top of the last grid bf16 can hold; one exponent lower would put
+    the block maximum above 6 unless E is already 0; E differs from the floor rule exactly
+    when the maximum's mantissa exceeds 1.5 and the floor rule's E is below 252."""
     b = pins.planted_mx_blocks()
     x = P.bf16_to_f32(b).astype(np.float64)
     a = np.abs(x).max(axis=-1)
@@ -315,11 +316,35 @@ def test_mxfp4_noclip_never_clips_and_is_minimal():
     _, Ef = mxfp4.quantize(b, rule="floor")
     E, Ef = E.astype(np.int64)[:, 0], Ef.astype(np.int64)[:, 0]
     X = np.ldexp(1.0, E - 127)
-    assert np.all(a / X <= 6.0)
+    top = a > np.ldexp(6.0, 125)
+    assert np.all((a / X <= 6.0) | top)
+    assert np.all(E[top] == 252) and top.sum() >= 2              # 0x7F7F and 1.75 * 2^127 are planted
     low = np.ldexp(6.0, E - 1 - 127)
     assert np.all((E == 0) | (a > low))
     mant = (b[:, 31] & 0x7F).astype(np.int64)
     normal = ((b[:, 31] >> 7) & 0xFF) >= 1
-    want = np.where(normal & (mant > 0x40) & (Ef + 1 <= 254) & (Ef > 0), Ef + 1, Ef)
+    want = np.where(normal & (mant > 0x40) & (Ef + 1 <= 252) & (Ef > 0), Ef + 1, Ef)
     ok = normal & (Ef > 0)                                    # above the clamp at E = 0
     assert np.array_equal(E[ok], want[ok])
+
+
+@pytest.mark.parametrize("rule", ["floor", "noclip"])
+def test_mxfp4_every_finite_input_stays_finite(rule):
+    """Every finite bf16 value, as the maximum of a block (the other elements a spread of
+    smaller values of both signs), gives finite QDQ'd values on the E2M1 grid of the block's
+    exponent; in particular the top binade [1.75, 2) * 2^127 must not round up to 2^128."""
+    allb = np.arange(0x10000, dtype=np.uint32).astype(np.uint16)
+    finite = allb[(allb & 0x7F80) != 0x7F80]
+    blocks = np.zeros((finite.size, 32), np.uint16)
+    blocks[:, 0] = finite
+    mag = finite & 0x7FFF
+    for j in range(1, 32):                                    # smaller magnitudes, alternating signs
+        blocks[:, j] = (mag >> (j % 8)) | (0x8000 if j % 2 else 0)
+    y = mxfp4.qdq(blocks, rule=rule)
+    assert not np.any((y & 0x7F80) == 0x7F80), "a finite input gave Inf or NaN"
+    codes, E = mxfp4.quantize(blocks, rule=rule)
+    grid = P.bf16_to_f32(y).astype(np.float64) / np.ldexp(1.0, E.astype(np.int64) - 127)
+    assert np.all(np.isin(np.abs(grid), pins.E2M1))
+    planted = np.array([[0x7F60] + [0x3F80] * 31, [0x7F7F] + [0xFF70] * 31, [0x7F70] * 32], np.uint16)
+    yp = P.bf16_to_f32(mxfp4.qdq(planted, rule=rule)).astype(np.float64)
+    assert np.all(np.isfinite(yp)) and np.abs(yp).max() == np.ldexp(6.0, 125)

@@ -4,7 +4,9 @@ import math
 
 import numpy as np
 
-from oracle import gemm, lora, ste
+import torch
+
+from oracle import gemm, lora, nvfp4, ste
 from oracle import primitives as P
 from oracle import mxfp4
 from tests import pins
@@ -98,3 +100,31 @@ def test_gemm_reference_against_fsum_and_bound():
     bound = gemm.elementwise_bound(Y, gemm.abs_dot(Xq, Wq), 96)
     assert np.all(np.abs(y - Y) <= bound)
     assert gemm.gamma(4096) < 2.45e-4
+
+
+def test_tracked_scale_is_the_scale_of_all_batches_seen():
+    """The tracked NVFP4 activation scale after any number of batches is the tensor scale of
+    all those batches taken together (a max over their union, from torch's amax of the
+    float values), in any order of the batches; a zero state with a zero batch gives 1."""
+    rng = np.random.default_rng(17)
+    batches = []
+    for i in range(6):
+        x = (rng.standard_t(3, size=(64, 128)) * (0.5 if i != 3 else 4.0)).astype(np.float32)
+        batches.append(P.f32_to_bf16(x))
+    for order in (range(6), [5, 2, 0, 4, 1, 3]):
+        amax = np.float32(0.0)
+        seen = []
+        for i in order:
+            amax, s_t = nvfp4.tracked_scale(amax, [batches[i]])
+            seen.append(batches[i])
+            union = torch.from_numpy(P.bf16_to_f32(np.concatenate(seen)))
+            want_amax = np.float32(union.abs().max().item())
+            assert amax == want_amax
+            assert s_t == np.float32(np.float64(want_amax) / 2688.0)      # one rounding of A / 2688
+        assert amax == np.float32(max(np.abs(P.bf16_to_f32(b)).max() for b in batches))
+    z = np.zeros((4, 16), np.uint16)
+    assert nvfp4.tracked_scale(np.float32(0.0), [z]) == (np.float32(0.0), np.float32(1.0))
+    # a batch below the state leaves it unchanged
+    big = np.float32(np.abs(P.bf16_to_f32(batches[3])).max() * 2)
+    amax, s_t = nvfp4.tracked_scale(big, [batches[0]])
+    assert amax == big and s_t == np.float32(np.float64(big) / 2688.0)

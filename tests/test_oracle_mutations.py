@@ -149,3 +149,47 @@ def test_mutation_lora_descending_order_is_caught(monkeypatch):
     except AssertionError:
         return
     raise AssertionError("descending merge order was not caught")
+
+
+def test_mutation_noclip_uncapped_exponent_is_caught(monkeypatch):
+    """The noclip rule clamped at E = 254 instead of 252 sends block maxima in
+    [1.75, 2) * 2^127 to 2^128 (Inf); the brute-force exponent pin notices it."""
+    monkeypatch.setattr(mxfp4, "NOCLIP_E_MAX", 254)
+    assert pins.check_mxfp4_noclip(pins.planted_mx_blocks()) > 0
+
+
+def test_mutation_q4k_mse_index_order_is_caught(monkeypatch):
+    """The mse rule's scores summed over all 32 elements in index order instead of the stated
+    tree: the planted near ties decide differently, and their pin fails."""
+    F = np.float32
+
+    def index_order(x, mn, mx):
+        base = ((mx - mn).astype(F) / F(15.0)).astype(F)
+        t = (x - mn[..., None]).astype(F)
+        errs, scales = [], []
+        for k in range(q4k.MSE_CANDIDATES):
+            s = (base * F(1.0 - k / 16.0)).astype(F)
+            zero = s == 0
+            with np.errstate(divide="ignore"):
+                r = np.where(zero, F(0.0), F(1.0) / np.where(zero, F(1.0), s)).astype(F)
+            q = np.clip(P.rint((t * r[..., None]).astype(F)), 0, 15).astype(F)
+            e = (((q * s[..., None]).astype(F) + mn[..., None]).astype(F) - x).astype(F)
+            sq = (e * e).astype(F)
+            acc = sq[..., 0]
+            for i in range(1, sq.shape[-1]):
+                acc = (acc + sq[..., i]).astype(F)
+            errs.append(acc)
+            scales.append(s)
+        err = np.stack(errs, -1)
+        best = np.argmin(err, -1)
+        scale = np.take_along_axis(np.stack(scales, -1), best[..., None], -1)[..., 0]
+        return scale.astype(F), err, best
+
+    from tests.test_oracle_q4k_mse import test_near_ties_follow_the_stated_order
+    test_near_ties_follow_the_stated_order()
+    monkeypatch.setattr(q4k, "mse_scale", index_order)
+    try:
+        test_near_ties_follow_the_stated_order()
+    except AssertionError:
+        return
+    raise AssertionError("the index summation order was not caught")
