@@ -112,6 +112,8 @@ SIGNATURES = {
                                               c_void_p]),
     "qf_linear_forward_mxfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64,
                                         ctypes.c_uint, c_void_p, c_i64, c_void_p, c_i64, c_void_p]),
+    "qf_noalloc_scratch_bytes": (c_size_t, []),
+    "qf_nvfp4_tensor_scale_grouped_noalloc": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]),
     "qf_write_safetensors": (c_int, [ctypes.c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_int]),
     "qf_write_gguf": (c_int, [ctypes.c_char_p, c_void_p, c_int, c_void_p, c_void_p, c_int]),
     "qf_linear_forward_nvfp4": (c_int, [c_void_p, c_i64, c_void_p, c_i64, c_void_p, c_i64, c_i64, c_i64, c_i64,

@@ -514,6 +514,22 @@ qf_status qf_linear_backward_mxfp4(const uint16_t* X, int64_t ldx, const uint16_
                                    uint16_t* dW, int64_t lddw, int64_t M, int64_t N, int64_t K,
                                    unsigned flags, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------- no-allocation variant ---- */
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): qf_nvfp4_tensor_scale_grouped with
+ * its amax partials in a fixed array the library keeps on each GPU (allocated with the
+ * code object, held until the process ends) instead of a caller workspace.  Same
+ * arguments, checks, kernels and bits as qf_nvfp4_tensor_scale_grouped.  Limit: the call's
+ * workspace need (qf_nvfp4_tensor_scale_workspace(d, n)) must not exceed
+ * qf_noalloc_scratch_bytes() = 128 KiB, i.e. at most 16 groups with a tensor (group
+ * indices below 16) for large launches, else QF_ERR_WORKSPACE before anything runs.  The
+ * call allocates nothing; its first call on a device looks up that device's array.  Calls
+ * on one GPU share the array: calls that overlap on the same GPU (different streams, or
+ * host threads) race and must be serialized by the caller. */
+size_t qf_noalloc_scratch_bytes(void);
+qf_status qf_nvfp4_tensor_scale_grouped_noalloc(const qf_tensor_desc* d, int n, int n_groups, float* d_scales,
+                                                uint32_t* d_nonfinite, void* stream);
+
 /* ------------------------------------------------ checkpoint containers ---- */
 /* "Method", "Export" on the project page: NVFP4 / MXFP4 checkpoints go to vLLM in the
  * compressed-tensors layout and Q4_K to llama.cpp as GGUF, so that the engine loads the

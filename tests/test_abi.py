@@ -392,3 +392,17 @@ def test_lora_layout_of_the_moe_launches():
     assert tuple(out) == (8, 576 + 288, 256, 12 * 6 + 12 * 3)
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, None) == 1
 
+
+def test_noalloc_tensor_scale_refuses_before_any_hip_call():
+    """The no-allocation variant checks its arguments and that its partials fit the fixed
+    array (16 groups of the persistent grid) before touching the GPU."""
+    L = _lib.lib()
+    q = _addr(0x10100000)
+    d = (_lib.TensorDesc * 1)()
+    d[0].x, d[0].rows, d[0].cols, d[0].ldx, d[0].group = 0x10000000, 4096, 4096, 4096, 63
+    assert L.qf_noalloc_scratch_bytes() == 4 * 2048 * 16
+    assert L.qf_nvfp4_tensor_scale_grouped_noalloc(ctypes.byref(d), 1, 64, q, None, None) == 4   # 64 x 2048 partials
+    assert L.qf_nvfp4_tensor_scale_grouped_noalloc(ctypes.byref(d), 1, 63, q, None, None) == 7   # group 63 >= 63
+    assert L.qf_nvfp4_tensor_scale_grouped_noalloc(ctypes.byref(d), 1, 64, None, None, None) == 1
+    d[0].x = 0x10000002
+    assert L.qf_nvfp4_tensor_scale_grouped_noalloc(ctypes.byref(d), 1, 64, q, None, None) == 3
