@@ -114,6 +114,28 @@ def pmc_summary(fetch_dir, write_dir, workload):
     print(json.dumps(data, indent=1, sort_keys=True))
 
 
+def counter_summary(folders):
+    """Markdown table: per kernel, the number of dispatches and the average of every counter
+    (summed over the counter's hardware instances within a dispatch)."""
+    per = {}
+    for folder in folders:
+        for r in _counter_rows(folder):
+            k = r["Kernel_Name"]
+            key = (r["Dispatch_Id"], k, r["Counter_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    table = {}
+    for (d, k, c), v in per.items():
+        table.setdefault(k, {}).setdefault(c, []).append(v)
+    counters = sorted({c for v in table.values() for c in v})
+    print("| kernel | dispatches | " + " | ".join(counters) + " |")
+    print("|---" * (len(counters) + 2) + "|")
+    for k in sorted(table):
+        row = table[k]
+        n = max(len(v) for v in row.values())
+        cells = [f"{sum(row[c]) / len(row[c]):.4g}" if c in row else "" for c in counters]
+        print(f"| `{k[:90]}` | {n} | " + " | ".join(cells) + " |")
+
+
 # ------------------------------------------------------------ workloads ----
 def _no_mark(kernel, edge):
     pass
@@ -296,6 +318,28 @@ class SteClippedDense:
             fq.qf_ste_backward_clipped_mxfp4(m["g"], m["x"], m["out"])
         t("ste_clipped_mxfp4", 1)
 
+    def cpu_baseline(self, budget_s=6.0):
+        """The oracle's saturation masks and clipped STE (NVFP4 and MXFP4) on the first rows
+        of the 4096x4096 O projection."""
+        import workloads
+        from oracle import mxfp4, nvfp4, ste
+        W, G = workloads.dense_layer_8b(names=["o"])["o"]
+        s_t = nvfp4.tensor_scale([W])
+
+        def run(r):
+            t0 = time.perf_counter()
+            ste.ste_backward_clipped(G[:r], nvfp4.saturated(W[:r], s_t))
+            ste.ste_backward_clipped(G[:r], mxfp4.saturated(W[:r]))
+            return time.perf_counter() - t0
+
+        dt = run(64)
+        r = max(64, min(W.shape[0], int(64 * budget_s / max(dt, 1e-3))))
+        dt = run(r)
+        nb = 2 * r * W.shape[1] * 8.0
+        return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the oracle's clipped STE under both FP4 masks on the first {r} rows of the 4096x4096 "
+                          f"O projection ({dt:.1f} s, numpy, 1 thread)"}
+
 
 class Q4KSetMSE(Q4KSet):
     """The Q4_K set under the mse sub-block scale rule (8 candidate scales per sub-block,
@@ -422,6 +466,29 @@ class MXFP4Operands:
         self.fq.qf_qdq_pack_mxfp4_grouped(self.items)
         t("mxfp4_qdq_pack", 1)
 
+    rule = "floor"
+
+    def cpu_baseline(self, budget_s=6.0):
+        """The oracle's MXFP4 QDQ + pack on the first rows of the activations X (host-drawn
+        with the same recipe)."""
+        import workloads
+        from oracle import mxfp4
+        X = workloads.w4a4_gemm(M=4096)["X"]
+
+        def run(r):
+            t0 = time.perf_counter()
+            c, E = mxfp4.quantize(X[:r], self.rule)
+            mxfp4.dequantize(c, E), mxfp4.pack(c, E)
+            return time.perf_counter() - t0
+
+        dt = run(64)
+        r = max(64, min(X.shape[0], int(64 * budget_s / max(dt, 1e-3))))
+        dt = run(r)
+        nb = r * X.shape[1] * (2 + 2 + 0.5 + 1 / 32)
+        return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+                "sample": f"the oracle's MXFP4 QDQ + pack ({self.rule} rule) on the first {r} rows of X "
+                          f"({dt:.1f} s, numpy, 1 thread)"}
+
 
 class MXFP4OperandsNoclip(MXFP4Operands):
     """The same operands under the noclip shared-exponent rule (the block maximum is never
@@ -431,7 +498,9 @@ class MXFP4OperandsNoclip(MXFP4Operands):
     def __init__(self, torch, fq):
         super().__init__(torch, fq)
         self.kernels = {"mxfp4_qdq_pack_noclip": self.kernels["mxfp4_qdq_pack"]}
-        self.config = dict(self.config, workload=self.name, rule="noclip (E = ceil(log2(amax / 6)))")
+        self.config = dict(self.config, workload=self.name, rule="noclip (E = ceil(log2(amax / 6)), at most 252)")
+
+    rule = "noclip"
 
     def step(self, mark=None):
         t = mark or _no_mark
@@ -493,32 +562,33 @@ class Single256x512:
     def controls(self, reps=500):
         """The same step captured once in a HIP graph and replayed: the GPU-side time of its
         six launches without the per-call host overhead."""
-        torch = self.torch
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            self.step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            self.step()
-        for _ in range(10):
-            graph.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            graph.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1000.0 / reps
-        return {"graph_replay": {"us_per_step": round(us, 2), "replays": reps,
-                                 "GB/s": round(self.bytes_per_step / us / 1e3, 1)}}
+        return {"graph_replay": graph_replay(self.torch, self.step, reps, self.bytes_per_step)}
+
+    def cpu_baseline(self, budget_s=5.0):
+        """The oracle's whole step (NVFP4 tensor scale, QDQ + pack of all three formats, STE)
+        on the 256x512 matrix, repeated for about budget_s."""
+        import workloads
+        from oracle import mxfp4, nvfp4, q4k, ste
+        w = workloads.single_256x512()
+        W, G = w["W"], w["G"]
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < budget_s or reps == 0:
+            s_t = nvfp4.tensor_scale([W])
+            c, S = nvfp4.quantize(W, s_t)
+            nvfp4.dequantize(c, S, s_t), nvfp4.pack(c, S)
+            c, E = mxfp4.quantize(W)
+            mxfp4.dequantize(c, E), mxfp4.pack(c, E)
+            p = q4k.quantize(W)
+            q4k.dequantize(p), q4k.pack(p)
+            ste.ste_backward(G)
+            reps += 1
+        dt = (time.perf_counter() - t0) / reps
+        return {"value": round(dt * 1e6, 1), "unit": "us per step", "cores": 1, "kind": "oracle",
+                "GB/s": self.bytes_per_step / dt / 1e9,
+                "sample": f"the oracle's whole step on the 256x512 matrix, {reps} repetitions (numpy, 1 thread)"}
 
 
 MFMA_BF16_PEAK_TFS = 2516.6     # 256 CUs x 4096 bf16 flop/clk x 2.4 GHz (dense)
-MFMA_FP4_PEAK_TFS = 10100.0     # MI355X dense MXFP4 matrix throughput
 
 
 class W4A4GemmMXFP4:
@@ -562,21 +632,43 @@ class W4A4GemmMXFP4:
         fq.qf_gemm_mxfp4(self.Xq, self.Wq, self.Y, flags=0)
         mark("gemm_bf16_on_qdq_operands", 1)
 
+    def cpu_baseline(self, budget_s=8.0):
+        """The oracle's path on a sample: MXFP4 QDQ of the first r rows of X and of W, then
+        the float64 BLAS reference product of those rows with the first c rows of W (host-
+        drawn with the same recipe); TFLOP/s over 2 r c K of the product and the QDQ time."""
+        import os as _os
+        import threadpoolctl
+        import workloads
+        from oracle import gemm, mxfp4
+        g = workloads.w4a4_gemm(M=2048, N=2048)
+        X, W = g["X"], g["W"]
+        K = X.shape[1]
+
+        def run(r):
+            t0 = time.perf_counter()
+            Xq, Wq = mxfp4.qdq(X[:r]), mxfp4.qdq(W[:r])
+            gemm.reference(Xq, Wq)
+            return time.perf_counter() - t0
+
+        dt = run(128)
+        r = max(128, min(X.shape[0], int(128 * (budget_s / max(dt, 1e-3)) ** 0.5)))
+        dt = run(r)
+        blas = [i.get("num_threads") for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        return {"value": 2.0 * r * r * K / dt / 1e12, "unit": "TFLOP/s", "cores": blas[0] if blas else None,
+                "kind": "oracle", "host_cores": len(_os.sched_getaffinity(0)),
+                "sample": f"the oracle's MXFP4 QDQ of {r} rows of X and of W, then the float64 BLAS reference "
+                          f"product {r}x{r}x{K} ({dt:.1f} s; numpy, {blas[0] if blas else '?'} BLAS threads)"}
+
     def controls(self, reps=10):
         """ms of: the fused kernel (QDQ inside the GEMM); the same kernel on the raw operands
         (flags = 0); the same forward under the MXFP4 noclip rule, in two passes and fused; torch.matmul
         (hipBLASLt) on the raw and on the QDQ'd operands; the NVFP4 W4A4 product,
         fused and in two passes (tensor scales of X and W included in the two-pass time and
         timed on their own); the layer's backward (dX = dY . Wq and dW = dY^T . Xq with
-        their three transposes; TFLOP/s over both products); the same MXFP4 W4A4 product on
-        the MXFP4 matrix cores: both operands quantized in the kernel, W pre-packed with X
-        quantized in the kernel, both pre-packed (the packs timed on their own), and both
-        packs followed by the packed GEMM."""
+        their three transposes; TFLOP/s over both products)."""
         torch = self.torch
         fq = self.fq
         out = {}
-        Wc, Ws = fq.qf_pack_mxfp4(self.W)
-        Xc, Xs = fq.qf_pack_mxfp4(self.X)
         sx, sw = fq.qf_nvfp4_tensor_scale(self.X), fq.qf_nvfp4_tensor_scale(self.W)
         # backward of the quantized linear: an N(0,1) upstream gradient of Y's shape
         gen = torch.Generator(device="cuda").manual_seed(11)
@@ -593,10 +685,6 @@ class W4A4GemmMXFP4:
             fq.qf_nvfp4_tensor_scale(self.W, sw)
             fq.qf_linear_forward_nvfp4(self.X, self.W, sx, sw, self.Y, Xq=Xq_nv, Wq=Wq_nv)
 
-        def fp4_cores_pack_then_gemm():
-            fq.qf_pack_mxfp4(self.X, Xc, Xs)
-            fq.qf_pack_mxfp4(self.W, Wc, Ws)
-            fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)
         noclip = fq.QF_QDQ_A | fq.QF_QDQ_W | fq.QF_MX_NOCLIP
         for name, fn in (("w4a4_mxfp4_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=3)),
                          ("w4a4_mxfp4_noclip_two_pass",
@@ -611,13 +699,8 @@ class W4A4GemmMXFP4:
                          ("backward_dx_dw_mxfp4", lambda: fq.qf_linear_backward_mxfp4(self.X, self.W, dY, dX, dW,
                                                                                         ws=bws)),
                          ("torch_matmul_hipblaslt", lambda: torch.matmul(self.X, self.W.t(), out=self.Y)),
-                         ("torch_matmul_hipblaslt_qdq_operands", lambda: torch.matmul(Xq, Wq.t(), out=self.Y)),
-                         ("w4a4_fp4_cores_fused", lambda: fq.qf_gemm_mxfp4(self.X, self.W, self.Y, flags=7)),
-                         ("w4a4_fp4_cores_packed_w", lambda: fq.qf_gemm_mxfp4_packed_w(self.X, Wc, Ws, self.Y)),
-                         ("w4a4_fp4_cores_both_packed", lambda: fq.qf_gemm_mxfp4_packed(Xc, Xs, Wc, Ws, self.Y)),
-                         ("w4a4_fp4_cores_pack_then_gemm", fp4_cores_pack_then_gemm),
-                         ("pack_w_mxfp4", lambda: fq.qf_pack_mxfp4(self.W, Wc, Ws)),
-                         ("pack_x_mxfp4", lambda: fq.qf_pack_mxfp4(self.X, Xc, Xs))):
+                         ("torch_matmul_hipblaslt_qdq_operands", lambda: torch.matmul(Xq, Wq.t(), out=self.Y))):
+
             for _ in range(3):
                 fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -628,33 +711,36 @@ class W4A4GemmMXFP4:
             e1.record()
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / reps
-            if name.startswith(("pack_", "tensor_scales")):
+            if name.startswith("tensor_scales"):
                 out[name] = {"ms": round(ms, 4)}
                 continue
             flop = 2 * self.flop if name.startswith("backward") else self.flop   # dX and dW: two products
             tf = flop / ms / 1e9
             out[name] = {"ms": round(ms, 4), "TFLOP/s": round(tf, 1), "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4)}
-            if "fp4_cores" in name:
-                out[name]["frac_mfma_fp4"] = round(tf / MFMA_FP4_PEAK_TFS, 4)
         return out
 
 
 class MoELoRANVFP4:
     """MoE layer share with LoRA: 128 experts, each with a fused gate/up 3072x3072 and a
     down 3072x1536 bf16 base weight and rank-16 adapters.  Per expert, in expert order:
-      1. merge M = W + B.A into a bounded scratch and the NVFP4 tensor scale of each
-         fused matrix (one tied group per expert per matrix),
-      2. NVFP4 QDQ + pack of M (QDQ'd bf16 into scratch; packed codes and E4M3 block
-         scales of every expert are kept),
-      3. the adapter gradients dA = B^T.G, dB = G.A^T from the upstream gradient G of
-         the QDQ'd weight (identity STE).
-    `experts_per_launch` experts share one launch of each call; the scratch holds that
-    many experts' merged and QDQ'd weights.  With merge_scratch=False there is no merged
-    weight in memory: step 1 only takes its maximum and step 2 merges again in registers
-    before the QDQ (same bits; W is read twice instead of M being written and read)."""
+      1. merge M = W + B.A and take the NVFP4 tensor scale of each fused matrix (one tied
+         group per expert per matrix),
+      2. merge again and NVFP4 QDQ + pack (the QDQ'd bf16 into a bounded scratch that holds
+         the experts of one launch; packed codes and E4M3 block scales of every expert
+         are kept),
+      3. the adapter gradients dA = B^T.G, dB = G.A^T from the upstream gradient G of the
+         QDQ'd weight (identity STE).
+    `experts_per_launch` experts share one launch of each call.  With merge_scratch=True
+    step 1 also stores M in a scratch of the launch's experts and step 2 quantizes M from
+    there (same bits; M is written and read once more, W read once less).
+    Algorithmic bytes are the method's minimum, 8.5625 per element: W read by each pass
+    (2 + 2), the QDQ'd bf16 (2), codes and block scales (0.5625) and G (2) (the adapters
+    and their gradients, 0.02 G elements, are not counted).  The scratch form's extra
+    traffic (the M write, 2 bytes per element, less nothing: M's read replaces W's) is
+    reported next to it, not in the figure."""
     name = "moe_lora_nvfp4"
 
-    def __init__(self, torch, fq, experts_per_launch=1, merge_scratch=True):
+    def __init__(self, torch, fq, experts_per_launch=1, merge_scratch=False):
         import workloads
         self.torch, self.fq = torch, fq
         mo = workloads.MOE
@@ -690,23 +776,18 @@ class MoELoRANVFP4:
             self.chunks.append((fq.LoraBatch(items), self.tscale[2 * c0: 2 * (c0 + k)]))
         self.ws = torch.empty(self.chunks[0][0].workspace_bytes, dtype=torch.uint8, device=dev)
         n = sum(x[m]["W"].numel() for m in mats)
-        adapters = sum(x[m]["A"].numel() + x[m]["B"].numel() for m in mats)
         self.numel = n
-        # algorithmic bytes: pass 1 reads W and the adapters, writes the merged bf16 weight
-        # to scratch; pass 2 reads it back, writes the QDQ'd bf16 + E2M1 codes (0.5 B) + E4M3
-        # scales (1/16 B); the gradients read G and the adapters and write fp32 dA, dB.
-        # Without the merge scratch, pass 1 writes nothing and pass 2 reads W and the
-        # adapters instead of M.
-        self.kernels = {
-            "lora_merge_amax": n * (4 if merge_scratch else 2) + adapters * 2,
-            "lora_qdq_pack": n * (2 + 2 + 0.5 + 1 / 16) + (0 if merge_scratch else adapters * 2),
-            "lora_adapter_grads": n * 2 + adapters * (2 + 4),
-        }
+        self.kernels = {"lora_merge_amax": 2.0 * n, "lora_merge_qdq_pack": (2 + 2 + 0.5 + 1 / 16) * n,
+                        "lora_adapter_grads": 2.0 * n}
         self.bytes_per_step = sum(self.kernels.values())
+        layout = fq.qf_lora_layout(self.chunks[0][0])
         self.config = {"workload": self.name,
                        "experts": E, "matrices_per_expert": {m: list(x[m]["W"].shape[1:]) for m in mats},
                        "rank": r, "elements": n, "experts_per_launch": k,
                        "merge_scratch": merge_scratch,
+                       "bytes_per_element": 8.5625,
+                       "extra_traffic_bytes": int(2 * n) if merge_scratch else 0,
+                       "merge_rows_per_unit": layout[0], "gradient_rows_per_workgroup": layout[2],
                        "scratch_bytes": sum(t.numel() * 2 for p in scratch.values() for t in p if t is not None),
                        "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale per expert per fused matrix)"}
 
@@ -717,14 +798,19 @@ class MoELoRANVFP4:
             t("lora_merge_amax", 0)
             fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
             t("lora_merge_amax", 1)
-            t("lora_qdq_pack", 0)
+            t("lora_merge_qdq_pack", 0)
             fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
-            t("lora_qdq_pack", 1)
+            t("lora_merge_qdq_pack", 1)
             t("lora_adapter_grads", 0)
             fq.qf_lora_adapter_grads_grouped(items, ws=ws)
             t("lora_adapter_grads", 1)
 
-    def cpu_baseline(self, budget_s=15.0):
+    def controls(self, reps=20):
+        """The whole 128-expert step captured once as a HIP graph and replayed (the launch
+        overhead of the many small launches of the one-expert-per-launch reading)."""
+        return {"graph_replay": graph_replay(self.torch, self.step, reps, self.bytes_per_step)}
+
+    def cpu_baseline(self, budget_s=8.0):
         """The oracle's merge + tensor scale + NVFP4 QDQ + pack + adapter gradients on the first
         rows of expert 0's two matrices (host-drawn with the same recipe)."""
         import workloads
@@ -742,7 +828,7 @@ class MoELoRANVFP4:
                 nvfp4.dequantize(c, S, s_t)
                 nvfp4.pack(c, S)
                 lora.adapter_grads(G[:rows], A, B[:rows])
-                nb += M.size * (4 + 4.5625 + 2)
+                nb += M.size * 8.5625
             return time.perf_counter() - t0, nb
 
         dt, _ = run(16)
@@ -750,37 +836,81 @@ class MoELoRANVFP4:
         dt, nb = run(rows)
         return {"value": nb / dt / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
                 "sample": f"the oracle's merge + tensor scale + QDQ + pack + adapter gradients on the first {rows} "
-                          f"rows of expert 0's gate/up and down matrices ({dt:.1f} s, numpy)"}
+                          f"rows of expert 0's gate/up and down matrices ({dt:.1f} s, numpy, 1 thread)"}
 
 
 class MoELoRANVFP4x8(MoELoRANVFP4):
-    """The same step with 8 experts per launch (scratch of 8 experts)."""
+    """The same step with 8 experts per launch (the QDQ'd scratch of 8 experts, no merge
+    scratch): the MoE share's figure."""
     name = "moe_lora_nvfp4_x8"
 
     def __init__(self, torch, fq):
         super().__init__(torch, fq, experts_per_launch=8)
 
+    def controls(self, reps=20):
+        return {}
 
-class MoELoRANVFP4x8Remerge(MoELoRANVFP4):
-    """8 experts per launch without the merged-weight scratch: the QDQ pass merges again."""
-    name = "moe_lora_nvfp4_x8_remerge"
+
+class MoELoRANVFP4x8Scratch(MoELoRANVFP4):
+    """8 experts per launch with the merged weights kept in a scratch between the passes."""
+    name = "moe_lora_nvfp4_x8_scratch"
 
     def __init__(self, torch, fq):
-        super().__init__(torch, fq, experts_per_launch=8, merge_scratch=False)
+        super().__init__(torch, fq, experts_per_launch=8, merge_scratch=True)
+
+    def controls(self, reps=20):
+        return {}
+
+
+def graph_replay(torch, step, reps, nbytes):
+    """us per step of `step` captured once in a HIP graph (on a side stream) and replayed."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
+    del graph
+    return {"us_per_step": round(us, 2), "replays": reps, "GB/s": round(nbytes / us / 1e3, 1)}
 
 
 WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, MXFP4OperandsNoclip, Single256x512,
                                  W4A4GemmMXFP4,
-                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Remerge, DequantDense,
+                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Scratch, DequantDense,
                                  SteClippedDense, Q4KSetMSE)}
 # measured next to the headline workload in a default run (fewer steps each)
-SECONDARY = [MXFP4Operands.name, MXFP4OperandsNoclip.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name, MoELoRANVFP4.name,
-             MoELoRANVFP4x8.name, MoELoRANVFP4x8Remerge.name, DequantDense.name, SteClippedDense.name,
-             Q4KSetMSE.name]
+SECONDARY = [MXFP4Operands.name, MXFP4OperandsNoclip.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name,
+             MoELoRANVFP4x8.name, MoELoRANVFP4.name, MoELoRANVFP4x8Scratch.name, DequantDense.name,
+             SteClippedDense.name, Q4KSetMSE.name]
 
 
-def measure(torch, wl, steps, warmup):
-    """(ms per step over `steps` back-to-back steps, per-kernel dict from a second, event-bracketed pass)."""
+FLUSH_BYTES = 512 << 20      # an untimed write of this size before each flushed iteration
+FLUSH_ITERS = 20
+
+
+def measure(torch, wl, steps, warmup, flush_iters=FLUSH_ITERS):
+    """(ms per step over `steps` back-to-back steps, per-kernel dict, flushed dict).
+
+    Per-kernel durations come from a second pass of `steps` steps with a HIP event pair
+    around every launch (events add a few microseconds between kernels, so they stay out
+    of the headline loop); the events sit on torch's current stream, where the library
+    launches.  The flushed figures time `flush_iters` further steps one at a time, each
+    after an untimed 512 MiB device write that evicts the 256 MB memory-side cache, and
+    report the median and the minimum (per step, and per kernel from a second such pass
+    with the per-launch events)."""
     for _ in range(warmup):
         wl.step()
     torch.cuda.synchronize()
@@ -789,9 +919,6 @@ def measure(torch, wl, steps, warmup):
         wl.step()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / steps
-    # per-kernel durations: the same steps again with a HIP event pair around every launch
-    # (events add a few microseconds between kernels, so they stay out of the headline
-    # loop); the events sit on torch's current stream, where the library launches
     pairs = {k: [] for k in wl.kernels}
 
     def mark(kernel, edge):
@@ -808,7 +935,33 @@ def measure(torch, wl, steps, warmup):
         kern[k] = {"ms": round(ms, 5), "GB/s": round(nbytes / ms / 1e6, 1),
                    "frac_hbm": round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(nbytes),
                    "launches_per_step": len(pairs[k]) // steps}
-    return ms_per_step, kern
+    # flushed iterations: median and min of single steps after a cache-evicting write
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    step_ms = []
+    for i in range(flush_iters):
+        flush.fill_(i & 0xFF)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wl.step()
+        e1.record()
+        torch.cuda.synchronize()
+        step_ms.append(e0.elapsed_time(e1))
+    per_kernel = {k: [] for k in wl.kernels}
+    for i in range(flush_iters):
+        flush.fill_((i + 7) & 0xFF)
+        for k in pairs:
+            pairs[k] = []
+        wl.step(mark)
+        torch.cuda.synchronize()
+        for k in wl.kernels:
+            per_kernel[k].append(sum(a.elapsed_time(b) for a, b in pairs[k]))
+    del flush
+    med = lambda v: sorted(v)[len(v) // 2]
+    flushed = {"iters": flush_iters, "flush_bytes": FLUSH_BYTES,
+               "step_ms_median": round(med(step_ms), 5), "step_ms_min": round(min(step_ms), 5),
+               "kernels": {k: {"ms_median": round(med(v), 5), "ms_min": round(min(v), 5)}
+                           for k, v in per_kernel.items()}}
+    return ms_per_step, kern, flushed
 
 
 def gemm_kernel_figures(wl, kern):
@@ -835,11 +988,18 @@ def main():
     ap.add_argument("--no-controls", action="store_true", help="skip the control timings (GEMM workload; graph replay of the 256x512 case)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="end with one 1 GiB device copy (the counter reference of a rocprofv3 --pmc run)")
+    ap.add_argument("--flush-iters", type=int, default=FLUSH_ITERS,
+                    help="single steps timed after a 512 MiB cache-evicting write (median and min reported)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc output folders into profiles/traffic.json and exit")
+    ap.add_argument("--counter-summary", nargs="+", metavar="DIR",
+                    help="print per-kernel averages of every counter in rocprofv3 --pmc output folders and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary, workload=args.workload)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for {args.gpus}): the hot path here is a "
@@ -851,7 +1011,8 @@ def main():
     torch.cuda.set_device(0)
     wl = WORKLOADS[args.workload](torch, fq)
 
-    ms_per_step, kern = measure(torch, wl, args.steps, args.warmup)
+    print(f"bench: {wl.name}", file=sys.stderr, flush=True)
+    ms_per_step, kern, flushed = measure(torch, wl, args.steps, args.warmup, args.flush_iters)
     dom = max(kern, key=lambda k: kern[k]["ms"])
     gemm = isinstance(wl, W4A4GemmMXFP4)
     if gemm:
@@ -877,14 +1038,17 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": wl.config,
         "roofline": roofline,
         "kernels": kern,
+        "flushed": flushed,
     }
-    if (gemm or isinstance(wl, Single256x512)) and not args.no_controls:
-        line["controls"] = wl.controls()
+    if hasattr(wl, "controls") and not args.no_controls:
+        c = wl.controls()
+        if c:
+            line["controls"] = c
     if not args.no_cpu_baseline and hasattr(wl, "cpu_baseline"):
         line["cpu_baseline"] = wl.cpu_baseline()
     if args.calibrate_copy:
@@ -897,28 +1061,43 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     if args.workload == DenseLayerNVFP4.name and not args.no_secondary:
-        # the other formats' QDQ+pack throughput, each on its own inputs, fewer steps
+        # the other configurations and formats, each on its own inputs, fewer steps
         del wl
         torch.cuda.empty_cache()
         other = {}
         for name in SECONDARY:
+            print(f"bench: {name}", file=sys.stderr, flush=True)
             w2 = WORKLOADS[name](torch, fq)
-            ms2, kern2 = measure(torch, w2, max(5, args.steps // 10), 3)
+            ms2, kern2, fl2 = measure(torch, w2, max(5, args.steps // 4), 3, args.flush_iters)
             if isinstance(w2, W4A4GemmMXFP4):
                 tf = w2.flop / ms2 / 1e9
                 other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5), "TFLOP/s": round(tf, 1),
                                "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFS, 4),
-                               "kernels": gemm_kernel_figures(w2, kern2), "controls": w2.controls()}
+                               "kernels": gemm_kernel_figures(w2, kern2), "flushed": fl2}
             else:
                 other[name] = {"config": w2.config, "ms_per_step": round(ms2, 5),
-                               "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1), "kernels": kern2}
-                if isinstance(w2, Single256x512):
-                    other[name]["controls"] = w2.controls()
+                               "GB/s": round(w2.bytes_per_step / ms2 / 1e6, 1),
+                               "frac_hbm": round(w2.bytes_per_step / ms2 / 1e6 / HBM_PEAK_GBS, 4),
+                               "kernels": kern2, "flushed": fl2}
+            if hasattr(w2, "controls") and not args.no_controls:
+                c = w2.controls()
+                if c:
+                    other[name]["controls"] = c
+            if not args.no_cpu_baseline and hasattr(w2, "cpu_baseline"):
+                other[name]["cpu_baseline"] = w2.cpu_baseline()
             del w2
             torch.cuda.empty_cache()
         line["per_workload"] = other
+        # the metric per format: each QDQ+pack kernel against the HBM peak, and the W4A4 GEMM
+        fmt = {"nvfp4": (kern, "nvfp4_qdq_pack"),
+               "mxfp4": (other[MXFP4Operands.name]["kernels"], "mxfp4_qdq_pack"),
+               "q4k": (other[Q4KSet.name]["kernels"], "q4k_qdq_pack")}
+        line["per_format"] = {f: {"kernel": k, "GB/s": d[k]["GB/s"], "frac_hbm": d[k]["frac_hbm"]}
+                              for f, (d, k) in fmt.items()}
+        g = other[W4A4GemmMXFP4.name]
+        line["per_format"]["w4a4_mxfp4_forward"] = {"TFLOP/s": g["TFLOP/s"], "frac_mfma_bf16": g["frac_mfma_bf16"],
+                                                    "gemm_kernel": g["kernels"]["gemm_bf16_on_qdq_operands"]}
     print(json.dumps(line))
-
 
 if __name__ == "__main__":
     main()
