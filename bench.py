@@ -787,7 +787,8 @@ class MoELoRANVFP4:
                        "merge_scratch": merge_scratch,
                        "bytes_per_element": 8.5625,
                        "extra_traffic_bytes": int(2 * n) if merge_scratch else 0,
-                       "merge_rows_per_unit": layout[0], "gradient_rows_per_workgroup": layout[2],
+                       "merge_tiles_per_wave": layout[0], "merge_workgroups": layout[1],
+                       "qdq_rows_per_unit": layout[4], "qdq_workgroups": layout[5], "gradient_rows_per_workgroup": layout[2],
                        "scratch_bytes": sum(t.numel() * 2 for p in scratch.values() for t in p if t is not None),
                        "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale per expert per fused matrix)"}
 

@@ -359,10 +359,11 @@ def qf_lora_workspace(items):
 
 
 def qf_lora_layout(items):
-    """(rows per merge unit, merge workgroups, rows per gradient workgroup, gradient workgroups)
-    the LoRA calls choose for these descriptors (a host query)."""
+    """(most pass-1 tiles per wave, pass-1 workgroups, rows per gradient workgroup, gradient
+    workgroups, rows per pass-2 unit, pass-2 workgroups) the LoRA calls choose for these
+    descriptors (a host query)."""
     b = _batch(items)
-    out = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 6)()
     _check(lib().qf_lora_layout(b.ref, b.n, out), "qf_lora_layout")
     return tuple(out)
 

@@ -1,5 +1,6 @@
 // C ABI of libqf: argument validation, descriptor marshalling and launches.
 // Every operation and its error behaviour is specified in include/qf.h.
+#include <algorithm>
 #include <string.h>
 
 #include "qf_kernels.h"
@@ -396,6 +397,7 @@ qf_status check_lora(const qf_lora_desc& d) {
   if (d.r < 1 || d.r > qf::LORA_MAX_R) return QF_ERR_ARG;
   if (d.group < 0) return QF_ERR_ARG;
   if ((uint64_t)d.rows * (uint64_t)(d.cols / 8) >= (1ull << 32)) return QF_ERR_SHAPE;
+  if ((uint64_t)d.rows * (uint64_t)d.r * 2u >= (1ull << 31)) return QF_ERR_SHAPE;   // B's byte offsets
   return QF_OK;
 }
 
@@ -406,15 +408,18 @@ qf_status check_lora_merge_inputs(const qf_lora_desc& d) {
 }
 
 struct LoraCounts {
-  int64_t merge_wg = 0, grad_wg = 0, dA_part = 0, dB_part = 0;
+  int64_t merge_tiles = 0, merge_wg = 0, qdq_wg = 0, grad_wg = 0, dA_part = 0, dB_part = 0;
 };
 
 int64_t slabs_of(int64_t cols) { return (cols + qf::LORA_SLAB - 1) / qf::LORA_SLAB; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Launch sizes of a descriptor list for merge units of merge_rows rows and dA
-// workgroups of da_rows rows; fills a (when given).
-LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da_rows, qf::LoraArgs* a,
+// Launch sizes of a descriptor list for pass-2 units of qdq_rows rows and dA workgroups
+// of da_rows rows; fills a (when given).  Pass 1: 32 x 64 tiles, descriptor by
+// descriptor; its grid is the resident maximum of 2 workgroups per CU, or fewer so that
+// every wave keeps at least LORA_MERGE_TILES_MIN tiles (one expert alone: 6,912 tiles,
+// 432 workgroups).
+LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int qdq_rows, int da_rows, qf::LoraArgs* a,
                             float* dA_part) {
   LoraCounts c;
   if (a) memset(a, 0, sizeof(*a));
@@ -422,7 +427,8 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da
   for (int i = 0; i < n; ++i) {
     if (d[i].rows <= 0 || d[i].cols <= 0) continue;
     const int64_t slabs = slabs_of(d[i].cols);
-    const int64_t mu = ceil_div(d[i].rows, merge_rows) * slabs;
+    const int64_t rt = ceil_div(d[i].rows, qf::LORA_MERGE_ROWS), ct = ceil_div(d[i].cols, qf::LORA_MERGE_COLS);
+    const int64_t qu = ceil_div(d[i].rows, qdq_rows) * slabs;
     const int64_t dblk = ceil_div(d[i].rows, da_rows);
     const int64_t du = dblk * slabs;
     if (a) {
@@ -435,15 +441,21 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da
       t.rows = d[i].rows; t.cols = d[i].cols; t.ldw = d[i].ldw;
       t.r = d[i].r; t.group = d[i].group;
       t.slabs = (int32_t)slabs;
-      t.merge_units = (int32_t)mu; t.merge_wg_begin = (int32_t)c.merge_wg;
+      t.merge_tile_begin = (int32_t)c.merge_tiles;
+      t.merge_rtiles = (int32_t)rt;
+      t.merge_ctiles = (int32_t)ct;
+      t.merge_units = (int32_t)qu;
+      t.merge_wg_begin = (int32_t)c.qdq_wg;
       t.grad_wg_begin = (int32_t)c.grad_wg;
     }
     ++k;
     if (d[i].group + 1 > groups) groups = d[i].group + 1;
-    c.merge_wg += ceil_div(mu, 4);
+    c.merge_tiles += rt * ct;
+    c.qdq_wg += ceil_div(qu, 4);
     c.grad_wg += du;
     c.dA_part += dblk * qf::LORA_MAX_R * d[i].cols;
   }
+  c.merge_wg = std::min<int64_t>(qf::LORA_MERGE_GRID_MAX, ceil_div(c.merge_tiles, 4 * qf::LORA_MERGE_TILES_MIN));
   // dB partials follow all dA partials: [slabs][rows][LORA_MAX_R] per descriptor
   int k2 = 0;
   for (int i = 0; i < n; ++i) {
@@ -455,26 +467,28 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int merge_rows, int da
   if (a) {
     a->n = k;
     a->n_groups = groups;
-    a->merge_rows = merge_rows;
+    a->merge_tiles = c.merge_tiles;
+    a->merge_band = (int)std::max<int64_t>(1, c.merge_wg > 0 ? ceil_div(c.merge_tiles, 4 * c.merge_wg) : 1);
+    a->merge_rows = qdq_rows;
     a->da_rows = da_rows;
   }
   return c;
 }
 
-// Merge units shrink (32 -> 16 -> 8 rows) until a launch has at least two workgroups
-// per CU, so that one expert alone still fills the chip (one expert per launch: merge
-// 3.53 -> 3.08 ms per 128 experts).  Gradient workgroups take 512 rows when that still
-// gives one workgroup per CU, else 256: fewer fp32 partials and all workgroups resident
-// at once (8 experts per launch: 73.8 -> 69.0 us from cold caches); smaller ones multiply
-// the partials, which cost more than the idle CUs (64 rows: grads 8.4 -> 10.1 ms).
-// A function of the descriptors only, so the workspace size and the launches agree.
+// Pass-2 units shrink (32 -> 16 -> 8 rows) until a launch has at least two workgroups per
+// CU, so that one expert alone still fills the chip.  Gradient workgroups take 512 rows
+// when that still gives one workgroup per CU, else 256: fewer fp32 partials and all
+// workgroups resident at once (8 experts per launch: 73.8 -> 69.0 us from cold caches);
+// smaller ones multiply the partials, which cost more than the idle CUs (64 rows: grads
+// 8.4 -> 10.1 ms).  A function of the descriptors only, so the workspace size and the
+// launches agree.
 LoraCounts lora_layout(const qf_lora_desc* d, int n, qf::LoraArgs* a, float* dA_part) {
   constexpr int64_t FILL = 2 * 256;
-  int mr = qf::LORA_ROWS;
+  int qr = qf::LORA_QDQ_ROWS;
   int dr = qf::LORA_DA_ROWS_MAX;
-  while (mr > 8 && lora_layout_with(d, n, mr, dr, nullptr, nullptr).merge_wg < FILL) mr /= 2;
-  if (lora_layout_with(d, n, mr, dr, nullptr, nullptr).grad_wg < 256) dr = qf::LORA_DA_ROWS;
-  return lora_layout_with(d, n, mr, dr, a, dA_part);
+  while (qr > 8 && lora_layout_with(d, n, qr, dr, nullptr, nullptr).qdq_wg < FILL) qr /= 2;
+  if (lora_layout_with(d, n, qr, dr, nullptr, nullptr).grad_wg < 256) dr = qf::LORA_DA_ROWS;
+  return lora_layout_with(d, n, qr, dr, a, dA_part);
 }
 
 int lora_groups(const qf_lora_desc* d, int n) {
@@ -508,10 +522,12 @@ qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out) {
   }
   qf::LoraArgs a;
   const LoraCounts c = lora_layout(d, n, &a, nullptr);
-  out[0] = a.merge_rows;
+  out[0] = c.merge_wg > 0 ? (int32_t)ceil_div(c.merge_tiles, 4 * c.merge_wg) : 0;
   out[1] = (int32_t)c.merge_wg;
   out[2] = a.da_rows;
   out[3] = (int32_t)c.grad_wg;
+  out[4] = a.merge_rows;
+  out[5] = (int32_t)c.qdq_wg;
   return QF_OK;
 }
 
@@ -532,7 +548,7 @@ qf_status qf_lora_merge_tensor_scale_nvfp4_grouped(const qf_lora_desc* d, int n,
   if (!aligned(ws, 16)) return QF_ERR_ALIGN;
   qf::LoraArgs a;
   const LoraCounts c = lora_layout(d, n, &a, nullptr);
-  if (c.merge_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (c.merge_tiles >= (1ll << 31)) return QF_ERR_SHAPE;
   a.partial = (uint32_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = qf::launch_lora_merge(a, (int)c.merge_wg, s);
@@ -584,9 +600,9 @@ qf_status qf_lora_merge_qdq_pack_nvfp4_grouped(const qf_lora_desc* d, int n, con
   if (nf == 0) return QF_OK;
   qf::LoraArgs a;
   const LoraCounts c = lora_layout(fused, nf, &a, nullptr);
-  if (c.merge_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (c.qdq_wg >= (1ll << 31)) return QF_ERR_SHAPE;
   a.tscale = d_scales;
-  return hip_status(qf::launch_lora_merge_qdq(a, (int)c.merge_wg, s));
+  return hip_status(qf::launch_lora_merge_qdq(a, (int)c.qdq_wg, s));
 }
 
 qf_status qf_lora_adapter_grads_grouped(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
@@ -880,10 +896,9 @@ size_t qf_workspace_size(int op, int64_t rows, int64_t cols, int n) {
     }
     case QF_OP_LORA: {
       if (n > QF_MAX_GROUPED || cols > QF_LORA_MAX_COLS) return 0;
-      // the most any layout asks for: 8-row merge units, 256-row gradient blocks, 64 groups
+      // the most any layout asks for: the full merge grid, 256-row gradient blocks, 64 groups
       const int64_t slabs = slabs_of(cols);
-      const int64_t merge_wg = (int64_t)n * ceil_div(ceil_div(rows, 8) * slabs, 4);
-      const int64_t merge_words = merge_wg * QF_MAX_GROUPS;
+      const int64_t merge_words = (int64_t)qf::LORA_MERGE_GRID_MAX * QF_MAX_GROUPS;
       const int64_t grad_words = (int64_t)n * (ceil_div(rows, qf::LORA_DA_ROWS) * qf::LORA_MAX_R * cols +
                                                slabs * rows * qf::LORA_MAX_R);
       const int64_t words = merge_words > grad_words ? merge_words : grad_words;

@@ -101,18 +101,21 @@ __device__ __forceinline__ uint32_t maxexp_bits8(uint4 w) {
 // ----------------------------------------------------------------- E4M3 ----
 // E4M3 ("FN": bias 7, max 448, no Inf) code of u >= 0: round to nearest even,
 // anything at or above 448 gives 448 (0x7E).  Below 2^-6 the step is 2^-9.
+// Both cases are computed with plain arithmetic and one is selected, so the code has no
+// branch: below 2^-6, u * 512 (exact) + 2^23 rounds to the integer code (ties to even) in
+// the low mantissa bits.
 __device__ __forceinline__ uint32_t e4m3_encode(float u) {
-  if (!(u < 448.0f)) return 0x7Eu;
-  if (u < 0.015625f) return (uint32_t)__builtin_rintf(u * 512.0f);   // 0..8; 8 is 2^-6
+  const uint32_t sub = __float_as_uint(u * 512.0f + 8388608.0f) - 0x4B000000u;   // 0..8; 8 is 2^-6
   uint32_t b = __float_as_uint(u);
   b += 0x7FFFFu + ((b >> 20) & 1u);                                   // RNE to 3 mantissa bits
-  return (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  const uint32_t nrm = (((b >> 23) - 120u) << 3) | ((b >> 20) & 7u);
+  return !(u < 448.0f) ? 0x7Eu : (u < 0.015625f ? sub : nrm);
 }
 
 __device__ __forceinline__ float e4m3_value(uint32_t c) {
-  uint32_t e = c >> 3, m = c & 7u;
-  if (e == 0) return (float)m * 0.001953125f;                        // m * 2^-9, exact
-  return __uint_as_float(((e + 120u) << 23) | (m << 20));
+  const uint32_t e = c >> 3, m = c & 7u;
+  const float sub = (__uint_as_float(0x4B000000u | m) - 8388608.0f) * 0.001953125f;   // m * 2^-9, exact
+  return e == 0 ? sub : __uint_as_float(((e + 120u) << 23) | (m << 20));
 }
 
 // ----------------------------------------------------------------- fp16 ----
@@ -195,15 +198,13 @@ struct Nvfp4Chunk {
   uint4 y;          // QDQ'd values, bf16
 };
 
-__device__ __forceinline__ Nvfp4Chunk nvfp4_qdq_chunk(uint4 w, float s_t, float k) {
-  uint32_t m = amax_bits8(w);
-  m = umax(m, dpp_xor1(m));
-  const float amax = __uint_as_float(m << 16);
-  Nvfp4Chunk o;
-  o.S = e4m3_encode(amax / k);
-  const float s = e4m3_value(o.S);
-  const float d = s * s_t;
-  const float r = (d == 0.0f) ? 0.0f : 1.0f / d;
+// NVFP4 element codes (4 bytes) and QDQ'd bf16 values of one 8-element chunk, given its
+// block's scale value s, the tensor scale s_t and r = fl(1/fl(s s_t)) (0 when d == 0).
+struct Nvfp4Enc {
+  uint32_t codes;
+  uint4 y;
+};
+__device__ __forceinline__ Nvfp4Enc nvfp4_encode_chunk(uint4 w, float s, float s_t, float r) {
   const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
   float y[8];
 #pragma unroll
@@ -226,6 +227,7 @@ __device__ __forceinline__ Nvfp4Chunk nvfp4_qdq_chunk(uint4 w, float s_t, float 
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[2], y[3], 1.0f, 1);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[4], y[5], 1.0f, 2);
   codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, y[6], y[7], 1.0f, 3);
+  Nvfp4Enc o;
   o.codes = codes;
   const f32x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
   const f32x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
@@ -235,6 +237,34 @@ __device__ __forceinline__ Nvfp4Chunk nvfp4_qdq_chunk(uint4 w, float s_t, float 
   o.y.y = pack_bf16x2((v1.x * s) * s_t, (v1.y * s) * s_t);
   o.y.z = pack_bf16x2((v2.x * s) * s_t, (v2.y * s) * s_t);
   o.y.w = pack_bf16x2((v3.x * s) * s_t, (v3.y * s) * s_t);
+  return o;
+}
+
+// The block scale of a 16-block with maximum |x| bits m (abs bf16 pattern): S = E4M3 of
+// fl(amax / k), k = fl(6 s_t); s its value; r = fl(1 / fl(s s_t)), or 0 when that is 0.
+struct Nvfp4Scale {
+  uint32_t S;
+  float s, r;
+};
+__device__ __forceinline__ Nvfp4Scale nvfp4_block_scale(uint32_t m, float s_t, float k) {
+  const float amax = __uint_as_float(m << 16);
+  Nvfp4Scale o;
+  o.S = e4m3_encode(amax / k);
+  o.s = e4m3_value(o.S);
+  const float d = o.s * s_t;
+  o.r = (d == 0.0f) ? 0.0f : 1.0f / d;
+  return o;
+}
+
+__device__ __forceinline__ Nvfp4Chunk nvfp4_qdq_chunk(uint4 w, float s_t, float k) {
+  uint32_t m = amax_bits8(w);
+  m = umax(m, dpp_xor1(m));
+  const Nvfp4Scale sc = nvfp4_block_scale(m, s_t, k);
+  const Nvfp4Enc e = nvfp4_encode_chunk(w, sc.s, s_t, sc.r);
+  Nvfp4Chunk o;
+  o.S = sc.S;
+  o.codes = e.codes;
+  o.y = e.y;
   return o;
 }
 

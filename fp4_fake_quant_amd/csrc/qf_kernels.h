@@ -66,14 +66,21 @@ struct ReduceArgs {
 
 // ------------------------------------------------------------------ LoRA ---
 constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
-constexpr int LORA_SLAB = 512;      // columns per wave: 64 lanes x 8
-constexpr int LORA_ROWS = 32;       // rows per merge unit (at most; smaller for small launches)
+constexpr int LORA_SLAB = 512;      // gradient columns per workgroup unit
+constexpr int LORA_MERGE_COLS = 64;     // pass-1 merge tile: 64 columns ...
+constexpr int LORA_MERGE_ROWS = 32;     // ... of 32 rows
+constexpr int LORA_MERGE_GRID_MAX = 512;    // pass-1 workgroups resident at once (2 per CU)
+constexpr int LORA_MERGE_TILES_MIN = 4;     // tiles per wave below which the grid shrinks
+constexpr int LORA_QDQ_ROWS = 32;       // rows per pass-2 unit (at most; fewer for small launches)
 constexpr int LORA_DA_ROWS = 256;       // rows per gradient workgroup (one dA partial each), or
 constexpr int LORA_DA_ROWS_MAX = 512;   // twice that when the launch still has a workgroup per CU
 
-// A unit is one wave's work: a slab of LORA_SLAB columns of a run of rows.  Units
-// of a descriptor are numbered row block major, and every descriptor starts on a
-// fresh workgroup of 4 waves, so a workgroup never mixes descriptors.
+// Pass 1 (merge + maximum): tiles numbered descriptor by descriptor, then by band of
+// merge_band row tiles, column tile, row tile; each wave of the grid takes an equal
+// contiguous run.  Pass 2 without M in memory (merge + QDQ): a unit is one wave's
+// LORA_SLAB-column slab of merge_rows rows, numbered row block major; every descriptor
+// starts on a fresh workgroup of 4 waves.  A gradient unit is
+// one workgroup's: a LORA_SLAB-column slab of da_rows rows.
 struct LoraTensor {
   const uint16_t* W;
   const uint16_t* A;
@@ -89,8 +96,10 @@ struct LoraTensor {
   float* dB_partial;   // workspace: [slabs][rows][LORA_MAX_R]
   int64_t rows, cols, ldw;
   int32_t r, group;
-  int32_t slabs;            // ceil(cols / LORA_SLAB)
-  int32_t merge_units, merge_wg_begin;
+  int32_t slabs;            // ceil(cols / LORA_SLAB), the gradient slabs
+  int32_t merge_tile_begin;         // pass 1: first tile of the descriptor in the launch,
+  int32_t merge_rtiles, merge_ctiles;  // its 32-row and 64-column tiles
+  int32_t merge_units, merge_wg_begin;  // pass 2: units and first workgroup
   int32_t grad_wg_begin;    // gradients: one workgroup per (row block, slab)
 };
 
@@ -98,7 +107,9 @@ struct LoraArgs {
   LoraTensor d[QF_MAX_GROUPED];
   int n;
   int n_groups;        // rows of merge partials
-  int merge_rows;      // rows per merge unit (32, 16 or 8)
+  int64_t merge_tiles; // pass-1 tiles of the launch
+  int merge_band;      // row tiles per band of the pass-1 order (the longest wave run)
+  int merge_rows;      // rows per pass-2 unit (32, 16 or 8)
   int da_rows;         // rows per gradient workgroup (LORA_DA_ROWS or LORA_DA_ROWS_MAX)
   uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
   const float* tscale; // merge-and-QDQ: NVFP4 tensor scale of every tied group

@@ -11,21 +11,21 @@
 // A[k,j], acc) (each bf16 x bf16 product is exact in fp32, so this is the sum
 // with one rounding per step, in k order); M[i,j] = bf16(fl(W[i,j] + acc)).
 //
-// Merge work split: a unit is one wave's share, LORA_SLAB = 512 columns (lane l owns
-// columns 8l .. 8l+7 of the slab) of a run of rows.  Lanes keep their 16 x 8 slice
-// of A in registers, so the per-row work is one 16-byte load, 128 FMAs and one
-// 16-byte store per lane.  The row's B values are the same for every lane: they are
-// loaded once per row through the scalar cache, where the FMAs read them.
+// The two merge passes compute this sum in two ways that give the same bits: pass 1 on
+// the fp32 matrix cores (a chain of K = 1 steps is the same sequence of fused steps),
+// pass 2 with vector FMAs.
 //
 // Kernels
-//   k_lora_merge     M = W + B.A for up to LORA_ROWS rows per unit; either stores M
-//                    (or not) and folds max|M| of the workgroup into its tied group's
-//                    partial (NVFP4 pass 1), or merges again and NVFP4-QDQs and packs
-//                    the merged rows in registers (pass 2 without M in memory).
-//   k_lora_grads     dB = G . A^T and dA = B^T . G in one pass over G, both on the
-//                    16x16x32 BF16 MFMA (G staged through LDS); per-slab dB partials and
-//                    per-row-block dA partials, added in a fixed order by
-//                    k_lora_dB_reduce and k_lora_dA_reduce (same inputs, same bits).
+//   k_lora_merge_amax  pass 1: M = W + B.A per 32 x 64 tile, S on the matrix cores with W
+//                      and B streamed through a per-wave LDS ring; stores M (or not, M
+//                      null) and folds max|M| into its tied group's partial.
+//   k_lora_merge_qdq   pass 2 without M in memory: merges again (vector FMAs, a 512-column
+//                      slab per wave, one row at a time) and NVFP4-QDQs and packs the
+//                      merged rows in registers.
+//   k_lora_grads       dB = G . A^T and dA = B^T . G in one pass over G, both on the
+//                      16x16x32 BF16 MFMA (G staged through LDS); per-slab dB partials and
+//                      per-row-block dA partials, added in a fixed order by
+//                      k_lora_dB_reduce and k_lora_dA_reduce (same inputs, same bits).
 #include <algorithm>
 
 #include "qf_device.h"
@@ -40,13 +40,6 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // steps) stay in program order, so each waits only for its own prefetched load.
 #define LORA_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// B[row, 0 .. r-1] as fp32 in scalar registers (entries past r are 0).  B is
-// contiguous [rows, r] and 4-byte aligned; the row starts at element row * r,
-// which may be odd: the 32-bit words holding it are read through the scalar
-// cache (B is never written while these kernels run) and realigned by one half
-// word if so.  With r odd, the last row's last word may hold the 2 bytes after B.
-// (fetch_b_words / b_row_values below.)
-typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 
 __device__ __forceinline__ void unpack8(uint4 w, float (&f)[8]) {
   f[0] = bf16_lo(w.x); f[1] = bf16_hi(w.x);
@@ -55,6 +48,452 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&f)[8]) {
   f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
+// --------------------------------------------------- merge, passes 1 and 2 ------
+// The low-rank product S = B.A runs on the fp32 matrix cores: v_mfma_f32_32x32x1_2b_f32
+// multiplies one fp32 value per lane of its A operand by one of its B operand (K = 1) and
+// adds the product to the accumulator with one fp32 rounding, ties to even, subnormals
+// kept -- the same operation as fma(b, a, acc), since every bf16 x bf16 product is exact
+// in fp32.  A chain of r such steps, k = 0 .. r-1, is therefore bit for bit the merge's
+// sequential sum.  (The BF16 K = 16 instruction is not: its 16-product sums round
+// differently.)
+//
+// Tile = 32 rows x 64 columns of one matrix.  The instruction works on two 32 x 32 blocks.
+// MFMA columns are the tile's 32 rows (B operand: lane l supplies B[row l % 32][k] for
+// block l / 32); MFMA rows are 32 of the 64 columns per block (A operand: lane l supplies
+// A[k][col(l)]).  Lane l then holds, in its 32 accumulators, block q's result for tile row
+// l % 32 at MFMA rows 8 (w / 4) + 4 h + w % 4 (w = 0..15, h = l / 32).  col() maps MFMA
+// row 8 (w / 4) + 4 h + w % 4 of block q to tile column 32 q + 16 h + w, so each lane ends
+// with two whole NVFP4 16-blocks of one row: columns 16 h .. 16 h + 15 and
+// 32 + 16 h .. 32 + 16 h + 15.  The block maximum, scale and codes stay in the lane.
+//
+// Work split: the launch's tiles in one flat order are cut into equal contiguous runs, one
+// per wave of a grid that stays resident on the chip, so every wave streams the same
+// number of tiles (give or take one).  The order is descriptor, band of merge_band row
+// tiles (the run length), 64-column tile, 32-row tile: a run goes down one column of a
+// band, with A's values for that column in registers (reloaded where the run enters the
+// next column or matrix), and the waves running side by side read the same rows of
+// neighbouring columns, so each row of W is read whole at about the same time.
+//
+// Loads: each wave streams its tiles through its own ring of MM_DEPTH LDS stages with
+// buffer loads that write LDS directly (no registers held while in flight), MM_DEPTH - 1
+// tiles ahead, across column and matrix boundaries.  A stage holds the W tile (32 rows x
+// 128 bytes, loaded as four fully coalesced 1 KiB windows; the 16-byte chunks of row r
+// are stored XOR-rotated by (r >> 1) & 7 so that the lanes' row reads hit distinct banks)
+// and the tile's 32 rows of B (contiguous in memory).  Columns past the matrix's last
+// 32-column group and rows past the matrix read zeros; their stores are dropped, and
+// rows past the matrix are left out of the maximum.
+constexpr int MM_COLS = LORA_MERGE_COLS;
+constexpr int MM_ROWS = LORA_MERGE_ROWS;
+constexpr int MM_DEPTH = 3;                      // ring stages per wave
+constexpr int MM_WBYTES = MM_ROWS * MM_COLS * 2; // 4 KiB of W per tile
+constexpr int MM_STAGE = MM_WBYTES + 1024;       // + B rows (32 x up to 16 bf16)
+constexpr int MM_LOADS = 4 + 4;                  // buffer-to-LDS loads per tile per lane
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// LDS byte address of a pointer into a __shared__ array
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// s_waitcnt vmcnt(n) with the LDS and export counters left at their maximum
+#define MM_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+typedef float f32x32_t __attribute__((ext_vector_type(32)));
+
+__device__ __forceinline__ uint16_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint16_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2_t, v), r, (int)off, 0, 0);
+}
+
+// A tile's place in the flat order (wave-uniform): descriptor, row tile, column tile, the
+// row band [b0, b1) of the row tile, and the descriptor's row and column tile counts.
+struct MmTile {
+  int di, ct, rt, b0, b1, rtiles, ctiles;
+};
+
+__device__ __forceinline__ void mm_next(const LoraArgs& a, MmTile& p) {
+  if (++p.rt < p.b1) return;
+  if (++p.ct == p.ctiles) {
+    p.ct = 0;
+    if (p.b1 == p.rtiles) {                                      // next descriptor, first band
+      if (++p.di >= a.n) return;
+      p.rtiles = a.d[p.di].merge_rtiles;
+      p.ctiles = a.d[p.di].merge_ctiles;
+      p.b0 = 0;
+      p.b1 = min(a.merge_band, p.rtiles);
+    } else {
+      p.b0 = p.b1;
+      p.b1 = min(p.b1 + a.merge_band, p.rtiles);
+    }
+  }
+  p.rt = p.b0;
+}
+
+// Place of tile tb of the launch.
+__device__ __forceinline__ MmTile mm_locate(const LoraArgs& a, int64_t tb) {
+  MmTile p;
+  int di = 0;
+#pragma unroll 1
+  while (di + 1 < a.n && tb >= a.d[di + 1].merge_tile_begin) ++di;
+  const LoraTensor& T = a.d[di];
+  p.rtiles = T.merge_rtiles;
+  p.ctiles = T.merge_ctiles;
+  const int loc = (int)(tb - T.merge_tile_begin);
+  const int bands = (p.rtiles + a.merge_band - 1) / a.merge_band;
+  const int band = min(loc / (a.merge_band * p.ctiles), bands - 1);
+  p.di = di;
+  p.b0 = band * a.merge_band;
+  p.b1 = min(p.b0 + a.merge_band, p.rtiles);
+  const int q = loc - p.b0 * p.ctiles, hb = p.b1 - p.b0;
+  p.ct = q / hb;
+  p.rt = p.b0 + (q - p.ct * hb);
+  return p;
+}
+
+// Keeps values computed where they stand in the source (an empty asm that takes them):
+// the finishing work of a merge step is placed between the steps of the next tile's chain
+// on purpose, and must not be moved down to where its results are stored.
+#define MM_PIN1(a) asm volatile("" : "+v"(a))
+#define MM_PIN3(a, b, c) asm volatile("" : "+v"(a), "+v"(b), "+v"(c))
+#define MM_PIN4(a, b, c, d) asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d))
+
+// Folds a lane maximum into the workgroup's maximum of group g (LDS).
+__device__ __forceinline__ void mm_flush(uint32_t m, uint32_t* gmax, int g) {
+  m = umax(m, dpp_xor1(m));
+  m = umax(m, dpp_xor2(m));
+  m = umax(m, dpp_hmirror(m));
+  m = umax(m, dpp_mirror(m));
+  m = umax(m, swz_xor16(m));
+  m = umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
+  if ((threadIdx.x & 63) == 0) atomicMax(gmax + g, m);
+}
+
+template <int RK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_lora_merge_amax(LoraArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t mm_lds[4 * MM_DEPTH * MM_STAGE];
+  __shared__ uint32_t gmax[QF_MAX_GROUPS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if ((int)threadIdx.x < QF_MAX_GROUPS) gmax[threadIdx.x] = 0;
+  __syncthreads();
+  // this wave's run of tiles [tb, tb + nt)
+  const int64_t nw = (int64_t)gridDim.x * 4, w = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t tb = w * a.merge_tiles / nw;
+  const int nt = (int)((w + 1) * a.merge_tiles / nw - tb);
+  uint32_t m = 0;                                                  // max |M| bits of group mg
+  int mg = -1;
+  if (nt > 0) {
+    const int h = lane >> 5, lr = lane & 31;
+    uint8_t* const ring = mm_lds + wave * (MM_DEPTH * MM_STAGE);
+    MmTile pe = mm_locate(a, tb);      // tile t: W + S, its maximum and stores
+    MmTile pm = pe;                    // tile t + 1: S = B.A on the matrix cores
+    MmTile pl = pe;                    // the next tile to load
+    // W window j of a tile: lane i fills row 8j + i/8 at chunk position i%8 with the row's
+    // global chunk (i%8) ^ ((row >> 1) & 7)
+    uint32_t wrow[4], wchunk[4];
+#pragma unroll
+    for (int jw = 0; jw < 4; ++jw) {
+      wrow[jw] = 8u * jw + (uint32_t)(lane >> 3);
+      wchunk[jw] = (uint32_t)(lane & 7) ^ ((wrow[jw] >> 1) & 7u);
+    }
+    // Loads of the wave's j-th tile into stage st: always MM_LOADS instructions (past the
+    // run they read nothing and write zeros), so that the waits below count right.
+    auto issue = [&](int j, uint8_t* st) {
+      __amdgpu_buffer_rsrc_t rw = make_buf(nullptr, 0), rb = make_buf(nullptr, 0);
+      uint32_t wo[4] = {BUF_OOR, BUF_OOR, BUF_OOR, BUF_OOR}, bo[4] = {BUF_OOR, BUF_OOR, BUF_OOR, BUF_OOR};
+      if (j < nt) {
+        const LoraTensor& T = a.d[pl.di];
+        const int r = RK ? RK : T.r;
+        const int64_t c0 = (int64_t)pl.ct * MM_COLS, r0 = (int64_t)pl.rt * MM_ROWS;
+        const int nrows = (int)min((int64_t)MM_ROWS, T.rows - r0);
+        const int cw = (int)min((int64_t)MM_COLS, T.cols - c0);
+        rw = make_buf(T.W + r0 * T.ldw + c0, ((int64_t)(nrows - 1) * T.ldw + cw) * 2);
+        // B rows of the tile (4-byte aligned; with an odd rank the last row may end in the
+        // middle of a word, so the 2 bytes after it are in range)
+        rb = make_buf(T.B + r0 * r, (int64_t)nrows * r * 2 + 2);
+#pragma unroll
+        for (int jw = 0; jw < 4; ++jw)
+          wo[jw] = cw > 32 * (int)(wchunk[jw] >> 2) ? (uint32_t)((wrow[jw] * T.ldw + 8 * wchunk[jw]) * 2) : BUF_OOR;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+          const int d = 64 * jb + lane;                              // dword of the tile's B bytes
+          bo[jb] = d < 16 * r ? (uint32_t)(4 * d) : BUF_OOR;
+        }
+        mm_next(a, pl);
+      }
+#pragma unroll
+      for (int jw = 0; jw < 4; ++jw)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(st + 1024 * jw), 16, wo[jw], 0, 0, 0);
+#pragma unroll
+      for (int jb = 0; jb < 4; ++jb)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + MM_WBYTES + 256 * jb), 4, bo[jb], 0, 0, 0);
+    };
+    // stores per tile (counted by vmcnt like the loads): 4 (M; dropped when M is null)
+    constexpr int STORES = 4;
+    const uint32_t rot = ((uint32_t)lr >> 1) & 7u;
+    // The chain always takes LORA_MAX_R steps: a rank r < 16 runs 16 - r leading steps on
+    // +0 x +0, which leave the accumulator at +0 exactly, so the sum is still the r-step one.
+    // A operand of step j: A[j - (16 - r)][c0 + colA], colA = this lane's MFMA row's column.
+    const int colA = 32 * h + 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
+    float av[LORA_MAX_R];
+    int a_di = -1, a_ct = -1;
+    // A's values for the column of tile p; then no load is left pending, so no later wait
+    // has to cover them
+    auto load_a = [&](const MmTile& p) {
+      const LoraTensor& T = a.d[p.di];
+      const int r = RK ? RK : T.r, lead = LORA_MAX_R - r;
+      const __amdgpu_buffer_rsrc_t ra = make_buf(T.A, (int64_t)r * T.cols * 2);
+      const int cA = p.ct * MM_COLS + colA, ncol = (int)T.cols;     // below 2^16 + 64
+#pragma unroll
+      for (int j = 0; j < LORA_MAX_R; ++j) {
+        const uint32_t off = (j >= lead && cA < ncol) ? (uint32_t)(((j - lead) * ncol + cA) * 2) : BUF_OOR;
+        av[j] = __uint_as_float((uint32_t)buf_load2(ra, off) << 16);
+      }
+      MM_WAIT_VM(0);
+      a_di = p.di;
+      a_ct = p.ct;
+    };
+    // The tile's LDS reads (stage st, rank r) in one block that waits for its own results:
+    // written as plain loads, the compiler cannot tell the ring stages' buffer-to-LDS writes
+    // apart and would wait for the next tiles' loads too (the caller's wait covers this
+    // tile's).  wc: the lane's W chunks, global chunks 2h, 2h+1 (group 0), 4+2h, 5+2h
+    // (group 1); bk[j]: B[lr][j - (16 - r)], 0 for the leading steps.
+    auto read_tile = [&](const uint8_t* st, int r, uint4 (&wc)[4], float (&bk)[LORA_MAX_R]) {
+      uint32_t wa[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t g = (uint32_t)(2 * h + (c & 1) + 4 * (c >> 1));
+        wa[c] = lds_addr(st + lr * 128 + ((g ^ rot) << 4));
+      }
+      u32x4_t w0, w1, w2, w3;
+      if constexpr (RK == LORA_MAX_R) {
+        const uint32_t ba = lds_addr(st + MM_WBYTES + lr * 32);
+        u32x4_t b0v, b1v;
+        asm volatile(
+            "ds_read_b128 %0, %6\n\t"
+            "ds_read_b128 %1, %7\n\t"
+            "ds_read_b128 %2, %8\n\t"
+            "ds_read_b128 %3, %9\n\t"
+            "ds_read_b128 %4, %10\n\t"
+            "ds_read_b128 %5, %10 offset:16\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(b0v), "=&v"(b1v)
+            : "v"(wa[0]), "v"(wa[1]), "v"(wa[2]), "v"(wa[3]), "v"(ba)
+            : "memory");
+        const uint32_t bwv[8] = {b0v[0], b0v[1], b0v[2], b0v[3], b1v[0], b1v[1], b1v[2], b1v[3]};
+#pragma unroll
+        for (int q2 = 0; q2 < 8; ++q2) {
+          bk[2 * q2] = bf16_lo(bwv[q2]);
+          bk[2 * q2 + 1] = bf16_hi(bwv[q2]);
+        }
+      } else {
+        // halfword j at B-row start + 2 (j - lead): from the W area's end (lead <= 15
+        // halfwords before row 0) to the B area's (31 r + r halfwords); k < 0 dropped
+        const int lead = LORA_MAX_R - r;
+        const uint32_t ba = lds_addr(st + MM_WBYTES + (lr * r - lead) * 2);
+        uint32_t bh[LORA_MAX_R];
+        asm volatile(
+            "ds_read_b128 %0, %20\n\t"
+            "ds_read_b128 %1, %21\n\t"
+            "ds_read_b128 %2, %22\n\t"
+            "ds_read_b128 %3, %23\n\t"
+            "ds_read_u16 %4, %24\n\t"
+            "ds_read_u16 %5, %24 offset:2\n\t"
+            "ds_read_u16 %6, %24 offset:4\n\t"
+            "ds_read_u16 %7, %24 offset:6\n\t"
+            "ds_read_u16 %8, %24 offset:8\n\t"
+            "ds_read_u16 %9, %24 offset:10\n\t"
+            "ds_read_u16 %10, %24 offset:12\n\t"
+            "ds_read_u16 %11, %24 offset:14\n\t"
+            "ds_read_u16 %12, %24 offset:16\n\t"
+            "ds_read_u16 %13, %24 offset:18\n\t"
+            "ds_read_u16 %14, %24 offset:20\n\t"
+            "ds_read_u16 %15, %24 offset:22\n\t"
+            "ds_read_u16 %16, %24 offset:24\n\t"
+            "ds_read_u16 %17, %24 offset:26\n\t"
+            "ds_read_u16 %18, %24 offset:28\n\t"
+            "ds_read_u16 %19, %24 offset:30\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(w0), "=&v"(w1), "=&v"(w2), "=&v"(w3), "=&v"(bh[0]), "=&v"(bh[1]), "=&v"(bh[2]),
+              "=&v"(bh[3]), "=&v"(bh[4]), "=&v"(bh[5]), "=&v"(bh[6]), "=&v"(bh[7]), "=&v"(bh[8]), "=&v"(bh[9]),
+              "=&v"(bh[10]), "=&v"(bh[11]), "=&v"(bh[12]), "=&v"(bh[13]), "=&v"(bh[14]), "=&v"(bh[15])
+            : "v"(wa[0]), "v"(wa[1]), "v"(wa[2]), "v"(wa[3]), "v"(ba)
+            : "memory");
+#pragma unroll
+        for (int j = 0; j < LORA_MAX_R; ++j) bk[j] = j >= lead ? __uint_as_float((bh[j] & 0xFFFFu) << 16) : 0.0f;
+      }
+      wc[0] = make_uint4(w0[0], w0[1], w0[2], w0[3]);
+      wc[1] = make_uint4(w1[0], w1[1], w1[2], w1[3]);
+      wc[2] = make_uint4(w2[0], w2[1], w2[2], w2[3]);
+      wc[3] = make_uint4(w3[0], w3[1], w3[2], w3[3]);
+    };
+    auto chain = [&](const float (&bk)[LORA_MAX_R]) {
+      f32x32_t acc;
+#pragma unroll
+      for (int v = 0; v < 32; ++v) acc[v] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < LORA_MAX_R; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av[j], bk[j], acc, 0, 0, 0);
+      return acc;
+    };
+    // Step t: tile t + 3 is loaded into tile t's stage (read one step earlier), tile t + 1
+    // is read from its stage and multiplied on the matrix cores while tile t is finished
+    // from the registers.
+    auto step = [&](int t, int si, f32x32_t& accP, uint4 (&wP)[4], f32x32_t& accN, uint4 (&wN)[4]) {
+      LORA_FENCE();
+      issue(t + MM_DEPTH, ring + si * MM_STAGE);
+      LORA_FENCE();
+      // wait for tile t + 1's loads: younger than them are the next two tiles' loads and
+      // the stores of the tiles since (none before tile 0's; A reloads drain everything)
+      if (t >= 2) MM_WAIT_VM((MM_DEPTH - 1) * (MM_LOADS + STORES));
+      else if (t == 1) MM_WAIT_VM((MM_DEPTH - 1) * MM_LOADS + STORES);
+      else MM_WAIT_VM((MM_DEPTH - 1) * MM_LOADS);
+      asm volatile("" ::: "memory");
+      const bool more = t + 1 < nt;                                // past the run: zeros, unused
+      if (more && (pm.di != a_di || pm.ct != a_ct)) load_a(pm);
+      // tile t's place and outputs: element (lr, 16 h [+ 32]) of rows r0 .. r0 + nrows - 1
+      // from column c0 on (rows past the matrix fall outside the ranges)
+      const LoraTensor& T = a.d[pe.di];
+      const int64_t cols = T.cols, c0 = (int64_t)pe.ct * MM_COLS, r0 = (int64_t)pe.rt * MM_ROWS;
+      const int nrows = (int)min((int64_t)MM_ROWS, T.rows - r0);
+      const int64_t e0 = r0 * cols + c0, ne = (int64_t)nrows * cols - c0;
+      const bool ok1 = c0 + 32 < cols;                             // the second 32-column group
+      LORA_FENCE();
+      float bk[LORA_MAX_R];
+      uint8_t* const sr = ring + (si == MM_DEPTH - 1 ? 0 : si + 1) * MM_STAGE;
+      read_tile(sr, RK ? RK : (more ? a.d[pm.di].r : LORA_MAX_R), wN, bk);
+      // Tile t's outputs leave through the stage just read (free until step t + 1 loads into
+      // it): the lanes write their pieces of rows there and read whole rows back, so that a
+      // store instruction writes 8 rows of 128 bytes of bf16 (32 rows of 32 code bytes, 2
+      // scale bytes) instead of 16-byte pieces of 32 rows.  The bf16 chunk c of the lane
+      // sits where the W chunk of the same place was; window k of the stage then holds rows
+      // 8k + lane / 8, global chunk wchunk[k] at lane position lane % 8.
+      uint32_t xa[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t g = (uint32_t)(2 * h + (c & 1) + 4 * (c >> 1));
+        xa[c] = lds_addr(sr + lr * 128 + ((g ^ rot) << 4));
+      }
+      const uint32_t xr = lds_addr(sr + 16 * lane);
+      uint32_t yoff[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        yoff[k] = ok1 || wchunk[k] < 4 ? (uint32_t)((wrow[k] * cols + 8 * wchunk[k]) * 2) : BUF_OOR;
+      // The chain of tile t + 1 with tile t's finishing work placed between its steps, in
+      // the order of its data flow: each step has a piece of independent vector work to
+      // overlap instead of waiting for the previous step.
+      f32x32_t an;
+#pragma unroll
+      for (int v = 0; v < 32; ++v) an[v] = 0.0f;
+      uint4 mo[4];
+      auto merge_chunk = [&](int c) {
+        float wf[8];
+        unpack8(wP[c], wf);
+        const int v0 = 16 * (c >> 1) + 8 * (c & 1);
+        mo[c].x = pack_bf16x2(wf[0] + accP[v0 + 0], wf[1] + accP[v0 + 1]);
+        mo[c].y = pack_bf16x2(wf[2] + accP[v0 + 2], wf[3] + accP[v0 + 3]);
+        mo[c].z = pack_bf16x2(wf[4] + accP[v0 + 4], wf[5] + accP[v0 + 5]);
+        mo[c].w = pack_bf16x2(wf[6] + accP[v0 + 6], wf[7] + accP[v0 + 7]);
+        MM_PIN4(mo[c].x, mo[c].y, mo[c].z, mo[c].w);
+      };
+      {
+        uint32_t mt = 0;
+#pragma unroll
+        for (int j = 0; j < LORA_MAX_R; ++j) {
+          an = __builtin_amdgcn_mfma_f32_32x32x1f32(av[j], bk[j], an, 0, 0, 0);
+          if (j < 4) merge_chunk(j);
+          if (j == 4) {
+            mt = umax(umax(amax_bits8(mo[0]), amax_bits8(mo[1])), umax(amax_bits8(mo[2]), amax_bits8(mo[3])));
+            mt = lr < nrows ? mt : 0u;                             // rows past the matrix: left out
+            MM_PIN1(mt);
+          }
+          LORA_FENCE();
+        }
+        accN = an;
+        // M through the stage just read, as y above
+        u32x4_t mo0, mo1, mo2, mo3;
+        const u32x4_t m0 = {mo[0].x, mo[0].y, mo[0].z, mo[0].w}, m1 = {mo[1].x, mo[1].y, mo[1].z, mo[1].w};
+        const u32x4_t m2 = {mo[2].x, mo[2].y, mo[2].z, mo[2].w}, m3 = {mo[3].x, mo[3].y, mo[3].z, mo[3].w};
+        asm volatile(
+            "ds_write_b128 %[a0], %[m0]\n\t"
+            "ds_write_b128 %[a1], %[m1]\n\t"
+            "ds_write_b128 %[a2], %[m2]\n\t"
+            "ds_write_b128 %[a3], %[m3]\n\t"
+            "ds_read_b128 %[o0], %[xr]\n\t"
+            "ds_read_b128 %[o1], %[xr] offset:1024\n\t"
+            "ds_read_b128 %[o2], %[xr] offset:2048\n\t"
+            "ds_read_b128 %[o3], %[xr] offset:3072\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : [o0] "=&v"(mo0), [o1] "=&v"(mo1), [o2] "=&v"(mo2), [o3] "=&v"(mo3)
+            : [a0] "v"(xa[0]), [a1] "v"(xa[1]), [a2] "v"(xa[2]), [a3] "v"(xa[3]), [m0] "v"(m0), [m1] "v"(m1),
+              [m2] "v"(m2), [m3] "v"(m3), [xr] "v"(xr)
+            : "memory");
+        const __amdgpu_buffer_rsrc_t rm = make_buf((const uint16_t*)((uintptr_t)T.M + (uintptr_t)(e0 * 2)),
+                                                   T.M ? ne * 2 : 0);
+        buf_store16(rm, yoff[0], make_uint4(mo0[0], mo0[1], mo0[2], mo0[3]));
+        buf_store16(rm, yoff[1], make_uint4(mo1[0], mo1[1], mo1[2], mo1[3]));
+        buf_store16(rm, yoff[2], make_uint4(mo2[0], mo2[1], mo2[2], mo2[3]));
+        buf_store16(rm, yoff[3], make_uint4(mo3[0], mo3[1], mo3[2], mo3[3]));
+        if (T.group != mg) {                                       // the run enters another group
+          if (mg >= 0) mm_flush(m, gmax, mg);
+          m = 0;
+          mg = T.group;
+        }
+        m = umax(m, mt);
+      }
+      pe = pm;
+      if (more) mm_next(a, pm);
+      LORA_FENCE();
+    };
+    // prologue: A for tile 0, tiles 0 .. MM_DEPTH - 1 in flight, tile 0 on the matrix cores
+    load_a(pm);
+#pragma unroll
+    for (int j = 0; j < MM_DEPTH; ++j) issue(j, ring + j * MM_STAGE);
+    MM_WAIT_VM((MM_DEPTH - 1) * MM_LOADS);
+    asm volatile("" ::: "memory");
+    f32x32_t acc0, acc1;
+    uint4 w0[4], w1[4];
+    {
+      float bk[LORA_MAX_R];
+      read_tile(ring, RK ? RK : a.d[pm.di].r, w0, bk);
+      acc0 = chain(bk);
+    }
+    if (nt > 1) mm_next(a, pm);
+    int si = 0;
+#pragma unroll 1
+    for (int t = 0; t < nt; t += 2) {
+      step(t, si, acc0, w0, acc1, w1);
+      si = si == MM_DEPTH - 1 ? 0 : si + 1;
+      if (t + 1 < nt) {
+        step(t + 1, si, acc1, w1, acc0, w0);
+        si = si == MM_DEPTH - 1 ? 0 : si + 1;
+      }
+    }
+    MM_WAIT_VM(0);                                                 // no load may still write LDS at exit
+    mm_flush(m, gmax, mg);
+  }
+  // workgroup maxima -> partial[g * grid + b] for every group (0 where none was seen)
+  __syncthreads();
+  if ((int)threadIdx.x < a.n_groups) a.partial[threadIdx.x * gridDim.x + blockIdx.x] = gmax[threadIdx.x];
+}
+
+// ------------------------------------------------ pass 2 without M in memory ---
+// Merge again and NVFP4-QDQ + pack in registers.  A unit is one wave's share: LORA_SLAB
+// = 512 columns of a run of merge_rows rows (lane l owns columns 8l .. 8l+7 of the slab,
+// lanes 2i and 2i+1 one 16-block), walked one row at a time with LORA_PREFETCH rows of W
+// in flight.  Lanes keep their 16 x 8 slice of A in registers, so a row costs one 16-byte
+// load, 128 FMAs, the QDQ of 8 values and row-contiguous stores; the row's B values are
+// the same for every lane and come through the scalar cache.  The sum is the same
+// sequential fp32 one as on the matrix cores in pass 1, so M has the same bits.  (This
+// layout keeps every load and store a whole contiguous row piece, which the QDQ outputs
+// need; pass 1 stores nothing when M is not kept.)
+constexpr int LORA_PREFETCH = 4;
+constexpr int BW = LORA_MAX_R / 2 + 1;   // 32-bit words that can hold one row of B
+typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
+
 __device__ __forceinline__ int find_desc_wg(const LoraArgs& a, int b) {
   int di = 0;
 #pragma unroll 1
@@ -62,14 +501,9 @@ __device__ __forceinline__ int find_desc_wg(const LoraArgs& a, int b) {
   return di;
 }
 
-// ------------------------------------------------------------- pass 1 ------
-// Rows are software-pipelined: LORA_PREFETCH rows of W are always in flight, and the
-// next row's B words are requested (scalar loads) while the current row is computed.
-constexpr int LORA_PREFETCH = 4;
-constexpr int BW = LORA_MAX_R / 2 + 1;   // 32-bit words that can hold one row of B
-
-// Scalar words of B's row `row`, realigned into fp32 values by b_row_values.  RK is
-// the rank when it is known at compile time (16: the row is 8 aligned words), else 0.
+// Scalar words of B's row `row` (B contiguous [rows, r], 4-byte aligned; the row starts
+// at element row * r, which may be odd; with r odd the last row's last word may hold the
+// 2 bytes after B).  RK is the rank when known at compile time (16: 8 aligned words).
 template <int RK>
 __device__ __forceinline__ void fetch_b_words(const uint16_t* B, int64_t row, int r, uint32_t (&w)[BW]) {
   if constexpr (RK == LORA_MAX_R) {
@@ -86,8 +520,9 @@ __device__ __forceinline__ void fetch_b_words(const uint16_t* B, int64_t row, in
   }
 }
 
-// B values of the row as fp32, zero past r: the padded steps fma(0, a, acc) leave acc
-// unchanged bit for bit (a zero product added to acc gives acc, also for acc = -0).
+// B values of the row as fp32, zero past r: the padded steps fma(+0, +0, acc) come after
+// the r real ones and leave acc unchanged bit for bit.  (Adding +0 changes only acc = -0,
+// and a sum that starts at +0 reaches -0 only through a product below fp32's range.)
 template <int RK>
 __device__ __forceinline__ void b_row_values(const uint32_t (&w)[BW], int64_t row, int r, float (&bk)[LORA_MAX_R]) {
   if constexpr (RK == LORA_MAX_R) {
@@ -107,110 +542,77 @@ __device__ __forceinline__ void b_row_values(const uint32_t (&w)[BW], int64_t ro
   }
 }
 
-// Loop bodies are branch-free: W, M, G and A are accessed through buffer resources
-// that span exactly the valid rows (and A's r rows), lanes past the last column use
-// an out-of-range offset, and the rows of the last group past the end are computed on
-// zeros and dropped by the range check, so the compiler can keep every prefetched
-// load in flight across rows.
-//
-// QDQ = false: M is stored (unless T.M is null: the resource is then empty and every
-// store is dropped) and the workgroup's max|M| goes to its tied group's partial.
-// QDQ = true: the merged row stays in registers and is NVFP4-QDQ'd and packed with the
-// group's tensor scale (lanes 2i and 2i+1 hold one 16-block), so no M round trip
-// through memory is needed; the merge arithmetic is the same, so the values are the
-// same bits as QDQ of the stored M.
-template <int RK, bool QDQ>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_merge(LoraArgs a) {
+// Loop bodies are branch-free: W and A are read through buffer resources that span
+// exactly the valid rows (and A's r rows), lanes past the last column use an
+// out-of-range offset, and the rows of the last group past the end are computed on zeros
+// and dropped by the range check, so the compiler keeps every prefetched load in flight.
+template <int RK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_merge_qdq(LoraArgs a) {
   const int b = blockIdx.x;
   const LoraTensor& T = a.d[find_desc_wg(a, b)];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;   // wave index: uniform
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int u = (b - T.merge_wg_begin) * 4 + wave;
-  uint32_t m = 0;
-  if (u < T.merge_units) {
-    const int64_t cols = T.cols, ldw = T.ldw;
-    const int r = RK ? RK : T.r;
-    const int rb = u / T.slabs;
-    const int64_t cs = (int64_t)(u - rb * T.slabs) * LORA_SLAB;        // first column of the slab
-    const int64_t r0 = (int64_t)rb * a.merge_rows;
-    const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);
-    const bool active = cs + 8 * lane < cols;
-    const uint32_t lo = active ? 16u * lane : BUF_OOR;                  // lane's byte offset in a row
-    const int64_t e0 = r0 * cols + cs;                                  // first element of the unit
-    const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
-    const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
-    const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
-    // outputs: M, or y / codes / scales (an empty resource drops the stores)
-    const bool wm = !QDQ && T.M, wy = QDQ && T.y, wp = QDQ && T.codes;
-    const __amdgpu_buffer_rsrc_t rm = make_buf(wm ? T.M + e0 : nullptr, wm ? (int64_t)rows * cols * 2 : 0);
-    const __amdgpu_buffer_rsrc_t ry = make_buf(wy ? T.y + e0 : nullptr, wy ? (int64_t)rows * cols * 2 : 0);
-    const __amdgpu_buffer_rsrc_t rc = make_buf(wp ? T.codes + e0 / 2 : nullptr, wp ? (int64_t)rows * cols / 2 : 0);
-    const __amdgpu_buffer_rsrc_t rs = make_buf(wp ? T.scales + e0 / 16 : nullptr, wp ? (int64_t)rows * cols / 16 : 0);
-    const uint32_t clo = active ? 4u * lane : BUF_OOR;
-    const uint32_t slo = active && (lane & 1) == 0 ? (uint32_t)lane / 2u : BUF_OOR;
-    const uint32_t cstride = (uint32_t)(cols / 2), sstride = (uint32_t)(cols / 16);
-    const float s_t = QDQ ? a.tscale[T.group] : 0.0f, k6 = 6.0f * s_t;
-    uint4 wv[LORA_PREFETCH];
+  if (u >= T.merge_units) return;
+  const int64_t cols = T.cols, ldw = T.ldw;
+  const int r = RK ? RK : T.r;
+  const int rb = u / T.slabs;
+  const int64_t cs = (int64_t)(u - rb * T.slabs) * LORA_SLAB;        // first column of the slab
+  const int64_t r0 = (int64_t)rb * a.merge_rows;
+  const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);
+  const bool active = cs + 8 * lane < cols;
+  const uint32_t lo = active ? 16u * lane : BUF_OOR;                  // lane's byte offset in a row
+  const int64_t e0 = r0 * cols + cs;                                  // first element of the unit
+  const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
+  const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
+  // outputs (an empty resource drops the stores)
+  const bool wy = T.y, wp = T.codes;
+  const __amdgpu_buffer_rsrc_t ry = make_buf(wy ? T.y + e0 : nullptr, wy ? (int64_t)rows * cols * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rc = make_buf(wp ? T.codes + e0 / 2 : nullptr, wp ? (int64_t)rows * cols / 2 : 0);
+  const __amdgpu_buffer_rsrc_t rs = make_buf(wp ? T.scales + e0 / 16 : nullptr, wp ? (int64_t)rows * cols / 16 : 0);
+  const uint32_t clo = active ? 4u * lane : BUF_OOR;
+  const uint32_t slo = active && (lane & 1) == 0 ? (uint32_t)lane / 2u : BUF_OOR;
+  const uint32_t cstride = (uint32_t)(cols / 2), sstride = (uint32_t)(cols / 16);
+  const float s_t = a.tscale[T.group], k6 = 6.0f * s_t;
+  uint4 wv[LORA_PREFETCH];
+#pragma unroll
+  for (int q = 0; q < LORA_PREFETCH; ++q) {
+    wv[q] = buf_load16_nt(rw, lo + q * wstride);
+    LORA_FENCE();
+  }
+  uint32_t bw[BW];
+  fetch_b_words<RK>(T.B, r0, r, bw);
+  float av[LORA_MAX_R][8];                                           // rows k >= r read as 0
+#pragma unroll
+  for (int k = 0; k < LORA_MAX_R; ++k) unpack8(buf_load16(ra, lo + k * mstride), av[k]);
+#pragma unroll 1
+  for (int i = 0; i < rows; i += LORA_PREFETCH) {
 #pragma unroll
     for (int q = 0; q < LORA_PREFETCH; ++q) {
-      wv[q] = buf_load16_nt(rw, lo + q * wstride);
       LORA_FENCE();
-    }
-    uint32_t bw[BW];
-    fetch_b_words<RK>(T.B, r0, r, bw);
-    float av[LORA_MAX_R][8];                                           // rows k >= r read as 0
+      const int ii = i + q;                                          // may pass the last row
+      float bk[LORA_MAX_R];
+      b_row_values<RK>(bw, r0 + min(ii, rows - 1), r, bk);
+      fetch_b_words<RK>(T.B, r0 + min(ii + 1, rows - 1), r, bw);
+      float acc[8];
 #pragma unroll
-    for (int k = 0; k < LORA_MAX_R; ++k) unpack8(buf_load16(ra, lo + k * mstride), av[k]);
-#pragma unroll 1
-    for (int i = 0; i < rows; i += LORA_PREFETCH) {
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
-      for (int q = 0; q < LORA_PREFETCH; ++q) {
-        LORA_FENCE();
-        const int ii = i + q;                                          // may pass the last row
-        float bk[LORA_MAX_R];
-        b_row_values<RK>(bw, r0 + min(ii, rows - 1), r, bk);
-        fetch_b_words<RK>(T.B, r0 + min(ii + 1, rows - 1), r, bw);
-        float acc[8];
+      for (int k = 0; k < LORA_MAX_R; ++k)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-#pragma unroll
-        for (int k = 0; k < LORA_MAX_R; ++k)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(bk[k], av[k][e], acc[e]);
-        float w[8];
-        unpack8(wv[q], w);
-        uint4 o;
-        o.x = pack_bf16x2(w[0] + acc[0], w[1] + acc[1]);
-        o.y = pack_bf16x2(w[2] + acc[2], w[3] + acc[3]);
-        o.z = pack_bf16x2(w[4] + acc[4], w[5] + acc[5]);
-        o.w = pack_bf16x2(w[6] + acc[6], w[7] + acc[7]);
-        if constexpr (QDQ) {                                           // rows past the end: dropped
-          const Nvfp4Chunk qc = nvfp4_qdq_chunk(o, s_t, k6);
-          buf_store16(ry, lo + ii * mstride, qc.y);
-          buf_store4(rc, clo + ii * cstride, qc.codes);
-          buf_store1(rs, slo + ii * sstride, (uint8_t)qc.S);
-        } else {
-          buf_store16(rm, lo + ii * mstride, o);                       // past the end: dropped
-          const uint32_t mo = amax_bits8(o);
-          m = umax(m, (active && ii < rows) ? mo : 0u);
-        }
-        wv[q] = buf_load16_nt(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
-      }
-    }
-  }
-  if constexpr (!QDQ) {
-    // workgroup maximum -> partial[g * grid + b]: this descriptor's group, 0 for the others
-    m = umax(m, dpp_xor1(m));
-    m = umax(m, dpp_xor2(m));
-    m = umax(m, dpp_hmirror(m));
-    m = umax(m, dpp_mirror(m));
-    m = umax(m, swz_xor16(m));
-    m = umax((uint32_t)__builtin_amdgcn_readlane((int)m, 0), (uint32_t)__builtin_amdgcn_readlane((int)m, 32));
-    __shared__ uint32_t wm[4];
-    if (lane == 0) wm[wave] = m;
-    __syncthreads();
-    if ((int)threadIdx.x < a.n_groups) {
-      const uint32_t v = (int)threadIdx.x == T.group ? umax(umax(wm[0], wm[1]), umax(wm[2], wm[3])) : 0u;
-      a.partial[threadIdx.x * gridDim.x + b] = v;
+        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(bk[k], av[k][e], acc[e]);
+      float w[8];
+      unpack8(wv[q], w);
+      uint4 o;
+      o.x = pack_bf16x2(w[0] + acc[0], w[1] + acc[1]);
+      o.y = pack_bf16x2(w[2] + acc[2], w[3] + acc[3]);
+      o.z = pack_bf16x2(w[4] + acc[4], w[5] + acc[5]);
+      o.w = pack_bf16x2(w[6] + acc[6], w[7] + acc[7]);
+      const Nvfp4Chunk qc = nvfp4_qdq_chunk(o, s_t, k6);               // rows past the end: dropped
+      buf_store16(ry, lo + ii * mstride, qc.y);
+      buf_store4(rc, clo + ii * cstride, qc.codes);
+      buf_store1(rs, slo + ii * sstride, (uint8_t)qc.S);
+      wv[q] = buf_load16_nt(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
     }
   }
 }
@@ -460,18 +862,18 @@ static bool all_rank16(const LoraArgs& a) {
 hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   if (all_rank16(a))
-    hipLaunchKernelGGL((k_lora_merge<LORA_MAX_R, false>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_lora_merge_amax<LORA_MAX_R>, dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_lora_merge<0, false>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_lora_merge_amax<0>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_lora_merge_qdq(const LoraArgs& a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   if (all_rank16(a))
-    hipLaunchKernelGGL((k_lora_merge<LORA_MAX_R, true>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_lora_merge_qdq<LORA_MAX_R>, dim3(grid), dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_lora_merge<0, true>), dim3(grid), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(k_lora_merge_qdq<0>, dim3(grid), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

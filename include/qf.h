@@ -288,8 +288,8 @@ qf_status qf_ste_backward_clipped_mxfp4(const uint16_t* g_q, const uint16_t* x, 
  *   G  bf16 [rows, cols] contiguous; dA fp32 [r, cols]; dB fp32 [rows, r].
  *   group  tied-group index for the NVFP4 tensor scale (one per expert per
  *      fused matrix: experts never share a scale).
- * Shapes: cols a multiple of 32 and at most QF_LORA_MAX_COLS; rows >= 0; ldw a
- * multiple of 8 and below 2^24.  W, A, M, G 16-byte aligned; B, dA, dB 4-byte aligned; the packed
+ * Shapes: cols a multiple of 32 and at most QF_LORA_MAX_COLS; rows >= 0 with rows * r
+ * below 2^30; ldw a multiple of 8 and below 2^24.  W, A, M, G 16-byte aligned; B, dA, dB 4-byte aligned; the packed
  * arrays as in qf_qdq_pack_nvfp4.  With r odd, the row of B that ends the array
  * may be read as a whole 4-byte word (the 2 bytes after B, never used).
  * Empty descriptors (rows or cols 0) are skipped.  Errors: QF_ERR_SHAPE for a
@@ -323,11 +323,15 @@ typedef struct qf_lora_desc {
  * descriptor is invalid). */
 size_t qf_lora_workspace(const qf_lora_desc* d, int n);
 /* Host query of the launch layout the LoRA calls choose for these descriptors (nothing
- * is launched; only shapes, ranks and groups are read): out[0] rows per merge unit (32,
- * 16 or 8: units shrink until a launch has at least 512 merge workgroups), out[1] merge
- * workgroups, out[2] rows per gradient workgroup (512 when that still gives 256
- * workgroups, else 256), out[3] gradient workgroups.  out is host int32[4].  Errors as
- * the LoRA calls' shape and argument checks. */
+ * is launched; only shapes, ranks and groups are read).  Pass 1 (merge + tensor scale)
+ * cuts the launch's 32-row x 64-column tiles into equal contiguous runs, one per wave of
+ * 4-wave workgroups: 512 workgroups, or fewer so that a wave keeps at least 4 tiles.
+ * Pass 2 without M (merge again + QDQ) works in units of a 512-column slab of 32 rows,
+ * shrinking to 16 or 8 until the launch has 512 workgroups.  out[0] most pass-1 tiles per
+ * wave, out[1] pass-1 workgroups, out[2] rows per gradient workgroup (512 when that still
+ * gives 256 workgroups, else 256), out[3] gradient workgroups, out[4] rows per pass-2
+ * unit, out[5] pass-2 workgroups.  out is host int32[6].  Errors as the LoRA calls'
+ * shape and argument checks. */
 qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out);
 /* Pass 1: merge into M (skipped for M == NULL) and the NVFP4 tensor scale of
  * every tied group (d_scales[g] as in qf_nvfp4_tensor_scale_grouped, computed

@@ -379,17 +379,23 @@ def _moe_descs(experts):
 
 
 def test_lora_layout_of_the_moe_launches():
-    """The MoE share's launches: 8 experts per launch (16 matrices) take 32-row merge units
-    (1,728 workgroups) and 512-row gradient blocks; 2 experts take 16-row units; one expert
-    8-row units and 256-row gradient blocks."""
+    """The MoE share's launches.  Pass 1: 8 experts per launch (16 matrices, 55,296 tiles of
+    32 x 64) run the full grid of 512 workgroups, 27 tiles per wave at most; 2 experts keep
+    the full grid (7 tiles per wave); one expert's 6,912 tiles take 432 workgroups of 4
+    tiles per wave.  Pass 2 (no M): units of a 512-column slab of 32 rows for 8 experts, 16
+    rows for 2 and 8 rows for one (units shrink until a launch has 512 workgroups).
+    Gradients: 512-row blocks for 8 experts, 256 for one."""
     L = _lib.lib()
-    out = (ctypes.c_int32 * 4)()
+    out = (ctypes.c_int32 * 6)()
+    tiles = (3072 // 32) * (3072 // 64) + (3072 // 32) * (1536 // 64)
+    slabs_rows = lambda rows: (3072 // rows) * 6 + (3072 // rows) * 3      # units per expert
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(8)), 16, out) == 0
-    assert tuple(out) == (32, 8 * (144 + 72), 512, 8 * (6 * 6 + 6 * 3))
+    assert tuple(out) == (27, 512, 512, 8 * (6 * 6 + 6 * 3), 32, 8 * slabs_rows(32) // 4)
+    assert -(-8 * tiles // 2048) == 27
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(2)), 4, out) == 0
-    assert tuple(out)[:2] == (16, 2 * (288 + 144))
+    assert tuple(out)[:2] == (7, 512) and tuple(out)[4:] == (16, 2 * slabs_rows(16) // 4)
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, out) == 0
-    assert tuple(out) == (8, 576 + 288, 256, 12 * 6 + 12 * 3)
+    assert tuple(out) == (4, tiles // 16, 256, 12 * 6 + 12 * 3, 8, slabs_rows(8) // 4)
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, None) == 1
 
 

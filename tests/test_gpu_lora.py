@@ -132,6 +132,24 @@ def test_lora_grouped_strided_and_large_adapters():
         check_grads(c, it["dA"].cpu().numpy(), it["dB"].cpu().numpy(), f"desc {i}")
 
 
+@pytest.mark.parametrize("rank16", [False, True])
+@pytest.mark.parametrize("with_M", [True, False])
+def test_lora_sixteen_descriptors_runs_cross_matrices(rank16, with_M):
+    """The most descriptors a launch takes, all small and ragged (1 to 130 rows, 32 to 640
+    columns), in 6 tied groups in no order: a wave's run of tiles crosses several matrices,
+    columns and groups, and a partial last 32-column group.  Odd and even ranks (the
+    general path) or all rank 16."""
+    rng = np.random.default_rng(123 + rank16 + 2 * with_M)
+    shapes = [(int(rng.integers(1, 131)), 32 * int(rng.integers(1, 21)), 16 if rank16 else int(rng.integers(1, 17)))
+              for _ in range(16)]
+    groups = [int(g) for g in rng.integers(0, 6, 16)]
+    cases = [make_case(r_, c_, k_, seed=500 + i, a_scale=0.1, b_scale=0.1) for i, (r_, c_, k_) in enumerate(shapes)]
+    items = [device_item(c, g, ldw_pad=(32 if i % 3 == 0 else 0), with_M=with_M)
+             for i, (c, g) in enumerate(zip(cases, groups))]
+    s = run_merge_quant(items, 6)
+    check_merge_quant(cases, groups, items, s, 6)
+
+
 def test_lora_zero_adapter_is_identity():
     """B = 0 gives M = W bit for bit, so the result is the plain NVFP4 QDQ of W."""
     c = make_case(64, 512, 16, seed=5)
@@ -261,13 +279,15 @@ def _expert_oracle(e):
     return _EXPERT_CACHE[e]
 
 
-@pytest.mark.parametrize("experts,merge_rows", [(8, 32), (2, 16)])
+@pytest.mark.parametrize("experts,tiles_per_wave", [(8, 27), (2, 7)])
 @pytest.mark.parametrize("with_M", [True, False])
-def test_moe_launch_layout(experts, merge_rows, with_M):
+def test_moe_launch_layout(experts, tiles_per_wave, with_M):
     """The layout the MoE step runs: `experts` full-size experts (gate/up 3072x3072 and
     down 3072x1536, rank 16) per launch, one tied group per matrix (2 x experts groups),
-    with and without the merge scratch.  8 experts per launch is the benchmark's
-    layout (32-row merge units, 512-row gradient blocks); 2 experts take 16-row units.
+    with and without the merge scratch.  8 experts per launch is the benchmark's layout
+    (512 merge workgroups whose waves stream runs of up to 27 tiles across column and
+    matrix boundaries, 512-row gradient blocks); 2 experts give runs of up to 7 tiles
+    (one expert is test_lora_full_size_expert).
     Every tensor scale and every merged weight bit for bit; y, codes and block scales on
     sampled rows of every matrix; dA and dB of every matrix within Higham's bound."""
     ids = list(range(11, 11 + experts))
@@ -278,7 +298,7 @@ def test_moe_launch_layout(experts, merge_rows, with_M):
         items.append(device_item(c, k, with_M=with_M))
     batch = fq.LoraBatch(items)
     layout = fq.qf_lora_layout(batch)
-    assert layout[0] == merge_rows, layout
+    assert tuple(layout[:2]) == (tiles_per_wave, 512), layout
     if experts == 8:
         assert layout[2] == 512, layout
     s = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(batch, len(items))
