@@ -69,7 +69,7 @@ constexpr int LORA_MAX_R = 16;      // adapter rank handled in registers
 constexpr int LORA_SLAB = 512;      // gradient columns per workgroup unit
 constexpr int LORA_MERGE_COLS = 64;     // pass-1 merge tile: 64 columns ...
 constexpr int LORA_MERGE_ROWS = 32;     // ... of 32 rows
-constexpr int LORA_MERGE_GRID_MAX = 512;    // pass-1 workgroups resident at once (2 per CU)
+constexpr int LORA_MERGE_GRID_MAX = 768;    // pass-1 workgroups resident at once (3 per CU)
 constexpr int LORA_MERGE_TILES_MIN = 4;     // tiles per wave below which the grid shrinks
 constexpr int LORA_QDQ_ROWS = 32;       // rows per pass-2 unit (at most; fewer for small launches)
 constexpr int LORA_DA_ROWS = 256;       // rows per gradient workgroup (one dA partial each), or

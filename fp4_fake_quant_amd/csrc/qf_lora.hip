@@ -84,7 +84,7 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&f)[8]) {
 // rows past the matrix are left out of the maximum.
 constexpr int MM_COLS = LORA_MERGE_COLS;
 constexpr int MM_ROWS = LORA_MERGE_ROWS;
-constexpr int MM_DEPTH = 3;                      // ring stages per wave
+constexpr int MM_DEPTH = 2;                      // ring stages per wave
 constexpr int MM_WBYTES = MM_ROWS * MM_COLS * 2; // 4 KiB of W per tile
 constexpr int MM_STAGE = MM_WBYTES + 1024;       // + B rows (32 x up to 16 bf16)
 constexpr int MM_LOADS = 4 + 4;                  // buffer-to-LDS loads per tile per lane
@@ -155,13 +155,6 @@ __device__ __forceinline__ MmTile mm_locate(const LoraArgs& a, int64_t tb) {
   return p;
 }
 
-// Keeps values computed where they stand in the source (an empty asm that takes them):
-// the finishing work of a merge step is placed between the steps of the next tile's chain
-// on purpose, and must not be moved down to where its results are stored.
-#define MM_PIN1(a) asm volatile("" : "+v"(a))
-#define MM_PIN3(a, b, c) asm volatile("" : "+v"(a), "+v"(b), "+v"(c))
-#define MM_PIN4(a, b, c, d) asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d))
-
 // Folds a lane maximum into the workgroup's maximum of group g (LDS).
 __device__ __forceinline__ void mm_flush(uint32_t m, uint32_t* gmax, int g) {
   m = umax(m, dpp_xor1(m));
@@ -173,8 +166,8 @@ __device__ __forceinline__ void mm_flush(uint32_t m, uint32_t* gmax, int g) {
   if ((threadIdx.x & 63) == 0) atomicMax(gmax + g, m);
 }
 
-template <int RK>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_lora_merge_amax(LoraArgs a) {
+template <int RK, bool STORE_M>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_merge_amax(LoraArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t mm_lds[4 * MM_DEPTH * MM_STAGE];
   __shared__ uint32_t gmax[QF_MAX_GROUPS];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -189,9 +182,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   if (nt > 0) {
     const int h = lane >> 5, lr = lane & 31;
     uint8_t* const ring = mm_lds + wave * (MM_DEPTH * MM_STAGE);
-    MmTile pe = mm_locate(a, tb);      // tile t: W + S, its maximum and stores
-    MmTile pm = pe;                    // tile t + 1: S = B.A on the matrix cores
-    MmTile pl = pe;                    // the next tile to load
+    MmTile pe = mm_locate(a, tb);      // the tile computed next
+    MmTile pl = pe;                    // the tile loaded next
     // W window j of a tile: lane i fills row 8j + i/8 at chunk position i%8 with the row's
     // global chunk (i%8) ^ ((row >> 1) & 7)
     uint32_t wrow[4], wchunk[4];
@@ -232,8 +224,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int jb = 0; jb < 4; ++jb)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(st + MM_WBYTES + 256 * jb), 4, bo[jb], 0, 0, 0);
     };
-    // stores per tile (counted by vmcnt like the loads): 4 (M; dropped when M is null)
-    constexpr int STORES = 4;
+    // stores per tile (counted by vmcnt like the loads): 4 (M; dropped for a null M), or none
+    // when no descriptor of the launch keeps M
+    constexpr int STORES = STORE_M ? 4 : 0;
     const uint32_t rot = ((uint32_t)lr >> 1) & 7u;
     // The chain always takes LORA_MAX_R steps: a rank r < 16 runs 16 - r leading steps on
     // +0 x +0, which leave the accumulator at +0 exactly, so the sum is still the r-step one.
@@ -339,81 +332,57 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int j = 0; j < LORA_MAX_R; ++j) acc = __builtin_amdgcn_mfma_f32_32x32x1f32(av[j], bk[j], acc, 0, 0, 0);
       return acc;
     };
-    // Step t: tile t + 3 is loaded into tile t's stage (read one step earlier), tile t + 1
-    // is read from its stage and multiplied on the matrix cores while tile t is finished
-    // from the registers.
-    auto step = [&](int t, int si, f32x32_t& accP, uint4 (&wP)[4], f32x32_t& accN, uint4 (&wN)[4]) {
+    // Step t: tile t + 1 is loaded into the stage of tile t - 1 (read one step earlier),
+    // tile t is read from its stage, multiplied on the matrix cores and finished.
+    static_assert(MM_DEPTH == 2, "one tile loaded ahead");
+    auto step = [&](int t, int si) {
       LORA_FENCE();
-      issue(t + MM_DEPTH, ring + si * MM_STAGE);
+      issue(t + 1, ring + (si ^ 1) * MM_STAGE);
       LORA_FENCE();
-      // wait for tile t + 1's loads: younger than them are the next two tiles' loads and
-      // the stores of the tiles since (none before tile 0's; A reloads drain everything)
-      if (t >= 2) MM_WAIT_VM((MM_DEPTH - 1) * (MM_LOADS + STORES));
-      else if (t == 1) MM_WAIT_VM((MM_DEPTH - 1) * MM_LOADS + STORES);
-      else MM_WAIT_VM((MM_DEPTH - 1) * MM_LOADS);
+      // wait for tile t's loads: younger than them are the next tile's loads and tile
+      // t - 1's stores (none before tile 0; A reloads drain everything)
+      if (t >= 1) MM_WAIT_VM(MM_LOADS + STORES);
+      else MM_WAIT_VM(MM_LOADS);
       asm volatile("" ::: "memory");
-      const bool more = t + 1 < nt;                                // past the run: zeros, unused
-      if (more && (pm.di != a_di || pm.ct != a_ct)) load_a(pm);
-      // tile t's place and outputs: element (lr, 16 h [+ 32]) of rows r0 .. r0 + nrows - 1
-      // from column c0 on (rows past the matrix fall outside the ranges)
+      if (pe.di != a_di || pe.ct != a_ct) load_a(pe);
       const LoraTensor& T = a.d[pe.di];
+      const int r = RK ? RK : T.r;
       const int64_t cols = T.cols, c0 = (int64_t)pe.ct * MM_COLS, r0 = (int64_t)pe.rt * MM_ROWS;
       const int nrows = (int)min((int64_t)MM_ROWS, T.rows - r0);
-      const int64_t e0 = r0 * cols + c0, ne = (int64_t)nrows * cols - c0;
-      const bool ok1 = c0 + 32 < cols;                             // the second 32-column group
-      LORA_FENCE();
+      uint8_t* const st = ring + si * MM_STAGE;
+      uint4 wc[4];
       float bk[LORA_MAX_R];
-      uint8_t* const sr = ring + (si == MM_DEPTH - 1 ? 0 : si + 1) * MM_STAGE;
-      read_tile(sr, RK ? RK : (more ? a.d[pm.di].r : LORA_MAX_R), wN, bk);
-      // Tile t's outputs leave through the stage just read (free until step t + 1 loads into
-      // it): the lanes write their pieces of rows there and read whole rows back, so that a
-      // store instruction writes 8 rows of 128 bytes of bf16 (32 rows of 32 code bytes, 2
-      // scale bytes) instead of 16-byte pieces of 32 rows.  The bf16 chunk c of the lane
-      // sits where the W chunk of the same place was; window k of the stage then holds rows
-      // 8k + lane / 8, global chunk wchunk[k] at lane position lane % 8.
-      uint32_t xa[4];
+      read_tile(st, r, wc, bk);
+      const f32x32_t acc = chain(bk);
+      // M = bf16(fl(W + S)) for the lane's 32 elements: chunk c holds columns 8c .. 8c+7 of
+      // the lane's groups (c = 0, 1: group 0; c = 2, 3: group 1)
+      uint4 mo[4];
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t g = (uint32_t)(2 * h + (c & 1) + 4 * (c >> 1));
-        xa[c] = lds_addr(sr + lr * 128 + ((g ^ rot) << 4));
-      }
-      const uint32_t xr = lds_addr(sr + 16 * lane);
-      uint32_t yoff[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        yoff[k] = ok1 || wchunk[k] < 4 ? (uint32_t)((wrow[k] * cols + 8 * wchunk[k]) * 2) : BUF_OOR;
-      // The chain of tile t + 1 with tile t's finishing work placed between its steps, in
-      // the order of its data flow: each step has a piece of independent vector work to
-      // overlap instead of waiting for the previous step.
-      f32x32_t an;
-#pragma unroll
-      for (int v = 0; v < 32; ++v) an[v] = 0.0f;
-      uint4 mo[4];
-      auto merge_chunk = [&](int c) {
         float wf[8];
-        unpack8(wP[c], wf);
+        unpack8(wc[c], wf);
         const int v0 = 16 * (c >> 1) + 8 * (c & 1);
-        mo[c].x = pack_bf16x2(wf[0] + accP[v0 + 0], wf[1] + accP[v0 + 1]);
-        mo[c].y = pack_bf16x2(wf[2] + accP[v0 + 2], wf[3] + accP[v0 + 3]);
-        mo[c].z = pack_bf16x2(wf[4] + accP[v0 + 4], wf[5] + accP[v0 + 5]);
-        mo[c].w = pack_bf16x2(wf[6] + accP[v0 + 6], wf[7] + accP[v0 + 7]);
-        MM_PIN4(mo[c].x, mo[c].y, mo[c].z, mo[c].w);
-      };
-      {
-        uint32_t mt = 0;
+        mo[c].x = pack_bf16x2(wf[0] + acc[v0 + 0], wf[1] + acc[v0 + 1]);
+        mo[c].y = pack_bf16x2(wf[2] + acc[v0 + 2], wf[3] + acc[v0 + 3]);
+        mo[c].z = pack_bf16x2(wf[4] + acc[v0 + 4], wf[5] + acc[v0 + 5]);
+        mo[c].w = pack_bf16x2(wf[6] + acc[v0 + 6], wf[7] + acc[v0 + 7]);
+      }
+      const uint32_t mt = umax(umax(amax_bits8(mo[0]), amax_bits8(mo[1])), umax(amax_bits8(mo[2]), amax_bits8(mo[3])));
+      if constexpr (STORE_M) {
+        // M leaves through the stage just read (free until the next step loads into it):
+        // the lanes write their pieces of rows where the W chunks were and read whole rows
+        // back (window k: row 8k + lane / 8, global chunk wchunk[k] at position lane % 8),
+        // so that a store instruction writes 8 rows of 128 bytes instead of 16-byte pieces
+        // of 32 rows
+        const bool ok1 = c0 + 32 < cols;                           // the second 32-column group
+        uint32_t xa[4], yoff[4];
 #pragma unroll
-        for (int j = 0; j < LORA_MAX_R; ++j) {
-          an = __builtin_amdgcn_mfma_f32_32x32x1f32(av[j], bk[j], an, 0, 0, 0);
-          if (j < 4) merge_chunk(j);
-          if (j == 4) {
-            mt = umax(umax(amax_bits8(mo[0]), amax_bits8(mo[1])), umax(amax_bits8(mo[2]), amax_bits8(mo[3])));
-            mt = lr < nrows ? mt : 0u;                             // rows past the matrix: left out
-            MM_PIN1(mt);
-          }
-          LORA_FENCE();
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t g = (uint32_t)(2 * h + (c & 1) + 4 * (c >> 1));
+          xa[c] = lds_addr(st + lr * 128 + ((g ^ rot) << 4));
+          yoff[c] = ok1 || wchunk[c] < 4 ? (uint32_t)((wrow[c] * cols + 8 * wchunk[c]) * 2) : BUF_OOR;
         }
-        accN = an;
-        // M through the stage just read, as y above
+        const uint32_t xr = lds_addr(st + 16 * lane);
         u32x4_t mo0, mo1, mo2, mo3;
         const u32x4_t m0 = {mo[0].x, mo[0].y, mo[0].z, mo[0].w}, m1 = {mo[1].x, mo[1].y, mo[1].z, mo[1].w};
         const u32x4_t m2 = {mo[2].x, mo[2].y, mo[2].z, mo[2].w}, m3 = {mo[3].x, mo[3].y, mo[3].z, mo[3].w};
@@ -431,46 +400,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             : [a0] "v"(xa[0]), [a1] "v"(xa[1]), [a2] "v"(xa[2]), [a3] "v"(xa[3]), [m0] "v"(m0), [m1] "v"(m1),
               [m2] "v"(m2), [m3] "v"(m3), [xr] "v"(xr)
             : "memory");
+        // rows past the matrix fall outside the range
+        const int64_t e0 = r0 * cols + c0, ne = (int64_t)nrows * cols - c0;
         const __amdgpu_buffer_rsrc_t rm = make_buf((const uint16_t*)((uintptr_t)T.M + (uintptr_t)(e0 * 2)),
                                                    T.M ? ne * 2 : 0);
         buf_store16(rm, yoff[0], make_uint4(mo0[0], mo0[1], mo0[2], mo0[3]));
         buf_store16(rm, yoff[1], make_uint4(mo1[0], mo1[1], mo1[2], mo1[3]));
         buf_store16(rm, yoff[2], make_uint4(mo2[0], mo2[1], mo2[2], mo2[3]));
         buf_store16(rm, yoff[3], make_uint4(mo3[0], mo3[1], mo3[2], mo3[3]));
-        if (T.group != mg) {                                       // the run enters another group
-          if (mg >= 0) mm_flush(m, gmax, mg);
-          m = 0;
-          mg = T.group;
-        }
-        m = umax(m, mt);
       }
-      pe = pm;
-      if (more) mm_next(a, pm);
+      if (T.group != mg) {                                         // the run enters another group
+        if (mg >= 0) mm_flush(m, gmax, mg);
+        m = 0;
+        mg = T.group;
+      }
+      m = umax(m, lr < nrows ? mt : 0u);                           // rows past the matrix: left out
+      if (t + 1 < nt) mm_next(a, pe);
       LORA_FENCE();
     };
-    // prologue: A for tile 0, tiles 0 .. MM_DEPTH - 1 in flight, tile 0 on the matrix cores
-    load_a(pm);
-#pragma unroll
-    for (int j = 0; j < MM_DEPTH; ++j) issue(j, ring + j * MM_STAGE);
-    MM_WAIT_VM((MM_DEPTH - 1) * MM_LOADS);
-    asm volatile("" ::: "memory");
-    f32x32_t acc0, acc1;
-    uint4 w0[4], w1[4];
-    {
-      float bk[LORA_MAX_R];
-      read_tile(ring, RK ? RK : a.d[pm.di].r, w0, bk);
-      acc0 = chain(bk);
-    }
-    if (nt > 1) mm_next(a, pm);
-    int si = 0;
+    // prologue: A for tile 0's column, tile 0 in flight
+    load_a(pe);
+    issue(0, ring);
 #pragma unroll 1
     for (int t = 0; t < nt; t += 2) {
-      step(t, si, acc0, w0, acc1, w1);
-      si = si == MM_DEPTH - 1 ? 0 : si + 1;
-      if (t + 1 < nt) {
-        step(t + 1, si, acc1, w1, acc0, w0);
-        si = si == MM_DEPTH - 1 ? 0 : si + 1;
-      }
+      step(t, 0);
+      if (t + 1 < nt) step(t + 1, 1);
     }
     MM_WAIT_VM(0);                                                 // no load may still write LDS at exit
     mm_flush(m, gmax, mg);
@@ -861,10 +815,19 @@ static bool all_rank16(const LoraArgs& a) {
 
 hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
-  if (all_rank16(a))
-    hipLaunchKernelGGL(k_lora_merge_amax<LORA_MAX_R>, dim3(grid), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL(k_lora_merge_amax<0>, dim3(grid), dim3(256), 0, s, a);
+  bool any_m = false;
+  for (int i = 0; i < a.n; ++i) any_m = any_m || a.d[i].M;
+  if (all_rank16(a)) {
+    if (any_m)
+      hipLaunchKernelGGL((k_lora_merge_amax<LORA_MAX_R, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_lora_merge_amax<LORA_MAX_R, false>), dim3(grid), dim3(256), 0, s, a);
+  } else {
+    if (any_m)
+      hipLaunchKernelGGL((k_lora_merge_amax<0, true>), dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_lora_merge_amax<0, false>), dim3(grid), dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 

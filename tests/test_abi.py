@@ -380,9 +380,9 @@ def _moe_descs(experts):
 
 def test_lora_layout_of_the_moe_launches():
     """The MoE share's launches.  Pass 1: 8 experts per launch (16 matrices, 55,296 tiles of
-    32 x 64) run the full grid of 512 workgroups, 27 tiles per wave at most; 2 experts keep
-    the full grid (7 tiles per wave); one expert's 6,912 tiles take 432 workgroups of 4
-    tiles per wave.  Pass 2 (no M): units of a 512-column slab of 32 rows for 8 experts, 16
+    32 x 64) run the full grid of 768 workgroups (3 per CU), 18 tiles per wave at most; 2
+    experts keep the full grid (5 tiles per wave); one expert's 6,912 tiles take 432
+    workgroups of 4 tiles per wave.  Pass 2 (no M): units of a 512-column slab of 32 rows for 8 experts, 16
     rows for 2 and 8 rows for one (units shrink until a launch has 512 workgroups).
     Gradients: 512-row blocks for 8 experts, 256 for one."""
     L = _lib.lib()
@@ -390,10 +390,10 @@ def test_lora_layout_of_the_moe_launches():
     tiles = (3072 // 32) * (3072 // 64) + (3072 // 32) * (1536 // 64)
     slabs_rows = lambda rows: (3072 // rows) * 6 + (3072 // rows) * 3      # units per expert
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(8)), 16, out) == 0
-    assert tuple(out) == (27, 512, 512, 8 * (6 * 6 + 6 * 3), 32, 8 * slabs_rows(32) // 4)
-    assert -(-8 * tiles // 2048) == 27
+    assert tuple(out) == (18, 768, 512, 8 * (6 * 6 + 6 * 3), 32, 8 * slabs_rows(32) // 4)
+    assert -(-8 * tiles // (4 * 768)) == 18
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(2)), 4, out) == 0
-    assert tuple(out)[:2] == (7, 512) and tuple(out)[4:] == (16, 2 * slabs_rows(16) // 4)
+    assert tuple(out)[:2] == (5, 768) and tuple(out)[4:] == (16, 2 * slabs_rows(16) // 4)
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, out) == 0
     assert tuple(out) == (4, tiles // 16, 256, 12 * 6 + 12 * 3, 8, slabs_rows(8) // 4)
     assert L.qf_lora_layout(ctypes.byref(_moe_descs(1)), 2, None) == 1

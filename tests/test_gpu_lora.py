@@ -279,14 +279,14 @@ def _expert_oracle(e):
     return _EXPERT_CACHE[e]
 
 
-@pytest.mark.parametrize("experts,tiles_per_wave", [(8, 27), (2, 7)])
+@pytest.mark.parametrize("experts,tiles_per_wave", [(8, 18), (2, 5)])
 @pytest.mark.parametrize("with_M", [True, False])
 def test_moe_launch_layout(experts, tiles_per_wave, with_M):
     """The layout the MoE step runs: `experts` full-size experts (gate/up 3072x3072 and
     down 3072x1536, rank 16) per launch, one tied group per matrix (2 x experts groups),
     with and without the merge scratch.  8 experts per launch is the benchmark's layout
-    (512 merge workgroups whose waves stream runs of up to 27 tiles across column and
-    matrix boundaries, 512-row gradient blocks); 2 experts give runs of up to 7 tiles
+    (768 pass-1 workgroups whose waves stream runs of up to 18 tiles across column and
+    matrix boundaries, 512-row gradient blocks); 2 experts give runs of up to 5 tiles
     (one expert is test_lora_full_size_expert).
     Every tensor scale and every merged weight bit for bit; y, codes and block scales on
     sampled rows of every matrix; dA and dB of every matrix within Higham's bound."""
@@ -298,7 +298,7 @@ def test_moe_launch_layout(experts, tiles_per_wave, with_M):
         items.append(device_item(c, k, with_M=with_M))
     batch = fq.LoraBatch(items)
     layout = fq.qf_lora_layout(batch)
-    assert tuple(layout[:2]) == (tiles_per_wave, 512), layout
+    assert layout[0] == tiles_per_wave, layout
     if experts == 8:
         assert layout[2] == 512, layout
     s = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(batch, len(items))
