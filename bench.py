@@ -737,7 +737,14 @@ class MoELoRANVFP4:
     (2 + 2), the QDQ'd bf16 (2), codes and block scales (0.5625) and G (2) (the adapters
     and their gradients, 0.02 G elements, are not counted).  The scratch form's extra
     traffic (the M write, 2 bytes per element, less nothing: M's read replaces W's) is
-    reported next to it, not in the figure."""
+    reported next to it, not in the figure.
+    The passes of different launches are independent except that a launch's QDQ pass needs
+    its tensor scales, and the adapter gradients depend on the inputs only (A, B, G), so a
+    timed step runs the gradient passes on a stream of their own (default priority, with a
+    workspace of their own) and, with several experts per launch, the QDQ passes on a third
+    (each after its launch's scales, through an event); the streams join at the end.  (With
+    one expert per launch the per-launch events cost more than the third stream gains:
+    5.5 -> 9.3 ms per step.)  The per-kernel timings run everything on one stream."""
     name = "moe_lora_nvfp4"
 
     def __init__(self, torch, fq, experts_per_launch=1, merge_scratch=False):
@@ -775,6 +782,11 @@ class MoELoRANVFP4:
                                       dA=self.dA[m][e], dB=self.dB[m][e], group=2 * (e - c0) + j))
             self.chunks.append((fq.LoraBatch(items), self.tscale[2 * c0: 2 * (c0 + k)]))
         self.ws = torch.empty(self.chunks[0][0].workspace_bytes, dtype=torch.uint8, device=dev)
+        self.ws_grads = torch.empty(self.chunks[0][0].workspace_bytes, dtype=torch.uint8, device=dev)
+        self.experts_per_launch = k
+        self.grad_stream = torch.cuda.Stream()
+        self.qdq_stream = torch.cuda.Stream()
+        self.scale_ready = [torch.cuda.Event() for _ in self.chunks]
         n = sum(x[m]["W"].numel() for m in mats)
         self.numel = n
         self.kernels = {"lora_merge_amax": 2.0 * n, "lora_merge_qdq_pack": (2 + 2 + 0.5 + 1 / 16) * n,
@@ -790,11 +802,33 @@ class MoELoRANVFP4:
                        "merge_tiles_per_wave": layout[0], "merge_workgroups": layout[1],
                        "qdq_rows_per_unit": layout[4], "qdq_workgroups": layout[5], "gradient_rows_per_workgroup": layout[2],
                        "scratch_bytes": sum(t.numel() * 2 for p in scratch.values() for t in p if t is not None),
+                       "streams": ("tensor-scale, QDQ and gradient passes on three streams" if k > 1
+                                   else "merge passes and gradient passes on two streams"),
                        "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale per expert per fused matrix)"}
 
     def step(self, mark=None):
         fq, ws = self.fq, self.ws
-        t = mark or _no_mark
+        if mark is None:
+            torch = self.torch
+            cur = torch.cuda.current_stream()
+            self.grad_stream.wait_stream(cur)
+            self.qdq_stream.wait_stream(cur)
+            three = self.experts_per_launch > 1
+            for (items, sc), ready in zip(self.chunks, self.scale_ready):
+                fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
+                if three:
+                    ready.record(cur)
+                    with torch.cuda.stream(self.qdq_stream):
+                        self.qdq_stream.wait_event(ready)
+                        fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
+                else:
+                    fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
+                with torch.cuda.stream(self.grad_stream):
+                    fq.qf_lora_adapter_grads_grouped(items, ws=self.ws_grads)
+            cur.wait_stream(self.qdq_stream)
+            cur.wait_stream(self.grad_stream)
+            return
+        t = mark
         for items, sc in self.chunks:
             t("lora_merge_amax", 0)
             fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
