@@ -470,6 +470,7 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int qdq_rows, int da_r
     a->merge_tiles = c.merge_tiles;
     a->merge_band = (int)std::max<int64_t>(1, c.merge_wg > 0 ? ceil_div(c.merge_tiles, 4 * c.merge_wg) : 1);
     a->merge_rows = qdq_rows;
+    a->qdq_wg = (int)c.qdq_wg;
     a->da_rows = da_rows;
   }
   return c;

@@ -110,6 +110,7 @@ struct LoraArgs {
   int64_t merge_tiles; // pass-1 tiles of the launch
   int merge_band;      // row tiles per band of the pass-1 order (the longest wave run)
   int merge_rows;      // rows per pass-2 unit (32, 16 or 8)
+  int qdq_wg;          // pass-2 workgroups (four units each)
   int da_rows;         // rows per gradient workgroup (LORA_DA_ROWS or LORA_DA_ROWS_MAX)
   uint32_t* partial;   // merge amax partials [n_groups][merge workgroups]
   const float* tscale; // merge-and-QDQ: NVFP4 tensor scale of every tied group

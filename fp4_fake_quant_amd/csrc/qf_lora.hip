@@ -602,6 +602,164 @@ __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumula
   }
 }
 
+// ------------------------------------------- pass 1 without M: bounded merge ---
+// max|M| of a tied group needs M exactly only where an element could reach the running
+// maximum L, and a cheap bound says where.  For element (i, j) the computed sum obeys
+// |S_ij| <= U_i,l = fl(bsum_i * a_l) + 2^-100, with bsum_i = sum_k |B[i][k]| (row i) and a_l
+// = 1.001 max |A| over the 16 x 8 slice of the lane: the relative slack (1e-3) covers the
+// sum's 16 roundings and those of bsum and the product many times over, the absolute one
+// products and sums below fp32's normal range.  Rounding is monotone, so
+// |M_ij| = |bf16(fl(W_ij + S_ij))| <= bf16(fl(|W_ij| + U)), and with t = fl(max|W| + U)
+// over the lane's 8 elements, t <= prev(L) (the bf16 value below L) proves that none of them
+// exceeds L.  The lane's row is merged exactly (the same sequential fp32 sum as everywhere
+// else) only when some lane of the wave fails that test; a NaN or an infinity anywhere in
+// W, A or B makes t fail it, and a NaN L makes every test fail.  L only ever holds exactly
+// merged values of the group, so the group's maximum (bit pattern included) is the one a
+// full merge finds.
+//
+// Work split: the units of the merge-and-QDQ pass (a 512-column slab of merge_rows rows,
+// lane l on columns 8l .. 8l+7), numbered four per workgroup of that pass, cut into equal
+// contiguous runs, one per wave of a grid that stays resident; the running maximum is kept
+// per wave across the units of one group, and shared through the workgroup's LDS maximum.
+constexpr int LORA_P1_PREFETCH = 8;                    // rows of W in flight per wave
+
+template <int RK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_merge_amax_bounded(LoraArgs a) {
+  __shared__ uint32_t gmax[QF_MAX_GROUPS];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if ((int)threadIdx.x < QF_MAX_GROUPS) gmax[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t units = 4 * (int64_t)a.qdq_wg;
+  const int64_t nw = (int64_t)gridDim.x * 4, w = (int64_t)blockIdx.x * 4 + wave;
+  const int64_t u0 = w * units / nw, u1 = (w + 1) * units / nw;
+  uint32_t L = 0;                                                    // wave-uniform, group mg
+  int mg = -1;
+#pragma unroll 1
+  for (int64_t uf = u0; uf < u1; ++uf) {
+    const int di = find_desc_wg(a, (int)(uf >> 2));
+    const LoraTensor& T = a.d[di];
+    const int ul = (int)(uf - 4 * (int64_t)T.merge_wg_begin);
+    if (ul >= T.merge_units) continue;                               // padding of the descriptor's last workgroup
+    if (T.group != mg) {
+      if (mg >= 0 && lane == 0) atomicMax(gmax + mg, L);
+      L = 0;
+      mg = T.group;
+    }
+    const int64_t cols = T.cols, ldw = T.ldw;
+    const int r = RK ? RK : T.r;
+    const int rb = ul / T.slabs;
+    const int64_t cs = (int64_t)(ul - rb * T.slabs) * LORA_SLAB;
+    const int64_t r0 = (int64_t)rb * a.merge_rows;
+    const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);   // at most 32
+    const bool active = cs + 8 * lane < cols;
+    const uint32_t lo = active ? 16u * lane : BUF_OOR;
+    const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
+    const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
+    uint4 ap[LORA_MAX_R];                                            // A's slice, bf16 (rows k >= r: 0)
+#pragma unroll
+    for (int k = 0; k < LORA_MAX_R; ++k) ap[k] = buf_load16(ra, lo + k * mstride);
+    // bsum of row r0 + lane (lanes below rows)
+    float bsum = 0.0f;
+    {
+      const __amdgpu_buffer_rsrc_t rbb = make_buf(T.B + r0 * r, (int64_t)rows * r * 2);
+      const uint32_t bo = lane < rows ? (uint32_t)(lane * r * 2) : BUF_OOR;
+      if constexpr (RK == LORA_MAX_R) {
+        const uint4 b0 = buf_load16(rbb, bo), b1 = buf_load16(rbb, bo + 16);
+        const uint32_t bwv[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+        for (int q = 0; q < 8; ++q) bsum = (bsum + fabsf(bf16_lo(bwv[q]))) + fabsf(bf16_hi(bwv[q]));
+      } else {
+#pragma unroll
+        for (int k = 0; k < LORA_MAX_R; ++k)
+          bsum += fabsf(__uint_as_float((uint32_t)buf_load2(rbb, k < r ? bo + 2u * k : BUF_OOR) << 16));
+      }
+    }
+    uint4 wv[LORA_P1_PREFETCH];
+#pragma unroll
+    for (int q = 0; q < LORA_P1_PREFETCH; ++q) {
+      LORA_FENCE();
+      wv[q] = buf_load16(rw, lo + q * wstride);
+    }
+    LORA_FENCE();
+    uint32_t amx = 0;
+#pragma unroll
+    for (int k = 0; k < LORA_MAX_R; ++k) amx = umax(amx, amax_bits8(ap[k]));
+    const float a_l = __uint_as_float(amx << 16) * 1.001f;
+    // t of the lane's 8 elements of row ii (w: the row's chunk); true where the lane's
+    // elements could exceed L
+    auto test = [&](const uint4& wq, int ii) {
+      const float sb = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(bsum), ii & 31));
+      const float ub = __builtin_fmaf(sb, a_l, 0x1p-100f);
+      const float t = __uint_as_float(amax_bits8(wq) << 16) + ub;
+      const float prevL = L ? __uint_as_float((L - 1u) << 16) : -1.0f;
+      return ii < rows && !(t <= prevL);
+    };
+#pragma unroll 1
+    for (int i = 0; i < rows; i += LORA_P1_PREFETCH) {
+      {
+        const uint32_t gl = __hip_atomic_load(gmax + mg, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        L = umax(L, (uint32_t)__builtin_amdgcn_readfirstlane((int)gl));
+      }
+      // the batch's rows are tested first; rows that may hold a new maximum are merged
+      // after, one at a time (their chunk loaded again, from the cache)
+      uint32_t cmask = 0;
+#pragma unroll
+      for (int q = 0; q < LORA_P1_PREFETCH; ++q) {
+        LORA_FENCE();
+        if (__builtin_amdgcn_ballot_w64(test(wv[q], i + q))) cmask |= 1u << q;
+        wv[q] = buf_load16(rw, lo + (i + q + LORA_P1_PREFETCH) * wstride);   // past the end: zeros
+      }
+      LORA_FENCE();
+#pragma unroll 1
+      while (cmask) {
+        const int ii = i + __builtin_ctz(cmask);
+        cmask &= cmask - 1;
+        const uint4 wq = buf_load16(rw, lo + ii * wstride);
+        if (!__builtin_amdgcn_ballot_w64(test(wq, ii))) continue;      // L has grown since
+        uint32_t bw[BW];
+        fetch_b_words<RK>(T.B, r0 + ii, r, bw);
+        float bk[LORA_MAX_R];
+        b_row_values<RK>(bw, r0 + ii, r, bk);
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+        // A is unpacked here, not once per unit (128 more registers would not fit): the
+        // packed words pass through an opaque zero made inside the loop, so the compiler
+        // cannot hoist the unpacking
+        uint32_t z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+#pragma unroll
+        for (int k = 0; k < LORA_MAX_R; ++k) {
+          const uint4 apk = make_uint4(ap[k].x ^ z, ap[k].y ^ z, ap[k].z ^ z, ap[k].w ^ z);
+          float av[8];
+          unpack8(apk, av);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(bk[k], av[e], acc[e]);
+        }
+        float wf[8];
+        unpack8(wq, wf);
+        uint4 o;
+        o.x = pack_bf16x2(wf[0] + acc[0], wf[1] + acc[1]);
+        o.y = pack_bf16x2(wf[2] + acc[2], wf[3] + acc[3]);
+        o.z = pack_bf16x2(wf[4] + acc[4], wf[5] + acc[5]);
+        o.w = pack_bf16x2(wf[6] + acc[6], wf[7] + acc[7]);
+        uint32_t mt = active ? amax_bits8(o) : 0u;
+        mt = umax(mt, dpp_xor1(mt));
+        mt = umax(mt, dpp_xor2(mt));
+        mt = umax(mt, dpp_hmirror(mt));
+        mt = umax(mt, dpp_mirror(mt));
+        mt = umax(mt, swz_xor16(mt));
+        mt = umax((uint32_t)__builtin_amdgcn_readlane((int)mt, 0), (uint32_t)__builtin_amdgcn_readlane((int)mt, 32));
+        L = umax(L, mt);
+      }
+    }
+  }
+  if (mg >= 0 && lane == 0) atomicMax(gmax + mg, L);
+  __syncthreads();
+  if ((int)threadIdx.x < a.n_groups) a.partial[threadIdx.x * gridDim.x + blockIdx.x] = gmax[threadIdx.x];
+}
+
 // --------------------------------------------- fused adapter gradients ---
 // One pass over G for both gradients.  A workgroup owns a unit of up to a.da_rows (256
 // or 512) rows of one LORA_SLAB-column slab and walks it 32 rows at a time: the
@@ -821,12 +979,12 @@ hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s) {
     if (any_m)
       hipLaunchKernelGGL((k_lora_merge_amax<LORA_MAX_R, true>), dim3(grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((k_lora_merge_amax<LORA_MAX_R, false>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_lora_merge_amax_bounded<LORA_MAX_R>, dim3(grid), dim3(256), 0, s, a);
   } else {
     if (any_m)
       hipLaunchKernelGGL((k_lora_merge_amax<0, true>), dim3(grid), dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL((k_lora_merge_amax<0, false>), dim3(grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(k_lora_merge_amax_bounded<0>, dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }
