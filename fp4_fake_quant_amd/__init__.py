@@ -13,7 +13,7 @@ import ctypes
 
 import torch
 
-from ._lib import GgufTensor, LoraDesc, StTensor, TensorDesc, lib
+from ._lib import GgufTensor, LoraDesc, LoraExpertsDesc, StTensor, TensorDesc, lib
 
 QF_OK = 0
 QF_QDQ_A, QF_QDQ_W, QF_FP4_CORES, QF_MX_NOCLIP = 1, 2, 4, 8
@@ -391,6 +391,76 @@ def qf_lora_adapter_grads_grouped(items, accumulate=False, ws=None):
     _check(lib().qf_lora_adapter_grads_grouped(b.ref, b.n, int(bool(accumulate)), _p(ws),
                                                ws.numel() * ws.element_size(), _stream()),
            "qf_lora_adapter_grads_grouped")
+
+
+class LoraExperts:
+    """Stacked-experts descriptors for the qf_lora_experts_* calls, built once and reusable.
+
+    items: list of dict(W, A, B, group, group_stride=1, y=None, codes=None, scales=None,
+    G=None, dA=None, dB=None) of contiguous device tensors with a leading expert axis:
+    W [E, rows, cols] bf16, A [E, r, cols], B [E, rows, r], y [E, rows, cols],
+    codes [E, rows, cols/2], scales [E, rows, cols/16], G [E, rows, cols],
+    dA [E, r, cols] and dB [E, rows, r] float32.  Expert e's tied group is
+    group + e * group_stride.  There is no merge scratch (M).
+    """
+
+    def __init__(self, items):
+        self.items = items
+        self.arr = (LoraExpertsDesc * max(len(items), 1))()
+        self.n = len(items)
+        self.device = items[0]["W"].device if items else torch.device("cuda")
+        for i, it in enumerate(items):
+            W, A, B = _bf16(it["W"], "W"), _bf16(it["A"], "A"), _bf16(it["B"], "B")
+            for t, name in ((W, "W"), (A, "A"), (B, "B")):
+                if t.dim() != 3 or not t.is_contiguous():
+                    raise ValueError(f"{name} must be a contiguous 3-D tensor [experts, ...]")
+            E, rows, cols = W.shape
+            r = A.shape[1]
+            if tuple(A.shape) != (E, r, cols) or tuple(B.shape) != (E, rows, r):
+                raise ValueError(f"adapter shapes {tuple(A.shape)}, {tuple(B.shape)} do not fit W {tuple(W.shape)}")
+            x = self.arr[i]
+            d = x.d
+            d.W, d.rows, d.cols, d.ldw = W.data_ptr(), rows, cols, cols
+            d.A, d.B, d.r, d.group = A.data_ptr(), B.data_ptr(), r, int(it.get("group", 0))
+            d.M = None
+            for name in ("y", "codes", "scales", "G", "dA", "dB"):
+                t = it.get(name)
+                if t is not None and (not t.is_contiguous() or t.shape[0] != E):
+                    raise ValueError(f"{name} must be contiguous with {E} experts")
+                setattr(d, name, t.data_ptr() if t is not None else None)
+            x.count = E
+            x.group_stride = int(it.get("group_stride", 1))
+        self.ref = ctypes.byref(self.arr)
+        self.workspace_bytes = lib().qf_lora_experts_workspace(self.ref, self.n)
+
+
+def qf_lora_experts_layout(ex):
+    """The launch layout of the stacked-experts calls (as qf_lora_layout)."""
+    out = (ctypes.c_int32 * 6)()
+    _check(lib().qf_lora_experts_layout(ex.ref, ex.n, out), "qf_lora_experts_layout")
+    return tuple(out)
+
+
+def qf_lora_experts_merge_tensor_scale_nvfp4(ex, n_groups, d_scales=None, d_nonfinite=None, ws=None):
+    ws = _lora_ws(ex, ws)
+    if d_scales is None:
+        d_scales = torch.empty(n_groups, dtype=torch.float32, device=ex.device)
+    _check(lib().qf_lora_experts_merge_tensor_scale_nvfp4(ex.ref, ex.n, n_groups, _p(d_scales), _p(d_nonfinite),
+                                                           _p(ws), ws.numel() * ws.element_size(), _stream()),
+           "qf_lora_experts_merge_tensor_scale_nvfp4")
+    return d_scales
+
+
+def qf_lora_experts_merge_qdq_pack_nvfp4(ex, d_scales):
+    _check(lib().qf_lora_experts_merge_qdq_pack_nvfp4(ex.ref, ex.n, _p(d_scales), _stream()),
+           "qf_lora_experts_merge_qdq_pack_nvfp4")
+
+
+def qf_lora_experts_adapter_grads(ex, accumulate=False, ws=None):
+    ws = _lora_ws(ex, ws)
+    _check(lib().qf_lora_experts_adapter_grads(ex.ref, ex.n, int(bool(accumulate)), _p(ws),
+                                               ws.numel() * ws.element_size(), _stream()),
+           "qf_lora_experts_adapter_grads")
 
 
 def _lora_single(W, A, B):

@@ -41,6 +41,11 @@ class LoraDesc(ctypes.Structure):
     ]
 
 
+class LoraExpertsDesc(ctypes.Structure):
+    """Mirror of qf_lora_experts in include/qf.h."""
+    _fields_ = [("d", LoraDesc), ("count", ctypes.c_int32), ("group_stride", ctypes.c_int32)]
+
+
 class StTensor(ctypes.Structure):
     """Mirror of qf_st_tensor in include/qf.h."""
     _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_char_p), ("ndim", ctypes.c_int32),
@@ -85,6 +90,12 @@ SIGNATURES = {
                                                          c_size_t, c_void_p]),
     "qf_lora_merge_qdq_pack_nvfp4_grouped": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
     "qf_lora_adapter_grads_grouped": (c_int, [c_void_p, c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "qf_lora_experts_workspace": (c_size_t, [c_void_p, c_int]),
+    "qf_lora_experts_layout": (c_int, [c_void_p, c_int, c_void_p]),
+    "qf_lora_experts_merge_tensor_scale_nvfp4": (c_int, [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                                         c_size_t, c_void_p]),
+    "qf_lora_experts_merge_qdq_pack_nvfp4": (c_int, [c_void_p, c_int, c_void_p, c_void_p]),
+    "qf_lora_experts_adapter_grads": (c_int, [c_void_p, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "qf_lora_merge_tensor_scale_nvfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_int, c_void_p,
                                                  c_void_p, c_size_t, c_void_p]),
     "qf_lora_merge_qdq_pack_nvfp4": (c_int, [c_void_p, c_void_p, c_void_p, c_i64, c_i64, c_int, c_void_p, c_void_p,

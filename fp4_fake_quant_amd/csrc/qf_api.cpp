@@ -408,7 +408,14 @@ qf_status check_lora_merge_inputs(const qf_lora_desc& d) {
 }
 
 struct LoraCounts {
-  int64_t merge_tiles = 0, merge_wg = 0, qdq_wg = 0, grad_wg = 0, dA_part = 0, dB_part = 0;
+  int64_t merge_tiles = 0, merge_wg = 0, qdq_wg = 0, grad_wg = 0, dA_part = 0, dB_part = 0, mats = 0;
+};
+
+// A descriptor and the experts stacked behind it (count 1 for the grouped calls).
+struct LoraIn {
+  qf_lora_desc d;
+  int64_t count;
+  int64_t gs;
 };
 
 int64_t slabs_of(int64_t cols) { return (cols + qf::LORA_SLAB - 1) / qf::LORA_SLAB; }
@@ -416,30 +423,31 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Launch sizes of a descriptor list for pass-2 units of qdq_rows rows and dA workgroups
 // of da_rows rows; fills a (when given).  Pass 1: 32 x 64 tiles, descriptor by
-// descriptor; its grid is the resident maximum of 2 workgroups per CU, or fewer so that
-// every wave keeps at least LORA_MERGE_TILES_MIN tiles (one expert alone: 6,912 tiles,
-// 432 workgroups).
-LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int qdq_rows, int da_rows, qf::LoraArgs* a,
-                            float* dA_part) {
+// descriptor and expert by expert; its grid is the resident maximum of 3 workgroups per
+// CU, or fewer so that every wave keeps at least LORA_MERGE_TILES_MIN tiles (one expert
+// alone: 6,912 tiles, 432 workgroups).
+LoraCounts lora_layout_with(const LoraIn* d, int n, int qdq_rows, int da_rows, qf::LoraArgs* a, float* dA_part) {
   LoraCounts c;
   if (a) memset(a, 0, sizeof(*a));
   int k = 0, groups = 0;
   for (int i = 0; i < n; ++i) {
-    if (d[i].rows <= 0 || d[i].cols <= 0) continue;
-    const int64_t slabs = slabs_of(d[i].cols);
-    const int64_t rt = ceil_div(d[i].rows, qf::LORA_MERGE_ROWS), ct = ceil_div(d[i].cols, qf::LORA_MERGE_COLS);
-    const int64_t qu = ceil_div(d[i].rows, qdq_rows) * slabs;
-    const int64_t dblk = ceil_div(d[i].rows, da_rows);
+    const qf_lora_desc& x = d[i].d;
+    const int64_t cnt = d[i].count;
+    if (x.rows <= 0 || x.cols <= 0 || cnt <= 0) continue;
+    const int64_t slabs = slabs_of(x.cols);
+    const int64_t rt = ceil_div(x.rows, qf::LORA_MERGE_ROWS), ct = ceil_div(x.cols, qf::LORA_MERGE_COLS);
+    const int64_t qu = ceil_div(x.rows, qdq_rows) * slabs;
+    const int64_t dblk = ceil_div(x.rows, da_rows);
     const int64_t du = dblk * slabs;
     if (a) {
       qf::LoraTensor& t = a->d[k];
-      t.W = d[i].W; t.A = d[i].A; t.B = d[i].B; t.M = d[i].M; t.G = d[i].G;
-      t.y = d[i].y; t.codes = d[i].codes; t.scales = d[i].scales;
-      t.dA = d[i].dA; t.dB = d[i].dB;
+      t.W = x.W; t.A = x.A; t.B = x.B; t.M = x.M; t.G = x.G;
+      t.y = x.y; t.codes = x.codes; t.scales = x.scales;
+      t.dA = x.dA; t.dB = x.dB;
       t.dA_partial = dA_part ? dA_part + c.dA_part : nullptr;
       t.dB_partial = nullptr;
-      t.rows = d[i].rows; t.cols = d[i].cols; t.ldw = d[i].ldw;
-      t.r = d[i].r; t.group = d[i].group;
+      t.rows = x.rows; t.cols = x.cols; t.ldw = x.ldw;
+      t.r = x.r; t.group = x.group;
       t.slabs = (int32_t)slabs;
       t.merge_tile_begin = (int32_t)c.merge_tiles;
       t.merge_rtiles = (int32_t)rt;
@@ -447,26 +455,33 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int qdq_rows, int da_r
       t.merge_units = (int32_t)qu;
       t.merge_wg_begin = (int32_t)c.qdq_wg;
       t.grad_wg_begin = (int32_t)c.grad_wg;
+      t.count = (int32_t)cnt;
+      t.group_stride = (int32_t)d[i].gs;
+      t.mat_begin = (int32_t)c.mats;
     }
     ++k;
-    if (d[i].group + 1 > groups) groups = d[i].group + 1;
-    c.merge_tiles += rt * ct;
-    c.qdq_wg += ceil_div(qu, 4);
-    c.grad_wg += du;
-    c.dA_part += dblk * qf::LORA_MAX_R * d[i].cols;
+    const int64_t g_end = x.group + (cnt - 1) * d[i].gs + 1;
+    if (g_end > groups) groups = (int)g_end;
+    c.mats += cnt;
+    c.merge_tiles += cnt * rt * ct;
+    c.qdq_wg += cnt * ceil_div(qu, 4);
+    c.grad_wg += cnt * du;
+    c.dA_part += cnt * dblk * qf::LORA_MAX_R * x.cols;
   }
   c.merge_wg = std::min<int64_t>(qf::LORA_MERGE_GRID_MAX, ceil_div(c.merge_tiles, 4 * qf::LORA_MERGE_TILES_MIN));
-  // dB partials follow all dA partials: [slabs][rows][LORA_MAX_R] per descriptor
+  // dB partials follow all dA partials: [count][slabs][rows][LORA_MAX_R] per descriptor
   int k2 = 0;
   for (int i = 0; i < n; ++i) {
-    if (d[i].rows <= 0 || d[i].cols <= 0) continue;
+    const qf_lora_desc& x = d[i].d;
+    if (x.rows <= 0 || x.cols <= 0 || d[i].count <= 0) continue;
     if (a) a->d[k2].dB_partial = dA_part ? dA_part + c.dA_part + c.dB_part : nullptr;
     ++k2;
-    c.dB_part += slabs_of(d[i].cols) * d[i].rows * qf::LORA_MAX_R;
+    c.dB_part += d[i].count * slabs_of(x.cols) * x.rows * qf::LORA_MAX_R;
   }
   if (a) {
     a->n = k;
     a->n_groups = groups;
+    a->n_mats = (int)c.mats;
     a->merge_tiles = c.merge_tiles;
     a->merge_band = (int)std::max<int64_t>(1, c.merge_wg > 0 ? ceil_div(c.merge_tiles, 4 * c.merge_wg) : 1);
     a->merge_rows = qdq_rows;
@@ -483,7 +498,7 @@ LoraCounts lora_layout_with(const qf_lora_desc* d, int n, int qdq_rows, int da_r
 // smaller ones multiply the partials, which cost more than the idle CUs (64 rows: grads
 // 8.4 -> 10.1 ms).  A function of the descriptors only, so the workspace size and the
 // launches agree.
-LoraCounts lora_layout(const qf_lora_desc* d, int n, qf::LoraArgs* a, float* dA_part) {
+LoraCounts lora_layout(const LoraIn* d, int n, qf::LoraArgs* a, float* dA_part) {
   constexpr int64_t FILL = 2 * 256;
   int qr = qf::LORA_QDQ_ROWS;
   int dr = qf::LORA_DA_ROWS_MAX;
@@ -492,21 +507,48 @@ LoraCounts lora_layout(const qf_lora_desc* d, int n, qf::LoraArgs* a, float* dA_
   return lora_layout_with(d, n, qr, dr, a, dA_part);
 }
 
-int lora_groups(const qf_lora_desc* d, int n) {
-  int g = 0;
-  for (int i = 0; i < n; ++i)
-    if (d[i].rows > 0 && d[i].cols > 0 && d[i].group + 1 > g) g = d[i].group + 1;
-  return g;
+int lora_groups(const LoraIn* d, int n) {
+  int64_t g = 0;
+  for (int i = 0; i < n; ++i) {
+    const qf_lora_desc& x = d[i].d;
+    if (x.rows > 0 && x.cols > 0 && d[i].count > 0) g = std::max<int64_t>(g, x.group + (d[i].count - 1) * d[i].gs + 1);
+  }
+  return (int)g;
 }
 
-}  // namespace
+// The grouped calls' descriptors as single experts.
+int lora_in(const qf_lora_desc* d, int n, LoraIn* out) {
+  for (int i = 0; i < n; ++i) {
+    out[i].d = d[i];
+    out[i].count = 1;
+    out[i].gs = 0;
+  }
+  return n;
+}
 
-extern "C" {
+// Argument checks of the stacked-experts calls (each expert is checked as one
+// descriptor by the shared code): count >= 1, group_stride >= 0, every expert's group
+// below QF_MAX_GROUPS, at most 65,535 matrices per call, no merge scratch.
+qf_status lora_experts_in(const qf_lora_experts* e, int n, LoraIn* out) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n > 0 && !e) return QF_ERR_NULL;
+  int64_t mats = 0;
+  for (int i = 0; i < n; ++i) {
+    if (e[i].count < 1 || e[i].group_stride < 0 || e[i].d.group < 0) return QF_ERR_ARG;
+    if (e[i].d.M) return QF_ERR_ARG;
+    if (e[i].d.group + (int64_t)(e[i].count - 1) * e[i].group_stride >= QF_MAX_GROUPS) return QF_ERR_ARG;
+    mats += e[i].count;
+    out[i].d = e[i].d;
+    out[i].count = e[i].count;
+    out[i].gs = e[i].group_stride;
+  }
+  if (mats > 65535) return QF_ERR_ARG;
+  return QF_OK;
+}
 
-size_t qf_lora_workspace(const qf_lora_desc* d, int n) {
-  if (n < 0 || n > QF_MAX_GROUPED || (n > 0 && !d)) return 0;
+size_t lora_workspace(const LoraIn* d, int n) {
   for (int i = 0; i < n; ++i)
-    if (check_lora(d[i]) != QF_OK) return 0;
+    if (check_lora(d[i].d) != QF_OK) return 0;
   const LoraCounts c = lora_layout(d, n, nullptr, nullptr);
   const int64_t merge_words = c.merge_wg * lora_groups(d, n);
   const int64_t grad_words = c.dA_part + c.dB_part;
@@ -514,11 +556,10 @@ size_t qf_lora_workspace(const qf_lora_desc* d, int n) {
   return (size_t)(words > 0 ? words : 1) * 4;
 }
 
-qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out) {
-  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
-  if ((n > 0 && !d) || !out) return QF_ERR_NULL;
+qf_status lora_layout_out(const LoraIn* d, int n, int32_t* out) {
+  if (!out) return QF_ERR_NULL;
   for (int i = 0; i < n; ++i) {
-    const qf_status st = check_lora(d[i]);
+    const qf_status st = check_lora(d[i].d);
     if (st != QF_OK) return st;
   }
   qf::LoraArgs a;
@@ -532,24 +573,25 @@ qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out) {
   return QF_OK;
 }
 
-qf_status qf_lora_merge_tensor_scale_nvfp4_grouped(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
-                                                   uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
-  if (n < 0 || n > QF_MAX_GROUPED || n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
-  if ((n > 0 && !d) || !d_scales) return QF_ERR_NULL;
+qf_status lora_tensor_scale(const LoraIn* d, int n, int n_groups, float* d_scales, uint32_t* d_nonfinite, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (n_groups < 1 || n_groups > QF_MAX_GROUPS) return QF_ERR_ARG;
+  if (!d_scales) return QF_ERR_NULL;
   for (int i = 0; i < n; ++i) {
-    const qf_status st = check_lora(d[i]);
+    const qf_lora_desc& x = d[i].d;
+    const qf_status st = check_lora(x);
     if (st != QF_OK) return st;
-    if (d[i].rows == 0 || d[i].cols == 0) continue;
-    if (d[i].group >= n_groups) return QF_ERR_ARG;
-    const qf_status sm = check_lora_merge_inputs(d[i]);
+    if (x.rows == 0 || x.cols == 0) continue;
+    if (x.group + (d[i].count - 1) * d[i].gs >= n_groups) return QF_ERR_ARG;
+    const qf_status sm = check_lora_merge_inputs(x);
     if (sm != QF_OK) return sm;
-    if (d[i].M && !aligned(d[i].M, 16)) return QF_ERR_ALIGN;
+    if (x.M && !aligned(x.M, 16)) return QF_ERR_ALIGN;
   }
-  if (!ws || ws_bytes < qf_lora_workspace(d, n)) return QF_ERR_WORKSPACE;
+  if (!ws || ws_bytes < lora_workspace(d, n)) return QF_ERR_WORKSPACE;
   if (!aligned(ws, 16)) return QF_ERR_ALIGN;
   qf::LoraArgs a;
   const LoraCounts c = lora_layout(d, n, &a, nullptr);
-  if (c.merge_tiles >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (c.merge_tiles >= (1ll << 31) || c.qdq_wg >= (1ll << 29)) return QF_ERR_SHAPE;
   a.partial = (uint32_t*)ws;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e = qf::launch_lora_merge(a, (int)c.merge_wg, s);
@@ -565,30 +607,29 @@ qf_status qf_lora_merge_tensor_scale_nvfp4_grouped(const qf_lora_desc* d, int n,
   return hip_status(qf::launch_nvfp4_scale_reduce(r, s));
 }
 
-qf_status qf_lora_merge_qdq_pack_nvfp4_grouped(const qf_lora_desc* d, int n, const float* d_scales, void* stream) {
-  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
-  if (n > 0 && !d) return QF_ERR_NULL;
+qf_status lora_qdq_pack(const LoraIn* d, int n, const float* d_scales, void* stream) {
   if (!d_scales) return QF_ERR_NULL;
   // descriptors with M: QDQ + pack of M; without: merge again and QDQ in registers
   qf_tensor_desc t[QF_MAX_GROUPED];
-  qf_lora_desc fused[QF_MAX_GROUPED];
+  LoraIn fused[QF_MAX_GROUPED];
   int nt = 0, nf = 0;
   for (int i = 0; i < n; ++i) {
-    const qf_status st = check_lora(d[i]);
+    const qf_lora_desc& x = d[i].d;
+    const qf_status st = check_lora(x);
     if (st != QF_OK) return st;
-    if (d[i].rows == 0 || d[i].cols == 0) continue;
-    if (d[i].group < 0) return QF_ERR_ARG;
-    const qf_tensor_desc q = one(d[i].M ? d[i].M : d[i].W, d[i].rows, d[i].cols, d[i].M ? d[i].cols : d[i].ldw,
-                                 d[i].y, d[i].cols, d[i].codes, d[i].scales);
-    const bool uy = d[i].y != nullptr, up = d[i].codes != nullptr;
+    if (x.rows == 0 || x.cols == 0) continue;
+    if (x.group < 0) return QF_ERR_ARG;
+    const qf_tensor_desc q = one(x.M ? x.M : x.W, x.rows, x.cols, x.M ? x.cols : x.ldw, x.y, x.cols, x.codes,
+                                 x.scales);
+    const bool uy = x.y != nullptr, up = x.codes != nullptr;
     if (!uy && !up) return QF_ERR_NULL;
     const qf_status sq = check_desc(q, QF_FMT_NVFP4, uy, up);
     if (sq != QF_OK) return sq;
-    if (d[i].M) {
+    if (x.M) {
       t[nt] = q;
-      t[nt++].group = d[i].group;
+      t[nt++].group = x.group;
     } else {
-      const qf_status sm = check_lora_merge_inputs(d[i]);
+      const qf_status sm = check_lora_merge_inputs(x);
       if (sm != QF_OK) return sm;
       fused[nf++] = d[i];
     }
@@ -601,30 +642,104 @@ qf_status qf_lora_merge_qdq_pack_nvfp4_grouped(const qf_lora_desc* d, int n, con
   if (nf == 0) return QF_OK;
   qf::LoraArgs a;
   const LoraCounts c = lora_layout(fused, nf, &a, nullptr);
-  if (c.qdq_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  if (c.qdq_wg >= (1ll << 29)) return QF_ERR_SHAPE;
   a.tscale = d_scales;
   return hip_status(qf::launch_lora_merge_qdq(a, (int)c.qdq_wg, s));
+}
+
+qf_status lora_grads(const LoraIn* d, int n, int accumulate, void* ws, size_t ws_bytes, void* stream) {
+  for (int i = 0; i < n; ++i) {
+    const qf_lora_desc& x = d[i].d;
+    const qf_status st = check_lora(x);
+    if (st != QF_OK) return st;
+    if (x.rows == 0 || x.cols == 0) continue;
+    if (!x.A || !x.B || !x.G || !x.dA || !x.dB) return QF_ERR_NULL;
+    if (!aligned(x.A, 16) || !aligned(x.B, 4) || !aligned(x.G, 16) || !aligned(x.dB, 4) || !aligned(x.dA, 4))
+      return QF_ERR_ALIGN;
+  }
+  if (!ws || ws_bytes < lora_workspace(d, n)) return QF_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return QF_ERR_ALIGN;
+  qf::LoraArgs a;
+  const LoraCounts c = lora_layout(d, n, &a, (float*)ws);
+  if (c.grad_wg >= (1ll << 31)) return QF_ERR_SHAPE;
+  return hip_status(qf::launch_lora_grads(a, (int)c.grad_wg, accumulate != 0, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t qf_lora_workspace(const qf_lora_desc* d, int n) {
+  if (n < 0 || n > QF_MAX_GROUPED || (n > 0 && !d)) return 0;
+  LoraIn in[QF_MAX_GROUPED];
+  return lora_workspace(in, lora_in(d, n, in));
+}
+
+qf_status qf_lora_layout(const qf_lora_desc* d, int n, int32_t* out) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if ((n > 0 && !d) || !out) return QF_ERR_NULL;
+  LoraIn in[QF_MAX_GROUPED];
+  return lora_layout_out(in, lora_in(d, n, in), out);
+}
+
+qf_status qf_lora_merge_tensor_scale_nvfp4_grouped(const qf_lora_desc* d, int n, int n_groups, float* d_scales,
+                                                   uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n > 0 && !d) return QF_ERR_NULL;
+  LoraIn in[QF_MAX_GROUPED];
+  return lora_tensor_scale(in, lora_in(d, n, in), n_groups, d_scales, d_nonfinite, ws, ws_bytes, stream);
+}
+
+qf_status qf_lora_merge_qdq_pack_nvfp4_grouped(const qf_lora_desc* d, int n, const float* d_scales, void* stream) {
+  if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
+  if (n > 0 && !d) return QF_ERR_NULL;
+  LoraIn in[QF_MAX_GROUPED];
+  return lora_qdq_pack(in, lora_in(d, n, in), d_scales, stream);
 }
 
 qf_status qf_lora_adapter_grads_grouped(const qf_lora_desc* d, int n, int accumulate, void* ws, size_t ws_bytes,
                                         void* stream) {
   if (n < 0 || n > QF_MAX_GROUPED) return QF_ERR_ARG;
   if (n > 0 && !d) return QF_ERR_NULL;
-  for (int i = 0; i < n; ++i) {
-    const qf_status st = check_lora(d[i]);
-    if (st != QF_OK) return st;
-    if (d[i].rows == 0 || d[i].cols == 0) continue;
-    if (!d[i].A || !d[i].B || !d[i].G || !d[i].dA || !d[i].dB) return QF_ERR_NULL;
-    if (!aligned(d[i].A, 16) || !aligned(d[i].B, 4) || !aligned(d[i].G, 16) || !aligned(d[i].dB, 4) ||
-        !aligned(d[i].dA, 4))
-      return QF_ERR_ALIGN;
-  }
-  if (!ws || ws_bytes < qf_lora_workspace(d, n)) return QF_ERR_WORKSPACE;
-  if (!aligned(ws, 16)) return QF_ERR_ALIGN;
-  qf::LoraArgs a;
-  const LoraCounts c = lora_layout(d, n, &a, (float*)ws);
-  if (c.grad_wg >= (1ll << 31)) return QF_ERR_SHAPE;
-  return hip_status(qf::launch_lora_grads(a, (int)c.grad_wg, accumulate != 0, (hipStream_t)stream));
+  LoraIn in[QF_MAX_GROUPED];
+  return lora_grads(in, lora_in(d, n, in), accumulate, ws, ws_bytes, stream);
+}
+
+size_t qf_lora_experts_workspace(const qf_lora_experts* e, int n) {
+  LoraIn in[QF_MAX_GROUPED];
+  if (lora_experts_in(e, n, in) != QF_OK) return 0;
+  return lora_workspace(in, n);
+}
+
+qf_status qf_lora_experts_layout(const qf_lora_experts* e, int n, int32_t* out) {
+  LoraIn in[QF_MAX_GROUPED];
+  const qf_status st = lora_experts_in(e, n, in);
+  if (st != QF_OK) return st;
+  return lora_layout_out(in, n, out);
+}
+
+qf_status qf_lora_experts_merge_tensor_scale_nvfp4(const qf_lora_experts* e, int n, int n_groups, float* d_scales,
+                                                   uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream) {
+  LoraIn in[QF_MAX_GROUPED];
+  const qf_status st = lora_experts_in(e, n, in);
+  if (st != QF_OK) return st;
+  return lora_tensor_scale(in, n, n_groups, d_scales, d_nonfinite, ws, ws_bytes, stream);
+}
+
+qf_status qf_lora_experts_merge_qdq_pack_nvfp4(const qf_lora_experts* e, int n, const float* d_scales,
+                                               void* stream) {
+  LoraIn in[QF_MAX_GROUPED];
+  const qf_status st = lora_experts_in(e, n, in);
+  if (st != QF_OK) return st;
+  return lora_qdq_pack(in, n, d_scales, stream);
+}
+
+qf_status qf_lora_experts_adapter_grads(const qf_lora_experts* e, int n, int accumulate, void* ws, size_t ws_bytes,
+                                        void* stream) {
+  LoraIn in[QF_MAX_GROUPED];
+  const qf_status st = lora_experts_in(e, n, in);
+  if (st != QF_OK) return st;
+  return lora_grads(in, n, accumulate, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -75,12 +75,14 @@ constexpr int LORA_QDQ_ROWS = 32;       // rows per pass-2 unit (at most; fewer 
 constexpr int LORA_DA_ROWS = 256;       // rows per gradient workgroup (one dA partial each), or
 constexpr int LORA_DA_ROWS_MAX = 512;   // twice that when the launch still has a workgroup per CU
 
-// Pass 1 (merge + maximum): tiles numbered descriptor by descriptor, then by band of
-// merge_band row tiles, column tile, row tile; each wave of the grid takes an equal
-// contiguous run.  Pass 2 without M in memory (merge + QDQ): a unit is one wave's
-// LORA_SLAB-column slab of merge_rows rows, numbered row block major; every descriptor
-// starts on a fresh workgroup of 4 waves.  A gradient unit is
-// one workgroup's: a LORA_SLAB-column slab of da_rows rows.
+// A descriptor holds `count` experts of one shape, stacked: every tensor of expert e
+// follows expert e - 1's contiguously (W [count][rows][ldw], A [count][r][cols], ...),
+// and expert e's tied group is group + e * group_stride.  Pass 1 (merge + maximum):
+// tiles numbered descriptor by descriptor, expert by expert, then by band of merge_band
+// row tiles, column tile, row tile; each wave of the grid takes an equal contiguous run.
+// Pass 2 without M in memory (merge + QDQ): a unit is one wave's LORA_SLAB-column slab of
+// merge_rows rows, numbered row block major; every expert starts on a fresh workgroup of
+// 4 waves.  A gradient unit is one workgroup's: a LORA_SLAB-column slab of da_rows rows.
 struct LoraTensor {
   const uint16_t* W;
   const uint16_t* A;
@@ -92,21 +94,24 @@ struct LoraTensor {
   const uint16_t* G;
   float* dA;
   float* dB;
-  float* dA_partial;   // workspace: [row blocks][LORA_MAX_R][cols]
-  float* dB_partial;   // workspace: [slabs][rows][LORA_MAX_R]
+  float* dA_partial;   // workspace: [count][row blocks][LORA_MAX_R][cols]
+  float* dB_partial;   // workspace: [count][slabs][rows][LORA_MAX_R]
   int64_t rows, cols, ldw;
   int32_t r, group;
   int32_t slabs;            // ceil(cols / LORA_SLAB), the gradient slabs
   int32_t merge_tile_begin;         // pass 1: first tile of the descriptor in the launch,
   int32_t merge_rtiles, merge_ctiles;  // its 32-row and 64-column tiles
-  int32_t merge_units, merge_wg_begin;  // pass 2: units and first workgroup
-  int32_t grad_wg_begin;    // gradients: one workgroup per (row block, slab)
+  int32_t merge_units, merge_wg_begin;  // pass 2: units per expert and first workgroup
+  int32_t grad_wg_begin;    // gradients: one workgroup per (expert, row block, slab)
+  int32_t count, group_stride;  // stacked experts
+  int32_t mat_begin;        // flat index of expert 0 among the launch's matrices
 };
 
 struct LoraArgs {
   LoraTensor d[QF_MAX_GROUPED];
   int n;
   int n_groups;        // rows of merge partials
+  int n_mats;          // matrices of the launch (experts of all descriptors)
   int64_t merge_tiles; // pass-1 tiles of the launch
   int merge_band;      // row tiles per band of the pass-1 order (the longest wave run)
   int merge_rows;      // rows per pass-2 unit (32, 16 or 8)

@@ -48,6 +48,48 @@ __device__ __forceinline__ void unpack8(uint4 w, float (&f)[8]) {
   f[6] = bf16_lo(w.w); f[7] = bf16_hi(w.w);
 }
 
+// Expert e of a descriptor: its tensors, each stacked contiguously after expert e - 1's,
+// and its tied group.
+struct LoraMat {
+  const uint16_t* W;
+  const uint16_t* A;
+  const uint16_t* B;
+  const uint16_t* G;
+  uint16_t* M;
+  uint16_t* y;
+  uint8_t* codes;
+  uint8_t* scales;
+  float* dA;
+  float* dB;
+  float* dA_partial;
+  float* dB_partial;
+  int group;
+};
+
+template <typename P>
+__device__ __forceinline__ P* lora_at(P* p, int64_t off) {
+  return p ? p + off : p;
+}
+
+__device__ __forceinline__ LoraMat lora_mat(const LoraTensor& T, int e, int da_rows) {
+  const int64_t rc = T.rows * T.cols, r = T.r;
+  LoraMat m;
+  m.W = lora_at(T.W, e * T.rows * T.ldw);
+  m.A = lora_at(T.A, e * r * T.cols);
+  m.B = lora_at(T.B, e * T.rows * r);
+  m.G = lora_at(T.G, e * rc);
+  m.M = lora_at(T.M, e * rc);
+  m.y = lora_at(T.y, e * rc);
+  m.codes = lora_at(T.codes, e * rc / 2);
+  m.scales = lora_at(T.scales, e * rc / 16);
+  m.dA = lora_at(T.dA, e * r * T.cols);
+  m.dB = lora_at(T.dB, e * T.rows * r);
+  m.dA_partial = lora_at(T.dA_partial, e * ((T.rows + da_rows - 1) / da_rows) * LORA_MAX_R * T.cols);
+  m.dB_partial = lora_at(T.dB_partial, e * (int64_t)T.slabs * T.rows * LORA_MAX_R);
+  m.group = T.group + e * T.group_stride;
+  return m;
+}
+
 // --------------------------------------------------- merge, passes 1 and 2 ------
 // The low-rank product S = B.A runs on the fp32 matrix cores: v_mfma_f32_32x32x1_2b_f32
 // multiplies one fp32 value per lane of its A operand by one of its B operand (K = 1) and
@@ -113,17 +155,20 @@ __device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t of
 // A tile's place in the flat order (wave-uniform): descriptor, row tile, column tile, the
 // row band [b0, b1) of the row tile, and the descriptor's row and column tile counts.
 struct MmTile {
-  int di, ct, rt, b0, b1, rtiles, ctiles;
+  int di, e, ct, rt, b0, b1, rtiles, ctiles;
 };
 
 __device__ __forceinline__ void mm_next(const LoraArgs& a, MmTile& p) {
   if (++p.rt < p.b1) return;
   if (++p.ct == p.ctiles) {
     p.ct = 0;
-    if (p.b1 == p.rtiles) {                                      // next descriptor, first band
-      if (++p.di >= a.n) return;
-      p.rtiles = a.d[p.di].merge_rtiles;
-      p.ctiles = a.d[p.di].merge_ctiles;
+    if (p.b1 == p.rtiles) {                                      // next expert or descriptor, first band
+      if (++p.e >= a.d[p.di].count) {
+        p.e = 0;
+        if (++p.di >= a.n) return;
+        p.rtiles = a.d[p.di].merge_rtiles;
+        p.ctiles = a.d[p.di].merge_ctiles;
+      }
       p.b0 = 0;
       p.b1 = min(a.merge_band, p.rtiles);
     } else {
@@ -143,7 +188,9 @@ __device__ __forceinline__ MmTile mm_locate(const LoraArgs& a, int64_t tb) {
   const LoraTensor& T = a.d[di];
   p.rtiles = T.merge_rtiles;
   p.ctiles = T.merge_ctiles;
-  const int loc = (int)(tb - T.merge_tile_begin);
+  int loc = (int)(tb - T.merge_tile_begin);
+  p.e = loc / (p.rtiles * p.ctiles);
+  loc -= p.e * p.rtiles * p.ctiles;
   const int bands = (p.rtiles + a.merge_band - 1) / a.merge_band;
   const int band = min(loc / (a.merge_band * p.ctiles), bands - 1);
   p.di = di;
@@ -199,14 +246,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       uint32_t wo[4] = {BUF_OOR, BUF_OOR, BUF_OOR, BUF_OOR}, bo[4] = {BUF_OOR, BUF_OOR, BUF_OOR, BUF_OOR};
       if (j < nt) {
         const LoraTensor& T = a.d[pl.di];
+        const LoraMat X = lora_mat(T, pl.e, a.da_rows);
         const int r = RK ? RK : T.r;
         const int64_t c0 = (int64_t)pl.ct * MM_COLS, r0 = (int64_t)pl.rt * MM_ROWS;
         const int nrows = (int)min((int64_t)MM_ROWS, T.rows - r0);
         const int cw = (int)min((int64_t)MM_COLS, T.cols - c0);
-        rw = make_buf(T.W + r0 * T.ldw + c0, ((int64_t)(nrows - 1) * T.ldw + cw) * 2);
+        rw = make_buf(X.W + r0 * T.ldw + c0, ((int64_t)(nrows - 1) * T.ldw + cw) * 2);
         // B rows of the tile (4-byte aligned; with an odd rank the last row may end in the
         // middle of a word, so the 2 bytes after it are in range)
-        rb = make_buf(T.B + r0 * r, (int64_t)nrows * r * 2 + 2);
+        rb = make_buf(X.B + r0 * r, (int64_t)nrows * r * 2 + 2);
 #pragma unroll
         for (int jw = 0; jw < 4; ++jw)
           wo[jw] = cw > 32 * (int)(wchunk[jw] >> 2) ? (uint32_t)((wrow[jw] * T.ldw + 8 * wchunk[jw]) * 2) : BUF_OOR;
@@ -233,13 +281,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // A operand of step j: A[j - (16 - r)][c0 + colA], colA = this lane's MFMA row's column.
     const int colA = 32 * h + 16 * ((lr >> 2) & 1) + 4 * (lr >> 3) + (lr & 3);
     float av[LORA_MAX_R];
-    int a_di = -1, a_ct = -1;
+    int a_di = -1, a_e = -1, a_ct = -1;
     // A's values for the column of tile p; then no load is left pending, so no later wait
     // has to cover them
     auto load_a = [&](const MmTile& p) {
       const LoraTensor& T = a.d[p.di];
       const int r = RK ? RK : T.r, lead = LORA_MAX_R - r;
-      const __amdgpu_buffer_rsrc_t ra = make_buf(T.A, (int64_t)r * T.cols * 2);
+      const __amdgpu_buffer_rsrc_t ra = make_buf(lora_mat(T, p.e, a.da_rows).A, (int64_t)r * T.cols * 2);
       const int cA = p.ct * MM_COLS + colA, ncol = (int)T.cols;     // below 2^16 + 64
 #pragma unroll
       for (int j = 0; j < LORA_MAX_R; ++j) {
@@ -248,6 +296,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       }
       MM_WAIT_VM(0);
       a_di = p.di;
+      a_e = p.e;
       a_ct = p.ct;
     };
     // The tile's LDS reads (stage st, rank r) in one block that waits for its own results:
@@ -344,8 +393,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       if (t >= 1) MM_WAIT_VM(MM_LOADS + STORES);
       else MM_WAIT_VM(MM_LOADS);
       asm volatile("" ::: "memory");
-      if (pe.di != a_di || pe.ct != a_ct) load_a(pe);
+      if (pe.di != a_di || pe.e != a_e || pe.ct != a_ct) load_a(pe);
       const LoraTensor& T = a.d[pe.di];
+      const LoraMat X = lora_mat(T, pe.e, a.da_rows);
       const int r = RK ? RK : T.r;
       const int64_t cols = T.cols, c0 = (int64_t)pe.ct * MM_COLS, r0 = (int64_t)pe.rt * MM_ROWS;
       const int nrows = (int)min((int64_t)MM_ROWS, T.rows - r0);
@@ -402,17 +452,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
             : "memory");
         // rows past the matrix fall outside the range
         const int64_t e0 = r0 * cols + c0, ne = (int64_t)nrows * cols - c0;
-        const __amdgpu_buffer_rsrc_t rm = make_buf((const uint16_t*)((uintptr_t)T.M + (uintptr_t)(e0 * 2)),
-                                                   T.M ? ne * 2 : 0);
+        const __amdgpu_buffer_rsrc_t rm = make_buf((const uint16_t*)((uintptr_t)X.M + (uintptr_t)(e0 * 2)),
+                                                   X.M ? ne * 2 : 0);
         buf_store16(rm, yoff[0], make_uint4(mo0[0], mo0[1], mo0[2], mo0[3]));
         buf_store16(rm, yoff[1], make_uint4(mo1[0], mo1[1], mo1[2], mo1[3]));
         buf_store16(rm, yoff[2], make_uint4(mo2[0], mo2[1], mo2[2], mo2[3]));
         buf_store16(rm, yoff[3], make_uint4(mo3[0], mo3[1], mo3[2], mo3[3]));
       }
-      if (T.group != mg) {                                         // the run enters another group
+      if (X.group != mg) {                                         // the run enters another group
         if (mg >= 0) mm_flush(m, gmax, mg);
         m = 0;
-        mg = T.group;
+        mg = X.group;
       }
       m = umax(m, lr < nrows ? mt : 0u);                           // rows past the matrix: left out
       if (t + 1 < nt) mm_next(a, pe);
@@ -453,6 +503,22 @@ __device__ __forceinline__ int find_desc_wg(const LoraArgs& a, int b) {
 #pragma unroll 1
   while (di + 1 < a.n && b >= a.d[di + 1].merge_wg_begin) ++di;
   return di;
+}
+
+// Workgroup b of the merge-and-QDQ layout: its descriptor, expert, and the unit of wave
+// `wave` (u >= merge_units: padding past the expert's last unit).
+struct LoraUnit {
+  int di, e, u;
+};
+__device__ __forceinline__ LoraUnit lora_unit(const LoraArgs& a, int b, int wave) {
+  LoraUnit q;
+  q.di = find_desc_wg(a, b);
+  const LoraTensor& T = a.d[q.di];
+  const int wpe = (T.merge_units + 3) / 4;                           // workgroups per expert
+  const int lb = b - T.merge_wg_begin;
+  q.e = lb / wpe;
+  q.u = (lb - q.e * wpe) * 4 + wave;
+  return q;
 }
 
 // Scalar words of B's row `row` (B contiguous [rows, r], 4-byte aligned; the row starts
@@ -502,11 +568,12 @@ __device__ __forceinline__ void b_row_values(const uint32_t (&w)[BW], int64_t ro
 // and dropped by the range check, so the compiler keeps every prefetched load in flight.
 template <int RK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_lora_merge_qdq(LoraArgs a) {
-  const int b = blockIdx.x;
-  const LoraTensor& T = a.d[find_desc_wg(a, b)];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int u = (b - T.merge_wg_begin) * 4 + wave;
+  const LoraUnit uq = lora_unit(a, blockIdx.x, wave);
+  const LoraTensor& T = a.d[uq.di];
+  const int u = uq.u;
   if (u >= T.merge_units) return;
+  const LoraMat X = lora_mat(T, uq.e, a.da_rows);
   const int64_t cols = T.cols, ldw = T.ldw;
   const int r = RK ? RK : T.r;
   const int rb = u / T.slabs;
@@ -516,18 +583,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const bool active = cs + 8 * lane < cols;
   const uint32_t lo = active ? 16u * lane : BUF_OOR;                  // lane's byte offset in a row
   const int64_t e0 = r0 * cols + cs;                                  // first element of the unit
-  const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
-  const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
+  const __amdgpu_buffer_rsrc_t rw = make_buf(X.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_buf(X.A + cs, (int64_t)r * cols * 2 - cs * 2);
   const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
   // outputs (an empty resource drops the stores)
-  const bool wy = T.y, wp = T.codes;
-  const __amdgpu_buffer_rsrc_t ry = make_buf(wy ? T.y + e0 : nullptr, wy ? (int64_t)rows * cols * 2 : 0);
-  const __amdgpu_buffer_rsrc_t rc = make_buf(wp ? T.codes + e0 / 2 : nullptr, wp ? (int64_t)rows * cols / 2 : 0);
-  const __amdgpu_buffer_rsrc_t rs = make_buf(wp ? T.scales + e0 / 16 : nullptr, wp ? (int64_t)rows * cols / 16 : 0);
+  const bool wy = X.y, wp = X.codes;
+  const __amdgpu_buffer_rsrc_t ry = make_buf(wy ? X.y + e0 : nullptr, wy ? (int64_t)rows * cols * 2 : 0);
+  const __amdgpu_buffer_rsrc_t rc = make_buf(wp ? X.codes + e0 / 2 : nullptr, wp ? (int64_t)rows * cols / 2 : 0);
+  const __amdgpu_buffer_rsrc_t rs = make_buf(wp ? X.scales + e0 / 16 : nullptr, wp ? (int64_t)rows * cols / 16 : 0);
   const uint32_t clo = active ? 4u * lane : BUF_OOR;
   const uint32_t slo = active && (lane & 1) == 0 ? (uint32_t)lane / 2u : BUF_OOR;
   const uint32_t cstride = (uint32_t)(cols / 2), sstride = (uint32_t)(cols / 16);
-  const float s_t = a.tscale[T.group], k6 = 6.0f * s_t;
+  const float s_t = a.tscale[X.group], k6 = 6.0f * s_t;
   uint4 wv[LORA_PREFETCH];
 #pragma unroll
   for (int q = 0; q < LORA_PREFETCH; ++q) {
@@ -535,7 +602,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     LORA_FENCE();
   }
   uint32_t bw[BW];
-  fetch_b_words<RK>(T.B, r0, r, bw);
+  // B's rows are addressed from expert 0's (4-byte aligned) base: expert e's rows follow
+  // as rows e * rows + i, which keeps the word alignment right when rows * r is odd
+  const int64_t br0 = (int64_t)uq.e * T.rows + r0;
+  fetch_b_words<RK>(T.B, br0, r, bw);
   float av[LORA_MAX_R][8];                                           // rows k >= r read as 0
 #pragma unroll
   for (int k = 0; k < LORA_MAX_R; ++k) unpack8(buf_load16(ra, lo + k * mstride), av[k]);
@@ -546,8 +616,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       LORA_FENCE();
       const int ii = i + q;                                          // may pass the last row
       float bk[LORA_MAX_R];
-      b_row_values<RK>(bw, r0 + min(ii, rows - 1), r, bk);
-      fetch_b_words<RK>(T.B, r0 + min(ii + 1, rows - 1), r, bw);
+      b_row_values<RK>(bw, br0 + min(ii, rows - 1), r, bk);
+      fetch_b_words<RK>(T.B, br0 + min(ii + 1, rows - 1), r, bw);
       float acc[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -591,14 +661,23 @@ __device__ __forceinline__ float sum_partials(const float* p, int64_t stride, in
   return s;
 }
 
+// Matrix m of the launch (blockIdx.y of the reduces): its descriptor.
+__device__ __forceinline__ int find_desc_mat(const LoraArgs& a, int m) {
+  int di = 0;
+#pragma unroll 1
+  while (di + 1 < a.n && m >= a.d[di + 1].mat_begin) ++di;
+  return di;
+}
+
 __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumulate) {
-  const LoraTensor& T = a.d[blockIdx.y];
+  const LoraTensor& T = a.d[find_desc_mat(a, blockIdx.y)];
+  const LoraMat X = lora_mat(T, (int)blockIdx.y - T.mat_begin, a.da_rows);
   const int64_t n = (int64_t)T.r * T.cols;
   const int nblk = (int)((T.rows + a.da_rows - 1) / a.da_rows);
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
     // partial q holds rows k = 0 .. 15 of cols columns; entry (k, j) of dA is at idx
-    const float s = sum_partials(T.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
-    T.dA[idx] = accumulate ? T.dA[idx] + s : s;
+    const float s = sum_partials(X.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
+    X.dA[idx] = accumulate ? X.dA[idx] + s : s;
   }
 }
 
@@ -636,14 +715,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   int mg = -1;
 #pragma unroll 1
   for (int64_t uf = u0; uf < u1; ++uf) {
-    const int di = find_desc_wg(a, (int)(uf >> 2));
-    const LoraTensor& T = a.d[di];
-    const int ul = (int)(uf - 4 * (int64_t)T.merge_wg_begin);
-    if (ul >= T.merge_units) continue;                               // padding of the descriptor's last workgroup
-    if (T.group != mg) {
+    const LoraUnit uq = lora_unit(a, (int)(uf >> 2), (int)(uf & 3));
+    const LoraTensor& T = a.d[uq.di];
+    const int ul = uq.u;
+    if (ul >= T.merge_units) continue;                               // padding of the expert's last workgroup
+    const LoraMat X = lora_mat(T, uq.e, a.da_rows);
+    if (X.group != mg) {
       if (mg >= 0 && lane == 0) atomicMax(gmax + mg, L);
       L = 0;
-      mg = T.group;
+      mg = X.group;
     }
     const int64_t cols = T.cols, ldw = T.ldw;
     const int r = RK ? RK : T.r;
@@ -653,8 +733,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);   // at most 32
     const bool active = cs + 8 * lane < cols;
     const uint32_t lo = active ? 16u * lane : BUF_OOR;
-    const __amdgpu_buffer_rsrc_t rw = make_buf(T.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
-    const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_buf(X.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
+    const __amdgpu_buffer_rsrc_t ra = make_buf(X.A + cs, (int64_t)r * cols * 2 - cs * 2);
     const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
     uint4 ap[LORA_MAX_R];                                            // A's slice, bf16 (rows k >= r: 0)
 #pragma unroll
@@ -662,7 +742,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // bsum of row r0 + lane (lanes below rows)
     float bsum = 0.0f;
     {
-      const __amdgpu_buffer_rsrc_t rbb = make_buf(T.B + r0 * r, (int64_t)rows * r * 2);
+      const __amdgpu_buffer_rsrc_t rbb = make_buf(X.B + r0 * r, (int64_t)rows * r * 2);
       const uint32_t bo = lane < rows ? (uint32_t)(lane * r * 2) : BUF_OOR;
       if constexpr (RK == LORA_MAX_R) {
         const uint4 b0 = buf_load16(rbb, bo), b1 = buf_load16(rbb, bo + 16);
@@ -718,9 +798,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const uint4 wq = buf_load16(rw, lo + ii * wstride);
         if (!__builtin_amdgcn_ballot_w64(test(wq, ii))) continue;      // L has grown since
         uint32_t bw[BW];
-        fetch_b_words<RK>(T.B, r0 + ii, r, bw);
+        // B's rows from expert 0's aligned base (expert e's row i is row e * rows + i)
+        fetch_b_words<RK>(T.B, (int64_t)uq.e * T.rows + r0 + ii, r, bw);
         float bk[LORA_MAX_R];
-        b_row_values<RK>(bw, r0 + ii, r, bk);
+        b_row_values<RK>(bw, (int64_t)uq.e * T.rows + r0 + ii, r, bk);
         float acc[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
@@ -798,7 +879,10 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63u;
   const uint32_t l16 = lane & 15u, lq = lane >> 4;
-  const int u = b - T.grad_wg_begin;
+  const int wpe = (int)((T.rows + a.da_rows - 1) / a.da_rows) * T.slabs;   // workgroups per expert
+  const int e = (b - T.grad_wg_begin) / wpe;
+  const int u = b - T.grad_wg_begin - e * wpe;
+  const LoraMat X = lora_mat(T, e, a.da_rows);
   const int rb = u / T.slabs;
   const int slab = u - rb * T.slabs;
   const int64_t cols = T.cols, cs = (int64_t)slab * LORA_SLAB;
@@ -808,7 +892,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   const int nchunk = (rows + GR_ROWS - 1) / GR_ROWS;
 
   // G loads: lane t takes 8 columns (t & 63) of rows (t >> 6) + 4 i of the chunk
-  const __amdgpu_buffer_rsrc_t rg = make_buf(T.G + r0 * cols + cs, (int64_t)rows * cols * 2);
+  const __amdgpu_buffer_rsrc_t rg = make_buf(X.G + r0 * cols + cs, (int64_t)rows * cols * 2);
   const bool col_ok = cs + 8 * (int64_t)lane < cols;
   const uint32_t goff = col_ok ? ((tid >> 6) * (uint32_t)cols + 8u * lane) * 2u : BUF_OOR;
   const uint32_t gstep = (uint32_t)(4 * cols) * 2u, gchunk = (uint32_t)(GR_ROWS * cols) * 2u;
@@ -823,7 +907,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
 
   // dB: adapter A fragments of this wave's columns (K steps 4w .. 4w+3 of the slab):
   // lane l supplies adapter row l%16, columns 32 ks + 8 (l/16) .. +7
-  const __amdgpu_buffer_rsrc_t ra = make_buf(T.A + cs, (int64_t)r * cols * 2 - cs * 2);
+  const __amdgpu_buffer_rsrc_t ra = make_buf(X.A + cs, (int64_t)r * cols * 2 - cs * 2);
   bf16x8_t af[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -832,10 +916,10 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
     af[s] = __builtin_bit_cast(bf16x8_t, buf_load16(ra, off));
   }
   // dA: B rows of the chunk transposed: lane l supplies adapter l%16, rows 8 (l/16) .. +7
-  const __amdgpu_buffer_rsrc_t rbb = make_buf(T.B + r0 * r, (int64_t)rows * r * 2);
+  const __amdgpu_buffer_rsrc_t rbb = make_buf(X.B + r0 * r, (int64_t)rows * r * 2);
   // dB partials of this unit's rows in this slab
   const __amdgpu_buffer_rsrc_t rdbp =
-      make_buf(T.dB_partial + ((int64_t)slab * T.rows + r0) * LORA_MAX_R, (int64_t)rows * LORA_MAX_R * 4);
+      make_buf(X.dB_partial + ((int64_t)slab * T.rows + r0) * LORA_MAX_R, (int64_t)rows * LORA_MAX_R * 4);
 
   // a chunk's B values for dA (rows past the end and adapters past r read 0), loaded
   // as 8 half words and packed into the MFMA operand only where it is used, so that
@@ -938,7 +1022,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
     stage_and_refill(ci, gv, braw, bt);
   }
   // dA partial of this unit: lane holds adapters 4 (l/16) + e of columns 128 w + 16 j + l%16
-  float* part = T.dA_partial + (int64_t)rb * LORA_MAX_R * cols + cs;
+  float* part = X.dA_partial + (int64_t)rb * LORA_MAX_R * cols + cs;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const int64_t col = 128 * wave + 16 * j + l16;
@@ -952,14 +1036,15 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
 
 // dB[row][k] (+)= sum over slabs, in slab order.
 __global__ __launch_bounds__(256) void k_lora_dB_reduce(LoraArgs a, int accumulate) {
-  const LoraTensor& T = a.d[blockIdx.y];
+  const LoraTensor& T = a.d[find_desc_mat(a, blockIdx.y)];
+  const LoraMat X = lora_mat(T, (int)blockIdx.y - T.mat_begin, a.da_rows);
   const int64_t n = T.rows * LORA_MAX_R;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = idx / LORA_MAX_R;
     const int k = (int)(idx - row * LORA_MAX_R);
     if (k >= T.r) continue;
-    const float s = sum_partials(T.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
-    float* dst = T.dB + row * T.r + k;
+    const float s = sum_partials(X.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
+    float* dst = X.dB + row * T.r + k;
     *dst = accumulate ? *dst + s : s;
   }
 }
@@ -1010,10 +1095,10 @@ hipError_t launch_lora_grads(const LoraArgs& a, int grid, int accumulate, hipStr
     nA = std::max<int64_t>(nA, (int64_t)a.d[i].r * a.d[i].cols);
   }
   const int gB = (int)std::min<int64_t>((nB + 255) / 256, 8192), gA = (int)std::min<int64_t>((nA + 255) / 256, 8192);
-  if (gB > 0) hipLaunchKernelGGL(k_lora_dB_reduce, dim3(gB, a.n), dim3(256), 0, s, a, accumulate);
+  if (gB > 0) hipLaunchKernelGGL(k_lora_dB_reduce, dim3(gB, a.n_mats), dim3(256), 0, s, a, accumulate);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (gA > 0) hipLaunchKernelGGL(k_lora_dA_reduce, dim3(gA, a.n), dim3(256), 0, s, a, accumulate);
+  if (gA > 0) hipLaunchKernelGGL(k_lora_dA_reduce, dim3(gA, a.n_mats), dim3(256), 0, s, a, accumulate);
   return hipGetLastError();
 }
 

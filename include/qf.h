@@ -362,6 +362,34 @@ qf_status qf_lora_adapter_grads(const uint16_t* G, const uint16_t* A, const uint
                                 int r, float* dA, float* dB, int accumulate, void* ws, size_t ws_bytes,
                                 void* stream);
 
+/* Stacked experts: one descriptor for `count` experts of one shape ("Method" section
+ * of the QATFactory project page: MoE models merge and quantize expert by expert, each
+ * expert with its own tied group).  d describes expert 0; every tensor of expert e
+ * follows expert e - 1's contiguously: W [count][rows][ldw], A [count][r][cols],
+ * B [count][rows][r], y [count][rows][cols], codes [count][rows][cols/2],
+ * scales [count][rows][cols/16], G [count][rows][cols], dA [count][r][cols],
+ * dB [count][rows][r].  Expert e's tied group is d.group + e * group_stride.
+ * d.M must be NULL (no merge scratch: pass 1 only takes the maximum and pass 2 merges
+ * again).  Every expert gives the bits the grouped calls give for it as a descriptor
+ * of its own.  Shapes, alignment and errors as the grouped calls, plus QF_ERR_ARG for
+ * count < 1, group_stride < 0, M not NULL, an expert's group at or above QF_MAX_GROUPS
+ * (or n_groups), or more than 65,535 experts in one call.  Up to QF_MAX_GROUPED
+ * descriptors per call: one launch of each kernel covers all their experts. */
+typedef struct qf_lora_experts {
+  qf_lora_desc d;
+  int32_t count;
+  int32_t group_stride;
+} qf_lora_experts;
+
+size_t qf_lora_experts_workspace(const qf_lora_experts* e, int n);
+qf_status qf_lora_experts_layout(const qf_lora_experts* e, int n, int32_t* out);
+qf_status qf_lora_experts_merge_tensor_scale_nvfp4(const qf_lora_experts* e, int n, int n_groups, float* d_scales,
+                                                   uint32_t* d_nonfinite, void* ws, size_t ws_bytes, void* stream);
+qf_status qf_lora_experts_merge_qdq_pack_nvfp4(const qf_lora_experts* e, int n, const float* d_scales,
+                                               void* stream);
+qf_status qf_lora_experts_adapter_grads(const qf_lora_experts* e, int n, int accumulate, void* ws, size_t ws_bytes,
+                                        void* stream);
+
 /* ------------------------------------------------------------ dequant ---- */
 /* Packed engine layout -> BF16, the inverse direction of the pack calls ("Method":
  * weights leave training in the engine's own format; "Supported formats" table for

@@ -412,3 +412,64 @@ def test_noalloc_tensor_scale_refuses_before_any_hip_call():
     assert L.qf_nvfp4_tensor_scale_grouped_noalloc(ctypes.byref(d), 1, 64, None, None, None) == 1
     d[0].x = 0x10000002
     assert L.qf_nvfp4_tensor_scale_grouped_noalloc(ctypes.byref(d), 1, 64, q, None, None) == 3
+
+
+def _moe_experts(k):
+    """Two stacked-experts descriptors (gate/up 3072x3072, down 3072x1536, rank 16) of k
+    experts each, tied groups 2e and 2e + 1."""
+    x = (_lib.LoraExpertsDesc * 2)()
+    for j, (rows, cols) in enumerate(((3072, 3072), (3072, 1536))):
+        d = x[j].d
+        d.W, d.A, d.B = 0x10000000, 0x10200000, 0x10300000
+        d.rows, d.cols, d.ldw, d.r, d.group = rows, cols, cols, 16, j
+        x[j].count, x[j].group_stride = k, 2
+    return x
+
+
+def test_lora_experts_layout_and_workspace_match_the_grouped_form():
+    """k stacked experts per descriptor lay out exactly like the 2k single-expert
+    descriptors of the grouped calls (same tiles, units, workgroups and workspace)."""
+    L = _lib.lib()
+    out_e, out_g = (ctypes.c_int32 * 6)(), (ctypes.c_int32 * 6)()
+    for k in (1, 2, 8):
+        x = _moe_experts(k)
+        assert L.qf_lora_experts_layout(ctypes.byref(x), 2, out_e) == 0
+        assert L.qf_lora_layout(ctypes.byref(_moe_descs(k)), 2 * k, out_g) == 0
+        assert tuple(out_e) == tuple(out_g)
+        assert L.qf_lora_experts_workspace(ctypes.byref(x), 2) == L.qf_lora_workspace(ctypes.byref(_moe_descs(k)), 2 * k)
+    # 32 experts in one call: 64 groups, beyond the grouped calls' 16 descriptors
+    x = _moe_experts(32)
+    assert L.qf_lora_experts_layout(ctypes.byref(x), 2, out_e) == 0
+    tiles = 32 * ((3072 // 32) * (3072 // 64) + (3072 // 32) * (1536 // 64))
+    assert tuple(out_e)[:2] == (-(-tiles // (4 * 768)), 768)
+    assert tuple(out_e)[4:] == (32, 32 * ((3072 // 32) * 6 + (3072 // 32) * 3) // 4)
+
+
+def test_lora_experts_validation():
+    L = _lib.lib()
+    q = _addr(0x10100000)
+    x = _moe_experts(8)
+    need = L.qf_lora_experts_workspace(ctypes.byref(x), 2)
+    assert need > 0
+    call = lambda n_groups=16, ws=need: L.qf_lora_experts_merge_tensor_scale_nvfp4(ctypes.byref(x), 2, n_groups, q,
+                                                                                  None, q, ws, None)
+    assert call(ws=need - 4) == 4                                  # workspace too small
+    assert call(n_groups=15) == 7                                  # expert 7 of down: group 15
+    x[1].count = 0
+    assert L.qf_lora_experts_workspace(ctypes.byref(x), 2) == 0
+    assert call() == 7
+    x[1].count = 8
+    x[1].group_stride = -1
+    assert call() == 7
+    x[1].group_stride = 2
+    x[0].count = x[1].count = 33                                   # group 65 >= QF_MAX_GROUPS
+    assert call(n_groups=64) == 7
+    x[0].count = x[1].count = 8
+    x[0].d.M = 0x10400000                                          # no merge scratch here
+    assert call() == 7
+    assert L.qf_lora_experts_merge_qdq_pack_nvfp4(ctypes.byref(x), 2, q, None) == 7
+    x[0].d.M = 0
+    assert L.qf_lora_experts_merge_qdq_pack_nvfp4(ctypes.byref(x), 2, q, None) == 1   # no y and no codes
+    assert L.qf_lora_experts_adapter_grads(ctypes.byref(x), 2, 0, q, need, None) == 1  # no G, dA, dB
+    assert L.qf_lora_experts_adapter_grads(ctypes.byref(x), 17, 0, q, need, None) == 7
+    assert L.qf_lora_experts_layout(ctypes.byref(x), 2, None) == 1
