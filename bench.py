@@ -747,13 +747,14 @@ class MoELoRANVFP4:
     5.5 -> 9.3 ms per step.)  The per-kernel timings run everything on one stream."""
     name = "moe_lora_nvfp4"
 
-    def __init__(self, torch, fq, experts_per_launch=1, merge_scratch=False):
+    def __init__(self, torch, fq, experts_per_launch=1, merge_scratch=False, api="grouped"):
         import workloads
         self.torch, self.fq = torch, fq
+        self.api = api
         mo = workloads.MOE
         E, r = mo["experts"], mo["rank"]
         k = experts_per_launch
-        assert E % k == 0 and 2 * k <= 16
+        assert E % k == 0 and 2 * k <= (64 if api == "experts" else 16)
         x = workloads.moe_experts_device(seed=0)
         dev = torch.device("cuda")
         mats = ("gate_up", "down")
@@ -772,6 +773,15 @@ class MoELoRANVFP4:
         self.tscale = torch.empty(2 * E, dtype=torch.float32, device=dev)
         self.chunks = []
         for c0 in range(0, E, k):
+            if api == "experts":
+                # one stacked-experts descriptor per matrix: expert e of the call in groups 2e, 2e + 1
+                assert not merge_scratch
+                descs = [dict(W=x[m]["W"][c0:c0 + k], A=x[m]["A"][c0:c0 + k], B=x[m]["B"][c0:c0 + k],
+                              G=x[m]["G"][c0:c0 + k], y=scratch[m][1], codes=self.codes[m][c0:c0 + k],
+                              scales=self.scl[m][c0:c0 + k], dA=self.dA[m][c0:c0 + k], dB=self.dB[m][c0:c0 + k],
+                              group=j, group_stride=2) for j, m in enumerate(mats)]
+                self.chunks.append((fq.LoraExperts(descs), self.tscale[2 * c0: 2 * (c0 + k)]))
+                continue
             items = []
             for e in range(c0, c0 + k):
                 for j, m in enumerate(mats):
@@ -792,10 +802,13 @@ class MoELoRANVFP4:
         self.kernels = {"lora_merge_amax": 2.0 * n, "lora_merge_qdq_pack": (2 + 2 + 0.5 + 1 / 16) * n,
                         "lora_adapter_grads": 2.0 * n}
         self.bytes_per_step = sum(self.kernels.values())
-        layout = fq.qf_lora_layout(self.chunks[0][0])
+        layout = (fq.qf_lora_experts_layout(self.chunks[0][0]) if api == "experts"
+                  else fq.qf_lora_layout(self.chunks[0][0]))
         self.config = {"workload": self.name,
                        "experts": E, "matrices_per_expert": {m: list(x[m]["W"].shape[1:]) for m in mats},
                        "rank": r, "elements": n, "experts_per_launch": k,
+                       "calls": ("stacked-experts calls (one descriptor per matrix, experts stacked)"
+                                 if api == "experts" else "grouped calls (one descriptor per expert matrix)"),
                        "merge_scratch": merge_scratch,
                        "bytes_per_element": 8.5625,
                        "extra_traffic_bytes": int(2 * n) if merge_scratch else 0,
@@ -806,6 +819,24 @@ class MoELoRANVFP4:
                                    else "merge passes and gradient passes on two streams"),
                        "format": "NVFP4 (E2M1, block 16, E4M3 + FP32 tensor scale per expert per fused matrix)"}
 
+    def _scale(self, items, sc, ws):
+        if self.api == "experts":
+            self.fq.qf_lora_experts_merge_tensor_scale_nvfp4(items, len(sc), sc, None, ws)
+        else:
+            self.fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
+
+    def _qdq(self, items, sc):
+        if self.api == "experts":
+            self.fq.qf_lora_experts_merge_qdq_pack_nvfp4(items, sc)
+        else:
+            self.fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
+
+    def _grads(self, items, ws):
+        if self.api == "experts":
+            self.fq.qf_lora_experts_adapter_grads(items, ws=ws)
+        else:
+            self.fq.qf_lora_adapter_grads_grouped(items, ws=ws)
+
     def step(self, mark=None):
         fq, ws = self.fq, self.ws
         if mark is None:
@@ -815,29 +846,29 @@ class MoELoRANVFP4:
             self.qdq_stream.wait_stream(cur)
             three = self.experts_per_launch > 1
             for (items, sc), ready in zip(self.chunks, self.scale_ready):
-                fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
+                self._scale(items, sc, ws)
                 if three:
                     ready.record(cur)
                     with torch.cuda.stream(self.qdq_stream):
                         self.qdq_stream.wait_event(ready)
-                        fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
+                        self._qdq(items, sc)
                 else:
-                    fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
+                    self._qdq(items, sc)
                 with torch.cuda.stream(self.grad_stream):
-                    fq.qf_lora_adapter_grads_grouped(items, ws=self.ws_grads)
+                    self._grads(items, self.ws_grads)
             cur.wait_stream(self.qdq_stream)
             cur.wait_stream(self.grad_stream)
             return
         t = mark
         for items, sc in self.chunks:
             t("lora_merge_amax", 0)
-            fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, items.n, sc, None, ws)
+            self._scale(items, sc, ws)
             t("lora_merge_amax", 1)
             t("lora_merge_qdq_pack", 0)
-            fq.qf_lora_merge_qdq_pack_nvfp4_grouped(items, sc)
+            self._qdq(items, sc)
             t("lora_merge_qdq_pack", 1)
             t("lora_adapter_grads", 0)
-            fq.qf_lora_adapter_grads_grouped(items, ws=ws)
+            self._grads(items, ws)
             t("lora_adapter_grads", 1)
 
     def controls(self, reps=20):
@@ -886,6 +917,18 @@ class MoELoRANVFP4x8(MoELoRANVFP4):
         return {}
 
 
+class MoELoRANVFP4x32(MoELoRANVFP4):
+    """The same step through the stacked-experts calls, 32 experts per call (two
+    descriptors, 64 tied groups; 4 calls of each pass per step)."""
+    name = "moe_lora_nvfp4_x32"
+
+    def __init__(self, torch, fq):
+        super().__init__(torch, fq, experts_per_launch=32, api="experts")
+
+    def controls(self, reps=20):
+        return {}
+
+
 class MoELoRANVFP4x8Scratch(MoELoRANVFP4):
     """8 experts per launch with the merged weights kept in a scratch between the passes."""
     name = "moe_lora_nvfp4_x8_scratch"
@@ -924,11 +967,12 @@ def graph_replay(torch, step, reps, nbytes):
 
 WORKLOADS = {c.name: c for c in (DenseLayerNVFP4, Q4KSet, MXFP4Operands, MXFP4OperandsNoclip, Single256x512,
                                  W4A4GemmMXFP4,
-                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x8Scratch, DequantDense,
+                                 MoELoRANVFP4, MoELoRANVFP4x8, MoELoRANVFP4x32, MoELoRANVFP4x8Scratch, DequantDense,
                                  SteClippedDense, Q4KSetMSE)}
 # measured next to the headline workload in a default run (fewer steps each)
 SECONDARY = [MXFP4Operands.name, MXFP4OperandsNoclip.name, Q4KSet.name, Single256x512.name, W4A4GemmMXFP4.name,
-             MoELoRANVFP4x8.name, MoELoRANVFP4.name, MoELoRANVFP4x8Scratch.name, DequantDense.name,
+             MoELoRANVFP4x32.name, MoELoRANVFP4x8.name, MoELoRANVFP4.name, MoELoRANVFP4x8Scratch.name,
+             DequantDense.name,
              SteClippedDense.name, Q4KSetMSE.name]
 
 
