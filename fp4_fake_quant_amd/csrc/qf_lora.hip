@@ -713,6 +713,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   const int64_t u0 = w * units / nw, u1 = (w + 1) * units / nw;
   uint32_t L = 0;                                                    // wave-uniform, group mg
   int mg = -1;
+  uint4 ap[LORA_MAX_R];                                              // A's slice, bf16 (rows k >= r: 0)
+  float a_l = 0.0f;
+  int a_di = -1, a_e = -1, a_slab = -1;
 #pragma unroll 1
   for (int64_t uf = u0; uf < u1; ++uf) {
     const LoraUnit uq = lora_unit(a, (int)(uf >> 2), (int)(uf & 3));
@@ -727,18 +730,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
     const int64_t cols = T.cols, ldw = T.ldw;
     const int r = RK ? RK : T.r;
-    const int rb = ul / T.slabs;
-    const int64_t cs = (int64_t)(ul - rb * T.slabs) * LORA_SLAB;
+    // units slab by slab (all row blocks of a slab in turn), so that a run of units keeps
+    // the slab's A in registers
+    const int rblocks = (int)((T.rows + a.merge_rows - 1) / a.merge_rows);
+    const int slab = ul / rblocks, rb = ul - slab * rblocks;
+    const int64_t cs = (int64_t)slab * LORA_SLAB;
     const int64_t r0 = (int64_t)rb * a.merge_rows;
     const int rows = (int)min((int64_t)a.merge_rows, T.rows - r0);   // at most 32
     const bool active = cs + 8 * lane < cols;
     const uint32_t lo = active ? 16u * lane : BUF_OOR;
     const __amdgpu_buffer_rsrc_t rw = make_buf(X.W + r0 * ldw + cs, (int64_t)rows * ldw * 2);
-    const __amdgpu_buffer_rsrc_t ra = make_buf(X.A + cs, (int64_t)r * cols * 2 - cs * 2);
     const uint32_t wstride = (uint32_t)(ldw * 2), mstride = (uint32_t)(cols * 2);
-    uint4 ap[LORA_MAX_R];                                            // A's slice, bf16 (rows k >= r: 0)
+    if (uq.di != a_di || uq.e != a_e || slab != a_slab) {
+      const __amdgpu_buffer_rsrc_t ra = make_buf(X.A + cs, (int64_t)r * cols * 2 - cs * 2);
 #pragma unroll
-    for (int k = 0; k < LORA_MAX_R; ++k) ap[k] = buf_load16(ra, lo + k * mstride);
+      for (int k = 0; k < LORA_MAX_R; ++k) ap[k] = buf_load16(ra, lo + k * mstride);
+      uint32_t amx = 0;
+#pragma unroll
+      for (int k = 0; k < LORA_MAX_R; ++k) amx = umax(amx, amax_bits8(ap[k]));
+      a_l = __uint_as_float(amx << 16) * 1.001f;
+      a_di = uq.di;
+      a_e = uq.e;
+      a_slab = slab;
+    }
     // bsum of row r0 + lane (lanes below rows)
     float bsum = 0.0f;
     {
@@ -762,10 +776,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
       wv[q] = buf_load16(rw, lo + q * wstride);
     }
     LORA_FENCE();
-    uint32_t amx = 0;
-#pragma unroll
-    for (int k = 0; k < LORA_MAX_R; ++k) amx = umax(amx, amax_bits8(ap[k]));
-    const float a_l = __uint_as_float(amx << 16) * 1.001f;
     // t of the lane's 8 elements of row ii (w: the row's chunk); true where the lane's
     // elements could exceed L
     auto test = [&](const uint4& wq, int ii) {
@@ -1060,16 +1070,25 @@ hipError_t launch_lora_merge(const LoraArgs& a, int grid, hipStream_t s) {
   if (grid == 0) return hipSuccess;
   bool any_m = false;
   for (int i = 0; i < a.n; ++i) any_m = any_m || a.d[i].M;
+  // Without M, launches large enough for 32-row slab units take the bounded pass; smaller
+  // ones (8- or 16-row units, e.g. one expert per launch) keep the matrix-core pass, where
+  // the bounded pass's per-unit loads of A and B would outweigh the merges it skips
+  // (one expert per launch: 2.28 against 3.01 ms per 128 experts).
+  const bool bounded = !any_m && a.merge_rows == LORA_QDQ_ROWS;
   if (all_rank16(a)) {
     if (any_m)
       hipLaunchKernelGGL((k_lora_merge_amax<LORA_MAX_R, true>), dim3(grid), dim3(256), 0, s, a);
-    else
+    else if (bounded)
       hipLaunchKernelGGL(k_lora_merge_amax_bounded<LORA_MAX_R>, dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_lora_merge_amax<LORA_MAX_R, false>), dim3(grid), dim3(256), 0, s, a);
   } else {
     if (any_m)
       hipLaunchKernelGGL((k_lora_merge_amax<0, true>), dim3(grid), dim3(256), 0, s, a);
-    else
+    else if (bounded)
       hipLaunchKernelGGL(k_lora_merge_amax_bounded<0>, dim3(grid), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_lora_merge_amax<0, false>), dim3(grid), dim3(256), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -1,7 +1,9 @@
 """GPU parity: the merged weight's tensor scale when pass 1 keeps no M.
 
-Without an M scratch the maximum pass merges exactly only the elements that a bound on
-|B.A| says could reach the running maximum.  These cases are built so that a wrong or
+Without an M scratch, launches large enough for 32-row units take a maximum pass that
+merges exactly only the elements that a bound on |B.A| says could reach the running
+maximum; each case here shares its launch with a large filler matrix so that it runs that
+pass (checked through the layout query).  These cases are built so that a wrong or
 too tight bound would change the result: the maximum of M sits where |W| is not the
 largest (the adapter decides it), the largest |W| is cancelled by the adapter, the
 maximum lies in the last row and column, values reach below fp32's normal range, and
@@ -31,16 +33,43 @@ def _case(rows, cols, r, seed, w=0.02, a=0.01, b=0.001):
             rng.standard_normal((rows, r)) * b)
 
 
+_FILLER = {}
+
+
+def _filler():
+    """A 4096 x 16384 matrix with zero adapters (M = W) in a group of its own: with it a
+    launch is large enough for 32-row units, the layout whose pass 1 without M merges
+    only where the bound requires (smaller launches take the matrix-core pass)."""
+    if not _FILLER:
+        g = torch.Generator(device="cuda").manual_seed(77)
+        W = (torch.randn((4096, 16384), generator=g, device="cuda") * 0.02).bfloat16()
+        _FILLER.update(W=W, A=torch.zeros((16, 16384), dtype=torch.bfloat16, device="cuda"),
+                       B=torch.zeros((4096, 16), dtype=torch.bfloat16, device="cuda"),
+                       s=np.float32(W.float().abs().max().item()) / np.float32(2688.0))   # IEEE on the host
+    return _FILLER
+
+
+def _with_filler(items):
+    f = _filler()
+    out = items + [dict(W=f["W"], A=f["A"], B=f["B"], group=max(it["group"] for it in items) + 1, M=None)]
+    if all(it.get("M") is None for it in items):
+        assert fq.qf_lora_layout(out)[4] == 32, "the launch must run 32-row units"
+    return out
+
+
 def _scales(cases, with_M):
     items = []
     for g, (W, A, B) in enumerate(cases):
         rows, cols = W.shape
         items.append(dict(W=dev(W), A=dev(A), B=dev(B), group=g,
                           M=torch.empty((rows, cols), dtype=torch.bfloat16, device="cuda") if with_M else None))
+    items = _with_filler(items)
     flag = torch.zeros(1, dtype=torch.int32, device="cuda")
     s = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, len(items), d_nonfinite=flag)
     torch.cuda.synchronize()
-    return s.cpu().numpy(), int(flag.item())
+    s = s.cpu().numpy()
+    assert f32bits(s[-1]) == f32bits(np.float32(_filler()["s"])), "filler matrix"
+    return s[:-1], int(flag.item())
 
 
 def _check(cases, what):
@@ -130,17 +159,18 @@ def test_nonfinite_inputs(where):
 
 
 def test_many_groups_one_launch():
-    """16 descriptors in one launch, 5 tied groups, the maxima spread over different
-    descriptors (two of each group share the group's maximum element value)."""
+    """15 descriptors (and the filler) in one launch, 5 tied groups, the maxima spread over
+    different descriptors."""
     cases, groups = [], []
-    for i in range(16):
+    for i in range(15):
         W, A, B = _case(48 + 7 * i, 512 + 32 * (i % 4), 1 + (i * 5) % 16, seed=100 + i, a=0.05, b=0.05)
         cases.append((_bf(W), _bf(A), _bf(B)))
         groups.append(i % 5)
     items = []
     for (W, A, B), g in zip(cases, groups):
         items.append(dict(W=dev(W), A=dev(A), B=dev(B), group=g, M=None))
-    got = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, 5).cpu().numpy()
+    items = _with_filler(items)
+    got = fq.qf_lora_merge_tensor_scale_nvfp4_grouped(items, 6).cpu().numpy()
     for g in range(5):
         members = [lora.merge(W, A, B) for (W, A, B), gg in zip(cases, groups) if gg == g]
         assert f32bits(got[g]) == f32bits(nvfp4.tensor_scale(members)), f"group {g}"
