@@ -90,6 +90,18 @@ __device__ __forceinline__ LoraMat lora_mat(const LoraTensor& T, int e, int da_r
   return m;
 }
 
+// Descriptor of a launch-wide index x: the number of descriptors after the first whose
+// first index (field F, increasing with the descriptor) is at most x.  All of them are
+// compared at once, so the kernel-argument reads are independent (no chain of dependent
+// scalar loads, as a search loop would make).
+template <int32_t LoraTensor::*F>
+__device__ __forceinline__ int lora_desc_of(const LoraArgs& a, int64_t x) {
+  int di = 0;
+#pragma unroll
+  for (int i = 1; i < QF_MAX_GROUPED; ++i) di += (i < a.n && x >= (int64_t)(a.d[i].*F)) ? 1 : 0;
+  return di;
+}
+
 // --------------------------------------------------- merge, passes 1 and 2 ------
 // The low-rank product S = B.A runs on the fp32 matrix cores: v_mfma_f32_32x32x1_2b_f32
 // multiplies one fp32 value per lane of its A operand by one of its B operand (K = 1) and
@@ -182,9 +194,7 @@ __device__ __forceinline__ void mm_next(const LoraArgs& a, MmTile& p) {
 // Place of tile tb of the launch.
 __device__ __forceinline__ MmTile mm_locate(const LoraArgs& a, int64_t tb) {
   MmTile p;
-  int di = 0;
-#pragma unroll 1
-  while (di + 1 < a.n && tb >= a.d[di + 1].merge_tile_begin) ++di;
+  const int di = lora_desc_of<&LoraTensor::merge_tile_begin>(a, tb);
   const LoraTensor& T = a.d[di];
   p.rtiles = T.merge_rtiles;
   p.ctiles = T.merge_ctiles;
@@ -499,10 +509,7 @@ constexpr int BW = LORA_MAX_R / 2 + 1;   // 32-bit words that can hold one row o
 typedef const __attribute__((address_space(4))) uint32_t* const_u32_ptr;
 
 __device__ __forceinline__ int find_desc_wg(const LoraArgs& a, int b) {
-  int di = 0;
-#pragma unroll 1
-  while (di + 1 < a.n && b >= a.d[di + 1].merge_wg_begin) ++di;
-  return di;
+  return lora_desc_of<&LoraTensor::merge_wg_begin>(a, b);
 }
 
 // Workgroup b of the merge-and-QDQ layout: its descriptor, expert, and the unit of wave
@@ -663,10 +670,7 @@ __device__ __forceinline__ float sum_partials(const float* p, int64_t stride, in
 
 // Matrix m of the launch (blockIdx.y of the reduces): its descriptor.
 __device__ __forceinline__ int find_desc_mat(const LoraArgs& a, int m) {
-  int di = 0;
-#pragma unroll 1
-  while (di + 1 < a.n && m >= a.d[di + 1].mat_begin) ++di;
-  return di;
+  return lora_desc_of<&LoraTensor::mat_begin>(a, m);
 }
 
 __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumulate) {
@@ -882,9 +886,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t gl[2 * GR_BUF];
   __shared__ float red[4][2][256];                         // dB sums of the 4 waves
   const int b = blockIdx.x;
-  int di = 0;
-#pragma unroll 1
-  while (di + 1 < a.n && b >= a.d[di + 1].grad_wg_begin) ++di;
+  const int di = lora_desc_of<&LoraTensor::grad_wg_begin>(a, b);
   const LoraTensor& T = a.d[di];
   const uint32_t tid = threadIdx.x;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63u;
