@@ -701,9 +701,10 @@ __global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumula
 // full merge finds.
 //
 // Work split: the units of the merge-and-QDQ pass (a 512-column slab of merge_rows rows,
-// lane l on columns 8l .. 8l+7), numbered four per workgroup of that pass, cut into equal
-// contiguous runs, one per wave of a grid that stays resident; the running maximum is kept
-// per wave across the units of one group, and shared through the workgroup's LDS maximum.
+// lane l on columns 8l .. 8l+7), four per workgroup of that pass, taken here slab by slab
+// within each expert (so that consecutive units share A's slice), cut into equal contiguous
+// runs, one per wave of a grid that stays resident; the running maximum is kept per wave
+// across the units of one group, and shared through the workgroup's LDS maximum.
 constexpr int LORA_P1_PREFETCH = 8;                    // rows of W in flight per wave
 
 template <int RK>

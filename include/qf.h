@@ -323,11 +323,13 @@ typedef struct qf_lora_desc {
  * descriptor is invalid). */
 size_t qf_lora_workspace(const qf_lora_desc* d, int n);
 /* Host query of the launch layout the LoRA calls choose for these descriptors (nothing
- * is launched; only shapes, ranks and groups are read).  Pass 1 (merge + tensor scale)
- * cuts the launch's 32-row x 64-column tiles into equal contiguous runs, one per wave of
- * 4-wave workgroups: 512 workgroups, or fewer so that a wave keeps at least 4 tiles.
- * Pass 2 without M (merge again + QDQ) works in units of a 512-column slab of 32 rows,
- * shrinking to 16 or 8 until the launch has 512 workgroups.  out[0] most pass-1 tiles per
+ * is launched; only shapes, ranks and groups are read).  Pass 2 without M (merge again +
+ * QDQ) works in units of a 512-column slab of 32 rows, shrinking to 16 or 8 until the
+ * launch has 512 workgroups.  Pass 1 (merge + tensor scale) runs a grid of 768 4-wave
+ * workgroups, or fewer so that a wave keeps at least 4 of the launch's 32-row x 64-column
+ * tiles; with M, or when pass-2 units shrank below 32 rows, its waves take equal
+ * contiguous runs of those tiles, and otherwise (no M, 32-row units) equal runs of the
+ * pass-2 units, where they merge only the rows that may hold a new maximum.  out[0] most pass-1 tiles per
  * wave, out[1] pass-1 workgroups, out[2] rows per gradient workgroup (512 when that still
  * gives 256 workgroups, else 256), out[3] gradient workgroups, out[4] rows per pass-2
  * unit, out[5] pass-2 workgroups.  out is host int32[6].  Errors as the LoRA calls'
