@@ -30,7 +30,10 @@
 //   - workgroups are mapped XCD-aware: consecutive workgroup ids go to the
 //     eight XCDs in turn, so XCD x is handed the x-th eighth of a grouped
 //     tile order (8 tile rows at a time) and its concurrently running
-//     workgroups share X and W panels in its L2.
+//     workgroups share X and W panels in its L2;
+//   - the grid is persistent (at most one workgroup per CU, each running
+//     several tiles in turn): a tile's last K step already loads the next
+//     tile's first slice, and its epilogue stores drain while that tile starts.
 #include "qf_device.h"
 #include "qf_gemm_epilogue.h"
 #include "qf_kernels.h"
@@ -120,26 +123,38 @@ __device__ __forceinline__ void store_chunk(uint8_t* lds, uint32_t r, uint32_t c
 
 #define QF_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// The workgroup's 256 x 256 tile of Y; smem is the kernel's 128 KiB of LDS, sx / sw the
-// NVFP4 tensor scales of X and W (unused for MXFP4).
-template <int GRID, bool QA, bool QW>
-__device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W,
-                                          int64_t ldw, uint16_t* __restrict__ Y, int64_t ldy, int M, int N, int K,
-                                          int y_vec, float sx, float sw, uint8_t* smem) {
-  const float kx = 6.0f * sx, kw = 6.0f * sw;
-
-  // ---- tile of this workgroup (XCD-aware grouped order) ----
-  const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
+// Origin (m0, n0) of tile t of the launch order, XCD-aware: when the tile count is a
+// multiple of 8, t & 7 picks one eighth of a grouped order (G_GROUP_M tile rows at a time)
+// and t >> 3 the tile within it, so the workgroups of one XCD (ids congruent mod 8) work
+// on neighbouring tiles and share X and W panels in that XCD's L2.
+__device__ __forceinline__ void tile_origin(int t, int tiles_m, int tiles_n, int& m0, int& n0) {
   const int total = tiles_m * tiles_n;
-  int t = blockIdx.x;
   if ((total & 7) == 0) t = (t & 7) * (total >> 3) + (t >> 3);
   const int group = t / (G_GROUP_M * tiles_n);
   const int first_m = group * G_GROUP_M;
   const int gsize = min(tiles_m - first_m, G_GROUP_M);
   const int in_group = t - group * G_GROUP_M * tiles_n;
-  const int tm = first_m + in_group % gsize;
-  const int tn = in_group / gsize;
-  const int m0 = tm * GBM, n0 = tn * GBN;
+  m0 = (first_m + in_group % gsize) * GBM;
+  n0 = (in_group / gsize) * GBN;
+}
+
+// The workgroup's tiles of Y: blockIdx.x, blockIdx.x + gridDim.x, ...  The grid holds at
+// most one workgroup per CU (the LDS admits no second one) and is a multiple of 8 when the
+// tiles outnumber it, so every tile of a workgroup comes from its XCD's part of the order.
+// Consecutive tiles overlap: the last K step of a tile loads the first K slice of the
+// workgroup's next tile, which is in flight during the epilogue, and the epilogue's
+// stores drain while the next tile starts.
+//
+// smem is the kernel's 128 KiB of LDS, sx / sw the NVFP4 tensor scales of X and W (unused
+// for MXFP4).  YLDS: Y leaves through LDS (store_tile_lds); otherwise from the
+// accumulators, 8 bytes (y_vec = 1) or one element (y_vec = 0) at a time.
+template <int GRID, bool QA, bool QW, bool YLDS>
+__device__ __forceinline__ void gemm_tiles(const uint16_t* __restrict__ X, int64_t ldx, const uint16_t* __restrict__ W,
+                                           int64_t ldw, uint16_t* __restrict__ Y, int64_t ldy, int M, int N, int K,
+                                           int y_vec, float sx, float sw, uint8_t* smem) {
+  const float kx = 6.0f * sx, kw = 6.0f * sw;
+  const int tiles_m = (M + GBM - 1) / GBM, tiles_n = (N + GBN - 1) / GBN;
+  const int total = tiles_m * tiles_n;
 
   const uint32_t lane = threadIdx.x & 63u;
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -147,24 +162,14 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X, int64_
   const uint32_t frow = lane & 31u, fhalf = lane >> 5;     // MFMA fragment row, k half
 
   // global -> register loads: lane t takes chunk (t & 7) of rows (t >> 3) + 64 i
-  const __amdgpu_buffer_rsrc_t rx = tile_rsrc(X + (int64_t)m0 * ldx, ldx, M - m0);
-  const __amdgpu_buffer_rsrc_t rw = tile_rsrc(W + (int64_t)n0 * ldw, ldw, N - n0);
   const uint32_t lrow = threadIdx.x >> 3, lchunk = threadIdx.x & 7u;
   const uint32_t xoff = (uint32_t)(lrow * ldx + lchunk * 8) * 2u, xstep = (uint32_t)(64 * ldx) * 2u;
   const uint32_t woff = (uint32_t)(lrow * ldw + lchunk * 8) * 2u, wstep = (uint32_t)(64 * ldw) * 2u;
 
-  f32x16_t acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
   uint4 raw[2 * G_LOADS];                                 // 4 X chunks, then 4 W chunks
-  auto issue_load = [&](int idx, uint32_t kbyte) {
-    if (idx < G_LOADS) raw[idx] = load_chunk_buf(rx, xoff + idx * xstep + kbyte);
-    else raw[idx] = load_chunk_buf(rw, woff + (idx - G_LOADS) * wstep + kbyte);
+  auto issue_load = [&](__amdgpu_buffer_rsrc_t lx, __amdgpu_buffer_rsrc_t lw, int idx, uint32_t kbyte) {
+    if (idx < G_LOADS) raw[idx] = load_chunk_buf(lx, xoff + idx * xstep + kbyte);
+    else raw[idx] = load_chunk_buf(lw, woff + (idx - G_LOADS) * wstep + kbyte);
   };
   auto stage_chunk = [&](int idx, uint8_t* stage) {
     if (idx < G_LOADS) store_chunk<GRID, QA>(stage, lrow + 64 * idx, lchunk, raw[idx], sx, kx);
@@ -172,129 +177,163 @@ __device__ __forceinline__ void gemm_tile(const uint16_t* __restrict__ X, int64_
   };
 
   const int nk = K / GBK;
-  // prologue: step 0's chunks into stage 0, then step 1's chunks into registers, in the
-  // loop's slot order (slot j stages and reloads chunk j)
-#pragma unroll
-  for (int idx = 0; idx < 2 * G_LOADS; ++idx) issue_load(idx, 0);
   const uint32_t kb1 = (uint32_t)min(1, nk - 1) * GBK * 2u;
+  int t = blockIdx.x, m0, n0;
+  tile_origin(t, tiles_m, tiles_n, m0, n0);
+  __amdgpu_buffer_rsrc_t rx = tile_rsrc(X + (int64_t)m0 * ldx, ldx, M - m0);
+  __amdgpu_buffer_rsrc_t rw = tile_rsrc(W + (int64_t)n0 * ldw, ldw, N - n0);
+  // step 0 of the first tile
 #pragma unroll
-  for (int slot = 0; slot < 2 * G_LOADS; ++slot) {
-    stage_chunk(slot, smem);
-    issue_load(slot, kb1);
-    QF_FENCE();
-  }
-  __syncthreads();
+  for (int idx = 0; idx < 2 * G_LOADS; ++idx) issue_load(rx, rw, idx, 0);
+  // Later tiles reach the loop head with their step-0 loads followed by the epilogue's
+  // stores in flight; stores to no memory put the first tile in the same state, so the
+  // wait for those loads is the same on both paths and never waits for the stores.
+  if constexpr (YLDS) epilogue_store_balance(Y);
+  QF_FENCE();
 
-  // fragments of substep s: fx[i] = X rows wm*128 + 32i + frow, fw[j] = W rows wn*64 + 32j + frow,
-  // k chunk 2s + fhalf; two register sets, so substep s+1's fragments load during substep s
-  bf16x8_t fx[2][4], fw[2][2];
-  auto read_x = [&](int set, const uint8_t* base, int s, int i) {
-    fx[set][i] = *reinterpret_cast<const bf16x8_t*>(base + lds_off(wm * 128 + i * 32 + frow, 2u * s + fhalf));
-  };
-  auto read_w = [&](int set, const uint8_t* base, int s, int j) {
-    fw[set][j] = *reinterpret_cast<const bf16x8_t*>(base + G_SLICE_BYTES + lds_off(wn * 64 + j * 32 + frow, 2u * s + fhalf));
-  };
-#pragma unroll
-  for (int i = 0; i < 4; ++i) read_x(0, smem, 0, i);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) read_w(0, smem, 0, j);
+  for (;;) {
+    // the workgroup's next tile (a resource of no bytes when there is none: its loads return 0)
+    const bool more = t < total - (int)gridDim.x;          // (t + gridDim.x could overflow)
+    int m1 = 0, n1 = 0;
+    if (more) tile_origin(t + (int)gridDim.x, tiles_m, tiles_n, m1, n1);
+    const __amdgpu_buffer_rsrc_t rx1 = tile_rsrc(X + (int64_t)m1 * ldx, ldx, more ? M - m1 : 0);
+    const __amdgpu_buffer_rsrc_t rw1 = tile_rsrc(W + (int64_t)n1 * ldw, ldw, more ? N - n1 : 0);
 
-  // Substep s (16 of K) is 8 MFMAs in 4 pairs; pair q of substeps 0-2 also reads
-  // fragments for substep s+1 and stages/reloads chunk slots (3, 3, 2 per substep).
-  // Substep 3 follows the barrier and reads the next step's first fragments.  Measured
-  // alternatives, all slower: a finer MFMA/VALU interleave asked of the scheduler with
-  // sched_group_barrier (-3%), one QDQ piece after every MFMA (-1%), staging spread
-  // over all four substeps with the barrier at the end of the step (-2%), and a
-  // ping-pong in which waves 0-3 run their MFMAs while waves 4-7 stage and then the
-  // reverse, with a barrier per phase (-26%).
-  for (int ks = 0; ks < nk; ++ks) {
-    const int cur = ks & 1;
-    const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
-    uint8_t* next = smem + 2 * (cur ^ 1) * G_SLICE_BYTES;
-    const uint32_t kb2 = (uint32_t)min(ks + 2, nk - 1) * GBK * 2u;
+    f32x16_t acc[4][2];
 #pragma unroll
-    for (int s = 0; s < GBK / 16; ++s) {
-      const int fs = s & 1;
-      if (s == 3) __syncthreads();                          // step ks+1's slice is in `next`
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        // plain product: the wave issuing an MFMA pair goes first (1% faster; with QDQ
-        // work between the pairs it measured 3% slower)
-        if constexpr (!QA && !QW) __builtin_amdgcn_s_setprio(1);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fs][j], fx[fs][q], acc[q][j], 0, 0, 0);
-        if constexpr (!QA && !QW) __builtin_amdgcn_s_setprio(0);
-        const uint8_t* rb = (s < 3) ? base : next;
-        const int rs = (s < 3) ? s + 1 : 0;
-        const int rset = (s < 3) ? (fs ^ 1) : 0;
-        if (q < 2) { read_x(rset, rb, rs, 2 * q); read_x(rset, rb, rs, 2 * q + 1); }
-        else if (q == 2) { read_w(rset, rb, rs, 0); read_w(rset, rb, rs, 1); }
-        if (s < 3) {
-          // slots: s=0 -> 0,1,2; s=1 -> 3,4,5; s=2 -> 6,7
-          const int slot = 3 * s + q;
-          if (q < 3 && slot < 2 * G_LOADS) {
-            stage_chunk(slot, next);                        // step ks+1's chunk (loaded during ks-1)
-            issue_load(slot, kb2);                          // step ks+2's chunk
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+    // prologue: step 0's chunks (in registers) into stage 0, then step 1's chunks into
+    // registers, in the loop's slot order (slot j stages and reloads chunk j)
+#pragma unroll
+    for (int slot = 0; slot < 2 * G_LOADS; ++slot) {
+      stage_chunk(slot, smem);
+      issue_load(rx, rw, slot, kb1);
+      QF_FENCE();
+    }
+    __syncthreads();
+
+    // fragments of substep s: fx[i] = X rows wm*128 + 32i + frow, fw[j] = W rows wn*64 + 32j + frow,
+    // k chunk 2s + fhalf; two register sets, so substep s+1's fragments load during substep s
+    bf16x8_t fx[2][4], fw[2][2];
+    auto read_x = [&](int set, const uint8_t* base, int s, int i) {
+      fx[set][i] = *reinterpret_cast<const bf16x8_t*>(base + lds_off(wm * 128 + i * 32 + frow, 2u * s + fhalf));
+    };
+    auto read_w = [&](int set, const uint8_t* base, int s, int j) {
+      fw[set][j] = *reinterpret_cast<const bf16x8_t*>(base + G_SLICE_BYTES + lds_off(wn * 64 + j * 32 + frow, 2u * s + fhalf));
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) read_x(0, smem, 0, i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) read_w(0, smem, 0, j);
+
+    // Substep s (16 of K) is 8 MFMAs in 4 pairs; pair q of substeps 0-2 also reads
+    // fragments for substep s+1 and stages/reloads chunk slots (3, 3, 2 per substep).
+    // Substep 3 follows the barrier and reads the next step's first fragments.  Measured
+    // alternatives, all slower: a finer MFMA/VALU interleave asked of the scheduler with
+    // sched_group_barrier (-3%), one QDQ piece after every MFMA (-1%), staging spread
+    // over all four substeps with the barrier at the end of the step (-2%), and a
+    // ping-pong in which waves 0-3 run their MFMAs while waves 4-7 stage and then the
+    // reverse, with a barrier per phase (-26%).
+    for (int ks = 0; ks < nk; ++ks) {
+      const int cur = ks & 1;
+      const uint8_t* base = smem + 2 * cur * G_SLICE_BYTES;
+      uint8_t* next = smem + 2 * (cur ^ 1) * G_SLICE_BYTES;
+      // loads of step ks+2 (the last step's repeated near the end); the last step loads
+      // step 0 of the next tile
+      const bool last = ks == nk - 1;
+      const __amdgpu_buffer_rsrc_t lx = last ? rx1 : rx, lw = last ? rw1 : rw;
+      const uint32_t kb2 = last ? 0u : (uint32_t)min(ks + 2, nk - 1) * GBK * 2u;
+#pragma unroll
+      for (int s = 0; s < GBK / 16; ++s) {
+        const int fs = s & 1;
+        if (s == 3) __syncthreads();                          // step ks+1's slice is in `next`
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // plain product: the wave issuing an MFMA pair goes first (1% faster; with QDQ
+          // work between the pairs it measured 3% slower)
+          if constexpr (!QA && !QW) __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[q][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[fs][j], fx[fs][q], acc[q][j], 0, 0, 0);
+          if constexpr (!QA && !QW) __builtin_amdgcn_s_setprio(0);
+          const uint8_t* rb = (s < 3) ? base : next;
+          const int rs = (s < 3) ? s + 1 : 0;
+          const int rset = (s < 3) ? (fs ^ 1) : 0;
+          if (q < 2) { read_x(rset, rb, rs, 2 * q); read_x(rset, rb, rs, 2 * q + 1); }
+          else if (q == 2) { read_w(rset, rb, rs, 0); read_w(rset, rb, rs, 1); }
+          if (s < 3) {
+            // slots: s=0 -> 0,1,2; s=1 -> 3,4,5; s=2 -> 6,7
+            const int slot = 3 * s + q;
+            if (q < 3 && slot < 2 * G_LOADS) {
+              stage_chunk(slot, next);                        // step ks+1's chunk (loaded during ks-1)
+              issue_load(lx, lw, slot, kb2);                  // step ks+2's chunk
+            }
+          }
+          QF_FENCE();
+        }
+      }
+    }
+
+    // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
+    if constexpr (YLDS) {
+      store_tile_lds(acc, smem, Y, ldy, m0, n0, M, N);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + (int)(wm * 128 + i * 32 + frow);
+        if (row >= M) continue;
+        uint16_t* yr = Y + (int64_t)row * ldy;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int col = n0 + (int)(wn * 64 + j * 32 + 8 * g + 4 * fhalf);
+            const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+            const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+            if (y_vec && col + 3 < N) {
+              *reinterpret_cast<uint2*>(yr + col) = make_uint2(lo, hi);
+            } else {
+              const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+              for (int e = 0; e < 4; ++e)
+                if (col + e < N) yr[col + e] = v[e];
+            }
           }
         }
-        QF_FENCE();
       }
     }
-  }
-
-
-  // ---- epilogue: lane holds Y row (i*32 + frow), columns j*32 + 8g + 4*fhalf + 0..3 ----
-  if (y_vec == 2) {                                          // 16-byte aligned rows: through LDS
-    store_tile_lds(acc, smem, Y, ldy, m0, n0, M, N);
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = m0 + (int)(wm * 128 + i * 32 + frow);
-    if (row >= M) continue;
-    uint16_t* yr = Y + (int64_t)row * ldy;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int col = n0 + (int)(wn * 64 + j * 32 + 8 * g + 4 * fhalf);
-        const uint32_t lo = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-        const uint32_t hi = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-        if (y_vec && col + 3 < N) {
-          *reinterpret_cast<uint2*>(yr + col) = make_uint2(lo, hi);
-        } else {
-          const uint16_t v[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
-          for (int e = 0; e < 4; ++e)
-            if (col + e < N) yr[col + e] = v[e];
-        }
-      }
-    }
+    if (!more) break;
+    t += (int)gridDim.x;
+    m0 = m1;
+    n0 = n1;
+    rx = rx1;
+    rw = rw1;
+    __syncthreads();                                        // no wave reads the LDS any more
   }
 }
 
-template <bool QA, bool QW>
-__global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4(const uint16_t* __restrict__ X, int64_t ldx,
-                                                            const uint16_t* __restrict__ W, int64_t ldw,
-                                                            uint16_t* __restrict__ Y, int64_t ldy,
-                                                            int M, int N, int K, int y_vec) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];   // 128 KiB of the 160 KiB
-  gemm_tile<GRID_MX, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, 1.0f, 1.0f, smem);
-}
+#define QF_GEMM_KERNEL(NAME, GRID)                                                                               \
+  template <bool QA, bool QW, bool YLDS>                                                                         \
+  __global__ __launch_bounds__(G_THREADS) void NAME(const uint16_t* __restrict__ X, int64_t ldx,                 \
+                                                    const uint16_t* __restrict__ W, int64_t ldw,                 \
+                                                    uint16_t* __restrict__ Y, int64_t ldy, int M, int N, int K, \
+                                                    int y_vec) {                                                 \
+    __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES]; /* 128 KiB of the 160 KiB */       \
+    gemm_tiles<GRID, QA, QW, YLDS>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, 1.0f, 1.0f, smem);                    \
+  }
 
+QF_GEMM_KERNEL(k_gemm_mxfp4, GRID_MX)
 // MXFP4 under the noclip shared-exponent rule.
-template <bool QA, bool QW>
-__global__ __launch_bounds__(G_THREADS) void k_gemm_mxfp4_noclip(const uint16_t* __restrict__ X, int64_t ldx,
-                                                                   const uint16_t* __restrict__ W, int64_t ldw,
-                                                                   uint16_t* __restrict__ Y, int64_t ldy,
-                                                                   int M, int N, int K, int y_vec) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];
-  gemm_tile<GRID_MX_NOCLIP, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, 1.0f, 1.0f, smem);
-}
+QF_GEMM_KERNEL(k_gemm_mxfp4_noclip, GRID_MX_NOCLIP)
+#undef QF_GEMM_KERNEL
 
 // NVFP4 W4A4: the tensor scales come from device memory (computed by the tensor-scale
 // pass, or any fp32 the caller keeps there, e.g. a tracked activation maximum).
-template <bool QA, bool QW>
+template <bool QA, bool QW, bool YLDS>
 __global__ __launch_bounds__(G_THREADS) void k_gemm_nvfp4(const uint16_t* __restrict__ X, int64_t ldx,
                                                             const uint16_t* __restrict__ W, int64_t ldw,
                                                             uint16_t* __restrict__ Y, int64_t ldy,
@@ -302,22 +341,36 @@ __global__ __launch_bounds__(G_THREADS) void k_gemm_nvfp4(const uint16_t* __rest
                                                             const float* __restrict__ d_sx,
                                                             const float* __restrict__ d_sw) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[4 * G_SLICE_BYTES];
-  gemm_tile<GRID_NV, QA, QW>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, QA ? *d_sx : 1.0f, QW ? *d_sw : 1.0f, smem);
+  gemm_tiles<GRID_NV, QA, QW, YLDS>(X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, QA ? *d_sx : 1.0f, QW ? *d_sw : 1.0f,
+                                    smem);
 }
+
+// Workgroups of a launch: one per tile up to one per CU, a multiple of 8 beyond that.
+static dim3 gemm_grid(int tiles) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  if (cus < 8) cus = 256;
+  return dim3(tiles <= cus ? tiles : cus & ~7);
+}
+
+// One of the eight instantiations (QA, QW, YLDS) of kernel K, launched with its arguments.
+#define QF_GEMM_LAUNCH(K, QA_, QW_, ...)                                                  \
+  do {                                                                                   \
+    if (y_vec == 2) hipLaunchKernelGGL((K<QA_, QW_, true>), g, b, 0, s, __VA_ARGS__);    \
+    else hipLaunchKernelGGL((K<QA_, QW_, false>), g, b, 0, s, __VA_ARGS__);              \
+  } while (0)
 
 hipError_t launch_gemm_nvfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw, uint16_t* Y,
                              int64_t ldy, int M, int N, int K, unsigned flags, const float* d_sx, const float* d_sw,
                              hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
-  const int y_vec = y_store_mode(Y, ldy);
-  const dim3 g(tiles), b(G_THREADS);
-  if (qa && qw)
-    hipLaunchKernelGGL((k_gemm_nvfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
-  else if (qa)
-    hipLaunchKernelGGL((k_gemm_nvfp4<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
-  else
-    hipLaunchKernelGGL((k_gemm_nvfp4<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
+  const int y_vec = y_store_mode(Y, ldy, N);
+  const dim3 g = gemm_grid(tiles), b(G_THREADS);
+  if (qa && qw) QF_GEMM_LAUNCH(k_gemm_nvfp4, true, true, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
+  else if (qa) QF_GEMM_LAUNCH(k_gemm_nvfp4, true, false, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
+  else QF_GEMM_LAUNCH(k_gemm_nvfp4, false, true, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec, d_sx, d_sw);
   return hipGetLastError();
 }
 
@@ -325,23 +378,21 @@ hipError_t launch_gemm_mxfp4(const uint16_t* X, int64_t ldx, const uint16_t* W, 
                              int64_t ldy, int M, int N, int K, unsigned flags, hipStream_t s) {
   const int tiles = ((M + GBM - 1) / GBM) * ((N + GBN - 1) / GBN);
   const bool qa = flags & QF_QDQ_A, qw = flags & QF_QDQ_W;
-  // 8-byte output stores need 8-byte aligned rows; otherwise the epilogue stores bf16 by bf16
-  const int y_vec = y_store_mode(Y, ldy);
-  const dim3 g(tiles), b(G_THREADS);
+  // 2: Y through LDS in 16-byte stores; 1: 8-byte stores from the accumulators; 0: element stores
+  const int y_vec = y_store_mode(Y, ldy, N);
+  const dim3 g = gemm_grid(tiles), b(G_THREADS);
   if (flags & QF_MX_NOCLIP) {
-    if (qa && qw)
-      hipLaunchKernelGGL((k_gemm_mxfp4_noclip<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
-    else if (qa)
-      hipLaunchKernelGGL((k_gemm_mxfp4_noclip<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
-    else
-      hipLaunchKernelGGL((k_gemm_mxfp4_noclip<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+    if (qa && qw) QF_GEMM_LAUNCH(k_gemm_mxfp4_noclip, true, true, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+    else if (qa) QF_GEMM_LAUNCH(k_gemm_mxfp4_noclip, true, false, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+    else QF_GEMM_LAUNCH(k_gemm_mxfp4_noclip, false, true, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
     return hipGetLastError();
   }
-  if (qa && qw) hipLaunchKernelGGL((k_gemm_mxfp4<true, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
-  else if (qa) hipLaunchKernelGGL((k_gemm_mxfp4<true, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
-  else if (qw) hipLaunchKernelGGL((k_gemm_mxfp4<false, true>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
-  else hipLaunchKernelGGL((k_gemm_mxfp4<false, false>), g, b, 0, s, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  if (qa && qw) QF_GEMM_LAUNCH(k_gemm_mxfp4, true, true, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  else if (qa) QF_GEMM_LAUNCH(k_gemm_mxfp4, true, false, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  else if (qw) QF_GEMM_LAUNCH(k_gemm_mxfp4, false, true, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
+  else QF_GEMM_LAUNCH(k_gemm_mxfp4, false, false, X, ldx, W, ldw, Y, ldy, M, N, K, y_vec);
   return hipGetLastError();
 }
+#undef QF_GEMM_LAUNCH
 
 }  // namespace qf

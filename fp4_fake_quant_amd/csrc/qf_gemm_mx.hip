@@ -535,7 +535,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_gemm_mx4pp(const uint8_t* __rest
 hipError_t launch_gemm_mx4pp(const uint8_t* Xc, const uint8_t* Xs, const uint8_t* Wc, const uint8_t* Ws, uint16_t* Y,
                              int64_t ldy, int M, int N, int K, hipStream_t s) {
   const int tiles = ((M + MX_BM - 1) / MX_BM) * ((N + MX_BN - 1) / MX_BN);
-  const int y_vec = y_store_mode(Y, ldy);
+  const int y_vec = y_store_mode(Y, ldy, N);
   hipLaunchKernelGGL(k_gemm_mx4pp, dim3(tiles), dim3(64 * WAVES), 0, s, Xc, Xs, Wc, Ws, Y, ldy, M, N, K, y_vec);
   return hipGetLastError();
 }

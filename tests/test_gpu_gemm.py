@@ -235,3 +235,35 @@ def test_gemm_mxfp4_noclip_top_binade():
         Y2, _, Wq_d = fq.qf_linear_forward_mxfp4(dev(X), dev(b), flags=flags | fq.QF_MX_NOCLIP)
         assert np.array_equal(host(Wq_d), Wq)
         assert np.array_equal(host(Y2), host(Y))
+
+
+# ------------------------------------------- more tiles than workgroups ----
+@pytest.mark.parametrize("K", [64, 192])
+def test_gemm_many_tiles_per_workgroup(K):
+    """22 x 15 tiles with ragged last tile row and column, more tiles than the launch has
+    workgroups (at most one per CU), so workgroups run several tiles in turn and load the
+    next tile's first K slice during the last one (K = 64: a single K step per tile).
+    Each product is checked against the oracle, and Y must be the same bits whichever way
+    it is stored: 16-byte rows through LDS, 8-byte stores (ldy = N + 4) and element stores
+    (ldy = N + 1); the fused kernel must equal the two-pass forward."""
+    M, N = 21 * 256 + 37, 14 * 256 + 96
+    X, W = _ops(M, N, K)
+    Xd, Wd = dev(X), dev(W)
+    Xq, Wq = mxfp4.qdq(X), mxfp4.qdq(W)
+    for flags in (0, 3):
+        ys = []
+        for pad in (0, 4, 1):
+            Yb = torch.full((M, N + pad), 7.0, dtype=torch.bfloat16, device="cuda")
+            fq.qf_gemm_mxfp4(Xd, Wd, Yb[:, :N], flags=flags)
+            if pad:
+                assert torch.all(Yb[:, N:] == 7.0)
+            ys.append(host(Yb[:, :N]))
+        _check(ys[0], Xq if flags else X, Wq if flags else W, K, f"many tiles K={K} flags={flags}")
+        assert np.array_equal(ys[0], ys[1]) and np.array_equal(ys[0], ys[2]), f"store modes, flags={flags}"
+        if flags:
+            Y2, _, _ = fq.qf_linear_forward_mxfp4(Xd, Wd)
+            assert np.array_equal(host(Y2), ys[0])
+    sx, sx_ref = _nv_scale(X)
+    sw, sw_ref = _nv_scale(W)
+    Y = fq.qf_gemm_nvfp4(Xd, Wd, sx, sw)
+    _check(host(Y), nvfp4.qdq(X, sx_ref), nvfp4.qdq(W, sw_ref), K, f"nvfp4 many tiles K={K}")
