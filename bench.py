@@ -794,8 +794,7 @@ class MoELoRANVFP4:
         self.ws = torch.empty(self.chunks[0][0].workspace_bytes, dtype=torch.uint8, device=dev)
         self.ws_grads = torch.empty(self.chunks[0][0].workspace_bytes, dtype=torch.uint8, device=dev)
         self.experts_per_launch = k
-        self.grad_stream = torch.cuda.Stream()
-        self.qdq_stream = torch.cuda.Stream()
+        self.qdq_stream, self.grad_stream = side_streams(torch)
         self.scale_ready = [torch.cuda.Event() for _ in self.chunks]
         n = sum(x[m]["W"].numel() for m in mats)
         self.numel = n
@@ -938,6 +937,19 @@ class MoELoRANVFP4x8Scratch(MoELoRANVFP4):
 
     def controls(self, reps=20):
         return {}
+
+
+_SIDE = []
+
+
+def side_streams(torch):
+    """The two default-priority side streams of the MoE steps, created once per process.
+    The runtime maps streams onto a few hardware queues in creation order; streams made per
+    workload would, after a few workloads, share a queue with the default stream and run
+    their passes after its kernels instead of beside them.  main() creates these first."""
+    if not _SIDE:
+        _SIDE.extend((torch.cuda.Stream(), torch.cuda.Stream()))
+    return _SIDE[0], _SIDE[1]
 
 
 def graph_replay(torch, step, reps, nbytes):
@@ -1088,6 +1100,7 @@ def main():
     import torch
     import fp4_fake_quant_amd as fq
     torch.cuda.set_device(0)
+    side_streams(torch)                          # before any other stream: hardware queues of their own
     wl = WORKLOADS[args.workload](torch, fq)
 
     print(f"bench: {wl.name}", file=sys.stderr, flush=True)
