@@ -944,11 +944,17 @@ _SIDE = []
 
 def side_streams(torch):
     """The two default-priority side streams of the MoE steps, created once per process.
-    The runtime maps streams onto a few hardware queues in creation order; streams made per
-    workload would, after a few workloads, share a queue with the default stream and run
-    their passes after its kernels instead of beside them.  main() creates these first."""
+    The runtime binds streams to a few hardware queues as they are first used; streams made
+    per workload, or first used after other side streams (graph captures make their own),
+    could share a queue with the default stream or with each other and run their passes
+    one after another instead of side by side.  main() creates and uses these first."""
     if not _SIDE:
         _SIDE.extend((torch.cuda.Stream(), torch.cuda.Stream()))
+        # a first command on each: the runtime binds a stream to its hardware queue on first use
+        for st in _SIDE:
+            with torch.cuda.stream(st):
+                torch.zeros(1, device="cuda")
+        torch.cuda.synchronize()
     return _SIDE[0], _SIDE[1]
 
 
