@@ -25,7 +25,7 @@
 //   k_lora_grads       dB = G . A^T and dA = B^T . G in one pass over G, both on the
 //                      16x16x32 BF16 MFMA (G staged through LDS); per-slab dB partials and
 //                      per-row-block dA partials, added in a fixed order by
-//                      k_lora_dB_reduce and k_lora_dA_reduce (same inputs, same bits).
+//                      k_lora_grad_reduce (same inputs, same bits).
 #include <algorithm>
 
 #include "qf_device.h"
@@ -673,15 +673,33 @@ __device__ __forceinline__ int find_desc_mat(const LoraArgs& a, int m) {
   return lora_desc_of<&LoraTensor::mat_begin>(a, m);
 }
 
-__global__ __launch_bounds__(256) void k_lora_dA_reduce(LoraArgs a, int accumulate) {
+// Adapter gradients from the partials of k_lora_grads, one thread per gradient entry:
+// dB[i][k] (+)= the slab partials and dA[k][j] (+)= the row-block partials, each added in
+// index order.  One launch for both: blocks [0, gB) of x walk dB, the others dA (each part
+// grid-strides over its own blocks); y is the matrix.
+__global__ __launch_bounds__(256) void k_lora_grad_reduce(LoraArgs a, int accumulate, int gB) {
   const LoraTensor& T = a.d[find_desc_mat(a, blockIdx.y)];
   const LoraMat X = lora_mat(T, (int)blockIdx.y - T.mat_begin, a.da_rows);
+  if ((int)blockIdx.x < gB) {
+    const int64_t n = T.rows * LORA_MAX_R;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gB * blockDim.x) {
+      // partial q holds LORA_MAX_R adapters of every row; entry (i, k) of dB is at idx
+      const int64_t row = idx / LORA_MAX_R;
+      const int k = (int)(idx - row * LORA_MAX_R);
+      if (k >= T.r) continue;
+      const float sum = sum_partials(X.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
+      float* dst = X.dB + row * T.r + k;
+      *dst = accumulate ? *dst + sum : sum;
+    }
+    return;
+  }
+  const int gA = (int)gridDim.x - gB;
   const int64_t n = (int64_t)T.r * T.cols;
   const int nblk = (int)((T.rows + a.da_rows - 1) / a.da_rows);
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t idx = (int64_t)(blockIdx.x - gB) * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gA * blockDim.x) {
     // partial q holds rows k = 0 .. 15 of cols columns; entry (k, j) of dA is at idx
-    const float s = sum_partials(X.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
-    X.dA[idx] = accumulate ? X.dA[idx] + s : s;
+    const float sum = sum_partials(X.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
+    X.dA[idx] = accumulate ? X.dA[idx] + sum : sum;
   }
 }
 
@@ -865,11 +883,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 //   dB (rows x 16): G rows as the MFMA's A operand in their natural layout, A's rows as
 //     its B operand (kept in registers for the unit); wave w sums columns 128w ..
 //     128w+127 of the chunk's 32 rows and the 4 waves' sums are added in LDS in a fixed
-//     order, giving one partial per slab (k_lora_dB_reduce adds the slabs in order);
+//     order, giving one partial per slab (k_lora_grad_reduce adds the slabs in order);
 //   dA (16 x cols): B's rows transposed as the A operand (K = the chunk's 32 rows), G as
 //     the B operand read transposed from LDS (each lane gathers 8 rows of one column);
 //     wave w owns columns 128w .. 128w+127 of the slab and sums over all rows of the
-//     unit, giving one partial per unit (k_lora_dA_reduce adds the units in order).
+//     unit, giving one partial per unit (k_lora_grad_reduce adds the units in order).
 // One pass instead of one per gradient: 149 us for 8 experts with a pass per gradient,
 // 73 us now (with both reduces, from cold caches).
 // Staged rows are 1040 bytes apart (16 B of padding) and rows 16..31 swap their 16-byte
@@ -1048,20 +1066,6 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
 }
 
 // dB[row][k] (+)= sum over slabs, in slab order.
-__global__ __launch_bounds__(256) void k_lora_dB_reduce(LoraArgs a, int accumulate) {
-  const LoraTensor& T = a.d[find_desc_mat(a, blockIdx.y)];
-  const LoraMat X = lora_mat(T, (int)blockIdx.y - T.mat_begin, a.da_rows);
-  const int64_t n = T.rows * LORA_MAX_R;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t row = idx / LORA_MAX_R;
-    const int k = (int)(idx - row * LORA_MAX_R);
-    if (k >= T.r) continue;
-    const float s = sum_partials(X.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
-    float* dst = X.dB + row * T.r + k;
-    *dst = accumulate ? *dst + s : s;
-  }
-}
-
 // ------------------------------------------------------------ launchers ----
 static bool all_rank16(const LoraArgs& a) {
   for (int i = 0; i < a.n; ++i)
@@ -1117,10 +1121,7 @@ hipError_t launch_lora_grads(const LoraArgs& a, int grid, int accumulate, hipStr
     nA = std::max<int64_t>(nA, (int64_t)a.d[i].r * a.d[i].cols);
   }
   const int gB = (int)std::min<int64_t>((nB + 255) / 256, 8192), gA = (int)std::min<int64_t>((nA + 255) / 256, 8192);
-  if (gB > 0) hipLaunchKernelGGL(k_lora_dB_reduce, dim3(gB, a.n_mats), dim3(256), 0, s, a, accumulate);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (gA > 0) hipLaunchKernelGGL(k_lora_dA_reduce, dim3(gA, a.n_mats), dim3(256), 0, s, a, accumulate);
+  hipLaunchKernelGGL(k_lora_grad_reduce, dim3(gB + gA, a.n_mats), dim3(256), 0, s, a, accumulate, gB);
   return hipGetLastError();
 }
 
