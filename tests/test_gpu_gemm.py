@@ -267,3 +267,18 @@ def test_gemm_many_tiles_per_workgroup(K):
     sw, sw_ref = _nv_scale(W)
     Y = fq.qf_gemm_nvfp4(Xd, Wd, sx, sw)
     _check(host(Y), nvfp4.qdq(X, sx_ref), nvfp4.qdq(W, sw_ref), K, f"nvfp4 many tiles K={K}")
+
+
+@pytest.mark.parametrize("ldy", [(1 << 22) - 8, (1 << 22) + 8])
+def test_gemm_output_stride_at_the_store_limit(ldy):
+    """Y rows 2^22 - 8 elements apart (the widest stride that still leaves through LDS in
+    16-byte buffer stores: a tile's rows then span just under 2^31 bytes) and 2^22 + 8
+    (8-byte stores from the accumulators instead), two tile rows with a ragged second;
+    the columns past N stay untouched."""
+    M, N, K = 260, 136, 128
+    X, W = _ops(M, N, K)
+    Yb = torch.full((M, ldy), 7.0, dtype=torch.bfloat16, device="cuda")
+    fq.qf_gemm_mxfp4(dev(X), dev(W), Yb[:, :N], flags=3)
+    _check(host(Yb[:, :N]), mxfp4.qdq(X), mxfp4.qdq(W), K, f"ldy={ldy}")
+    assert torch.all(Yb[:, N:N + 256] == 7.0) and torch.all(Yb[:, -8:] == 7.0)
+    del Yb
