@@ -998,12 +998,32 @@ FLUSH_BYTES = 512 << 20      # an untimed write of this size before each flushed
 FLUSH_ITERS = 20
 
 
+_SPIN_CYCLES_PER_MS = None
+
+
+def gpu_backlog(torch, ms):
+    """Keep the current stream busy for about `ms` milliseconds (torch's one-wave spin
+    kernel, calibrated once against HIP events), so that work enqueued behind it finds
+    the GPU already loaded."""
+    global _SPIN_CYCLES_PER_MS
+    if _SPIN_CYCLES_PER_MS is None:
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(1_000_000)
+        e1.record()
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_MS = 1_000_000 / max(e0.elapsed_time(e1), 1e-3)
+    torch.cuda._sleep(int(min(ms, 2000.0) * _SPIN_CYCLES_PER_MS))
+
+
 def measure(torch, wl, steps, warmup, flush_iters=FLUSH_ITERS):
     """(ms per step over `steps` back-to-back steps, per-kernel dict, flushed dict).
 
     Per-kernel durations come from a second pass of `steps` steps with a HIP event pair
     around every launch (events add a few microseconds between kernels, so they stay out
-    of the headline loop); the events sit on torch's current stream, where the library
+    of the headline loop), queued behind a spin kernel so that the GPU never waits for the
+    host inside a pair; the events sit on torch's current stream, where the library
     launches.  The flushed figures time `flush_iters` further steps one at a time, each
     after an untimed 512 MiB device write that evicts the 256 MB memory-side cache, and
     report the median and the minimum (per step, and per kernel from a second such pass
@@ -1023,6 +1043,19 @@ def measure(torch, wl, steps, warmup, flush_iters=FLUSH_ITERS):
             pairs[kernel].append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
         pairs[kernel][-1][edge].record()
 
+    # Enqueueing a step with an event pair around every launch can take the host longer
+    # than the GPU needs for the step; the GPU then idles inside an event pair while the
+    # host prepares the next launch, and that gap would be booked to the kernel.  So the
+    # marked steps are queued behind a spin kernel that lasts longer than their enqueue:
+    # a first marked pass measures the host's enqueue time, the second is the timed one.
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        wl.step(mark)
+    host_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    for k in pairs:
+        pairs[k] = []
+    gpu_backlog(torch, 1.5 * host_ms + 2.0)
     for _ in range(steps):
         wl.step(mark)
     torch.cuda.synchronize()
@@ -1045,9 +1078,10 @@ def measure(torch, wl, steps, warmup, flush_iters=FLUSH_ITERS):
         step_ms.append(e0.elapsed_time(e1))
     per_kernel = {k: [] for k in wl.kernels}
     for i in range(flush_iters):
-        flush.fill_((i + 7) & 0xFF)
         for k in pairs:
             pairs[k] = []
+        gpu_backlog(torch, 3.0 * host_ms / steps + 2.0)
+        flush.fill_((i + 7) & 0xFF)
         wl.step(mark)
         torch.cuda.synchronize()
         for k in wl.kernels:
