@@ -34,6 +34,8 @@
 namespace qf {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 // Keeps the scheduler from moving instructions across this point: rows (or column
@@ -998,14 +1000,20 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) red[wave][g][(4u * lq + e) * 16u + l16] = accB[e];
     }
-    // dA over this wave's 8 column tiles (16 columns each) and the chunk's 32 rows
+    // dA over this wave's 8 column tiles (16 columns each) and the chunk's 32 rows.  The
+    // operand lane l needs is column l%16 of the tile at rows 8 (l/16) .. +7; two LDS
+    // transpose reads give it: lane L of a 16-lane group points at 4 columns 4 (L%4) ..
+    // +3 of row 8 (l/16) + L/4 (+ 4 for the second read), and lane i of the group then
+    // receives element i%4 from lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4, i.e. column i of
+    // those 4 rows.
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const uint32_t col = 128u * wave + 16u * j + l16;   // column within the slab
-      bf16x8_t gt;
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-        gt[t] = *reinterpret_cast<const __bf16*>(buf + gr_off(8u * lq + t, col >> 3) + 2u * (col & 7u));
+      const uint32_t c8 = 16u * wave + 2u * j + ((l16 & 3u) >> 1);   // 16-byte chunk of the 4 columns
+      const uint32_t half = 8u * (l16 & 1u);
+      const uint32_t row = 8u * lq + (l16 >> 2);
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(buf + gr_off(row, c8) + half));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(buf + gr_off(row + 4u, c8) + half));
+      const bf16x8_t gt = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       accA[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bt, gt, accA[j], 0, 0, 0);
     }
     __syncthreads();                                       // red is complete
