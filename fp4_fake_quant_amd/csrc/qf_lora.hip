@@ -618,34 +618,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   float av[LORA_MAX_R][8];                                           // rows k >= r read as 0
 #pragma unroll
   for (int k = 0; k < LORA_MAX_R; ++k) unpack8(buf_load16(ra, lo + k * mstride), av[k]);
+  const bool odd = lane & 1;
 #pragma unroll 1
   for (int i = 0; i < rows; i += LORA_PREFETCH) {
 #pragma unroll
-    for (int q = 0; q < LORA_PREFETCH; ++q) {
-      LORA_FENCE();
-      const int ii = i + q;                                          // may pass the last row
-      float bk[LORA_MAX_R];
-      b_row_values<RK>(bw, br0 + min(ii, rows - 1), r, bk);
-      fetch_b_words<RK>(T.B, br0 + min(ii + 1, rows - 1), r, bw);
-      float acc[8];
+    for (int q = 0; q < LORA_PREFETCH; q += 2) {
+      uint4 o[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+      for (int h = 0; h < 2; ++h) {
+        LORA_FENCE();
+        const int ii = i + q + h;                                    // may pass the last row
+        float bk[LORA_MAX_R];
+        b_row_values<RK>(bw, br0 + min(ii, rows - 1), r, bk);
+        fetch_b_words<RK>(T.B, br0 + min(ii + 1, rows - 1), r, bw);
+        float acc[8];
 #pragma unroll
-      for (int k = 0; k < LORA_MAX_R; ++k)
+        for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(bk[k], av[k][e], acc[e]);
-      float w[8];
-      unpack8(wv[q], w);
-      uint4 o;
-      o.x = pack_bf16x2(w[0] + acc[0], w[1] + acc[1]);
-      o.y = pack_bf16x2(w[2] + acc[2], w[3] + acc[3]);
-      o.z = pack_bf16x2(w[4] + acc[4], w[5] + acc[5]);
-      o.w = pack_bf16x2(w[6] + acc[6], w[7] + acc[7]);
-      const Nvfp4Chunk qc = nvfp4_qdq_chunk(o, s_t, k6);               // rows past the end: dropped
-      buf_store16(ry, lo + ii * mstride, qc.y);
-      buf_store4(rc, clo + ii * cstride, qc.codes);
-      buf_store1(rs, slo + ii * sstride, (uint8_t)qc.S);
-      wv[q] = buf_load16_nt(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
+        for (int k = 0; k < LORA_MAX_R; ++k)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(bk[k], av[k][e], acc[e]);
+        float w[8];
+        unpack8(wv[q + h], w);
+        o[h].x = pack_bf16x2(w[0] + acc[0], w[1] + acc[1]);
+        o[h].y = pack_bf16x2(w[2] + acc[2], w[3] + acc[3]);
+        o[h].z = pack_bf16x2(w[4] + acc[4], w[5] + acc[5]);
+        o[h].w = pack_bf16x2(w[6] + acc[6], w[7] + acc[7]);
+      }
+      // Block scales of the two rows: lanes 2j and 2j + 1 hold the two halves of one
+      // 16-block in each row, so the even lane works out row q's scale, the odd lane row
+      // q + 1's, and each takes the other row's from its neighbour (one scale computation
+      // per lane for two rows instead of one per row, the same arithmetic).
+      uint32_t m0 = amax_bits8(o[0]);
+      m0 = umax(m0, dpp_xor1(m0));
+      uint32_t m1 = amax_bits8(o[1]);
+      m1 = umax(m1, dpp_xor1(m1));
+      const Nvfp4Scale mine = nvfp4_block_scale(odd ? m1 : m0, s_t, k6);
+      const uint32_t oS = dpp_xor1(mine.S);
+      const float os = __uint_as_float(dpp_xor1(__float_as_uint(mine.s)));
+      const float orr = __uint_as_float(dpp_xor1(__float_as_uint(mine.r)));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int ii = i + q + h;
+        const bool own = odd == (h == 1);                            // this lane computed row h's scale
+        const uint32_t S = own ? mine.S : oS;
+        const Nvfp4Enc e = nvfp4_encode_chunk(o[h], own ? mine.s : os, s_t, own ? mine.r : orr);
+        buf_store16(ry, lo + ii * mstride, e.y);                     // rows past the end: dropped
+        buf_store4(rc, clo + ii * cstride, e.codes);
+        buf_store1(rs, slo + ii * sstride, (uint8_t)S);
+        wv[q + h] = buf_load16_nt(rw, lo + (ii + LORA_PREFETCH) * wstride);   // past the end: zeros
+      }
     }
   }
 }
