@@ -672,25 +672,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
   }
 }
 
-// dA[k][j] (+)= sum over row blocks, in block order.
-// Sum of count partials p[0], p[stride], ... added in index order from +0.  The loads
-// are issued LORA_RED_BATCH at a time before any add, so one element costs a few memory
-// latencies instead of one per partial; the order of the adds is unchanged.
+// dA[k][j] (+)= sum over row blocks, in block order; dB[i][k] (+)= sum over slabs, in slab
+// order.  The partial loads are issued LORA_RED_BATCH at a time before any add, so an
+// entry costs a few memory latencies instead of one per partial; the order of the adds
+// is unchanged.
 constexpr int LORA_RED_BATCH = 8;
-
-__device__ __forceinline__ float sum_partials(const float* p, int64_t stride, int count) {
-  float s = 0.0f;
-#pragma unroll 1
-  for (int q0 = 0; q0 < count; q0 += LORA_RED_BATCH) {
-    float v[LORA_RED_BATCH];
-#pragma unroll
-    for (int i = 0; i < LORA_RED_BATCH; ++i) v[i] = q0 + i < count ? p[(int64_t)(q0 + i) * stride] : 0.0f;
-#pragma unroll
-    for (int i = 0; i < LORA_RED_BATCH; ++i)
-      if (q0 + i < count) s += v[i];
-  }
-  return s;
-}
 
 // Matrix m of the launch (blockIdx.y of the reduces): its descriptor.
 __device__ __forceinline__ int find_desc_mat(const LoraArgs& a, int m) {
@@ -701,8 +687,9 @@ __device__ __forceinline__ int find_desc_mat(const LoraArgs& a, int m) {
 // dB[i][k] (+)= the slab partials and dA[k][j] (+)= the row-block partials, each added in
 // index order.  One launch for both: blocks [0, gB) of x walk dB, the others dA (each part
 // grid-strides over its own blocks); y is the matrix.
-// Four adjacent entries at a time (16-byte partial loads, the same additions in the same
-// order per entry), for partial buffers 16-byte aligned.
+// Sums of four adjacent entries: count partials p[0], p[stride], ... of each, loaded 16
+// bytes at a time (the partial buffers are 16-byte aligned: the workspace is, and every
+// offset into it is a multiple of 16 floats) and added per entry in index order from +0.
 __device__ __forceinline__ float4 sum_partials4(const float* p, int64_t stride, int count) {
   float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll 1
@@ -724,48 +711,37 @@ __device__ __forceinline__ float4 sum_partials4(const float* p, int64_t stride, 
   return s;
 }
 
-template <int VW>
 __global__ __launch_bounds__(256) void k_lora_grad_reduce(LoraArgs a, int accumulate, int gB) {
   const LoraTensor& T = a.d[find_desc_mat(a, blockIdx.y)];
   const LoraMat X = lora_mat(T, (int)blockIdx.y - T.mat_begin, a.da_rows);
   if ((int)blockIdx.x < gB) {
     const int64_t n = T.rows * LORA_MAX_R;
-    for (int64_t idx = VW * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x); idx < n;
-         idx += (int64_t)VW * gB * blockDim.x) {
+    for (int64_t idx = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x); idx < n;
+         idx += (int64_t)4 * gB * blockDim.x) {
       // partial q holds LORA_MAX_R adapters of every row; entry (i, k) of dB is at idx
       const int64_t row = idx / LORA_MAX_R;
-      const int k = (int)(idx - row * LORA_MAX_R);                   // VW = 4: a multiple of 4
+      const int k = (int)(idx - row * LORA_MAX_R);                   // a multiple of 4
       if (k >= T.r) continue;
       float* dst = X.dB + row * T.r + k;
-      if constexpr (VW == 4) {
-        const float4 s4 = sum_partials4(X.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
-        const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+      const float4 s4 = sum_partials4(X.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
+      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};                 // entries k + e >= r: unused
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (k + e < T.r) dst[e] = accumulate ? dst[e] + sv[e] : sv[e];
-      } else {
-        const float sum = sum_partials(X.dB_partial + idx, T.rows * LORA_MAX_R, T.slabs);
-        *dst = accumulate ? *dst + sum : sum;
-      }
+      for (int e = 0; e < 4; ++e)
+        if (k + e < T.r) dst[e] = accumulate ? dst[e] + sv[e] : sv[e];
     }
     return;
   }
   const int gA = (int)gridDim.x - gB;
   const int64_t n = (int64_t)T.r * T.cols;
   const int nblk = (int)((T.rows + a.da_rows - 1) / a.da_rows);
-  for (int64_t idx = VW * ((int64_t)(blockIdx.x - gB) * blockDim.x + threadIdx.x); idx < n;
-       idx += (int64_t)VW * gA * blockDim.x) {
+  for (int64_t idx = 4 * ((int64_t)(blockIdx.x - gB) * blockDim.x + threadIdx.x); idx < n;
+       idx += (int64_t)4 * gA * blockDim.x) {
     // partial q holds rows k = 0 .. 15 of cols columns; entry (k, j) of dA is at idx
     // (cols is a multiple of 32, so four adjacent entries share k)
-    if constexpr (VW == 4) {
-      const float4 s4 = sum_partials4(X.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
-      const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
+    const float4 s4 = sum_partials4(X.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
+    const float sv[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) X.dA[idx + e] = accumulate ? X.dA[idx + e] + sv[e] : sv[e];
-    } else {
-      const float sum = sum_partials(X.dA_partial + idx, (int64_t)LORA_MAX_R * T.cols, nblk);
-      X.dA[idx] = accumulate ? X.dA[idx] + sum : sum;
-    }
+    for (int e = 0; e < 4; ++e) X.dA[idx + e] = accumulate ? X.dA[idx + e] + sv[e] : sv[e];
   }
 }
 
@@ -1137,7 +1113,6 @@ __global__ __launch_bounds__(256) void k_lora_grads(LoraArgs a) {
   }
 }
 
-// dB[row][k] (+)= sum over slabs, in slab order.
 // ------------------------------------------------------------ launchers ----
 static bool all_rank16(const LoraArgs& a) {
   for (int i = 0; i < a.n; ++i)
@@ -1186,22 +1161,16 @@ hipError_t launch_lora_grads(const LoraArgs& a, int grid, int accumulate, hipStr
   hipLaunchKernelGGL(k_lora_grads, dim3(grid), dim3(256), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // one thread per gradient entry, or per four adjacent entries when every partial buffer is
-  // 16-byte aligned (their offsets are multiples of 16 floats; grid-stride past 8192
-  // workgroups)
+  // one thread per four adjacent gradient entries (grid-stride past 8192 workgroups); the
+  // partial buffers' 16-byte alignment comes from the entry point's check on the workspace
   int64_t nB = 0, nA = 0;
-  bool vec = true;
   for (int i = 0; i < a.n; ++i) {
     nB = std::max<int64_t>(nB, a.d[i].rows * LORA_MAX_R);
     nA = std::max<int64_t>(nA, (int64_t)a.d[i].r * a.d[i].cols);
-    vec = vec && ((uintptr_t)a.d[i].dA_partial % 16 == 0) && ((uintptr_t)a.d[i].dB_partial % 16 == 0);
+    if ((uintptr_t)a.d[i].dA_partial % 16 != 0 || (uintptr_t)a.d[i].dB_partial % 16 != 0) return hipErrorInvalidValue;
   }
-  const int vw = vec ? 4 : 1;
-  const int gB = (int)std::min<int64_t>((nB / vw + 255) / 256, 8192), gA = (int)std::min<int64_t>((nA / vw + 255) / 256, 8192);
-  if (vec)
-    hipLaunchKernelGGL(k_lora_grad_reduce<4>, dim3(gB + gA, a.n_mats), dim3(256), 0, s, a, accumulate, gB);
-  else
-    hipLaunchKernelGGL(k_lora_grad_reduce<1>, dim3(gB + gA, a.n_mats), dim3(256), 0, s, a, accumulate, gB);
+  const int gB = (int)std::min<int64_t>((nB / 4 + 255) / 256, 8192), gA = (int)std::min<int64_t>((nA / 4 + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_lora_grad_reduce, dim3(gB + gA, a.n_mats), dim3(256), 0, s, a, accumulate, gB);
   return hipGetLastError();
 }
 
